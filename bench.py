@@ -1,0 +1,236 @@
+"""Benchmark of one verification round on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole resident hot path over one batch of
+synthetic input already in HBM: ss_verify_chunk over every history chunk,
+ss_verify_candidates (mask build + masked attention) and ss_merge_states.
+The default workload is the Qwen3-8B-like layer: 16 requests, 32 query heads
+over 8 KV heads, head_dim 128, 32768 committed bf16 tokens in chunks of 4096,
+6 queries (5 drafts + 1) under a causal candidate mask.
+
+Prints ONE JSON line. value = effective KV GB/s = (history + candidate K/V
+bytes) / time per step. Also reported: verified query-tokens/s, the chunk
+kernel's roofline (algorithmic bytes per launch / its event-timed launch
+duration), the streamed path on the streamed workload (host-link GB/s against
+a plain pinned H2D copy of the same bytes), and the fp64 CPU oracle timed on
+a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from long_context_speculative_amd import rounds  # noqa: E402
+from long_context_speculative_amd import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+CHUNK_KERNEL_SOURCES = ["long_context_speculative_amd/csrc/ss_mfma.hip", "long_context_speculative_amd/csrc/ss_valu.hip",
+                        "long_context_speculative_amd/csrc/ss_common.h"]
+
+
+def kv_bytes(cfg, hist_len) -> tuple[int, int]:
+    row = 2 * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes
+    return int(np.asarray(hist_len, dtype=np.int64).sum()) * row, cfg.batch * cfg.n_queries * row
+
+
+def chunk_kernel_bytes(cfg, hist_len, n_slots) -> int:
+    """Algorithmic bytes of one chunk-kernel launch: the history K and V once,
+    Q once, and the state slots written (acc + m + l, fp32)."""
+    hist, _ = kv_bytes(cfg, hist_len)
+    q = cfg.batch * cfg.n_queries * cfg.n_q_heads * cfg.head_dim * cfg.elem_bytes
+    states = n_slots * cfg.batch * cfg.n_queries * cfg.n_q_heads * (cfg.head_dim + 2) * 4
+    return hist + q + states
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in CHUNK_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per chunk-kernel launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"chunk_kernel_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def time_resident(cfg, steps, warmup):
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp)
+    del inp
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        rnd.run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for k in range(steps):
+        ev[k][0].record(stream)
+        rnd.chunks()
+        ev[k][1].record(stream)
+        rnd.candidates()
+        rnd.merge()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_begin.elapsed_time(t_end) / steps
+    ms_chunk = sum(a.elapsed_time(b) for a, b in ev) / steps
+    hist_len = np.full(cfg.batch, cfg.hist_len) if not cfg.ragged else rnd.hist_len.cpu().numpy()
+    return rnd, hist_len, ms_step, ms_chunk
+
+
+def time_streamed(cfg, reps=3):
+    inp = wl.make_inputs(cfg)
+    srd = rounds.StreamedRound(inp, n_buf=2)
+    del inp
+    srd.run()
+    torch.cuda.synchronize()
+    walls = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        srd.run(record_timings=True)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t0)
+    from long_context_speculative_amd import ssverify as ss
+    c0, c1, k0, k1 = ss.ss_stream_timings(srd.n_chunks)
+    bubble = sum(max(0.0, c1[j] - k1[j - 1]) for j in range(1, srd.n_chunks))
+    # plain pinned H2D copy of the same bytes, same chunking, one stream
+    dst = srd.staging
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    s = srd.copy_stream
+    with torch.cuda.stream(s):
+        for j in range(srd.n_chunks):
+            dst[j % srd.n_buf].copy_(srd.host_kv[j], non_blocking=True)
+    torch.cuda.synchronize()
+    copy_wall = time.perf_counter() - t0
+    hist_bytes = srd.host_kv.numel() * srd.host_kv.element_size()
+    wall = min(walls)
+    return {
+        "workload": cfg.name,
+        "host_link_GBps": hist_bytes / wall / 1e9,
+        "plain_h2d_GBps": hist_bytes / copy_wall / 1e9,
+        "frac_of_plain_h2d": copy_wall / wall,
+        "ms_per_round": wall * 1e3,
+        "exposed_wait_ms": bubble,
+        "chunk_compute_ms_mean": float(np.mean([k1[j] - k0[j] for j in range(srd.n_chunks)])),
+        "chunk_copy_ms_mean": float(np.mean([c1[j] - c0[j] for j in range(srd.n_chunks)])),
+        "query_tokens_per_s": cfg.batch * cfg.n_queries / wall,
+    }
+
+
+def cpu_baseline(cfg, budget_s=15.0):
+    """The fp64 oracle, as it stands, on (request, KV head) slices of the same
+    workload until about budget_s seconds of CPU time are spent."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    inp = wl.make_inputs(cfg.with_(batch=min(cfg.batch, 2)))
+    vis = np.stack([oracle.chain_mask(cfg.n_queries)] * inp.cfg.batch) if cfg.mask != "tree" else \
+        np.stack([oracle.tree_mask(inp.parents[b]) for b in range(inp.cfg.batch)])
+    q = inp.q.float().numpy()
+    kc, vc = inp.k_cand.float().numpy(), inp.v_cand.float().numpy()
+    kh, vh = inp.hist_per_request("k"), inp.hist_per_request("v")
+    done, slices = 0.0, 0
+    t0 = time.perf_counter()
+    while done < budget_s:
+        b, g = divmod(slices % (inp.cfg.batch * cfg.n_kv_heads), cfg.n_kv_heads)
+        oracle.attention_reference(q, kh, vh, inp.hist_len, kc, vc, vis, cfg.scale, requests=[b], kv_heads=[g])
+        slices += 1
+        done = time.perf_counter() - t0
+    row = 2 * cfg.head_dim * cfg.elem_bytes
+    kv = slices * (int(inp.hist_len.max()) + cfg.n_queries) * row
+    cores = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    return {"value": kv / done / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{slices} (request, KV head) slices of {cfg.name}, fp64 NumPy, {done:.1f} s",
+            "query_tokens_per_s": slices / (cfg.batch * cfg.n_kv_heads) * cfg.batch * cfg.n_queries / done}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c2_qwen3_8b", choices=[k for k in wl.CONFIGS if not wl.CONFIGS[k].streamed])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-streamed", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the verification path runs on a "
+              f"single MI355X; sharding across GPUs is described, not built).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    cfg = wl.CONFIGS[args.workload]
+    rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup)
+    hist_b, cand_b = kv_bytes(cfg, hist_len)
+    gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9
+    alg = chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)
+    achieved = alg / (ms_chunk * 1e-3) / 1e9
+    traffic = read_traffic(cfg.name)
+    del rnd
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": "verification-attn effective KV GB/s (% of HBM peak) + verified query-tokens/s",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1), bf16)",
+        "config": {"workload": f"{cfg.name}: B={cfg.batch}, Hq={cfg.n_q_heads}, Hkv={cfg.n_kv_heads}, "
+                               f"d={cfg.head_dim}, history={cfg.hist_len} ({'ragged' if cfg.ragged else 'uniform'}),"
+                               f" chunk={cfg.chunk_len}, q={cfg.n_queries}, mask={cfg.mask}",
+                   "batch": cfg.batch, "history_tokens": cfg.hist_len, "queries": cfg.n_queries},
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "query_tokens_per_s": round(cfg.batch * cfg.n_queries / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else int(traffic),
+                     "kernel": "ss_verify_chunk", "ms_per_launch": round(ms_chunk, 4),
+                     "algorithmic_bytes_per_launch": alg},
+    }
+    if not args.no_streamed:
+        out["streamed"] = time_streamed(wl.CONFIGS["c5_streamed"])
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

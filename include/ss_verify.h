@@ -1,0 +1,252 @@
+/*
+ * ss_verify.h -- C ABI of libssverify, multi-query verification attention for
+ * long-context speculative decoding on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (SpecStream, "Resource-Efficient Speculative
+ * Decoding for Long-Context LLM Serving", section 4.2):
+ *   All q queries of a verification round share one committed KV history.
+ *   The history is consumed chunk by chunk; every chunk yields a partial
+ *   online-softmax state (m, l, acc) per query and head (Eq. 7). States are
+ *   merged onto a common maximum (Eq. 8) and the output is O = acc / l
+ *   (Eq. 9), which equals one softmax over every visible key (Eq. 6). The
+ *   GPU-resident candidate rows are attended under a causal or tree mask.
+ *
+ * Conventions (apply to every call):
+ *   - Status: every call returns SS_OK (0) or a negative SS_ERR_* code; the
+ *     message of the last failure on the calling thread is ss_last_error().
+ *     Nothing throws across this boundary.
+ *   - Validation is synchronous and complete before anything is enqueued: a
+ *     call that returns an error has enqueued no work.
+ *   - Ownership: the caller owns every buffer. The library never allocates
+ *     or frees a caller buffer, and allocates no device memory. Buffers must
+ *     stay valid until the caller has synchronised the streams it passed.
+ *   - Asynchrony: device work is enqueued on the stream(s) passed in (a
+ *     hipStream_t handle given as ss_stream_t; NULL = the default stream).
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *   - Element types: SS_F32 (float) or SS_BF16 (bfloat16 bit patterns).
+ *     Q, K and V share the problem's dtype. States, O and lse are float32.
+ *   - Heads: G = n_q_heads / n_kv_heads; query head h reads KV head h / G
+ *     (grouped-query attention, contiguous groups).
+ *   - Rows: for one request and KV head the "rows" are the R = n_queries * G
+ *     pairs (query i, head-in-group hh), row r = i * G + hh.
+ *   - Scores are scale * <q, k>; lse is the natural-log softmax denominator
+ *     over scaled scores, lse = m + ln(l).
+ *   - Supported head_dim: 64 and 128.
+ */
+#ifndef SS_VERIFY_H
+#define SS_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SS_API __attribute__((visibility("default")))
+#else
+#define SS_API
+#endif
+
+#define SS_ABI_VERSION 1
+
+/* status codes */
+#define SS_OK 0
+#define SS_ERR_INVALID_ARG (-1) /* null pointer, bad size, inconsistent shape   */
+#define SS_ERR_UNSUPPORTED (-2) /* valid request this build does not implement */
+#define SS_ERR_HIP (-3)         /* the HIP runtime reported an error           */
+
+/* element types */
+#define SS_F32 0
+#define SS_BF16 1
+
+/* A hipStream_t handle (NULL = default stream). */
+typedef void* ss_stream_t;
+
+/* Shape of one verification round. */
+typedef struct ss_problem {
+    int32_t batch;      /* B requests of the round (a Cohort, section 4.2)    */
+    int32_t n_q_heads;  /* Hq                                                 */
+    int32_t n_kv_heads; /* Hkv, divides Hq                                    */
+    int32_t head_dim;   /* d: 64 or 128                                       */
+    int32_t n_queries;  /* q queries per request (k drafts + 1, or tree nodes)*/
+    int32_t dtype;      /* SS_F32 or SS_BF16                                  */
+    float scale;        /* score scale, normally 1/sqrt(d)                    */
+} ss_problem_t;
+
+/*
+ * A view of device-resident keys and values. Element (b, h, t, x) -- request
+ * b, KV head h, token t, feature x -- sits at
+ *     base + off_b + h * stride_h + t * stride_t + x
+ * (in elements), where off_b = req_offset[b] if req_offset is not NULL and
+ * b * stride_b otherwise. The feature axis is contiguous. K and V share the
+ * strides. Request b holds len_b tokens: req_len[b] (device array) if not
+ * NULL, else max_len. A len_b above max_len is read as max_len.
+ * Alignment: k and v 16-byte aligned; strides and offsets multiples of
+ * 16 bytes' worth of elements.
+ * Covers head-major [B][Hkv][N][d], token-major ragged [sum N_b][Hkv][d]
+ * and staging-chunk layouts.
+ */
+typedef struct ss_kv_view {
+    const void* k;
+    const void* v;
+    int64_t stride_b;
+    int64_t stride_h;
+    int64_t stride_t;
+    const int64_t* req_offset; /* device [B] or NULL */
+    const int32_t* req_len;    /* device [B] or NULL */
+    int32_t max_len;           /* uniform length, or upper bound of req_len */
+} ss_kv_view_t;
+
+/*
+ * Online-softmax state slots (Eq. 7-8), float32, caller-allocated:
+ *     acc [n_slots][B][n_queries][Hq][d]
+ *     m   [n_slots][B][n_queries][Hq]   running maximum of scaled scores
+ *     l   [n_slots][B][n_queries][Hq]   sum of exp(score - m)
+ * A slot that saw no key is empty: m = -inf, l = 0, acc = 0 (the initial
+ * state of section 4.2).
+ */
+typedef struct ss_state {
+    float* acc;
+    float* m;
+    float* l;
+    int32_t n_slots;
+} ss_state_t;
+
+/* ABI version this library implements (SS_ABI_VERSION). */
+SS_API int32_t ss_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). The pointer
+ * stays valid until the next call on this thread. */
+SS_API const char* ss_last_error(void);
+
+/* Bytes of acc + m + l for n_slots state slots of this problem, or a
+ * negative status if the problem is invalid. Host only. */
+SS_API int64_t ss_state_bytes(const ss_problem_t* problem, int32_t n_slots);
+
+/*
+ * ss_verify_chunk -- partial states of history chunks (section 4.2: the
+ * chunk scores S_j = Q K_j^T / sqrt(d_h) for the whole query group, then the
+ * chunk-local state of Eq. 7; consecutive chunks merged by Eq. 8).
+ *
+ *   q          device [B][n_queries][Hq][d], problem dtype
+ *   hist       committed history (every key visible to every query)
+ *   chunk_len  C > 0; chunk j of request b covers tokens
+ *              [j*C, min((j+1)*C, len_b))
+ *   chunk_begin, n_chunks   the chunks [chunk_begin, chunk_begin+n_chunks)
+ *              are processed (n_chunks == 0: nothing is enqueued)
+ *   chunks_per_slot  cps >= 1: slot slot_begin + s receives the state over
+ *              chunks [chunk_begin + s*cps, chunk_begin + (s+1)*cps) clipped
+ *              to the range; a slot with no token of a request is written
+ *              empty for that request
+ *   out        slots [slot_begin, slot_begin + ceil(n_chunks/cps)) must lie
+ *              in [0, out->n_slots); they are overwritten
+ * Rows R = n_queries * G: bf16 with 16 <= R <= 32 runs on the MFMA kernel,
+ * other shapes on the VALU kernel.
+ * Errors: SS_ERR_INVALID_ARG for null pointers, non-positive sizes, slots
+ * out of range, bad alignment; SS_ERR_UNSUPPORTED for head_dim outside
+ * {64, 128}; SS_ERR_HIP if the launch fails.
+ */
+SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                               int32_t chunk_len, int32_t chunk_begin, int32_t n_chunks,
+                               int32_t chunks_per_slot, const ss_state_t* out, int32_t slot_begin,
+                               ss_stream_t stream);
+
+/*
+ * ss_verify_candidates -- the state of the GPU-resident candidate region
+ * (section 4.2: the GPU region attended under a mask by each query's
+ * position), written to one slot.
+ *
+ *   q        device [B][n_queries][Hq][d]
+ *   cand     candidate keys/values; row i of request b is candidate i.
+ *            n_cand = n_queries rows per request (cand->req_len is ignored,
+ *            cand->max_len must equal n_queries); n_queries <= 64
+ *   parents  device int32 [B][n_queries], or NULL for the causal mask
+ *            (query i sees candidates j <= i). With parents, query i sees
+ *            the ancestors of node i and itself: bits are built as
+ *            anc[i] = anc[parents[i]] | (1 << i). parents[i] must satisfy
+ *            0 <= parents[i] < i, or be -1 for a root; any other value is
+ *            read as -1.
+ *   mask_out optional device uint64 [B][n_queries]: receives the visibility
+ *            bits (bit j of word i set iff query i sees candidate j)
+ *   out, slot  the slot written, 0 <= slot < out->n_slots
+ * Errors: as ss_verify_chunk; n_queries > 64 is SS_ERR_UNSUPPORTED.
+ */
+SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, const void* q, const ss_kv_view_t* cand,
+                                    const int32_t* parents, uint64_t* mask_out, const ss_state_t* out,
+                                    int32_t slot, ss_stream_t stream);
+
+/*
+ * ss_merge_states -- fold slots with Eq. 8 and finalise (O = acc / l,
+ * lse = m + ln l; section 4.2 and Eq. 9).
+ *
+ *   in             slots [0, in->n_slots)
+ *   slots_per_req  device int32 [B] or NULL: request b folds its first
+ *                  min(slots_per_req[b], n_slots) slots (NULL = all)
+ *   o              device float [B][n_queries][Hq][d]
+ *   lse            device float [B][n_queries][Hq]
+ * A row whose slots are all empty gets O = 0 and lse = -inf.
+ */
+SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in, const int32_t* slots_per_req,
+                               float* o, float* lse, ss_stream_t stream);
+
+/*
+ * ss_stream_history -- streamed verification over a history held in pinned
+ * host memory (section 4.2, pipelined KV transfers: staging buffers, a
+ * transfer stream and a compute stream; each chunk is attended as soon as it
+ * has landed).
+ *
+ *   host_kv      pinned host, chunk-major [n_chunks][2][B][Hkv][C][d]
+ *                (K block then V block of each chunk, one contiguous copy
+ *                per chunk); every request holds n_chunks * C tokens
+ *   staging      device buffer of n_buf chunks (n_buf >= 1, each
+ *                2*B*Hkv*C*d elements)
+ *   out          chunk j's state goes to slot slot_begin + j
+ *   copy_stream, compute_stream  must differ; the copies run on the first,
+ *                the chunk kernels on the second
+ *   record_timings  nonzero: per-chunk copy and compute events are recorded
+ *                for ss_stream_timings
+ * For chunk j: the copy stream waits until the compute that last used
+ * staging buffer j % n_buf has finished, copies chunk j into it and marks it
+ * arrived; the compute stream waits for that mark, runs ss_verify_chunk on
+ * the buffer and marks the buffer free. Before the first copy the copy
+ * stream waits for all work already enqueued on the compute stream. The
+ * call returns without synchronising; candidates and merge may follow on
+ * the compute stream.
+ * Errors: as ss_verify_chunk; SS_ERR_INVALID_ARG if the streams are equal.
+ */
+SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, const void* host_kv,
+                                 int32_t chunk_len, int32_t n_chunks, void* staging, int32_t n_buf,
+                                 const ss_state_t* out, int32_t slot_begin, ss_stream_t copy_stream,
+                                 ss_stream_t compute_stream, int32_t record_timings);
+
+/*
+ * ss_stream_timings -- per-chunk event times of the last ss_stream_history
+ * call on this process that recorded timings, in milliseconds from the
+ * start of the first copy. Call after synchronising both streams.
+ * n_chunks must equal that call's n_chunks. Any output pointer may be NULL.
+ * The exposed wait (compute bubble) of chunk j is
+ * max(0, copy_end[j] - compute_end[j-1]).
+ */
+SS_API int32_t ss_stream_timings(int32_t n_chunks, float* copy_begin, float* copy_end, float* compute_begin,
+                                 float* compute_end);
+
+/*
+ * Host-side helpers that expose the integer rules the kernels apply. They run
+ * on the CPU, touch no device, and are the same code the kernels compile.
+ *
+ * ss_tree_mask_host: visibility bits of a candidate tree (n <= 64):
+ *   out[i] = (1 << i) | out[parents[i]] when 0 <= parents[i] < i, else
+ *   (1 << i). parents and out are host arrays of n entries.
+ * ss_slot_tokens_host: the token range [*t0, *t1) that slot s of a chunk call
+ *   covers for a request of len tokens.
+ */
+SS_API int32_t ss_tree_mask_host(const int32_t* parents, int32_t n, uint64_t* out);
+SS_API int32_t ss_slot_tokens_host(int32_t len, int32_t chunk_len, int32_t chunk_begin, int32_t n_chunks,
+                                   int32_t chunks_per_slot, int32_t s, int64_t* t0, int64_t* t1);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_VERIFY_H */

@@ -1,0 +1,398 @@
+// C ABI of libssverify: argument validation, kernel dispatch and the
+// streamed-history pipeline (SpecStream section 4.2, "pipelined KV transfers":
+// staging buffers, a transfer stream and a compute stream, per-chunk events).
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ss_common.h"
+
+using namespace ssv;
+
+namespace {
+
+thread_local std::string g_err;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int32_t ok() {
+    g_err.clear();
+    return SS_OK;
+}
+
+int64_t elem_size(const ss_problem_t* p) { return p->dtype == SS_F32 ? 4 : 2; }
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int32_t check_problem(const ss_problem_t* p) {
+    if (!p) return fail(SS_ERR_INVALID_ARG, "problem is NULL");
+    if (p->batch <= 0 || p->n_q_heads <= 0 || p->n_kv_heads <= 0 || p->n_queries <= 0 || p->head_dim <= 0)
+        return fail(SS_ERR_INVALID_ARG, "batch, heads, head_dim and n_queries must be positive");
+    if (p->n_q_heads % p->n_kv_heads != 0)
+        return fail(SS_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", p->n_q_heads,
+                    p->n_kv_heads);
+    if (p->dtype != SS_F32 && p->dtype != SS_BF16) return fail(SS_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
+    if (!isfinite(p->scale)) return fail(SS_ERR_INVALID_ARG, "scale must be finite");
+    if (p->head_dim != 64 && p->head_dim != 128)
+        return fail(SS_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", p->head_dim);
+    if (p->batch > 65535) return fail(SS_ERR_UNSUPPORTED, "batch above 65535");
+    const int64_t rows = (int64_t)p->n_queries * (p->n_q_heads / p->n_kv_heads);
+    const int64_t row_blocks = (rows + kValuRows - 1) / kValuRows;
+    if ((int64_t)p->n_kv_heads * row_blocks > 65535) return fail(SS_ERR_UNSUPPORTED, "too many rows per request");
+    return SS_OK;
+}
+
+int32_t check_view(const ss_problem_t* p, const ss_kv_view_t* v, const char* name) {
+    if (!v) return fail(SS_ERR_INVALID_ARG, "%s view is NULL", name);
+    if (!v->k || !v->v) return fail(SS_ERR_INVALID_ARG, "%s keys or values pointer is NULL", name);
+    if (!aligned16(v->k) || !aligned16(v->v))
+        return fail(SS_ERR_INVALID_ARG, "%s keys and values must be 16-byte aligned", name);
+    if (v->max_len < 0) return fail(SS_ERR_INVALID_ARG, "%s max_len is negative", name);
+    if (v->stride_b < 0 || v->stride_h < 0 || v->stride_t < 0)
+        return fail(SS_ERR_INVALID_ARG, "%s strides must be non-negative", name);
+    const int64_t es = elem_size(p);
+    if ((v->stride_b * es) % 16 || (v->stride_h * es) % 16 || (v->stride_t * es) % 16)
+        return fail(SS_ERR_INVALID_ARG, "%s strides must be multiples of 16 bytes", name);
+    if (v->max_len > 1 && v->stride_t < p->head_dim)
+        return fail(SS_ERR_INVALID_ARG, "%s stride_t is smaller than head_dim", name);
+    return SS_OK;
+}
+
+int32_t check_state(const ss_state_t* s, const char* name) {
+    if (!s) return fail(SS_ERR_INVALID_ARG, "%s state is NULL", name);
+    if (!s->acc || !s->m || !s->l) return fail(SS_ERR_INVALID_ARG, "%s state has a NULL array", name);
+    if (s->n_slots <= 0) return fail(SS_ERR_INVALID_ARG, "%s state has no slots", name);
+    return SS_OK;
+}
+
+// Which chunk kernel serves a problem: MFMA bf16 when the rows of one KV head
+// fill a 16-row tile and fit two, the VALU kernel otherwise.
+bool use_mfma(const ss_problem_t* p) {
+    const int rows = p->n_queries * (p->n_q_heads / p->n_kv_heads);
+    return p->dtype == SS_BF16 && rows >= 16 && rows <= 32 && p->head_dim == 128 && kMfmaChunkKernel;
+}
+
+int32_t validate_chunk(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist, int32_t chunk_len,
+                       int32_t chunk_begin, int32_t n_chunks, int32_t cps, const ss_state_t* out,
+                       int32_t slot_begin) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if (!q) return fail(SS_ERR_INVALID_ARG, "q is NULL");
+    if (!aligned16(q)) return fail(SS_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if ((rc = check_view(problem, hist, "history"))) return rc;
+    if ((rc = check_state(out, "output"))) return rc;
+    if (chunk_len <= 0) return fail(SS_ERR_INVALID_ARG, "chunk_len must be positive");
+    if (chunk_begin < 0 || n_chunks < 0) return fail(SS_ERR_INVALID_ARG, "negative chunk range");
+    if (cps <= 0) return fail(SS_ERR_INVALID_ARG, "chunks_per_slot must be positive");
+    if (slot_begin < 0) return fail(SS_ERR_INVALID_ARG, "slot_begin is negative");
+    const int64_t items = ((int64_t)n_chunks + cps - 1) / cps;
+    if ((int64_t)slot_begin + items > out->n_slots)
+        return fail(SS_ERR_INVALID_ARG, "slots [%d, %lld) exceed n_slots %d", slot_begin,
+                    (long long)(slot_begin + items), out->n_slots);
+    if (items > 0x7fffffff) return fail(SS_ERR_UNSUPPORTED, "too many slots in one call");
+    return SS_OK;
+}
+
+ChunkParams make_chunk_params(const ss_problem_t* p, const void* q, const ss_kv_view_t* h, int32_t chunk_len,
+                              int32_t chunk_begin, int32_t n_chunks, int32_t cps, const ss_state_t* out,
+                              int32_t slot_begin) {
+    ChunkParams c{};
+    c.q = q;
+    c.k = h->k;
+    c.v = h->v;
+    c.stride_b = h->stride_b;
+    c.stride_h = h->stride_h;
+    c.stride_t = h->stride_t;
+    c.req_offset = h->req_offset;
+    c.req_len = h->req_len;
+    c.max_len = h->max_len;
+    c.batch = p->batch;
+    c.n_q_heads = p->n_q_heads;
+    c.n_kv_heads = p->n_kv_heads;
+    c.group = p->n_q_heads / p->n_kv_heads;
+    c.n_queries = p->n_queries;
+    c.rows = c.n_queries * c.group;
+    c.scale = p->scale;
+    c.chunk_len = chunk_len;
+    c.chunk_begin = chunk_begin;
+    c.n_chunks = n_chunks;
+    c.cps = cps;
+    c.n_items = (int32_t)(((int64_t)n_chunks + cps - 1) / cps);
+    c.acc = out->acc;
+    c.m = out->m;
+    c.l = out->l;
+    c.slot_begin = slot_begin;
+    c.row_blocks = (c.rows + kValuRows - 1) / kValuRows;
+    return c;
+}
+
+hipError_t enqueue_chunk(const ss_problem_t* p, const ChunkParams& c, hipStream_t stream) {
+    if (use_mfma(p)) return launch_chunk_mfma(c, p->head_dim, stream);
+    return launch_chunk_valu(c, p->dtype, p->head_dim, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Event pool of the streaming pipeline (one per device, reused across calls).
+// ---------------------------------------------------------------------------
+
+struct StreamEvents {
+    int device = -1;
+    std::vector<hipEvent_t> arrived, freed;  // per staging buffer, no timing
+    hipEvent_t start = nullptr;              // compute-stream frontier at call start
+    std::vector<hipEvent_t> t_copy0, t_copy1, t_comp0, t_comp1;  // timing events
+    int32_t timed_chunks = -1;
+};
+
+std::mutex g_ev_mutex;
+std::vector<StreamEvents> g_events;
+
+hipError_t grow(std::vector<hipEvent_t>& v, size_t n, unsigned flags) {
+    while (v.size() < n) {
+        hipEvent_t e;
+        hipError_t err = hipEventCreateWithFlags(&e, flags);
+        if (err != hipSuccess) return err;
+        v.push_back(e);
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+// ===========================================================================
+// exported calls
+// ===========================================================================
+
+extern "C" SS_API int32_t ss_abi_version(void) { return SS_ABI_VERSION; }
+
+extern "C" SS_API const char* ss_last_error(void) { return g_err.c_str(); }
+
+extern "C" SS_API int64_t ss_state_bytes(const ss_problem_t* problem, int32_t n_slots) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if (n_slots <= 0) return fail(SS_ERR_INVALID_ARG, "n_slots must be positive");
+    const int64_t rows = (int64_t)n_slots * problem->batch * problem->n_queries * problem->n_q_heads;
+    ok();
+    return rows * (problem->head_dim + 2) * 4;
+}
+
+extern "C" SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                          int32_t chunk_len, int32_t chunk_begin, int32_t n_chunks,
+                                          int32_t chunks_per_slot, const ss_state_t* out, int32_t slot_begin,
+                                          ss_stream_t stream) {
+    int32_t rc = validate_chunk(problem, q, hist, chunk_len, chunk_begin, n_chunks, chunks_per_slot, out, slot_begin);
+    if (rc) return rc;
+    if (n_chunks == 0) return ok();
+    ChunkParams c = make_chunk_params(problem, q, hist, chunk_len, chunk_begin, n_chunks, chunks_per_slot, out,
+                                      slot_begin);
+    hipError_t e = enqueue_chunk(problem, c, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, const void* q, const ss_kv_view_t* cand,
+                                               const int32_t* parents, uint64_t* mask_out, const ss_state_t* out,
+                                               int32_t slot, ss_stream_t stream) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if (!q) return fail(SS_ERR_INVALID_ARG, "q is NULL");
+    if (!aligned16(q)) return fail(SS_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if ((rc = check_view(problem, cand, "candidate"))) return rc;
+    if ((rc = check_state(out, "output"))) return rc;
+    if (problem->n_queries > 64) return fail(SS_ERR_UNSUPPORTED, "more than 64 candidates per request");
+    if (cand->max_len != problem->n_queries)
+        return fail(SS_ERR_INVALID_ARG, "candidate max_len (%d) must equal n_queries (%d)", cand->max_len,
+                    problem->n_queries);
+    if (slot < 0 || slot >= out->n_slots) return fail(SS_ERR_INVALID_ARG, "slot %d outside [0, %d)", slot, out->n_slots);
+
+    CandParams c{};
+    c.q = q;
+    c.k = cand->k;
+    c.v = cand->v;
+    c.stride_b = cand->stride_b;
+    c.stride_h = cand->stride_h;
+    c.stride_t = cand->stride_t;
+    c.req_offset = cand->req_offset;
+    c.batch = problem->batch;
+    c.n_q_heads = problem->n_q_heads;
+    c.n_kv_heads = problem->n_kv_heads;
+    c.group = problem->n_q_heads / problem->n_kv_heads;
+    c.n_queries = problem->n_queries;
+    c.rows = c.n_queries * c.group;
+    c.scale = problem->scale;
+    c.parents = parents;
+    c.mask_out = mask_out;
+    c.acc = out->acc;
+    c.m = out->m;
+    c.l = out->l;
+    c.slot = slot;
+    c.row_blocks = (c.rows + kValuRows - 1) / kValuRows;
+    hipError_t e = launch_candidates(c, problem->dtype, problem->head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "candidate kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in,
+                                          const int32_t* slots_per_req, float* o, float* lse, ss_stream_t stream) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if ((rc = check_state(in, "input"))) return rc;
+    if (!o || !lse) return fail(SS_ERR_INVALID_ARG, "o or lse is NULL");
+    const int64_t n = (int64_t)problem->batch * problem->n_queries * problem->n_q_heads * problem->head_dim;
+    if ((n + 255) / 256 > 0x7fffffff) return fail(SS_ERR_UNSUPPORTED, "output too large");
+    MergeParams m{};
+    m.acc = in->acc;
+    m.m = in->m;
+    m.l = in->l;
+    m.n_slots = in->n_slots;
+    m.slots_per_req = slots_per_req;
+    m.batch = problem->batch;
+    m.n_queries = problem->n_queries;
+    m.n_q_heads = problem->n_q_heads;
+    m.head_dim = problem->head_dim;
+    m.o = o;
+    m.lse = lse;
+    hipError_t e = launch_merge(m, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, const void* host_kv,
+                                            int32_t chunk_len, int32_t n_chunks, void* staging, int32_t n_buf,
+                                            const ss_state_t* out, int32_t slot_begin, ss_stream_t copy_stream,
+                                            ss_stream_t compute_stream, int32_t record_timings) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if (!q || !host_kv || !staging) return fail(SS_ERR_INVALID_ARG, "q, host_kv or staging is NULL");
+    if (!aligned16(q) || !aligned16(staging)) return fail(SS_ERR_INVALID_ARG, "q and staging must be 16-byte aligned");
+    if ((rc = check_state(out, "output"))) return rc;
+    if (chunk_len <= 0 || n_chunks < 0 || n_buf <= 0)
+        return fail(SS_ERR_INVALID_ARG, "chunk_len and n_buf must be positive, n_chunks non-negative");
+    if (slot_begin < 0 || (int64_t)slot_begin + n_chunks > out->n_slots)
+        return fail(SS_ERR_INVALID_ARG, "slots [%d, %d) exceed n_slots %d", slot_begin, slot_begin + n_chunks,
+                    out->n_slots);
+    if (copy_stream == compute_stream) return fail(SS_ERR_INVALID_ARG, "copy and compute streams must differ");
+    if (n_chunks == 0) return ok();
+
+    const int64_t es = elem_size(problem);
+    const int64_t half = (int64_t)problem->batch * problem->n_kv_heads * chunk_len * problem->head_dim;
+    const int64_t chunk_bytes = 2 * half * es;
+    hipStream_t cs = static_cast<hipStream_t>(copy_stream);
+    hipStream_t ks = static_cast<hipStream_t>(compute_stream);
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+
+    std::lock_guard<std::mutex> lock(g_ev_mutex);
+    if ((int)g_events.size() <= dev) g_events.resize(dev + 1);
+    StreamEvents& ev = g_events[dev];
+    ev.device = dev;
+    const unsigned sync_flags = hipEventDisableTiming;
+    if ((e = grow(ev.arrived, n_buf, sync_flags)) != hipSuccess || (e = grow(ev.freed, n_buf, sync_flags)) != hipSuccess)
+        return fail(SS_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+    if (!ev.start && (e = hipEventCreateWithFlags(&ev.start, sync_flags)) != hipSuccess)
+        return fail(SS_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+    if (record_timings) {
+        if ((e = grow(ev.t_copy0, n_chunks, hipEventDefault)) != hipSuccess ||
+            (e = grow(ev.t_copy1, n_chunks, hipEventDefault)) != hipSuccess ||
+            (e = grow(ev.t_comp0, n_chunks, hipEventDefault)) != hipSuccess ||
+            (e = grow(ev.t_comp1, n_chunks, hipEventDefault)) != hipSuccess)
+            return fail(SS_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+    }
+
+    ss_kv_view_t view{};
+    view.stride_b = (int64_t)problem->n_kv_heads * chunk_len * problem->head_dim;
+    view.stride_h = (int64_t)chunk_len * problem->head_dim;
+    view.stride_t = problem->head_dim;
+    view.max_len = chunk_len;
+
+#define SS_TRY(call)                                                                              \
+    do {                                                                                          \
+        hipError_t err_ = (call);                                                                 \
+        if (err_ != hipSuccess) return fail(SS_ERR_HIP, "%s: %s", #call, hipGetErrorString(err_)); \
+    } while (0)
+
+    // The first copy may overwrite staging buffers that earlier compute work
+    // still reads: order it after everything already on the compute stream.
+    SS_TRY(hipEventRecord(ev.start, ks));
+    SS_TRY(hipStreamWaitEvent(cs, ev.start, 0));
+    for (int32_t j = 0; j < n_chunks; ++j) {
+        const int32_t bi = j % n_buf;
+        char* buf = static_cast<char*>(staging) + (int64_t)bi * chunk_bytes;
+        const char* src = static_cast<const char*>(host_kv) + (int64_t)j * chunk_bytes;
+        if (j >= n_buf) SS_TRY(hipStreamWaitEvent(cs, ev.freed[bi], 0));
+        if (record_timings) SS_TRY(hipEventRecord(ev.t_copy0[j], cs));
+        SS_TRY(hipMemcpyAsync(buf, src, chunk_bytes, hipMemcpyHostToDevice, cs));
+        if (record_timings) SS_TRY(hipEventRecord(ev.t_copy1[j], cs));
+        SS_TRY(hipEventRecord(ev.arrived[bi], cs));
+
+        SS_TRY(hipStreamWaitEvent(ks, ev.arrived[bi], 0));
+        if (record_timings) SS_TRY(hipEventRecord(ev.t_comp0[j], ks));
+        view.k = buf;
+        view.v = buf + half * es;
+        ChunkParams c = make_chunk_params(problem, q, &view, chunk_len, 0, 1, 1, out, slot_begin + j);
+        SS_TRY(enqueue_chunk(problem, c, ks));
+        if (record_timings) SS_TRY(hipEventRecord(ev.t_comp1[j], ks));
+        SS_TRY(hipEventRecord(ev.freed[bi], ks));
+    }
+#undef SS_TRY
+    ev.timed_chunks = record_timings ? n_chunks : -1;
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_stream_timings(int32_t n_chunks, float* copy_begin, float* copy_end,
+                                            float* compute_begin, float* compute_end) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_ev_mutex);
+    if ((int)g_events.size() <= dev || g_events[dev].timed_chunks < 0)
+        return fail(SS_ERR_INVALID_ARG, "no timed streaming call on this device");
+    StreamEvents& ev = g_events[dev];
+    if (n_chunks != ev.timed_chunks)
+        return fail(SS_ERR_INVALID_ARG, "n_chunks %d differs from the timed call's %d", n_chunks, ev.timed_chunks);
+    for (int32_t j = 0; j < n_chunks; ++j) {
+        float t;
+        struct {
+            float* out;
+            hipEvent_t ev;
+        } items[4] = {{copy_begin, ev.t_copy0[j]}, {copy_end, ev.t_copy1[j]}, {compute_begin, ev.t_comp0[j]},
+                      {compute_end, ev.t_comp1[j]}};
+        for (auto& it : items) {
+            if (!it.out) continue;
+            e = hipEventElapsedTime(&t, ev.t_copy0[0], it.ev);
+            if (e != hipSuccess) return fail(SS_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+            it.out[j] = t;
+        }
+    }
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_tree_mask_host(const int32_t* parents, int32_t n, uint64_t* out) {
+    if (!parents || !out) return fail(SS_ERR_INVALID_ARG, "parents or out is NULL");
+    if (n < 0 || n > 64) return fail(SS_ERR_INVALID_ARG, "n must be in [0, 64]");
+    for (int32_t i = 0; i < n; ++i) out[i] = tree_bits_step(out, i, parents[i]);
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_slot_tokens_host(int32_t len, int32_t chunk_len, int32_t chunk_begin, int32_t n_chunks,
+                                              int32_t chunks_per_slot, int32_t s, int64_t* t0, int64_t* t1) {
+    if (!t0 || !t1) return fail(SS_ERR_INVALID_ARG, "t0 or t1 is NULL");
+    if (len < 0 || chunk_len <= 0 || chunk_begin < 0 || n_chunks < 0 || chunks_per_slot <= 0 || s < 0)
+        return fail(SS_ERR_INVALID_ARG, "invalid chunk arguments");
+    slot_tokens(len, chunk_len, chunk_begin, n_chunks, chunks_per_slot, s, t0, t1);
+    return ok();
+}

@@ -1,0 +1,116 @@
+"""One verification round on the GPU, composed from the C-ABI calls.
+
+ResidentRound: history resident in HBM -> ss_verify_chunk over every chunk,
+ss_verify_candidates into the last slot, ss_merge_states -> O, lse.
+StreamedRound: history in pinned host memory -> ss_stream_history on a copy
+and a compute stream, then candidates and merge on the compute stream.
+
+Only device buffers and the order of calls live here; all arithmetic is in
+the HIP library.
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import ssverify as ss
+from .workloads import VerifyInputs, to_chunk_major
+
+
+def _problem(cfg) -> ss.Problem:
+    return ss.make_problem(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_queries,
+                           cfg.torch_dtype, cfg.scale)
+
+
+class ResidentRound:
+    def __init__(self, inp: VerifyInputs, device="cuda", chunk_len=None, chunks_per_slot=1):
+        cfg = inp.cfg
+        self.cfg = cfg
+        self.problem = _problem(cfg)
+        self.chunk_len = chunk_len or cfg.chunk_len
+        self.cps = chunks_per_slot
+        self.q = inp.q.to(device)
+        self.k_hist = inp.k_hist.to(device)
+        self.v_hist = inp.v_hist.to(device)
+        self.max_len = int(inp.hist_len.max()) if len(inp.hist_len) else 0
+        if cfg.ragged:
+            self.hist_offset = torch.as_tensor(inp.hist_offset, dtype=torch.int64, device=device)
+            self.hist_len = torch.as_tensor(inp.hist_len, dtype=torch.int32, device=device)
+            self.hist_view = ss.token_major_view(self.k_hist, self.v_hist, self.hist_offset, self.hist_len,
+                                                 self.max_len)
+        else:
+            self.hist_view = ss.head_major_view(self.k_hist, self.v_hist)
+        self.k_cand = inp.k_cand.to(device)
+        self.v_cand = inp.v_cand.to(device)
+        self.cand_view = ss.head_major_view(self.k_cand, self.v_cand)
+        self.parents = None
+        if inp.parents is not None:
+            self.parents = torch.as_tensor(inp.parents, dtype=torch.int32, device=device).contiguous()
+        self.n_chunks = math.ceil(self.max_len / self.chunk_len)
+        self.n_hist_slots = math.ceil(self.n_chunks / self.cps)
+        self.state = ss.StateBuffers(self.problem, self.n_hist_slots + 1, device)
+        self.mask_out = torch.zeros((cfg.batch, cfg.n_queries), dtype=torch.int64, device=device)
+        self.o = torch.empty((cfg.batch, cfg.n_queries, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32,
+                             device=device)
+        self.lse = torch.empty((cfg.batch, cfg.n_queries, cfg.n_q_heads), dtype=torch.float32, device=device)
+
+    def chunks(self, stream=None):
+        if self.n_chunks == 0:          # no history at all: nothing to enqueue
+            return
+        ss.ss_verify_chunk(self.problem, self.q, self.hist_view, self.chunk_len, 0, self.n_chunks, self.cps,
+                           self.state, 0, stream)
+
+    def candidates(self, stream=None):
+        ss.ss_verify_candidates(self.problem, self.q, self.cand_view, self.parents, self.mask_out, self.state,
+                                self.n_hist_slots, stream)
+
+    def merge(self, stream=None):
+        ss.ss_merge_states(self.problem, self.state, None, self.o, self.lse, stream)
+
+    def run(self, stream=None):
+        self.chunks(stream)
+        self.candidates(stream)
+        self.merge(stream)
+
+
+class StreamedRound:
+    def __init__(self, inp: VerifyInputs, device="cuda", n_buf=2, chunk_len=None):
+        cfg = inp.cfg
+        self.cfg = cfg
+        self.problem = _problem(cfg)
+        self.chunk_len = chunk_len or cfg.chunk_len
+        n = int(inp.hist_len[0])
+        if (inp.hist_len != n).any() or n % self.chunk_len:
+            raise ValueError("streamed rounds need one history length, a multiple of the chunk length")
+        self.n_chunks = n // self.chunk_len
+        self.n_buf = n_buf
+        b_, hkv, d = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+        self.chunk_elems = 2 * b_ * hkv * self.chunk_len * d
+        self.host_kv = torch.empty((self.n_chunks, self.chunk_elems), dtype=cfg.torch_dtype, pin_memory=True)
+        to_chunk_major(inp.k_hist, inp.v_hist, self.chunk_len, self.host_kv)
+        self.staging = torch.empty((n_buf, self.chunk_elems), dtype=cfg.torch_dtype, device=device)
+        self.q = inp.q.to(device)
+        self.k_cand = inp.k_cand.to(device)
+        self.v_cand = inp.v_cand.to(device)
+        self.cand_view = ss.head_major_view(self.k_cand, self.v_cand)
+        self.parents = None
+        if inp.parents is not None:
+            self.parents = torch.as_tensor(inp.parents, dtype=torch.int32, device=device).contiguous()
+        self.state = ss.StateBuffers(self.problem, self.n_chunks + 1, device)
+        self.o = torch.empty((b_, cfg.n_queries, cfg.n_q_heads, d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((b_, cfg.n_queries, cfg.n_q_heads), dtype=torch.float32, device=device)
+        self.copy_stream = torch.cuda.Stream(device=device)
+        self.compute_stream = torch.cuda.Stream(device=device)
+
+    def run(self, record_timings=False):
+        """Enqueues the whole round; the result is ready once compute_stream is."""
+        cs = self.compute_stream
+        cs.wait_stream(torch.cuda.current_stream())
+        ss.ss_stream_history(self.problem, self.q, self.host_kv, self.chunk_len, self.n_chunks, self.staging,
+                             self.n_buf, self.state, 0, self.copy_stream, cs, record_timings)
+        ss.ss_verify_candidates(self.problem, self.q, self.cand_view, self.parents, None, self.state,
+                                self.n_chunks, cs)
+        ss.ss_merge_states(self.problem, self.state, None, self.o, self.lse, cs)
+        torch.cuda.current_stream().wait_stream(cs)

@@ -1,0 +1,209 @@
+"""ctypes binding of libssverify (the C ABI in include/ss_verify.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. torch supplies device memory and stream handles. The library is
+loaded on first use; if it is missing, every call raises (there is no other
+implementation to fall back to).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssverify.so")
+
+SS_OK = 0
+SS_ERR_INVALID_ARG = -1
+SS_ERR_UNSUPPORTED = -2
+SS_ERR_HIP = -3
+
+SS_F32 = 0
+SS_BF16 = 1
+
+EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chunk", "ss_verify_candidates",
+            "ss_merge_states", "ss_stream_history", "ss_stream_timings", "ss_tree_mask_host", "ss_slot_tokens_host")
+
+
+class SSError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"libssverify error {code}: {message}")
+        self.code = code
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("n_queries", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+class KVView(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64), ("req_offset", ctypes.c_void_p),
+                ("req_len", ctypes.c_void_p), ("max_len", ctypes.c_int32)]
+
+
+class State(ctypes.Structure):
+    _fields_ = [("acc", ctypes.c_void_p), ("m", ctypes.c_void_p), ("l", ctypes.c_void_p),
+                ("n_slots", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with python -m long_context_speculative_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        P, VP, I32, I64 = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        L.ss_abi_version.restype = I32
+        L.ss_abi_version.argtypes = []
+        L.ss_last_error.restype = ctypes.c_char_p
+        L.ss_last_error.argtypes = []
+        L.ss_state_bytes.restype = I64
+        L.ss_state_bytes.argtypes = [P(Problem), I32]
+        L.ss_verify_chunk.restype = I32
+        L.ss_verify_chunk.argtypes = [P(Problem), VP, P(KVView), I32, I32, I32, I32, P(State), I32, VP]
+        L.ss_verify_candidates.restype = I32
+        L.ss_verify_candidates.argtypes = [P(Problem), VP, P(KVView), VP, VP, P(State), I32, VP]
+        L.ss_merge_states.restype = I32
+        L.ss_merge_states.argtypes = [P(Problem), P(State), VP, VP, VP, VP]
+        L.ss_stream_history.restype = I32
+        L.ss_stream_history.argtypes = [P(Problem), VP, VP, I32, I32, VP, I32, P(State), I32, VP, VP, I32]
+        L.ss_stream_timings.restype = I32
+        L.ss_stream_timings.argtypes = [I32, VP, VP, VP, VP]
+        L.ss_tree_mask_host.restype = I32
+        L.ss_tree_mask_host.argtypes = [VP, I32, VP]
+        L.ss_slot_tokens_host.restype = I32
+        L.ss_slot_tokens_host.argtypes = [I32, I32, I32, I32, I32, I32, P(I64), P(I64)]
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != SS_OK:
+        raise SSError(rc, lib().ss_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# struct builders
+# ---------------------------------------------------------------------------
+
+def make_problem(batch, n_q_heads, n_kv_heads, head_dim, n_queries, dtype, scale) -> Problem:
+    if isinstance(dtype, torch.dtype):
+        dtype = SS_F32 if dtype == torch.float32 else SS_BF16
+    return Problem(batch, n_q_heads, n_kv_heads, head_dim, n_queries, dtype, scale)
+
+
+def make_view(k: torch.Tensor, v: torch.Tensor, stride_b: int, stride_h: int, stride_t: int, max_len: int,
+              req_offset: Optional[torch.Tensor] = None, req_len: Optional[torch.Tensor] = None) -> KVView:
+    return KVView(k.data_ptr(), v.data_ptr(), stride_b, stride_h, stride_t, _ptr(req_offset), _ptr(req_len), max_len)
+
+
+def head_major_view(k: torch.Tensor, v: torch.Tensor, req_len: Optional[torch.Tensor] = None,
+                    max_len: Optional[int] = None) -> KVView:
+    """View of [B][Hkv][N][d] tensors (contiguous in the last three axes)."""
+    sb, sh, st, sx = k.stride()
+    return make_view(k, v, sb, sh, st, k.shape[2] if max_len is None else max_len, None, req_len)
+
+
+def token_major_view(k: torch.Tensor, v: torch.Tensor, req_offset: torch.Tensor, req_len: torch.Tensor,
+                     max_len: int) -> KVView:
+    """View of packed ragged [sum N_b][Hkv][d] tensors with device offsets
+    (elements) and lengths per request."""
+    st, sh, sx = k.stride()
+    return make_view(k, v, 0, sh, st, max_len, req_offset, req_len)
+
+
+class StateBuffers:
+    """Device tensors of n_slots state slots plus the C struct over them."""
+
+    def __init__(self, problem: Problem, n_slots: int, device="cuda"):
+        rows = (n_slots, problem.batch, problem.n_queries, problem.n_q_heads)
+        self.acc = torch.empty(rows + (problem.head_dim,), dtype=torch.float32, device=device)
+        self.m = torch.empty(rows, dtype=torch.float32, device=device)
+        self.l = torch.empty(rows, dtype=torch.float32, device=device)
+        self.n_slots = n_slots
+        self.struct = State(self.acc.data_ptr(), self.m.data_ptr(), self.l.data_ptr(), n_slots)
+
+
+# ---------------------------------------------------------------------------
+# the calls (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def ss_abi_version() -> int:
+    return lib().ss_abi_version()
+
+
+def ss_state_bytes(problem: Problem, n_slots: int) -> int:
+    r = lib().ss_state_bytes(ctypes.byref(problem), n_slots)
+    if r < 0:
+        _check(int(r))
+    return int(r)
+
+
+def ss_verify_chunk(problem: Problem, q: torch.Tensor, hist: KVView, chunk_len: int, chunk_begin: int,
+                    n_chunks: int, chunks_per_slot: int, out: StateBuffers, slot_begin: int, stream=None) -> None:
+    _check(lib().ss_verify_chunk(ctypes.byref(problem), q.data_ptr(), ctypes.byref(hist), chunk_len, chunk_begin,
+                                 n_chunks, chunks_per_slot, ctypes.byref(out.struct), slot_begin, _stream(stream)))
+
+
+def ss_verify_candidates(problem: Problem, q: torch.Tensor, cand: KVView, parents: Optional[torch.Tensor],
+                         mask_out: Optional[torch.Tensor], out: StateBuffers, slot: int, stream=None) -> None:
+    _check(lib().ss_verify_candidates(ctypes.byref(problem), q.data_ptr(), ctypes.byref(cand), _ptr(parents),
+                                      _ptr(mask_out), ctypes.byref(out.struct), slot, _stream(stream)))
+
+
+def ss_merge_states(problem: Problem, states: StateBuffers, slots_per_req: Optional[torch.Tensor],
+                    o: torch.Tensor, lse: torch.Tensor, stream=None) -> None:
+    _check(lib().ss_merge_states(ctypes.byref(problem), ctypes.byref(states.struct), _ptr(slots_per_req),
+                                 o.data_ptr(), lse.data_ptr(), _stream(stream)))
+
+
+def ss_stream_history(problem: Problem, q: torch.Tensor, host_kv: torch.Tensor, chunk_len: int, n_chunks: int,
+                      staging: torch.Tensor, n_buf: int, out: StateBuffers, slot_begin: int, copy_stream,
+                      compute_stream, record_timings: bool = False) -> None:
+    _check(lib().ss_stream_history(ctypes.byref(problem), q.data_ptr(), host_kv.data_ptr(), chunk_len, n_chunks,
+                                   staging.data_ptr(), n_buf, ctypes.byref(out.struct), slot_begin,
+                                   _stream(copy_stream), _stream(compute_stream), int(bool(record_timings))))
+
+
+def ss_stream_timings(n_chunks: int):
+    """Per-chunk (copy_begin, copy_end, compute_begin, compute_end) in ms."""
+    bufs = [(ctypes.c_float * n_chunks)() for _ in range(4)]
+    _check(lib().ss_stream_timings(n_chunks, *[ctypes.addressof(b) for b in bufs]))
+    return [list(b) for b in bufs]
+
+
+def ss_tree_mask_host(parents) -> list:
+    n = len(parents)
+    par = (ctypes.c_int32 * max(n, 1))(*[int(x) for x in parents])
+    out = (ctypes.c_uint64 * max(n, 1))()
+    _check(lib().ss_tree_mask_host(ctypes.addressof(par), n, ctypes.addressof(out)))
+    return [int(out[i]) for i in range(n)]
+
+
+def ss_slot_tokens_host(length: int, chunk_len: int, chunk_begin: int, n_chunks: int, chunks_per_slot: int,
+                        s: int):
+    t0, t1 = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().ss_slot_tokens_host(length, chunk_len, chunk_begin, n_chunks, chunks_per_slot, s,
+                                     ctypes.byref(t0), ctypes.byref(t1)))
+    return t0.value, t1.value

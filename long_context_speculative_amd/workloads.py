@@ -6,17 +6,20 @@ and the fp64 oracle consume what it produces.
 
 Recipe (every tensor is independent of the others and of the draw order):
 
-* A config carries one integer seed. Each random stream is a numpy PCG64
-  generator built from ``SeedSequence(seed, spawn_key=(stream, b))`` where
-  ``stream`` names the tensor (see ``_STREAM``) and ``b`` is the request.
+* A config carries one integer seed. Each random stream is keyed by
+  ``SeedSequence(seed, spawn_key=(stream, b))`` where ``stream`` names the
+  tensor (see ``_STREAM``) and ``b`` is the request; lengths and trees draw
+  from numpy PCG64 generators built from it.
 * Ragged history lengths: integer uniform on [lo, hi], both ends included,
   one draw of B values from stream "len".
 * Candidate trees: node 0 is the root (parent -1, depth 0); for i = 1..n-1 the
   parent is uniform over the earlier nodes whose depth is below the depth cap,
   so every node sits at depth <= cap and parent[i] < i (topological order).
-* Values: float32 N(0, 1), drawn per request in the logical layout order of
-  the tensor, then rounded to the config's dtype (bf16 by round-to-nearest-even
-  through torch).
+* Values: float32 N(0, 1) from torch's CPU generator, one generator per
+  (tensor, request) seeded with 63 bits of ``SeedSequence(seed,
+  spawn_key=(stream, b)).generate_state``; drawn in the logical layout order
+  of the tensor in pieces of 2^24 values, then rounded to the config's dtype
+  (bf16 by round-to-nearest-even through torch).
 
 Logical layouts handed out:
   q        [B][nq][Hq][d]
@@ -122,24 +125,28 @@ def draw_tree(seed: int, b: int, n: int, depth_cap: int) -> np.ndarray:
     return parents
 
 
+def _torch_seed(seed: int, stream: str, b: int) -> int:
+    ss = np.random.SeedSequence(seed, spawn_key=(_STREAM[stream], b))
+    return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
 def _fill_normal(out: torch.Tensor, seed: int, stream: str, pieces) -> None:
     """Fill ``out`` (a CPU tensor) with N(0,1) values, piece by piece.
 
-    pieces: list of (b, flat_start, count); piece b draws from its own stream.
-    Pieces are drawn in parallel threads (numpy releases the GIL while filling).
+    pieces: list of (b, flat_start, count); piece b draws float32 normals from
+    its own torch CPU generator, then they are rounded into ``out`` (bf16:
+    round-to-nearest-even). Pieces run in parallel threads.
     """
     flat = out.view(-1)
 
     def work(piece):
         b, start, count = piece
-        rng = _rng(seed, stream, b)
-        buf = np.empty(count, dtype=np.float32)
+        g = torch.Generator().manual_seed(_torch_seed(seed, stream, b))
         step = 1 << 24
         for off in range(0, count, step):
             n = min(step, count - off)
-            rng.standard_normal(out=buf[off:off + n], dtype=np.float32)
-        src = torch.from_numpy(buf)
-        flat[start:start + count].copy_(src)   # rounds to bf16 (RNE) when out is bf16
+            vals = torch.randn(n, generator=g, dtype=torch.float32)
+            flat[start + off:start + off + n].copy_(vals)
 
     threads = max(1, min(16, os.cpu_count() or 1))
     if len(pieces) == 1:

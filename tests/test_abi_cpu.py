@@ -1,0 +1,182 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every call the
+header declares, rejects bad arguments before touching a device, and its
+host-side integer rules (tree mask, chunk-to-slot token ranges) agree bit for
+bit with the oracle."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from long_context_speculative_amd import ssverify as ss
+from long_context_speculative_amd import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss_verify.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SS_API\s+[\w\s\*]*?\b(ss_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_call():
+    names = header_functions()
+    assert len(names) >= 10
+    L = ss.lib()
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(ss.EXPORTED)
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define\s+SS_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert ss.ss_abi_version() == int(m.group(1))
+
+
+def _problem(**kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_queries=6, dtype=ss.SS_BF16, scale=0.088)
+    base.update(kw)
+    return ss.Problem(**base)
+
+
+def test_state_bytes():
+    p = _problem()
+    assert ss.ss_state_bytes(p, 3) == 3 * 2 * 6 * 8 * (128 + 2) * 4
+    with pytest.raises(ss.SSError) as e:
+        ss.ss_state_bytes(_problem(head_dim=96), 1)
+    assert e.value.code == ss.SS_ERR_UNSUPPORTED
+
+
+class _Fake:
+    """Something with a data_ptr(), for calls that must fail validation
+    before any device work (the pointers are never dereferenced)."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _view(max_len=64, stride_t=128, k=4096, v=8192):
+    return ss.KVView(k, v, 0, 0, stride_t, None, None, max_len)
+
+
+def _state(n_slots=4):
+    st = ss.StateBuffers.__new__(ss.StateBuffers)
+    st.struct = ss.State(4096, 8192, 12288, n_slots)
+    return st
+
+
+@pytest.mark.parametrize("case,code", [
+    ("null_problem", ss.SS_ERR_INVALID_ARG),
+    ("bad_heads", ss.SS_ERR_INVALID_ARG),
+    ("head_dim_96", ss.SS_ERR_UNSUPPORTED),
+    ("null_q", ss.SS_ERR_INVALID_ARG),
+    ("misaligned_k", ss.SS_ERR_INVALID_ARG),
+    ("zero_chunk", ss.SS_ERR_INVALID_ARG),
+    ("slot_overflow", ss.SS_ERR_INVALID_ARG),
+    ("bad_cps", ss.SS_ERR_INVALID_ARG),
+    ("bad_stride", ss.SS_ERR_INVALID_ARG),
+])
+def test_verify_chunk_rejects(case, code):
+    L = ss.lib()
+    p = _problem()
+    q = 4096
+    view = _view()
+    st = _state(4)
+    args = dict(chunk_len=64, chunk_begin=0, n_chunks=4, cps=1, slot_begin=0)
+    if case == "null_problem":
+        rc = L.ss_verify_chunk(None, q, ctypes.byref(view), 64, 0, 4, 1, ctypes.byref(st.struct), 0, None)
+        assert rc == code
+        return
+    if case == "bad_heads":
+        p = _problem(n_q_heads=7)
+    if case == "head_dim_96":
+        p = _problem(head_dim=96)
+    if case == "null_q":
+        q = None
+    if case == "misaligned_k":
+        view = _view(k=4098)
+    if case == "zero_chunk":
+        args["chunk_len"] = 0
+    if case == "slot_overflow":
+        args["slot_begin"] = 1
+    if case == "bad_cps":
+        args["cps"] = 0
+    if case == "bad_stride":
+        view = _view(stride_t=100)
+    rc = L.ss_verify_chunk(ctypes.byref(p), q, ctypes.byref(view), args["chunk_len"], args["chunk_begin"],
+                           args["n_chunks"], args["cps"], ctypes.byref(st.struct), args["slot_begin"], None)
+    assert rc == code
+    assert L.ss_last_error().decode()
+
+
+def test_candidates_and_stream_reject():
+    L = ss.lib()
+    p = _problem(n_queries=65)
+    rc = L.ss_verify_candidates(ctypes.byref(p), 4096, ctypes.byref(_view(max_len=65)), None, None,
+                                ctypes.byref(_state().struct), 0, None)
+    assert rc == ss.SS_ERR_UNSUPPORTED
+    p = _problem()
+    rc = L.ss_verify_candidates(ctypes.byref(p), 4096, ctypes.byref(_view(max_len=5)), None, None,
+                                ctypes.byref(_state().struct), 0, None)
+    assert rc == ss.SS_ERR_INVALID_ARG          # max_len must equal n_queries
+    rc = L.ss_verify_candidates(ctypes.byref(p), 4096, ctypes.byref(_view(max_len=6)), None, None,
+                                ctypes.byref(_state(2).struct), 2, None)
+    assert rc == ss.SS_ERR_INVALID_ARG          # slot out of range
+    # equal copy and compute streams
+    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, 64, 4, 8192, 2, ctypes.byref(_state(4).struct), 0,
+                             None, None, 0)
+    assert rc == ss.SS_ERR_INVALID_ARG
+    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, 64, 5, 8192, 2, ctypes.byref(_state(4).struct), 0,
+                             1, 2, 0)
+    assert rc == ss.SS_ERR_INVALID_ARG          # 5 chunks, 4 slots
+    rc = L.ss_merge_states(ctypes.byref(p), ctypes.byref(_state().struct), None, None, 4096, None)
+    assert rc == ss.SS_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tree_mask_host_matches_oracle(seed):
+    n = [1, 5, 17, 33, 63, 64][seed]
+    parents = workloads.draw_tree(seed, 0, n, 8)
+    got = ss.ss_tree_mask_host(parents)
+    want = [int(x) for x in oracle.mask_to_bits(oracle.tree_mask(parents))]
+    assert got == want
+
+
+def test_tree_mask_host_chain_and_invalid_parents():
+    for n in (1, 2, 6, 64):
+        assert ss.ss_tree_mask_host([-1] + list(range(n - 1))) == [int(x) for x in
+                                                                     oracle.mask_to_bits(oracle.chain_mask(n))]
+    # pointers that do not point strictly backwards are read as roots
+    assert ss.ss_tree_mask_host([-1, 5, 1, -7, 0]) == [0b1, 0b10, 0b110, 0b1000, 0b10001]
+
+
+def test_slot_tokens_host_tile_history():
+    rng = np.random.default_rng(5)
+    for _ in range(40):
+        c = int(rng.choice([1, 7, 64, 2048, 4096]))
+        n = int(rng.integers(0, min(20000, 60 * c)))
+        cps = int(rng.integers(1, 5))
+        n_chunks = -(-n // c) if n else 0
+        ref = oracle.chunk_list([n], c)
+        covered = []
+        for s in range(-(-n_chunks // cps) if n_chunks else 0):
+            t0, t1 = ss.ss_slot_tokens_host(n, c, 0, n_chunks, cps, s)
+            # the slot's range is exactly the union of its chunks in the oracle's list
+            mine = [(st, ln) for (_, j, st, ln) in ref if s * cps <= j < (s + 1) * cps]
+            assert (t0, t1) == (mine[0][0], mine[-1][0] + mine[-1][1])
+            covered.append((t0, t1))
+        if covered:
+            assert covered[0][0] == 0 and covered[-1][1] == n
+            assert all(a[1] == b[0] for a, b in zip(covered, covered[1:]))
+    # a chunk beyond the request's length gives an empty range
+    assert ss.ss_slot_tokens_host(100, 64, 2, 1, 1, 0) == (100, 100)
+    # a sub-range of chunks
+    assert ss.ss_slot_tokens_host(1000, 64, 3, 5, 2, 1) == (5 * 64, 7 * 64)
+    assert ss.ss_slot_tokens_host(1000, 64, 3, 5, 2, 2) == (7 * 64, 8 * 64)

@@ -1,0 +1,295 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Small cases compare every output element; they span several key tiles and
+chunks, ragged tails, and the degenerate cases (empty history, chunks beyond
+a request's end, one-token history). Full-size cases run the verification
+workloads in the launch configuration the benchmark times and compare sampled
+(request, KV head) slices, which the oracle computes one at a time.
+
+Tolerances (max-abs on O and on lse): 2e-3 for bf16 inputs, 1e-5 for fp32.
+Masks compare bit for bit.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_speculative_amd import rounds
+from long_context_speculative_amd import ssverify as ss
+from long_context_speculative_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+C = wl.CONFIGS
+
+SMALL = {
+    "c1": C["c1_tiny_f32"],
+    "c2_small": C["c2_qwen3_8b"].with_(batch=2, hist_len=4500, chunk_len=1024),
+    "c3_small": C["c3_internlm25_7b_ragged"].with_(batch=6, hist_len=3000, ragged_lo=1, chunk_len=512),
+    "c4_small": C["c4_tree_72b"].with_(batch=2, hist_len=1500, chunk_len=512),
+    "c5_small": C["c5_streamed"].with_(batch=2, hist_len=2048, chunk_len=512),
+    "f32_g8_tree": C["c4_tree_72b"].with_(batch=1, hist_len=700, chunk_len=128, dtype="f32", n_queries=20),
+    "bf16_d64": C["c2_qwen3_8b"].with_(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64, hist_len=333,
+                                       chunk_len=100),
+    "bf16_small_rows": C["c2_qwen3_8b"].with_(batch=3, n_queries=2, hist_len=1000, chunk_len=256),
+}
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def cand_visibility(inp):
+    cfg = inp.cfg
+    if cfg.mask == "tree":
+        return np.stack([oracle.tree_mask(inp.parents[b]) for b in range(cfg.batch)])
+    return np.stack([oracle.chain_mask(cfg.n_queries)] * cfg.batch)
+
+
+def oracle_round(inp, requests=None, kv_heads=None):
+    return oracle.attention_reference(inp.q.float().numpy(), inp.hist_per_request("k"), inp.hist_per_request("v"),
+                                      inp.hist_len, inp.k_cand.float().numpy(), inp.v_cand.float().numpy(),
+                                      cand_visibility(inp), inp.cfg.scale, requests=requests, kv_heads=kv_heads)
+
+
+def rows_of(cfg, b, g):
+    """Index arrays selecting the O/lse entries of (request b, KV head g)."""
+    hs = np.arange(g * cfg.group, (g + 1) * cfg.group)
+    return b, slice(None), hs
+
+
+def compare(cfg, o_gpu, lse_gpu, o_ref, lse_ref, sel=None):
+    tol = TOL[cfg.dtype]
+    if sel is None:
+        eo = np.abs(o_gpu - o_ref).max()
+        el = np.abs(lse_gpu - lse_ref).max()
+    else:
+        b, _, hs = sel
+        eo = np.abs(o_gpu[b][:, hs] - o_ref[b][:, hs]).max()
+        el = np.abs(lse_gpu[b][:, hs] - lse_ref[b][:, hs]).max()
+    log(f"  {cfg.name}: max|dO| = {eo:.3e}, max|dlse| = {el:.3e} (tol {tol})")
+    assert eo <= tol and el <= tol, (eo, el)
+
+
+def check_mask(rnd, inp):
+    want = np.stack([oracle.mask_to_bits(v) for v in cand_visibility(inp)]).astype(np.uint64)
+    got = rnd.mask_out.cpu().numpy().view(np.uint64)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_round_small(name):
+    cfg = SMALL[name]
+    log(f"[round_small] {name}: {cfg}")
+    inp = wl.make_inputs(cfg)
+    if cfg.streamed:
+        rnd = rounds.StreamedRound(inp, n_buf=2)
+    else:
+        rnd = rounds.ResidentRound(inp)
+    rnd.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    if not cfg.streamed:
+        check_mask(rnd, inp)
+
+
+@pytest.mark.parametrize("chunk_len,cps", [(64, 1), (100, 3), (512, 2), (4096, 1)])
+def test_chunk_slot_states(chunk_len, cps):
+    """Per-slot states of ss_verify_chunk against the oracle's local states
+    (Eq. 7 over each slot's chunks), including slots past a request's end."""
+    cfg = SMALL["c3_small"]
+    log(f"[slot_states] chunk {chunk_len} cps {cps}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, chunk_len=chunk_len, chunks_per_slot=cps)
+    rnd.chunks()
+    torch.cuda.synchronize()
+    m, l, acc = oracle.chunk_slot_states(inp.q.float().numpy(), inp.hist_per_request("k"),
+                                         inp.hist_per_request("v"), inp.hist_len, chunk_len, 0, rnd.n_chunks, cps,
+                                         cfg.scale)
+    gm = rnd.state.m[:rnd.n_hist_slots].cpu().numpy()
+    gl = rnd.state.l[:rnd.n_hist_slots].cpu().numpy()
+    gacc = rnd.state.acc[:rnd.n_hist_slots].cpu().numpy()
+    empty = np.isneginf(m)
+    assert np.array_equal(np.isneginf(gm), empty)
+    assert (gl[empty] == 0).all() and (gacc[empty] == 0).all()
+    full = ~empty
+    tol = TOL[cfg.dtype]
+    assert np.abs(gm[full] - m[full]).max() <= tol
+    assert np.abs(gl[full] / l[full] - 1).max() <= tol
+    assert np.abs(gacc[full] / gl[full][:, None] - acc[full] / l[full][:, None]).max() <= tol
+
+
+def test_chunk_size_and_split_invariance():
+    cfg = SMALL["c2_small"]
+    inp = wl.make_inputs(cfg)
+    o_ref, lse_ref = oracle_round(inp)
+    outs = []
+    for c, cps in ((64, 1), (512, 4), (2048, 1), (4500, 1), (1000, 2)):
+        log(f"[invariance] chunk {c} cps {cps}")
+        rnd = rounds.ResidentRound(inp, chunk_len=c, chunks_per_slot=cps)
+        rnd.run()
+        torch.cuda.synchronize()
+        compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+        outs.append(rnd.o.cpu().numpy())
+    # reversed slot order in the merge: fold the same slots in reverse
+    rnd = rounds.ResidentRound(inp, chunk_len=512)
+    rnd.chunks()
+    rnd.candidates()
+    for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
+        t.copy_(t.flip(0))
+    rnd.merge()
+    torch.cuda.synchronize()
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+
+
+def test_empty_history_and_zero_lengths():
+    cfg = SMALL["c3_small"].with_(batch=4)
+    inp = wl.make_inputs(cfg)
+    # request 1 has no history at all, request 2 a single token
+    inp.hist_len = inp.hist_len.copy()
+    inp.hist_len[1] = 0
+    inp.hist_len[2] = 1
+    rnd = rounds.ResidentRound(inp)
+    rnd.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    # uniform empty history: every chunk call is a no-op, candidates alone
+    cfg0 = SMALL["c2_small"].with_(hist_len=0)
+    inp0 = wl.make_inputs(cfg0)
+    rnd0 = rounds.ResidentRound(inp0)
+    assert rnd0.n_chunks == 0
+    rnd0.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp0)
+    compare(cfg0, rnd0.o.cpu().numpy(), rnd0.lse.cpu().numpy(), o_ref, lse_ref)
+
+
+def test_merge_all_empty_and_slots_per_req():
+    cfg = SMALL["c2_small"]
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, chunk_len=1024)
+    rnd.chunks()
+    rnd.candidates()
+    torch.cuda.synchronize()
+    # request 0 folds only its first two slots, request 1 none at all
+    spr = torch.tensor([2, 0], dtype=torch.int32, device="cuda")
+    ss.ss_merge_states(rnd.problem, rnd.state, spr, rnd.o, rnd.lse)
+    torch.cuda.synchronize()
+    o = rnd.o.cpu().numpy()
+    lse = rnd.lse.cpu().numpy()
+    assert (o[1] == 0).all() and np.isneginf(lse[1]).all()
+    m, l, acc = oracle.chunk_slot_states(inp.q.float().numpy(), inp.hist_per_request("k"),
+                                         inp.hist_per_request("v"), inp.hist_len, 1024, 0, 2, 1, cfg.scale)
+    o_ref, lse_ref = oracle.merge_slots(m, l, acc)
+    assert np.abs(o[0] - o_ref[0]).max() <= 2e-3 and np.abs(lse[0] - lse_ref[0]).max() <= 2e-3
+
+
+def test_closed_forms_on_gpu():
+    """Q = 0 gives the mean of the visible values and lse = ln(#visible); a
+    planted needle key dominates its rows."""
+    cfg = SMALL["c2_small"]
+    inp = wl.make_inputs(cfg)
+    inp.q.zero_()
+    rnd = rounds.ResidentRound(inp)
+    rnd.run()
+    torch.cuda.synchronize()
+    lse = rnd.lse.cpu().numpy()
+    n = cfg.hist_len
+    want = np.log(n + np.arange(cfg.n_queries) + 1.0)
+    assert np.abs(lse - want[None, :, None]).max() <= 1e-4
+    o = rnd.o.cpu().numpy()
+    vh = inp.v_hist.float().numpy()
+    vc = inp.v_cand.float().numpy()
+    for b in range(cfg.batch):
+        for i in range(cfg.n_queries):
+            for h in range(0, cfg.n_q_heads, 5):
+                g = h // cfg.group
+                ref = (vh[b, g].sum(0) + vc[b, g, :i + 1].sum(0)) / (n + i + 1)
+                assert np.abs(o[b, i, h] - ref).max() <= 1e-4
+    # needle: one key in chunk 3 scores +30 for every row of KV head 1 of request 0
+    inp = wl.make_inputs(cfg)
+    u = torch.randn(cfg.head_dim, generator=torch.Generator().manual_seed(9))
+    u = u / u.norm()
+    inp.q[0, :, cfg.group:2 * cfg.group, :] = u.to(inp.q.dtype)
+    qrow = inp.q[0, 0, cfg.group].float()
+    t = 3 * cfg.chunk_len + 77
+    inp.k_hist[0, 1, t] = (30.0 / cfg.scale * qrow / qrow.dot(qrow)).to(inp.k_hist.dtype)
+    rnd = rounds.ResidentRound(inp)
+    rnd.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp, requests=[0], kv_heads=[1])
+    sel = rows_of(cfg, 0, 1)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref, sel)
+    assert np.abs(rnd.o.cpu().numpy()[0][:, sel[2]] - inp.v_hist[0, 1, t].float().numpy()).max() < 5e-3
+
+
+@pytest.mark.parametrize("n_buf", [1, 2, 3])
+def test_streamed_matches_resident_and_oracle(n_buf):
+    cfg = SMALL["c5_small"].with_(hist_len=8 * 256, chunk_len=256)
+    log(f"[streamed] n_buf {n_buf}")
+    inp = wl.make_inputs(cfg)
+    srd = rounds.StreamedRound(inp, n_buf=n_buf)
+    srd.run(record_timings=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, srd.o.cpu().numpy(), srd.lse.cpu().numpy(), o_ref, lse_ref)
+    rrd = rounds.ResidentRound(inp, chunk_len=256)
+    rrd.run()
+    torch.cuda.synchronize()
+    assert np.abs(srd.o.cpu().numpy() - rrd.o.cpu().numpy()).max() <= 1e-5
+    c0, c1, k0, k1 = ss.ss_stream_timings(srd.n_chunks)
+    for j in range(srd.n_chunks):
+        assert c0[j] <= c1[j] <= k0[j] + 1e-3 and k0[j] <= k1[j]     # compute starts after its chunk landed
+
+
+def test_invalid_call_enqueues_nothing():
+    cfg = SMALL["c2_small"]
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp)
+    rnd.state.m.fill_(7.0)
+    with pytest.raises(ss.SSError) as e:
+        ss.ss_verify_chunk(rnd.problem, rnd.q, rnd.hist_view, cfg.chunk_len, 0, rnd.n_chunks + 10, 1, rnd.state, 0)
+    assert e.value.code == ss.SS_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert (rnd.state.m == 7.0).all()
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled slices
+# ---------------------------------------------------------------------------
+
+FULL = ["c1_tiny_f32", "c2_qwen3_8b", "c3_internlm25_7b_ragged", "c4_tree_72b", "c5_streamed"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = C[name]
+    log(f"[full] {name}: generating inputs")
+    inp = wl.make_inputs(cfg)
+    log(f"[full] {name}: running")
+    rnd = rounds.StreamedRound(inp, n_buf=2) if cfg.streamed else rounds.ResidentRound(inp)
+    rnd.run()
+    torch.cuda.synchronize()
+    o = rnd.o.cpu().numpy()
+    lse = rnd.lse.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    if not cfg.streamed:
+        check_mask(rnd, inp)
+    rng = np.random.default_rng(cfg.seed)
+    picks = [(0, 0), (cfg.batch - 1, cfg.n_kv_heads - 1)]
+    picks.append((int(rng.integers(cfg.batch)), int(rng.integers(cfg.n_kv_heads))))
+    if cfg.ragged:
+        picks.append((int(np.argmax(inp.hist_len)), 2))
+        picks.append((int(np.argmin(inp.hist_len)), 5))
+    for b, g in picks:
+        log(f"[full] {name}: oracle slice b={b} g={g}")
+        o_ref, lse_ref = oracle_round(inp, requests=[b], kv_heads=[g])
+        compare(cfg, o, lse, o_ref, lse_ref, rows_of(cfg, b, g))
