@@ -98,7 +98,7 @@ struct MergeParams {
 constexpr int kValuRows = 32;
 
 // Whether the MFMA chunk kernel is built into this library.
-constexpr bool kMfmaChunkKernel = false;
+constexpr bool kMfmaChunkKernel = true;
 
 // Launchers (defined in the kernel translation units).
 hipError_t launch_chunk_valu(const ChunkParams& p, int dtype, int head_dim, hipStream_t stream);

@@ -37,6 +37,8 @@ SMALL = {
     "bf16_d64": C["c2_qwen3_8b"].with_(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64, hist_len=333,
                                        chunk_len=100),
     "bf16_small_rows": C["c2_qwen3_8b"].with_(batch=3, n_queries=2, hist_len=1000, chunk_len=256),
+    "bf16_rows16": C["c2_qwen3_8b"].with_(batch=3, n_queries=4, hist_len=2100, chunk_len=700),
+    "bf16_rows32_g8": C["c4_tree_72b"].with_(batch=2, n_queries=4, hist_len=1337, chunk_len=512),
 }
 
 
@@ -121,9 +123,18 @@ def test_chunk_slot_states(chunk_len, cps):
     assert (gl[empty] == 0).all() and (gacc[empty] == 0).all()
     full = ~empty
     tol = TOL[cfg.dtype]
-    assert np.abs(gm[full] - m[full]).max() <= tol
-    assert np.abs(gl[full] / l[full] - 1).max() <= tol
-    assert np.abs(gacc[full] / gl[full][:, None] - acc[full] / l[full][:, None]).max() <= tol
+    # A slot state is an intermediate: the MFMA path rounds each weight
+    # e^(s - m) to bf16 (relative error <= 2^-9) and uses the same rounded
+    # weights in acc and l, so the slot's normalised output acc / l moves by at
+    # most 2 * 2^-9 * max|V| (a weighted average whose weights move by 2^-9).
+    # The final O and lse are held to the 2e-3 bound elsewhere.
+    vmax = float(inp.v_hist.float().abs().max())
+    tol_norm = max(tol, 2 * 2 ** -9 * vmax) if cfg.dtype == "bf16" else tol
+    e_m = np.abs(gm[full] - m[full]).max()
+    e_l = np.abs(gl[full] / l[full] - 1).max()
+    e_a = np.abs(gacc[full] / gl[full][:, None] - acc[full] / l[full][:, None]).max()
+    log(f"  slot states: max|dm| {e_m:.2e}, max|dl/l| {e_l:.2e}, max|d(acc/l)| {e_a:.2e} (tol {tol_norm:.2e})")
+    assert e_m <= tol and e_l <= tol and e_a <= tol_norm
 
 
 def test_chunk_size_and_split_invariance():
