@@ -172,6 +172,28 @@ def cpu_baseline(cfg, budget_s=15.0):
             "query_tokens_per_s": slices / (cfg.batch * cfg.n_kv_heads) * cfg.batch * cfg.n_queries / done}
 
 
+def counters_pass(cfg):
+    """One calibration kernel of known traffic (torch.neg over 2^30 bytes of
+    bf16: reads 1 GiB, writes 1 GiB), then one step of the workload."""
+    src = torch.randn(1 << 29, device="cuda").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp)
+    del inp
+    torch.cuda.synchronize()
+    rnd.run()
+    torch.cuda.synchronize()
+    hist_len = np.full(cfg.batch, cfg.hist_len) if not cfg.ragged else rnd.hist_len.cpu().numpy()
+    print(json.dumps({"counters_pass": cfg.name, "calibration_bytes": 1 << 30,
+                      "chunk_kernel_algorithmic_bytes": chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)}),
+          flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +202,9 @@ def main():
     ap.add_argument("--workload", default="c2_qwen3_8b", choices=[k for k in wl.CONFIGS if not wl.CONFIGS[k].streamed])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="counter-collection pass: one plain elementwise copy of 1 GiB (the calibration kernel "
+                         "of known size), then one step of the workload; prints nothing else")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the verification path runs on a "
@@ -190,6 +215,9 @@ def main():
         sys.exit(2)
 
     cfg = wl.CONFIGS[args.workload]
+    if args.counters:
+        counters_pass(cfg)
+        return
     rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup)
     hist_b, cand_b = kv_bytes(cfg, hist_len)
     gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9

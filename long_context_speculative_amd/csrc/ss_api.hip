@@ -51,7 +51,8 @@ int32_t check_problem(const ss_problem_t* p) {
     if (p->batch > 65535) return fail(SS_ERR_UNSUPPORTED, "batch above 65535");
     const int64_t rows = (int64_t)p->n_queries * (p->n_q_heads / p->n_kv_heads);
     const int64_t row_blocks = (rows + kValuRows - 1) / kValuRows;
-    if ((int64_t)p->n_kv_heads * row_blocks > 65535) return fail(SS_ERR_UNSUPPORTED, "too many rows per request");
+    if ((int64_t)p->n_kv_heads * row_blocks > 65535 || (int64_t)p->n_kv_heads * cand_row_blocks((int)rows) > 65535)
+        return fail(SS_ERR_UNSUPPORTED, "too many rows per request");
     return SS_OK;
 }
 
@@ -238,7 +239,7 @@ extern "C" SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, cons
     c.m = out->m;
     c.l = out->l;
     c.slot = slot;
-    c.row_blocks = (c.rows + kValuRows - 1) / kValuRows;
+    c.row_blocks = cand_row_blocks(c.rows);
     hipError_t e = launch_candidates(c, problem->dtype, problem->head_dim, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SS_ERR_HIP, "candidate kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -104,6 +104,8 @@ constexpr bool kMfmaChunkKernel = true;
 hipError_t launch_chunk_valu(const ChunkParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_candidates(const CandParams& p, int dtype, int head_dim, hipStream_t stream);
+// Row blocks of the candidate kernel for `rows` rows per KV head.
+int cand_row_blocks(int rows);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 
 }  // namespace ssv

@@ -1,11 +1,10 @@
-// VALU kernels of libssverify: the fp32 / small-row chunk kernel, the masked
-// candidate kernel and the state merge.
+// VALU chunk kernel of libssverify: fp32 inputs, and bf16 shapes whose rows
+// do not fill a 16-row MFMA tile.
 //
 // SpecStream ("Resource-Efficient Speculative Decoding for Long-Context LLM
 // Serving"), section 4.2: per chunk, scores of the whole query group against
-// the chunk's keys, the chunk-local state of Eq. (7), merged across key tiles
-// by Eq. (8); the candidate region under its mask; the final merge and
-// O = a / l (Eq. 9).
+// the chunk's keys and the chunk-local state of Eq. (7), merged across key
+// tiles by Eq. (8).
 //
 // Layout of work: one work-group per (slot, KV head x row block, request).
 // A tile of 64 keys is staged in LDS once and read by every row of the block
@@ -184,94 +183,9 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(ChunkParams p) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void candidates_kernel(CandParams p) {
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    ValuSmem<D>& sm = *reinterpret_cast<ValuSmem<D>*>(smem_raw);
-    __shared__ uint64_t bits[64];
-    __shared__ int32_t par[64];
-
-    const int g = blockIdx.y / p.row_blocks;
-    const int rb = blockIdx.y % p.row_blocks;
-    const int b = blockIdx.z;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n = p.n_queries;
-    const int r0 = rb * kValuRows;
-    const int nr = min(kValuRows, p.rows - r0);
-
-    // Candidate visibility bits (causal, or tree ancestors built in order).
-    if (p.parents) {
-        if (threadIdx.x < n) par[threadIdx.x] = p.parents[(int64_t)b * n + threadIdx.x];
-        __syncthreads();
-        if (threadIdx.x == 0)
-            for (int i = 0; i < n; ++i) bits[i] = tree_bits_step(bits, i, par[i]);
-    } else if (threadIdx.x < n) {
-        bits[threadIdx.x] = chain_bits(threadIdx.x);
-    }
-    __syncthreads();
-    if (p.mask_out && g == 0 && rb == 0 && threadIdx.x < n) p.mask_out[(int64_t)b * n + threadIdx.x] = bits[threadIdx.x];
-
-    load_rows<T, D>(sm.q, static_cast<const T*>(p.q), b, g, r0, nr, p.n_queries, p.n_q_heads, p.group);
-    const int64_t base = (p.req_offset ? p.req_offset[b] : (int64_t)b * p.stride_b) + (int64_t)g * p.stride_h;
-    load_tile<T, D>(sm, static_cast<const T*>(p.k) + base, static_cast<const T*>(p.v) + base, p.stride_t, 0, n);
-    __syncthreads();
-
-#pragma unroll
-    for (int ri = 0; ri < kRowsPerWave; ++ri) {
-        const int rr = w + kWaves * ri;
-        if (rr < nr) {
-            const int r = r0 + rr;
-            const int i = r / p.group, h = g * p.group + r % p.group;
-            const bool visible = lane < n && ((bits[i] >> lane) & 1);
-            float m_run = -INFINITY, l_run = 0.f, acc[D / 64];
-#pragma unroll
-            for (int j = 0; j < D / 64; ++j) acc[j] = 0.f;
-            row_tile_update<D>(sm, rr, lane, w, visible, p.scale, n, m_run, l_run, acc);
-            const int64_t row = (((int64_t)p.slot * p.batch + b) * p.n_queries + i) * p.n_q_heads + h;
-            write_row_state<D>(p.m, p.l, p.acc, row, lane, m_run, l_run, acc);
-        }
-    }
-}
-
-// Eq. (8) over the slots of each row, then O = a / l and lse = m + ln l.
-__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
-    const int64_t n_rows = (int64_t)p.batch * p.n_queries * p.n_q_heads;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= n_rows * p.head_dim) return;
-    const int64_t row = idx / p.head_dim;
-    const int x = (int)(idx % p.head_dim);
-    const int b = (int)(row / ((int64_t)p.n_queries * p.n_q_heads));
-    int ns = p.n_slots;
-    if (p.slots_per_req) ns = min(max(p.slots_per_req[b], 0), p.n_slots);
-
-    float mx = -INFINITY;
-    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, p.m[s * n_rows + row]);
-    float lsum = 0.f, a = 0.f;
-    if (mx != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const float ms = p.m[s * n_rows + row];
-            if (ms != -INFINITY) {
-                const float f = exp2_hw((ms - mx) * kLog2e);
-                lsum = fmaf(f, p.l[s * n_rows + row], lsum);
-                a = fmaf(f, p.acc[(s * n_rows + row) * p.head_dim + x], a);
-            }
-        }
-    }
-    const bool seen = lsum > 0.f;
-    p.o[row * p.head_dim + x] = seen ? a / lsum : 0.f;
-    if (x == 0) p.lse[row] = seen ? mx + __builtin_amdgcn_logf(lsum) * kLn2 : -INFINITY;
-}
-
-template <typename T, int D>
 hipError_t launch_chunk_valu_t(const ChunkParams& p, hipStream_t stream) {
     dim3 grid(p.n_items, p.n_kv_heads * p.row_blocks, p.batch);
     hipLaunchKernelGGL((chunk_valu_kernel<T, D>), grid, dim3(kThreads), sizeof(ValuSmem<D>), stream, p);
-    return hipGetLastError();
-}
-
-template <typename T, int D>
-hipError_t launch_cand_t(const CandParams& p, hipStream_t stream) {
-    dim3 grid(1, p.n_kv_heads * p.row_blocks, p.batch);
-    hipLaunchKernelGGL((candidates_kernel<T, D>), grid, dim3(kThreads), sizeof(ValuSmem<D>), stream, p);
     return hipGetLastError();
 }
 
@@ -284,22 +198,6 @@ hipError_t launch_chunk_valu(const ChunkParams& p, int dtype, int head_dim, hipS
     }
     if (head_dim == 64) return launch_chunk_valu_t<uint16_t, 64>(p, stream);
     return launch_chunk_valu_t<uint16_t, 128>(p, stream);
-}
-
-hipError_t launch_candidates(const CandParams& p, int dtype, int head_dim, hipStream_t stream) {
-    if (dtype == SS_F32) {
-        if (head_dim == 64) return launch_cand_t<float, 64>(p, stream);
-        return launch_cand_t<float, 128>(p, stream);
-    }
-    if (head_dim == 64) return launch_cand_t<uint16_t, 64>(p, stream);
-    return launch_cand_t<uint16_t, 128>(p, stream);
-}
-
-hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
-    const int64_t n = (int64_t)p.batch * p.n_queries * p.n_q_heads * p.head_dim;
-    const int64_t blocks = (n + 255) / 256;
-    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
-    return hipGetLastError();
 }
 
 }  // namespace ssv
