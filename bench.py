@@ -38,8 +38,20 @@ from long_context_speculative_amd import rounds  # noqa: E402
 from long_context_speculative_amd import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-CHUNK_KERNEL_SOURCES = ["long_context_speculative_amd/csrc/ss_mfma.hip", "long_context_speculative_amd/csrc/ss_valu.hip",
-                        "long_context_speculative_amd/csrc/ss_common.h"]
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+CSRC = "long_context_speculative_amd/csrc/"
+
+
+def chunk_kernel_sources(cfg):
+    """Source files of the chunk kernel that serves cfg (mirrors the library's
+    engine choice)."""
+    if cfg.dtype != "bf16" or cfg.head_dim != 128 or cfg.rows < 16:
+        main = "ss_valu.hip"
+    elif cfg.rows <= 32:
+        main = "ss_mfma.hip"
+    else:
+        main = "ss_mfma_wide.hip"
+    return [CSRC + main, CSRC + "ss_common.h"]
 
 
 def kv_bytes(cfg, hist_len) -> tuple[int, int]:
@@ -56,31 +68,37 @@ def chunk_kernel_bytes(cfg, hist_len, n_slots) -> int:
     return hist + q + states
 
 
-def source_hash() -> str:
+def chunk_kernel_flops(cfg, hist_len) -> int:
+    """Algorithmic FLOPs of one chunk-kernel launch: S = Q K^T and O = P V,
+    2 * d FLOPs each per (query head, query, history key)."""
+    return 4 * cfg.n_q_heads * cfg.n_queries * cfg.head_dim * int(np.asarray(hist_len, dtype=np.int64).sum())
+
+
+def source_hash(cfg) -> str:
     h = hashlib.sha256()
-    for p in CHUNK_KERNEL_SOURCES:
+    for p in chunk_kernel_sources(cfg):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
+def read_traffic(cfg):
     """HBM bytes per chunk-kernel launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"chunk_kernel_{workload}_counters.md")
+    path = os.path.join(ROOT, "profiles", f"chunk_kernel_{cfg.name}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(cfg):
         return None
     return float(m_bytes.group(1))
 
 
-def time_resident(cfg, steps, warmup):
+def time_resident(cfg, steps, warmup, cps=1):
     inp = wl.make_inputs(cfg)
-    rnd = rounds.ResidentRound(inp)
+    rnd = rounds.ResidentRound(inp, chunks_per_slot=cps)
     del inp
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -200,6 +218,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2_qwen3_8b", choices=[k for k in wl.CONFIGS if not wl.CONFIGS[k].streamed])
+    ap.add_argument("--chunks-per-slot", type=int, default=0,
+                    help="chunks merged per state slot (0: 1 for HBM-bound shapes, 4 for wide-row shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true")
     ap.add_argument("--counters", action="store_true",
@@ -218,12 +238,26 @@ def main():
     if args.counters:
         counters_pass(cfg)
         return
-    rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup)
+    cps = args.chunks_per_slot or (4 if cfg.rows > 32 else 1)
+    rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup, cps)
     hist_b, cand_b = kv_bytes(cfg, hist_len)
     gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9
     alg = chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)
-    achieved = alg / (ms_chunk * 1e-3) / 1e9
-    traffic = read_traffic(cfg.name)
+    traffic = read_traffic(cfg)
+    if cfg.rows > 32:
+        # wide row groups: the chunk kernel is bound by the matrix cores
+        flops = chunk_kernel_flops(cfg, hist_len)
+        roof = {"bound": "mfma", "achieved": round(flops / (ms_chunk * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / (ms_chunk * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None if traffic is None else int(traffic), "kernel": "ss_verify_chunk",
+                "ms_per_launch": round(ms_chunk, 4), "algorithmic_flops_per_launch": flops,
+                "algorithmic_bytes_per_launch": alg,
+                "hbm_GBps_algorithmic": round(alg / (ms_chunk * 1e-3) / 1e9, 2)}
+    else:
+        achieved = alg / (ms_chunk * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic),
+                "kernel": "ss_verify_chunk", "ms_per_launch": round(ms_chunk, 4), "algorithmic_bytes_per_launch": alg}
     del rnd
     torch.cuda.empty_cache()
 
@@ -243,14 +277,11 @@ def main():
         "config": {"workload": f"{cfg.name}: B={cfg.batch}, Hq={cfg.n_q_heads}, Hkv={cfg.n_kv_heads}, "
                                f"d={cfg.head_dim}, history={cfg.hist_len} ({'ragged' if cfg.ragged else 'uniform'}),"
                                f" chunk={cfg.chunk_len}, q={cfg.n_queries}, mask={cfg.mask}",
-                   "batch": cfg.batch, "history_tokens": cfg.hist_len, "queries": cfg.n_queries},
+                   "batch": cfg.batch, "history_tokens": cfg.hist_len, "queries": cfg.n_queries,
+                   "chunks_per_slot": cps},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(cfg.batch * cfg.n_queries / (ms_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if traffic is None else int(traffic),
-                     "kernel": "ss_verify_chunk", "ms_per_launch": round(ms_chunk, 4),
-                     "algorithmic_bytes_per_launch": alg},
+        "roofline": roof,
     }
     if not args.no_streamed:
         out["streamed"] = time_streamed(wl.CONFIGS["c5_streamed"])

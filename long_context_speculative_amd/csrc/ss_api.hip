@@ -79,11 +79,16 @@ int32_t check_state(const ss_state_t* s, const char* name) {
     return SS_OK;
 }
 
-// Which chunk kernel serves a problem: MFMA bf16 when the rows of one KV head
-// fill a 16-row tile and fit two, the VALU kernel otherwise.
-bool use_mfma(const ss_problem_t* p) {
+// Which chunk kernel serves a problem. bf16 with head_dim 128: the MFMA
+// kernel when the rows of one KV head fill one or two 16-row tiles, the
+// wide-row MFMA kernel above 32 rows. Everything else (fp32, fewer than 16
+// rows, head_dim 64) runs on the VALU kernel.
+enum class ChunkEngine { kValu, kMfma, kMfmaWide };
+
+ChunkEngine chunk_engine(const ss_problem_t* p) {
     const int rows = p->n_queries * (p->n_q_heads / p->n_kv_heads);
-    return p->dtype == SS_BF16 && rows >= 16 && rows <= 32 && p->head_dim == 128 && kMfmaChunkKernel;
+    if (p->dtype != SS_BF16 || p->head_dim != 128 || rows < 16) return ChunkEngine::kValu;
+    return rows <= 32 ? ChunkEngine::kMfma : ChunkEngine::kMfmaWide;
 }
 
 int32_t validate_chunk(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist, int32_t chunk_len,
@@ -141,8 +146,11 @@ ChunkParams make_chunk_params(const ss_problem_t* p, const void* q, const ss_kv_
 }
 
 hipError_t enqueue_chunk(const ss_problem_t* p, const ChunkParams& c, hipStream_t stream) {
-    if (use_mfma(p)) return launch_chunk_mfma(c, p->head_dim, stream);
-    return launch_chunk_valu(c, p->dtype, p->head_dim, stream);
+    switch (chunk_engine(p)) {
+        case ChunkEngine::kMfma: return launch_chunk_mfma(c, p->head_dim, stream);
+        case ChunkEngine::kMfmaWide: return launch_chunk_mfma_wide(c, p->head_dim, stream);
+        default: return launch_chunk_valu(c, p->dtype, p->head_dim, stream);
+    }
 }
 
 // ---------------------------------------------------------------------------

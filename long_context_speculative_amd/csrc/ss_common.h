@@ -97,12 +97,10 @@ struct MergeParams {
 // Rows per work-group in the VALU kernels.
 constexpr int kValuRows = 32;
 
-// Whether the MFMA chunk kernel is built into this library.
-constexpr bool kMfmaChunkKernel = true;
-
 // Launchers (defined in the kernel translation units).
 hipError_t launch_chunk_valu(const ChunkParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_chunk_mfma_wide(const ChunkParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_candidates(const CandParams& p, int dtype, int head_dim, hipStream_t stream);
 // Row blocks of the candidate kernel for `rows` rows per KV head.
 int cand_row_blocks(int rows);

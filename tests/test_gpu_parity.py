@@ -39,6 +39,13 @@ SMALL = {
     "bf16_small_rows": C["c2_qwen3_8b"].with_(batch=3, n_queries=2, hist_len=1000, chunk_len=256),
     "bf16_rows16": C["c2_qwen3_8b"].with_(batch=3, n_queries=4, hist_len=2100, chunk_len=700),
     "bf16_rows32_g8": C["c4_tree_72b"].with_(batch=2, n_queries=4, hist_len=1337, chunk_len=512),
+    # wide-row MFMA kernel: one wave (64 rows), two waves, four with one idle,
+    # two row groups with the second mostly idle
+    "wide_r64": C["c2_qwen3_8b"].with_(batch=2, n_queries=16, hist_len=1500, chunk_len=512),
+    "wide_r96_ragged": C["c3_internlm25_7b_ragged"].with_(batch=5, n_queries=24, hist_len=2000, ragged_lo=1,
+                                                           chunk_len=300),
+    "wide_r192_tree": C["c4_tree_72b"].with_(batch=2, n_queries=24, hist_len=999, chunk_len=256),
+    "wide_r320_tree": C["c4_tree_72b"].with_(batch=1, n_queries=40, hist_len=1200, chunk_len=1000),
 }
 
 
