@@ -190,7 +190,7 @@ def cpu_baseline(cfg, budget_s=15.0):
             "query_tokens_per_s": slices / (cfg.batch * cfg.n_kv_heads) * cfg.batch * cfg.n_queries / done}
 
 
-def counters_pass(cfg):
+def counters_pass(cfg, cps=1):
     """One calibration kernel of known traffic (torch.neg over 2^30 bytes of
     bf16: reads 1 GiB, writes 1 GiB), then one step of the workload."""
     src = torch.randn(1 << 29, device="cuda").to(torch.bfloat16)
@@ -201,7 +201,7 @@ def counters_pass(cfg):
     del src, dst
     torch.cuda.empty_cache()
     inp = wl.make_inputs(cfg)
-    rnd = rounds.ResidentRound(inp)
+    rnd = rounds.ResidentRound(inp, chunks_per_slot=cps)
     del inp
     torch.cuda.synchronize()
     rnd.run()
@@ -235,10 +235,10 @@ def main():
         sys.exit(2)
 
     cfg = wl.CONFIGS[args.workload]
-    if args.counters:
-        counters_pass(cfg)
-        return
     cps = args.chunks_per_slot or (4 if cfg.rows > 32 else 1)
+    if args.counters:
+        counters_pass(cfg, cps)
+        return
     rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup, cps)
     hist_b, cand_b = kv_bytes(cfg, hist_len)
     gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9

@@ -5,16 +5,26 @@
 // Serving"), section 4.2: one history chunk serves the whole query group; its
 // local state (Eq. 7) is merged tile by tile (Eq. 8).
 //
-// With hundreds of rows per KV head the work is bound by the matrix cores,
-// not by HBM: every key feeds 512 rows. A work-group of NW waves owns 64*NW
-// rows (each wave 64 rows = four 16-row MFMA tiles, with its Q^T fragments
-// and its O^T accumulator in registers). Key tiles of 32 are staged once in
-// LDS per work-group, double-buffered, and read by every wave: K row-major
-// (A operand of S^T = K Q^T), V transposed to key-contiguous rows (A operand
-// of O^T = V^T P^T). Row groups beyond the first re-read the chunk; the
-// launch places all row groups of one (slot, KV head, request) on the same
-// XCD one after another (work-group ids 8 apart), so the re-read is served by
-// that XCD's L2.
+// With hundreds of rows per KV head the work is bound by the matrix cores and
+// the softmax arithmetic, not by HBM: every key feeds 512 rows. Layout:
+//   - a work-group of NW waves owns 32*NW rows; each wave holds 32 rows (two
+//     16-row MFMA tiles) with its Q^T fragments and O^T accumulator in
+//     registers, small enough for two waves per SIMD, so one wave's softmax
+//     overlaps the other's matrix work;
+//   - key tiles of 32 are copied once per work-group into LDS, K and V both
+//     in their natural [key][feature] layout (16-byte row pad), double
+//     buffered, loads issued two tiles ahead;
+//   - S^T = K Q^T reads K fragments with 16-byte LDS reads; O^T = V^T P^T
+//     reads V^T fragments with the transposing LDS read ds_read_b64_tr_b16;
+//   - l (the softmax denominator) comes out of the same MFMA as O^T through
+//     an all-ones A operand, so it sums exactly the bf16 weights that enter
+//     the numerator;
+//   - the score scale is folded into the exponent (one FMA per score), and the
+//     running maximum is moved only when a row's maximum grows by more than
+//     2^8 over it (weights then stay <= 256; the rescale is rare);
+//   - row groups beyond the first re-read the chunk; all row groups of one
+//     (slot, KV head, request) are placed on the same XCD (work-group ids 8
+//     apart, dispatched back to back) so the re-read hits that XCD's L2.
 
 #include "ss_common.h"
 
@@ -24,28 +34,35 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int kTile = 32;       // keys per iteration
-constexpr int kKRow = D + 8;    // bf16 per staged K row (16-byte pad)
-constexpr int kVtRow = 36;      // bf16 per transposed V row (32 keys + 4 pad)
-constexpr int kRT = 4;          // 16-row tiles per wave (64 rows)
+constexpr int kRow = D + 8;     // bf16 per staged K/V row (16-byte pad)
+constexpr int kRT = 2;          // 16-row tiles per wave (32 rows)
 constexpr int kNS = D / 32;     // 32-feature steps of S = K Q^T
 constexpr int kNXT = D / 16;    // 16-feature tiles of O^T
+constexpr float kGrowLog2 = 8.f;  // rescale threshold (log2 units)
 
 struct WideSmem {
-    uint16_t k[2][kTile][kKRow];
-    uint16_t vt[2][D][kVtRow];
+    uint16_t k[2][kTile][kRow];
+    uint16_t v[2][kTile][kRow];
 };
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+__device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
+}
+
 template <int NW>
-__global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_wide_kernel(ChunkParams p, int row_groups) {
+__global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams p, int row_groups) {
     constexpr int T = 64 * NW;
-    constexpr int kUnits = 256 / T;  // cooperative load units per thread (4 loads of 16 bytes each)
+    constexpr int kPieces = kTile * (D / 8);   // 16-byte pieces per K (or V) tile
+    constexpr int kPer = kPieces / T;          // pieces of K and of V per thread
+    static_assert(kPieces % T == 0, "tile pieces must divide evenly");
     __shared__ WideSmem sm;
 
     // Work-group -> (slot, row group): row groups of one slot are 8 ids apart.
@@ -71,10 +88,9 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_wide_kernel(ChunkParams
     const int64_t st = p.stride_t;
     const int sti = (int)st;
 
-    const int row0 = rg * 64 * NW + 64 * w;  // first row of this wave
+    const int row0 = rg * 32 * NW + 32 * w;  // first row of this wave
     const bool active = row0 < p.rows;
 
-    // Q^T fragments of the wave's 64 rows.
     bf16x8 qf[kRT][kNS];
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
@@ -90,163 +106,154 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_wide_kernel(ChunkParams
         }
     }
 
-    floatx4 o[kNXT][kRT];
-#pragma unroll
-    for (int xt = 0; xt < kNXT; ++xt)
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) o[xt][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float m_run[kRT], l_run[kRT];
+    floatx4 o[kNXT][kRT], ol[kRT];  // O^T accumulators and the row-sum tile
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
-        m_run[rt] = -INFINITY;
-        l_run[rt] = 0.f;
+        ol[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int xt = 0; xt < kNXT; ++xt) o[xt][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
+    float m_run[kRT];  // reference maximum of c-scaled (log2) scores per row
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) m_run[rt] = -INFINITY;
     const float c = p.scale * kLog2e;
+    const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
     const int n_tiles = (int)((t1 - t0 + kTile - 1) / kTile);
 
-    // Cooperative staging. Unit u < 128: V keys 4*(u/16)..+3, features
-    // 8*(u%16)..+7; unit u >= 128: the same for K. Keys past the range are
-    // clamped to its last key (finite values; their scores are masked).
-    u32x4 pre_a[kUnits][4], pre_b[kUnits][4];
-    auto fetch = [&](int64_t tk, u32x4(&pre)[kUnits][4]) {
+    // Staging: thread tid copies K and V pieces u = tid + j*T (key u / 16,
+    // features 8*(u % 16) .. +7). Keys past the range are clamped to its last
+    // key (finite values; their scores are masked).
+    u32x4 pa[2][kPer], pb[2][kPer];
+    auto fetch = [&](int64_t tk, u32x4(&pre)[2][kPer]) {
         const int last = (int)min((int64_t)kTile, t1 - tk) - 1;
+        const uint16_t* kb = kp + tk * st;
+        const uint16_t* vb = vp + tk * st;
 #pragma unroll
-        for (int j = 0; j < kUnits; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int u = tid + j * T;
-            const int uu = u & 127;
-            const int kg = uu >> 4, piece = uu & 15;
-            const uint16_t* src = (u < 128 ? vp : kp) + tk * st + 8 * piece;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pre[j][e] = *reinterpret_cast<const u32x4*>(src + min(4 * kg + e, last) * sti);
+            const int off = min(u >> 4, last) * sti + 8 * (u & 15);
+            pre[0][j] = *reinterpret_cast<const u32x4*>(kb + off);
+            pre[1][j] = *reinterpret_cast<const u32x4*>(vb + off);
         }
     };
-    auto stage = [&](int buf, const u32x4(&pre)[kUnits][4]) {
+    auto stage = [&](int buf, const u32x4(&pre)[2][kPer]) {
 #pragma unroll
-        for (int j = 0; j < kUnits; ++j) {
+        for (int j = 0; j < kPer; ++j) {
             const int u = tid + j * T;
-            const int uu = u & 127;
-            const int kg = uu >> 4, piece = uu & 15;
-            if (u < 128) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t d0 = pre[j][0][i], d1 = pre[j][1][i], d2 = pre[j][2][i], d3 = pre[j][3][i];
-                    const u32x2 lo{(d0 & 0xffffu) | (d1 << 16), (d2 & 0xffffu) | (d3 << 16)};
-                    const u32x2 hi{(d0 >> 16) | (d1 & 0xffff0000u), (d2 >> 16) | (d3 & 0xffff0000u)};
-                    const int xx = 8 * piece + 2 * i;
-                    *reinterpret_cast<u32x2*>(&sm.vt[buf][xx][4 * kg]) = lo;
-                    *reinterpret_cast<u32x2*>(&sm.vt[buf][xx + 1][4 * kg]) = hi;
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) *reinterpret_cast<u32x4*>(&sm.k[buf][4 * kg + e][8 * piece]) = pre[j][e];
-            }
+            *reinterpret_cast<u32x4*>(&sm.k[buf][u >> 4][8 * (u & 15)]) = pre[0][j];
+            *reinterpret_cast<u32x4*>(&sm.v[buf][u >> 4][8 * (u & 15)]) = pre[1][j];
         }
     };
 
-    // Key tiles go HBM -> registers two tiles ahead, registers -> LDS one
-    // tile ahead (double-buffered LDS, two register sets), so a tile's loads
-    // have two iterations to land.
     auto process = [&](const int cur, const int64_t tk) {
         if (!active) return;
-        // S^T = K Q^T over the tile's 32 keys and the wave's 64 rows.
+        // S^T = K Q^T (raw dot products)
         floatx4 sc[2][kRT];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int rt = 0; rt < kRT; ++rt) sc[kt][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < kNS; ++k) {
+        for (int k = 0; k < kNS; ++k)
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
                 const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[cur][16 * kt + l16][32 * k + 8 * q4]));
 #pragma unroll
                 for (int rt = 0; rt < kRT; ++rt)
                     sc[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][k], sc[kt][rt], 0, 0, 0);
             }
-        }
 
-        // Online softmax in base 2 (Eq. 7-8); rescale only when a max grows.
+        // Keys past the range (last tile only) never enter the max or the sums.
         const int valid = (int)min((int64_t)kTile, t1 - tk);
-        bool grow = false;
-        float alpha[kRT];
-#pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-            float mx = -INFINITY;
+        if (valid < kTile) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int key = 16 * kt + 4 * q4 + j;
-                    const float v = key < valid ? sc[kt][rt][j] * c : -INFINITY;
-                    sc[kt][rt][j] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (16 * kt + 4 * q4 + j >= valid) sc[kt][rt][j] = -INFINITY;
+        }
+
+        // Row maxima (c > 0, so the max of raw scores picks the max of scaled ones).
+        bool grow = false;
+        float m_cand[kRT];
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) {
+            float mx = fmaxf(fmaxf(fmaxf(sc[0][rt][0], sc[0][rt][1]), fmaxf(sc[0][rt][2], sc[0][rt][3])),
+                             fmaxf(fmaxf(sc[1][rt][0], sc[1][rt][1]), fmaxf(sc[1][rt][2], sc[1][rt][3])));
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[rt], mx);
-            alpha[rt] = (m_run[rt] == -INFINITY) ? 0.f : exp2_hw(m_run[rt] - m_new);
-            grow |= m_new > m_run[rt];
-            m_run[rt] = m_new;
+            m_cand[rt] = mx * c;
+            grow |= m_cand[rt] > m_run[rt] + kGrowLog2;
         }
         if (__ballot(grow)) {
+            // Move the reference maximum (Eq. 8 with the accumulated state).
 #pragma unroll
             for (int rt = 0; rt < kRT; ++rt) {
-                l_run[rt] *= alpha[rt];
+                const float m_new = fmaxf(m_run[rt], m_cand[rt]);
+                const float alpha = (m_run[rt] == -INFINITY) ? 0.f : exp2_hw(m_run[rt] - m_new);
+                m_run[rt] = m_new;
+                ol[rt] *= alpha;
 #pragma unroll
-                for (int xt = 0; xt < kNXT; ++xt) o[xt][rt] *= alpha[rt];
+                for (int xt = 0; xt < kNXT; ++xt) o[xt][rt] *= alpha;
             }
         }
+
+        // P = 2^(c*S - m) in bf16: slot j of a lane = key 4*q4 + j (kt = 0),
+        // slot 4 + j = key 16 + 4*q4 + j (kt = 1).
         bf16x8 pf[kRT];
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
-            float ls = 0.f;
+            const float nm = -m_run[rt];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const __bf16 pb = (__bf16)exp2_hw(sc[kt][rt][j] - m_run[rt]);
-                    pf[rt][4 * kt + j] = pb;
-                    ls += (float)pb;
-                }
-            l_run[rt] += ls;
+                for (int j = 0; j < 4; ++j) pf[rt][4 * kt + j] = (__bf16)exp2_hw(fmaf(sc[kt][rt][j], c, nm));
         }
 
-        // O^T += V^T P^T
+        // O^T += V^T P^T and l += 1^T P^T. For the transposing read, lane
+        // (group q4, index l16) points at features 16*xt + 4*(l16 % 4) .. +3
+        // of key 4*q4 + l16 / 4 (and of key 16 + ...); it receives feature
+        // 16*xt + l16 of keys 4*q4 .. +3 (and 16 + 4*q4 .. +3): the keys of
+        // the P slots it holds.
+        const uint16_t* vrow0 = &sm.v[cur][4 * q4 + (l16 >> 2)][4 * (l16 & 3)];
+        const uint16_t* vrow1 = vrow0 + 16 * kRow;
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) ol[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[rt], ol[rt], 0, 0, 0);
 #pragma unroll
         for (int xt = 0; xt < kNXT; ++xt) {
-            const uint16_t* row = sm.vt[cur][16 * xt + l16];
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(row + 4 * q4);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16 + 4 * q4);
-            const bf16x8 a = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+            const s16x4 lo = lds_read_tr(vrow0 + 16 * xt);
+            const s16x4 hi = lds_read_tr(vrow1 + 16 * xt);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int rt = 0; rt < kRT; ++rt)
                 o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[xt][rt], 0, 0, 0);
         }
     };
 
+    // Tiles go HBM -> registers two tiles ahead and registers -> LDS one tile
+    // ahead (two register sets, double-buffered LDS).
     if (n_tiles > 0) {
-        fetch(t0, pre_a);
-        stage(0, pre_a);
+        fetch(t0, pa);
+        stage(0, pa);
     }
-    if (n_tiles > 1) fetch(t0 + kTile, pre_b);
+    if (n_tiles > 1) fetch(t0 + kTile, pb);
     __syncthreads();
     for (int t = 0; t < n_tiles; t += 2) {
         const int64_t tk = t0 + (int64_t)kTile * t;
-        if (t + 2 < n_tiles) fetch(tk + 2 * kTile, pre_a);
+        if (t + 2 < n_tiles) fetch(tk + 2 * kTile, pa);
         process(0, tk);
-        if (t + 1 < n_tiles) stage(1, pre_b);
+        if (t + 1 < n_tiles) stage(1, pb);
         __syncthreads();
         if (t + 1 >= n_tiles) break;
-        if (t + 3 < n_tiles) fetch(tk + 3 * kTile, pre_b);
+        if (t + 3 < n_tiles) fetch(tk + 3 * kTile, pb);
         process(1, tk + kTile);
-        if (t + 2 < n_tiles) stage(0, pre_a);
+        if (t + 2 < n_tiles) stage(0, pa);
         __syncthreads();
     }
 
     if (!active) return;
-#pragma unroll
-    for (int rt = 0; rt < kRT; ++rt) {
-        l_run[rt] += __shfl_xor(l_run[rt], 16);
-        l_run[rt] += __shfl_xor(l_run[rt], 32);
-    }
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
         const int r = row0 + 16 * rt + l16;
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_wide_kernel(ChunkParams
         const int64_t row = (((int64_t)(p.slot_begin + s) * p.batch + b) * p.n_queries + i) * p.n_q_heads + h;
         if (q4 == 0) {
             p.m[row] = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
-            p.l[row] = l_run[rt];
+            p.l[row] = ol[rt][0];
         }
 #pragma unroll
         for (int xt = 0; xt < kNXT; ++xt)
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(64 * NW, 1) void chunk_mfma_wide_kernel(ChunkParams
 
 template <int NW>
 hipError_t launch_wide_t(const ChunkParams& p, hipStream_t stream) {
-    const int row_groups = (p.rows + 64 * NW - 1) / (64 * NW);
+    const int row_groups = (p.rows + 32 * NW - 1) / (32 * NW);
     const int64_t gx = (int64_t)((p.n_items + 7) / 8) * 8 * row_groups;
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     dim3 grid((unsigned)gx, p.n_kv_heads, p.batch);
@@ -277,11 +284,10 @@ hipError_t launch_wide_t(const ChunkParams& p, hipStream_t stream) {
 
 hipError_t launch_chunk_mfma_wide(const ChunkParams& p, int head_dim, hipStream_t stream) {
     if (head_dim != D || p.rows <= 32) return hipErrorInvalidValue;
-    const int waves = (p.rows + 63) / 64;
-    // Up to 128 rows: two waves (for 33..64 rows the second wave only helps
-    // stage tiles); more rows: four waves per row group.
-    if (waves >= 3) return launch_wide_t<4>(p, stream);
-    return launch_wide_t<2>(p, stream);
+    // 32 rows per wave: up to 128 rows in one group of four waves, more rows
+    // in groups of eight waves (two per SIMD).
+    if (p.rows <= 128) return launch_wide_t<4>(p, stream);
+    return launch_wide_t<8>(p, stream);
 }
 
 }  // namespace ssv
