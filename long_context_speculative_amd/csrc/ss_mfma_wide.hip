@@ -12,8 +12,12 @@
 //     registers, small enough for two waves per SIMD, so one wave's softmax
 //     overlaps the other's matrix work;
 //   - key tiles of 32 are copied once per work-group into LDS, K and V both
-//     in their natural [key][feature] layout (16-byte row pad), double
-//     buffered, loads issued two tiles ahead;
+//     in their natural [key][feature] layout (rows padded so the reads are
+//     free of bank conflicts), in a ring of three buffers, loads issued three
+//     tiles ahead;
+//   - the loop is software-pipelined: the S products of tile t+1 are issued
+//     next to the softmax and P V of tile t, so matrix and vector work of one
+//     wave overlap, on top of the two waves per SIMD;
 //   - S^T = K Q^T reads K fragments with 16-byte LDS reads; O^T = V^T P^T
 //     reads V^T fragments with the transposing LDS read ds_read_b64_tr_b16;
 //   - l (the softmax denominator) comes out of the same MFMA as O^T through
@@ -25,6 +29,8 @@
 //   - row groups beyond the first re-read the chunk; all row groups of one
 //     (slot, KV head, request) are placed on the same XCD (work-group ids 8
 //     apart, dispatched back to back) so the re-read hits that XCD's L2.
+
+#include <type_traits>
 
 #include "ss_common.h"
 
@@ -38,15 +44,16 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int kTile = 32;       // keys per iteration
-constexpr int kRow = D + 8;     // bf16 per staged K/V row (16-byte pad)
+constexpr int kRow = D + 8;     // bf16 per staged K row (16-byte pad: 16-byte reads of 16 rows hit 64 banks)
+constexpr int kVRow = D + 16;   // bf16 per staged V row (32-byte pad: 8-byte transposing reads of 8 rows hit 64 banks)
 constexpr int kRT = 2;          // 16-row tiles per wave (32 rows)
 constexpr int kNS = D / 32;     // 32-feature steps of S = K Q^T
 constexpr int kNXT = D / 16;    // 16-feature tiles of O^T
 constexpr float kGrowLog2 = 8.f;  // rescale threshold (log2 units)
 
 struct WideSmem {
-    uint16_t k[2][kTile][kRow];
-    uint16_t v[2][kTile][kRow];
+    uint16_t k[3][kTile][kRow];
+    uint16_t v[3][kTile][kVRow];
 };
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -145,10 +152,8 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
         }
     };
 
-    auto process = [&](const int cur, const int64_t tk) {
-        if (!active) return;
-        // S^T = K Q^T (raw dot products)
-        floatx4 sc[2][kRT];
+    // S^T = K Q^T (raw dot products) of the tile in LDS buffer buf.
+    auto qk = [&](const int buf, const int /*t*/, floatx4(&sc)[2][kRT]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -157,41 +162,34 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
         for (int k = 0; k < kNS; ++k)
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
-                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[cur][16 * kt + l16][32 * k + 8 * q4]));
+                const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[buf][16 * kt + l16][32 * k + 8 * q4]));
 #pragma unroll
                 for (int rt = 0; rt < kRT; ++rt)
                     sc[kt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[rt][k], sc[kt][rt], 0, 0, 0);
             }
-
-        // Keys past the range (last tile only) never enter the max or the sums.
-        const int valid = (int)min((int64_t)kTile, t1 - tk);
-        if (valid < kTile) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (16 * kt + 4 * q4 + j >= valid) sc[kt][rt][j] = -INFINITY;
-        }
-
-        // Row maxima (c > 0, so the max of raw scores picks the max of scaled ones).
-        bool grow = false;
-        float m_cand[kRT];
+    };
+    // Row maxima of a tile, in c-scaled log2 units (c > 0, so the max of raw
+    // scores picks the max of scaled ones).
+    auto row_max = [&](const floatx4(&sc)[2][kRT], float(&mc)[kRT]) {
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
             float mx = fmaxf(fmaxf(fmaxf(sc[0][rt][0], sc[0][rt][1]), fmaxf(sc[0][rt][2], sc[0][rt][3])),
                              fmaxf(fmaxf(sc[1][rt][0], sc[1][rt][1]), fmaxf(sc[1][rt][2], sc[1][rt][3])));
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            m_cand[rt] = mx * c;
-            grow |= m_cand[rt] > m_run[rt] + kGrowLog2;
+            mc[rt] = mx * c;
         }
+    };
+    // Moves the reference maximum when some row's tile maximum exceeds it by
+    // more than 2^8, rescaling the accumulated state (Eq. 8).
+    auto rescale = [&](const float(&mc)[kRT]) {
+        bool grow = false;
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) grow |= mc[rt] > m_run[rt] + kGrowLog2;
         if (__ballot(grow)) {
-            // Move the reference maximum (Eq. 8 with the accumulated state).
 #pragma unroll
             for (int rt = 0; rt < kRT; ++rt) {
-                const float m_new = fmaxf(m_run[rt], m_cand[rt]);
+                const float m_new = fmaxf(m_run[rt], mc[rt]);
                 const float alpha = (m_run[rt] == -INFINITY) ? 0.f : exp2_hw(m_run[rt] - m_new);
                 m_run[rt] = m_new;
                 ol[rt] *= alpha;
@@ -199,9 +197,14 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
                 for (int xt = 0; xt < kNXT; ++xt) o[xt][rt] *= alpha;
             }
         }
-
-        // P = 2^(c*S - m) in bf16: slot j of a lane = key 4*q4 + j (kt = 0),
-        // slot 4 + j = key 16 + 4*q4 + j (kt = 1).
+    };
+    // P = 2^(c*S - m) in bf16 (slot j of a lane = key 4*q4 + j, slot 4 + j =
+    // key 16 + 4*q4 + j), then O^T += V^T P^T and l += 1^T P^T from LDS
+    // buffer buf. For the transposing read, lane (group q4, index l16) points
+    // at features 16*xt + 4*(l16 % 4) .. +3 of key 4*q4 + l16 / 4 (and of
+    // key 16 + ...); it receives feature 16*xt + l16 of keys 4*q4 .. +3 (and
+    // 16 + 4*q4 .. +3): the keys of the P slots it holds.
+    auto softmax_pv = [&](const int buf, const floatx4(&sc)[2][kRT]) {
         bf16x8 pf[kRT];
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
@@ -211,14 +214,8 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
 #pragma unroll
                 for (int j = 0; j < 4; ++j) pf[rt][4 * kt + j] = (__bf16)exp2_hw(fmaf(sc[kt][rt][j], c, nm));
         }
-
-        // O^T += V^T P^T and l += 1^T P^T. For the transposing read, lane
-        // (group q4, index l16) points at features 16*xt + 4*(l16 % 4) .. +3
-        // of key 4*q4 + l16 / 4 (and of key 16 + ...); it receives feature
-        // 16*xt + l16 of keys 4*q4 .. +3 (and 16 + 4*q4 .. +3): the keys of
-        // the P slots it holds.
-        const uint16_t* vrow0 = &sm.v[cur][4 * q4 + (l16 >> 2)][4 * (l16 & 3)];
-        const uint16_t* vrow1 = vrow0 + 16 * kRow;
+        const uint16_t* vrow0 = &sm.v[buf][4 * q4 + (l16 >> 2)][4 * (l16 & 3)];
+        const uint16_t* vrow1 = vrow0 + 16 * kVRow;
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) ol[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[rt], ol[rt], 0, 0, 0);
 #pragma unroll
@@ -232,25 +229,89 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
         }
     };
 
-    // Tiles go HBM -> registers two tiles ahead and registers -> LDS one tile
-    // ahead (two register sets, double-buffered LDS).
+    // Software pipeline over the key tiles. Tiles 0 .. n_full-1 hold 32 keys;
+    // a last partial tile (the tail) is handled after the loop, so the loop
+    // body needs no masking and has no branch: the scheduler can interleave
+    // the S(t+1) products with the softmax of tile t.
+    //
+    // At the top of iteration t: LDS buffers t%3 and (t+1)%3 hold tiles t and
+    // t+1, sc_cur holds S(t) with the reference maximum already covering it,
+    // and one register set holds tile t+2 (loads in flight). Iteration t loads
+    // tile t+3 into the other set, forms S(t+1), the softmax and P V of tile
+    // t, the maxima of S(t+1), stages tile t+2, then (after the branch-free
+    // part) moves the reference maximum for tile t+1. Tile indices past the
+    // last tile are clamped to it: their loads and staging are harmless
+    // (the buffer they land in is not read again).
+    const int n_full = (int)((t1 - t0) / kTile);
+    const bool has_tail = (t1 - t0) % kTile != 0;
+    auto tile_start = [&](int t) { return t0 + (int64_t)kTile * min(t, n_tiles - 1); };
+    auto next_buf = [](int bi) { return bi == 2 ? 0 : bi + 1; };
+
+    floatx4 sc_a[2][kRT], sc_b[2][kRT];
+    float mc[kRT];
     if (n_tiles > 0) {
-        fetch(t0, pa);
+        fetch(tile_start(0), pa);
         stage(0, pa);
+        fetch(tile_start(1), pb);
+        stage(1, pb);
+        fetch(tile_start(2), pa);
     }
-    if (n_tiles > 1) fetch(t0 + kTile, pb);
     __syncthreads();
-    for (int t = 0; t < n_tiles; t += 2) {
-        const int64_t tk = t0 + (int64_t)kTile * t;
-        if (t + 2 < n_tiles) fetch(tk + 2 * kTile, pa);
-        process(0, tk);
-        if (t + 1 < n_tiles) stage(1, pb);
+    if (active && n_full > 0) {
+        qk(0, 0, sc_a);
+        row_max(sc_a, mc);
+        rescale(mc);
+    }
+
+    // Main loop: iterations t = 0 .. n_full - 2, unrolled by two (register
+    // sets pa / pb, score sets sc_a / sc_b alternate roles).
+    auto step = [&](auto compute, int t, int b_cur, floatx4(&sc_cur)[2][kRT], floatx4(&sc_next)[2][kRT],
+                    u32x4(&stage_set)[2][kPer], u32x4(&fetch_set)[2][kPer]) {
+        const int b1 = next_buf(b_cur), b2 = next_buf(b1);
+        fetch(tile_start(t + 3), fetch_set);
+        if constexpr (decltype(compute)::value) {
+            qk(b1, t + 1, sc_next);
+            softmax_pv(b_cur, sc_cur);
+            row_max(sc_next, mc);
+        }
+        stage(b2, stage_set);
+        if constexpr (decltype(compute)::value) rescale(mc);
         __syncthreads();
-        if (t + 1 >= n_tiles) break;
-        if (t + 3 < n_tiles) fetch(tk + 3 * kTile, pb);
-        process(1, tk + kTile);
-        if (t + 2 < n_tiles) stage(0, pa);
-        __syncthreads();
+    };
+    auto main_loop = [&](auto compute) {
+        int bi = 0;
+        for (int t = 0; t + 1 < n_full; t += 2) {
+            step(compute, t, bi, sc_a, sc_b, pa, pb);
+            bi = next_buf(bi);
+            if (t + 2 >= n_full) break;
+            step(compute, t + 1, bi, sc_b, sc_a, pb, pa);
+            bi = next_buf(bi);
+        }
+    };
+    if (active)
+        main_loop(std::integral_constant<bool, true>{});
+    else
+        main_loop(std::integral_constant<bool, false>{});
+
+    if (active) {
+        // Last full tile: S is in sc_a if n_full is odd, else in sc_b.
+        if (n_full > 0) softmax_pv((n_full - 1) % 3, (n_full & 1) ? sc_a : sc_b);
+        // The tail tile (staged by the loop or the prologue), with masking.
+        if (has_tail) {
+            const int bt = n_full % 3;
+            qk(bt, n_full, sc_a);
+            const int valid = (int)(t1 - t0 - (int64_t)kTile * n_full);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (16 * kt + 4 * q4 + j >= valid) sc_a[kt][rt][j] = -INFINITY;
+            row_max(sc_a, mc);
+            rescale(mc);
+            softmax_pv(bt, sc_a);
+        }
     }
 
     if (!active) return;
