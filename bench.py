@@ -205,9 +205,10 @@ def counters_pass(cfg, cps=1):
     del inp
     torch.cuda.synchronize()
     rnd.run()
+    cps = rnd.cps
     torch.cuda.synchronize()
     hist_len = np.full(cfg.batch, cfg.hist_len) if not cfg.ragged else rnd.hist_len.cpu().numpy()
-    print(json.dumps({"counters_pass": cfg.name, "calibration_bytes": 1 << 30,
+    print(json.dumps({"counters_pass": cfg.name, "calibration_bytes": 1 << 30, "chunks_per_slot": cps,
                       "chunk_kernel_algorithmic_bytes": chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)}),
           flush=True)
 
@@ -219,7 +220,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c2_qwen3_8b", choices=[k for k in wl.CONFIGS if not wl.CONFIGS[k].streamed])
     ap.add_argument("--chunks-per-slot", type=int, default=0,
-                    help="chunks merged per state slot (0: 1 for HBM-bound shapes, 4 for wide-row shapes)")
+                    help="chunks merged per state slot (0: automatic, about two work-groups per compute unit)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true")
     ap.add_argument("--counters", action="store_true",
@@ -235,11 +236,12 @@ def main():
         sys.exit(2)
 
     cfg = wl.CONFIGS[args.workload]
-    cps = args.chunks_per_slot or (4 if cfg.rows > 32 else 1)
+    cps = args.chunks_per_slot or "auto"
     if args.counters:
         counters_pass(cfg, cps)
         return
     rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup, cps)
+    cps = rnd.cps
     hist_b, cand_b = kv_bytes(cfg, hist_len)
     gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9
     alg = chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)

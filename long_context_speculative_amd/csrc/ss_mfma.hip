@@ -69,8 +69,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) 
     constexpr int NXT = D / 16;  // 16-feature output tiles for O^T = V^T P^T
     __shared__ MfmaSmem<D, NRT> sm;
 
-    const int s = blockIdx.x;
-    const int g = blockIdx.y;
+    // KV head fastest: the heads of one (slot, request) are dispatched
+    // together, so with token-major layouts they stream the same rows.
+    const int g = blockIdx.x % p.n_kv_heads;
+    const int s = blockIdx.x / p.n_kv_heads;
     const int b = blockIdx.z;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
@@ -321,7 +323,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) 
 
 template <int D, int NRT>
 hipError_t launch_t(const ChunkParams& p, hipStream_t stream) {
-    dim3 grid(p.n_items, p.n_kv_heads, p.batch);
+    const int64_t gx = (int64_t)p.n_items * p.n_kv_heads;
+    if (gx > 0x7fffffff) return hipErrorInvalidValue;
+    dim3 grid((unsigned)gx, 1, p.batch);
     hipLaunchKernelGGL((chunk_mfma_kernel<D, NRT>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

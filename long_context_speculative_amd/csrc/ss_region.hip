@@ -39,8 +39,23 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(uint16_t x) { return __uint_as_float(static_cast<uint32_t>(x) << 16); }
+// One 16-byte load of consecutive elements, widened to fp32 in LDS.
+template <typename T>
+__device__ __forceinline__ void load16_f32(const T* src, float* dst);
+template <>
+__device__ __forceinline__ void load16_f32<float>(const float* src, float* dst) {
+    *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+}
+template <>
+__device__ __forceinline__ void load16_f32<uint16_t>(const uint16_t* src, float* dst) {
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        dst[2 * j] = __uint_as_float(w[j] << 16);
+        dst[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+}
 
 // LDS carve-up (floats): K [n][D + 4] | V [n][D] | Q [16][D] | P [16][64] | m, l [16]
 template <int D>
@@ -84,21 +99,23 @@ __global__ __launch_bounds__(kThreads) void candidates_kernel(CandParams p) {
         bits[tid] = chain_bits(tid);
     }
 
-    // Stage Q rows, candidate keys and values (fp32).
+    // Stage Q rows, candidate keys and values as fp32, 16 bytes per load
+    // (rows are contiguous and 16-byte aligned).
+    constexpr int E = 16 / sizeof(T);  // elements per 16-byte load
     const T* q = static_cast<const T*>(p.q);
-    for (int e = tid; e < nr * D; e += kThreads) {
-        const int rr = e / D, x = e % D;
+    for (int e = tid; e < nr * (D / E); e += kThreads) {
+        const int rr = e / (D / E), x = E * (e % (D / E));
         const int r = r0 + rr;
         const int i = r / p.group, h = g * p.group + r % p.group;
-        qs[rr * D + x] = to_f32(q[((int64_t)(b * p.n_queries + i) * p.n_q_heads + h) * D + x]);
+        load16_f32<T>(q + ((int64_t)(b * p.n_queries + i) * p.n_q_heads + h) * D + x, qs + rr * D + x);
     }
     const int64_t base = (p.req_offset ? p.req_offset[b] : (int64_t)b * p.stride_b) + (int64_t)g * p.stride_h;
     const T* kp = static_cast<const T*>(p.k) + base;
     const T* vp = static_cast<const T*>(p.v) + base;
-    for (int e = tid; e < n * D; e += kThreads) {
-        const int k = e / D, x = e % D;
-        ks[k * KS + x] = to_f32(kp[(int64_t)k * p.stride_t + x]);
-        vs[k * D + x] = to_f32(vp[(int64_t)k * p.stride_t + x]);
+    for (int e = tid; e < n * (D / E); e += kThreads) {
+        const int k = e / (D / E), x = E * (e % (D / E));
+        load16_f32<T>(kp + (int64_t)k * p.stride_t + x, ks + k * KS + x);
+        load16_f32<T>(vp + (int64_t)k * p.stride_t + x, vs + k * D + x);
     }
     __syncthreads();
     if (p.mask_out && g == 0 && rb == 0 && tid < n) p.mask_out[(int64_t)b * n + tid] = bits[tid];
@@ -197,11 +214,22 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
             }
             lsum += wave_sum(lf);
             const int cnt = min(64, ns - s0);
-            for (int j = 0; j < cnt; ++j) {
-                const float fj = __shfl(f, j);
-                const float* src = p.acc + ((s0 + j) * n_rows + row) * D + F * lane;
+            // issue the loads of up to 8 slots, then fold them
+            for (int j0 = 0; j0 < cnt; j0 += 8) {
+                float vals[8][F];
+                float fs[8];
 #pragma unroll
-                for (int t = 0; t < F; ++t) a[t] = fmaf(fj, src[t], a[t]);
+                for (int u = 0; u < 8; ++u) {
+                    const int j = min(j0 + u, cnt - 1);
+                    fs[u] = (j0 + u < cnt) ? __shfl(f, j) : 0.f;
+                    const float* src = p.acc + ((s0 + j) * n_rows + row) * D + F * lane;
+#pragma unroll
+                    for (int t = 0; t < F; ++t) vals[u][t] = src[t];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int t = 0; t < F; ++t) a[t] = fmaf(fs[u], vals[u][t], a[t]);
             }
         }
     }

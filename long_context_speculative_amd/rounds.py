@@ -1,7 +1,8 @@
 """One verification round on the GPU, composed from the C-ABI calls.
 
-ResidentRound: history resident in HBM -> ss_verify_chunk over every chunk,
-ss_verify_candidates into the last slot, ss_merge_states -> O, lse.
+ResidentRound: history resident in HBM -> ss_verify_candidates into slot 0,
+ss_verify_chunk over every chunk into slots 1.., ss_merge_states -> O, lse
+(ragged rounds fold only the slots each request's history reaches).
 StreamedRound: history in pinned host memory -> ss_stream_history on a copy
 and a compute stream, then candidates and merge on the compute stream.
 
@@ -19,6 +20,22 @@ from . import ssverify as ss
 from .workloads import VerifyInputs, to_chunk_major
 
 
+def device_cus(device="cuda") -> int:
+    return torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
+
+
+def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int) -> int:
+    """Chunks merged per state slot for a resident round. Wide row groups
+    (compute-bound) take 4. Otherwise the slot count is chosen so that the
+    chunk kernel launches about two work-groups per compute unit (one full
+    wave of work-groups): fewer launches leave units idle, more leave
+    partly filled rounds and cost a state slot each."""
+    if cfg.rows > 32:
+        return 4
+    units = sum(-(-int(n) // chunk_len) for n in hist_len) * cfg.n_kv_heads
+    return max(1, units // (2 * cus))
+
+
 def _problem(cfg) -> ss.Problem:
     return ss.make_problem(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_queries,
                            cfg.torch_dtype, cfg.scale)
@@ -26,10 +43,13 @@ def _problem(cfg) -> ss.Problem:
 
 class ResidentRound:
     def __init__(self, inp: VerifyInputs, device="cuda", chunk_len=None, chunks_per_slot=1):
+        """chunks_per_slot: an integer, or "auto" (auto_chunks_per_slot)."""
         cfg = inp.cfg
         self.cfg = cfg
         self.problem = _problem(cfg)
         self.chunk_len = chunk_len or cfg.chunk_len
+        if chunks_per_slot == "auto":
+            chunks_per_slot = auto_chunks_per_slot(cfg, inp.hist_len, self.chunk_len, device_cus(device))
         self.cps = chunks_per_slot
         self.q = inp.q.to(device)
         self.k_hist = inp.k_hist.to(device)
@@ -38,8 +58,12 @@ class ResidentRound:
         if cfg.ragged:
             self.hist_offset = torch.as_tensor(inp.hist_offset, dtype=torch.int64, device=device)
             self.hist_len = torch.as_tensor(inp.hist_len, dtype=torch.int32, device=device)
-            self.hist_view = ss.token_major_view(self.k_hist, self.v_hist, self.hist_offset, self.hist_len,
-                                                 self.max_len)
+            if cfg.packing == "head":
+                self.hist_view = ss.head_packed_view(self.k_hist, self.v_hist, self.hist_offset, self.hist_len,
+                                                     self.max_len)
+            else:
+                self.hist_view = ss.token_major_view(self.k_hist, self.v_hist, self.hist_offset, self.hist_len,
+                                                     self.max_len)
         else:
             self.hist_view = ss.head_major_view(self.k_hist, self.v_hist)
         self.k_cand = inp.k_cand.to(device)
@@ -50,7 +74,13 @@ class ResidentRound:
             self.parents = torch.as_tensor(inp.parents, dtype=torch.int32, device=device).contiguous()
         self.n_chunks = math.ceil(self.max_len / self.chunk_len)
         self.n_hist_slots = math.ceil(self.n_chunks / self.cps)
+        # slot 0: candidate region; slots 1 .. n_hist_slots: history
         self.state = ss.StateBuffers(self.problem, self.n_hist_slots + 1, device)
+        self.slots_per_req = None
+        if cfg.ragged:
+            per_slot = self.chunk_len * self.cps
+            counts = [1 + math.ceil(int(n) / per_slot) for n in inp.hist_len]
+            self.slots_per_req = torch.tensor(counts, dtype=torch.int32, device=device)
         self.mask_out = torch.zeros((cfg.batch, cfg.n_queries), dtype=torch.int64, device=device)
         self.o = torch.empty((cfg.batch, cfg.n_queries, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32,
                              device=device)
@@ -60,14 +90,15 @@ class ResidentRound:
         if self.n_chunks == 0:          # no history at all: nothing to enqueue
             return
         ss.ss_verify_chunk(self.problem, self.q, self.hist_view, self.chunk_len, 0, self.n_chunks, self.cps,
-                           self.state, 0, stream)
+                           self.state, 1, stream)
 
     def candidates(self, stream=None):
         ss.ss_verify_candidates(self.problem, self.q, self.cand_view, self.parents, self.mask_out, self.state,
-                                self.n_hist_slots, stream)
+                                0, stream)
 
     def merge(self, stream=None):
-        ss.ss_merge_states(self.problem, self.state, None, self.o, self.lse, stream)
+        # ragged requests fold only the slots their history reaches
+        ss.ss_merge_states(self.problem, self.state, self.slots_per_req, self.o, self.lse, stream)
 
     def run(self, stream=None):
         self.chunks(stream)

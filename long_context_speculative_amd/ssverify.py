@@ -125,6 +125,14 @@ def head_major_view(k: torch.Tensor, v: torch.Tensor, req_len: Optional[torch.Te
     return make_view(k, v, sb, sh, st, k.shape[2] if max_len is None else max_len, None, req_len)
 
 
+def head_packed_view(k: torch.Tensor, v: torch.Tensor, req_offset: torch.Tensor, req_len: torch.Tensor,
+                     max_len: int) -> KVView:
+    """View of packed ragged [Hkv][sum N_b][d] tensors (each head's tokens of
+    all requests back to back) with device offsets (elements) and lengths."""
+    sh, st, sx = k.stride()
+    return make_view(k, v, 0, sh, st, max_len, req_offset, req_len)
+
+
 def token_major_view(k: torch.Tensor, v: torch.Tensor, req_offset: torch.Tensor, req_len: torch.Tensor,
                      max_len: int) -> KVView:
     """View of packed ragged [sum N_b][Hkv][d] tensors with device offsets

@@ -18,13 +18,15 @@ Recipe (every tensor is independent of the others and of the draw order):
 * Values: float32 N(0, 1) from torch's CPU generator, one generator per
   (tensor, request) seeded with 63 bits of ``SeedSequence(seed,
   spawn_key=(stream, b)).generate_state``; drawn in the logical layout order
-  of the tensor in pieces of 2^24 values, then rounded to the config's dtype
-  (bf16 by round-to-nearest-even through torch).
+  of the tensor (a ragged history in [Hkv][N_b][d] order per request), then
+  rounded to the config's dtype (bf16 by round-to-nearest-even through
+  torch).
 
 Logical layouts handed out:
   q        [B][nq][Hq][d]
-  k_hist   uniform: [B][Hkv][N][d]; ragged: token-major packed [sum N_b][Hkv][d]
-           with per-request element offsets ``hist_offset`` [B] (int64)
+  k_hist   uniform: [B][Hkv][N][d]; ragged: head-packed [Hkv][sum N_b][d]
+           (or token-packed [sum N_b][Hkv][d]) with per-request element
+           offsets ``hist_offset`` [B] (int64)
   k_cand   [B][Hkv][nc][d]
   parents  [B][nc] int32 (tree configs), -1 = root
   hist_len [B] int32
@@ -60,6 +62,7 @@ class VerifyConfig:
     ragged_lo: int = 0          # > 0 means ragged lengths in [ragged_lo, hist_len]
     tree_depth_cap: int = 8
     streamed: bool = False      # history sits in pinned host memory
+    packing: str = "head"       # ragged layout: "head" [Hkv][sum N][d] or "token" [sum N][Hkv][d]
 
     @property
     def group(self) -> int:
@@ -156,6 +159,27 @@ def _fill_normal(out: torch.Tensor, seed: int, stream: str, pieces) -> None:
             list(ex.map(work, pieces))
 
 
+def _fill_ragged(out: torch.Tensor, cfg: VerifyConfig, stream: str, lens, cum) -> None:
+    """Ragged history: request b draws its [Hkv][N_b][d] block in that order
+    from its own generator (the values do not depend on the packing), then
+    the block is placed head-packed or token-packed."""
+    hkv, d = cfg.n_kv_heads, cfg.head_dim
+
+    def work(b):
+        n = int(lens[b])
+        g = torch.Generator().manual_seed(_torch_seed(cfg.seed, stream, b))
+        block = torch.randn(hkv * n * d, generator=g, dtype=torch.float32).view(hkv, n, d)
+        c0 = int(cum[b])
+        if cfg.packing == "head":
+            out[:, c0:c0 + n, :].copy_(block)
+        else:
+            out[c0:c0 + n].copy_(block.transpose(0, 1))
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(work, range(cfg.batch)))
+
+
 @dataclasses.dataclass
 class VerifyInputs:
     cfg: VerifyConfig
@@ -198,7 +222,10 @@ class _HistHeads:
         inp, src, b = self._view._inp, self._view._src, self._b
         cfg = inp.cfg
         n = int(inp.hist_len[b])
-        if cfg.ragged:
+        if cfg.ragged and cfg.packing == "head":
+            t0 = int(inp.hist_offset[b]) // cfg.head_dim
+            sl = src[int(g), t0:t0 + n, :]
+        elif cfg.ragged:
             t0 = int(inp.hist_offset[b]) // (cfg.n_kv_heads * cfg.head_dim)
             sl = src[t0:t0 + n, int(g), :]
         else:
@@ -223,15 +250,19 @@ def make_inputs(cfg: VerifyConfig, with_history: bool = True) -> VerifyInputs:
         k_hist = torch.empty(0, dtype=dt)
         v_hist = torch.empty(0, dtype=dt)
     elif cfg.ragged:
-        row = hkv * d
-        offsets = np.zeros(b_, dtype=np.int64)
-        offsets[1:] = np.cumsum(lens[:-1].astype(np.int64)) * row
         total = int(lens.astype(np.int64).sum())
-        k_hist = torch.empty((total, hkv, d), dtype=dt)
-        v_hist = torch.empty((total, hkv, d), dtype=dt)
-        pieces = [(b, int(offsets[b]), int(lens[b]) * row) for b in range(b_)]
-        _fill_normal(k_hist, cfg.seed, "k_hist", pieces)
-        _fill_normal(v_hist, cfg.seed, "v_hist", pieces)
+        cum = np.zeros(b_, dtype=np.int64)
+        cum[1:] = np.cumsum(lens[:-1].astype(np.int64))
+        if cfg.packing == "head":
+            k_hist = torch.empty((hkv, total, d), dtype=dt)
+            v_hist = torch.empty((hkv, total, d), dtype=dt)
+            offsets = cum * d
+        else:
+            k_hist = torch.empty((total, hkv, d), dtype=dt)
+            v_hist = torch.empty((total, hkv, d), dtype=dt)
+            offsets = cum * hkv * d
+        _fill_ragged(k_hist, cfg, "k_hist", lens, cum)
+        _fill_ragged(v_hist, cfg, "v_hist", lens, cum)
     else:
         n = cfg.hist_len
         per = hkv * n * d

@@ -31,6 +31,8 @@ SMALL = {
     "c1": C["c1_tiny_f32"],
     "c2_small": C["c2_qwen3_8b"].with_(batch=2, hist_len=4500, chunk_len=1024),
     "c3_small": C["c3_internlm25_7b_ragged"].with_(batch=6, hist_len=3000, ragged_lo=1, chunk_len=512),
+    "c3_small_token": C["c3_internlm25_7b_ragged"].with_(batch=6, hist_len=3000, ragged_lo=1, chunk_len=512,
+                                                         packing="token"),
     "c4_small": C["c4_tree_72b"].with_(batch=2, hist_len=1500, chunk_len=512),
     "c5_small": C["c5_streamed"].with_(batch=2, hist_len=2048, chunk_len=512),
     "f32_g8_tree": C["c4_tree_72b"].with_(batch=1, hist_len=700, chunk_len=128, dtype="f32", n_queries=20),
@@ -122,9 +124,10 @@ def test_chunk_slot_states(chunk_len, cps):
     m, l, acc = oracle.chunk_slot_states(inp.q.float().numpy(), inp.hist_per_request("k"),
                                          inp.hist_per_request("v"), inp.hist_len, chunk_len, 0, rnd.n_chunks, cps,
                                          cfg.scale)
-    gm = rnd.state.m[:rnd.n_hist_slots].cpu().numpy()
-    gl = rnd.state.l[:rnd.n_hist_slots].cpu().numpy()
-    gacc = rnd.state.acc[:rnd.n_hist_slots].cpu().numpy()
+    hs = slice(1, 1 + rnd.n_hist_slots)          # slot 0 holds the candidate region
+    gm = rnd.state.m[hs].cpu().numpy()
+    gl = rnd.state.l[hs].cpu().numpy()
+    gacc = rnd.state.acc[hs].cpu().numpy()
     empty = np.isneginf(m)
     assert np.array_equal(np.isneginf(gm), empty)
     assert (gl[empty] == 0).all() and (gacc[empty] == 0).all()
@@ -197,16 +200,21 @@ def test_merge_all_empty_and_slots_per_req():
     rnd.chunks()
     rnd.candidates()
     torch.cuda.synchronize()
-    # request 0 folds only its first two slots, request 1 none at all
+    # request 0 folds only its first two slots (candidates + chunk 0),
+    # request 1 none at all
     spr = torch.tensor([2, 0], dtype=torch.int32, device="cuda")
     ss.ss_merge_states(rnd.problem, rnd.state, spr, rnd.o, rnd.lse)
     torch.cuda.synchronize()
     o = rnd.o.cpu().numpy()
     lse = rnd.lse.cpu().numpy()
     assert (o[1] == 0).all() and np.isneginf(lse[1]).all()
-    m, l, acc = oracle.chunk_slot_states(inp.q.float().numpy(), inp.hist_per_request("k"),
-                                         inp.hist_per_request("v"), inp.hist_len, 1024, 0, 2, 1, cfg.scale)
-    o_ref, lse_ref = oracle.merge_slots(m, l, acc)
+    q = inp.q.float().numpy()
+    m, l, acc = oracle.chunk_slot_states(q, inp.hist_per_request("k"), inp.hist_per_request("v"), inp.hist_len,
+                                         1024, 0, 1, 1, cfg.scale)
+    cm, cl, cacc = oracle.candidate_state(q, inp.k_cand.float().numpy(), inp.v_cand.float().numpy(),
+                                          cand_visibility(inp), cfg.scale)
+    o_ref, lse_ref = oracle.merge_slots(np.concatenate([cm[None], m]), np.concatenate([cl[None], l]),
+                                        np.concatenate([cacc[None], acc]))
     assert np.abs(o[0] - o_ref[0]).max() <= 2e-3 and np.abs(lse[0] - lse_ref[0]).max() <= 2e-3
 
 
