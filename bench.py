@@ -45,8 +45,10 @@ CSRC = "long_context_speculative_amd/csrc/"
 def chunk_kernel_sources(cfg):
     """Source files of the chunk kernel that serves cfg (mirrors the library's
     engine choice)."""
-    if cfg.dtype != "bf16" or cfg.head_dim != 128 or cfg.rows < 16:
+    if cfg.dtype != "bf16" or cfg.head_dim != 128:
         main = "ss_valu.hip"
+    elif cfg.rows < 16:
+        main = "ss_valu_small.hip"
     elif cfg.rows <= 32:
         main = "ss_mfma.hip"
     else:

@@ -141,9 +141,10 @@ SS_API int64_t ss_state_bytes(const ss_problem_t* problem, int32_t n_slots);
  *              empty for that request
  *   out        slots [slot_begin, slot_begin + ceil(n_chunks/cps)) must lie
  *              in [0, out->n_slots); they are overwritten
- * Rows R = n_queries * G: bf16 with head_dim 128 runs on MFMA kernels (one
- * for 16 <= R <= 32, one for R > 32); fp32, R < 16 and head_dim 64 run on
- * the VALU kernel.
+ * Rows R = n_queries * G: bf16 with head_dim 128 runs on MFMA kernels when
+ * R fills a 16-row tile (one kernel for 16 <= R <= 32, one for R > 32) and
+ * on a VALU kernel below 16 rows; fp32 and head_dim 64 run on a general
+ * VALU kernel.
  * Errors: SS_ERR_INVALID_ARG for null pointers, non-positive sizes, slots
  * out of range, bad alignment; SS_ERR_UNSUPPORTED for head_dim outside
  * {64, 128}; SS_ERR_HIP if the launch fails.

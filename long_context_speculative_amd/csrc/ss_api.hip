@@ -81,13 +81,15 @@ int32_t check_state(const ss_state_t* s, const char* name) {
 
 // Which chunk kernel serves a problem. bf16 with head_dim 128: the MFMA
 // kernel when the rows of one KV head fill one or two 16-row tiles, the
-// wide-row MFMA kernel above 32 rows. Everything else (fp32, fewer than 16
-// rows, head_dim 64) runs on the VALU kernel.
-enum class ChunkEngine { kValu, kMfma, kMfmaWide };
+// wide-row MFMA kernel above 32 rows, the small-row VALU kernel below 16 rows
+// (the rows do not fill an MFMA tile). fp32 and head_dim 64 run on the
+// general VALU kernel.
+enum class ChunkEngine { kValu, kValuSmall, kMfma, kMfmaWide };
 
 ChunkEngine chunk_engine(const ss_problem_t* p) {
     const int rows = p->n_queries * (p->n_q_heads / p->n_kv_heads);
-    if (p->dtype != SS_BF16 || p->head_dim != 128 || rows < 16) return ChunkEngine::kValu;
+    if (p->dtype != SS_BF16 || p->head_dim != 128) return ChunkEngine::kValu;
+    if (rows < 16) return ChunkEngine::kValuSmall;
     return rows <= 32 ? ChunkEngine::kMfma : ChunkEngine::kMfmaWide;
 }
 
@@ -149,6 +151,7 @@ hipError_t enqueue_chunk(const ss_problem_t* p, const ChunkParams& c, hipStream_
     switch (chunk_engine(p)) {
         case ChunkEngine::kMfma: return launch_chunk_mfma(c, p->head_dim, stream);
         case ChunkEngine::kMfmaWide: return launch_chunk_mfma_wide(c, p->head_dim, stream);
+        case ChunkEngine::kValuSmall: return launch_chunk_valu_small(c, p->head_dim, stream);
         default: return launch_chunk_valu(c, p->dtype, p->head_dim, stream);
     }
 }

@@ -101,6 +101,7 @@ constexpr int kValuRows = 32;
 hipError_t launch_chunk_valu(const ChunkParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_chunk_mfma_wide(const ChunkParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_chunk_valu_small(const ChunkParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_candidates(const CandParams& p, int dtype, int head_dim, hipStream_t stream);
 // Row blocks of the candidate kernel for `rows` rows per KV head.
 int cand_row_blocks(int rows);

@@ -39,6 +39,12 @@ SMALL = {
     "bf16_d64": C["c2_qwen3_8b"].with_(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64, hist_len=333,
                                        chunk_len=100),
     "bf16_small_rows": C["c2_qwen3_8b"].with_(batch=3, n_queries=2, hist_len=1000, chunk_len=256),
+    # small-row VALU kernel: 4, 12 and 15 rows, ragged
+    "valu_r4": C["c2_qwen3_8b"].with_(batch=2, n_queries=1, hist_len=777, chunk_len=200),
+    "valu_r12_ragged": C["c3_internlm25_7b_ragged"].with_(batch=4, n_queries=3, hist_len=1500, ragged_lo=1,
+                                                          chunk_len=300),
+    "valu_r15": C["c2_qwen3_8b"].with_(batch=2, n_q_heads=15, n_kv_heads=5, n_queries=5, hist_len=1000,
+                                       chunk_len=512),
     "bf16_rows16": C["c2_qwen3_8b"].with_(batch=3, n_queries=4, hist_len=2100, chunk_len=700),
     "bf16_rows32_g8": C["c4_tree_72b"].with_(batch=2, n_queries=4, hist_len=1337, chunk_len=512),
     # wide-row MFMA kernel: one wave (64 rows), two waves, four with one idle,
@@ -109,6 +115,20 @@ def test_round_small(name):
     compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
     if not cfg.streamed:
         check_mask(rnd, inp)
+
+
+@pytest.mark.parametrize("width", [2, 4, 6, 8])
+def test_verification_widths(width):
+    """Verification widths q in {2, 4, 6, 8} under 4-way GQA: 8 rows per KV
+    head run on the small-row VALU kernel, 16..32 rows on the MFMA kernel."""
+    cfg = C["c2_qwen3_8b"].with_(batch=3, n_queries=width, hist_len=2500, chunk_len=1024)
+    log(f"[width] q={width} rows={cfg.rows}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp)
+    rnd.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
 
 
 @pytest.mark.parametrize("chunk_len,cps", [(64, 1), (100, 3), (512, 2), (4096, 1)])
