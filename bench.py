@@ -42,13 +42,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 CSRC = "long_context_speculative_amd/csrc/"
 
 
-def chunk_kernel_sources(cfg):
+def chunk_kernel_sources(cfg, engine="auto"):
     """Source files of the chunk kernel that serves cfg (mirrors the library's
     engine choice)."""
-    if cfg.dtype != "bf16" or cfg.head_dim != 128:
-        main = "ss_valu.hip"
-    elif cfg.rows < 16:
-        main = "ss_valu_small.hip"
+    mfma_ok = cfg.dtype == "bf16" and cfg.head_dim == 128
+    if engine == "valu" or not mfma_ok:
+        main = "ss_valu_small.hip" if mfma_ok and cfg.rows < 16 else "ss_valu.hip"
     elif cfg.rows <= 32:
         main = "ss_mfma.hip"
     else:
@@ -76,9 +75,9 @@ def chunk_kernel_flops(cfg, hist_len) -> int:
     return 4 * cfg.n_q_heads * cfg.n_queries * cfg.head_dim * int(np.asarray(hist_len, dtype=np.int64).sum())
 
 
-def source_hash(cfg) -> str:
+def source_hash(cfg, engine="auto") -> str:
     h = hashlib.sha256()
-    for p in chunk_kernel_sources(cfg):
+    for p in chunk_kernel_sources(cfg, engine):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -98,9 +97,9 @@ def read_traffic(cfg):
     return float(m_bytes.group(1))
 
 
-def time_resident(cfg, steps, warmup, cps=1):
+def time_resident(cfg, steps, warmup, cps=1, engine="auto"):
     inp = wl.make_inputs(cfg)
-    rnd = rounds.ResidentRound(inp, chunks_per_slot=cps)
+    rnd = rounds.ResidentRound(inp, chunks_per_slot=cps, engine=engine)
     del inp
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -192,7 +191,7 @@ def cpu_baseline(cfg, budget_s=15.0):
             "query_tokens_per_s": slices / (cfg.batch * cfg.n_kv_heads) * cfg.batch * cfg.n_queries / done}
 
 
-def counters_pass(cfg, cps=1):
+def counters_pass(cfg, cps=1, engine="auto"):
     """One calibration kernel of known traffic (torch.neg over 2^30 bytes of
     bf16: reads 1 GiB, writes 1 GiB), then one step of the workload."""
     src = torch.randn(1 << 29, device="cuda").to(torch.bfloat16)
@@ -203,7 +202,7 @@ def counters_pass(cfg, cps=1):
     del src, dst
     torch.cuda.empty_cache()
     inp = wl.make_inputs(cfg)
-    rnd = rounds.ResidentRound(inp, chunks_per_slot=cps)
+    rnd = rounds.ResidentRound(inp, chunks_per_slot=cps, engine=engine)
     del inp
     torch.cuda.synchronize()
     rnd.run()
@@ -223,6 +222,9 @@ def main():
     ap.add_argument("--workload", default="c2_qwen3_8b", choices=[k for k in wl.CONFIGS if not wl.CONFIGS[k].streamed])
     ap.add_argument("--chunks-per-slot", type=int, default=0,
                     help="chunks merged per state slot (0: automatic, about two work-groups per compute unit)")
+    ap.add_argument("--engine", default="auto", choices=list(rounds.ENGINES),
+                    help="chunk-kernel engine (ss_problem_t.engine)")
+    ap.add_argument("--queries", type=int, default=0, help="override the workload's queries per request")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true")
     ap.add_argument("--counters", action="store_true",
@@ -238,16 +240,18 @@ def main():
         sys.exit(2)
 
     cfg = wl.CONFIGS[args.workload]
+    if args.queries:
+        cfg = cfg.with_(n_queries=args.queries, name=f"{cfg.name}_q{args.queries}")
     cps = args.chunks_per_slot or "auto"
     if args.counters:
-        counters_pass(cfg, cps)
+        counters_pass(cfg, cps, args.engine)
         return
-    rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup, cps)
+    rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup, cps, args.engine)
     cps = rnd.cps
     hist_b, cand_b = kv_bytes(cfg, hist_len)
     gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9
     alg = chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)
-    traffic = read_traffic(cfg)
+    traffic = read_traffic(cfg) if args.engine == "auto" else None
     if cfg.rows > 32:
         # wide row groups: the chunk kernel is bound by the matrix cores
         flops = chunk_kernel_flops(cfg, hist_len)
@@ -282,7 +286,7 @@ def main():
                                f"d={cfg.head_dim}, history={cfg.hist_len} ({'ragged' if cfg.ragged else 'uniform'}),"
                                f" chunk={cfg.chunk_len}, q={cfg.n_queries}, mask={cfg.mask}",
                    "batch": cfg.batch, "history_tokens": cfg.hist_len, "queries": cfg.n_queries,
-                   "chunks_per_slot": cps},
+                   "chunks_per_slot": cps, "engine": args.engine},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(cfg.batch * cfg.n_queries / (ms_step * 1e-3), 1),
         "roofline": roof,

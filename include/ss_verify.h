@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 1
+#define SS_ABI_VERSION 2
 
 /* status codes */
 #define SS_OK 0
@@ -59,6 +59,11 @@ extern "C" {
 /* element types */
 #define SS_F32 0
 #define SS_BF16 1
+
+/* chunk-kernel engines (ss_problem_t.engine) */
+#define SS_ENGINE_AUTO 0 /* measured choice, see ss_verify_chunk                 */
+#define SS_ENGINE_VALU 1 /* vector ALU only (keeps the matrix cores free)      */
+#define SS_ENGINE_MFMA 2 /* matrix cores; bf16 with head_dim 128 only          */
 
 /* A hipStream_t handle (NULL = default stream). */
 typedef void* ss_stream_t;
@@ -71,7 +76,8 @@ typedef struct ss_problem {
     int32_t head_dim;   /* d: 64 or 128                                       */
     int32_t n_queries;  /* q queries per request (k drafts + 1, or tree nodes)*/
     int32_t dtype;      /* SS_F32 or SS_BF16                                  */
-    float scale;        /* score scale, normally 1/sqrt(d)                    */
+    float scale;        /* score scale, normally 1/sqrt(d); must be > 0       */
+    int32_t engine;     /* SS_ENGINE_*: which units run the chunk kernel       */
 } ss_problem_t;
 
 /*
@@ -141,10 +147,14 @@ SS_API int64_t ss_state_bytes(const ss_problem_t* problem, int32_t n_slots);
  *              empty for that request
  *   out        slots [slot_begin, slot_begin + ceil(n_chunks/cps)) must lie
  *              in [0, out->n_slots); they are overwritten
- * Rows R = n_queries * G: bf16 with head_dim 128 runs on MFMA kernels when
- * R fills a 16-row tile (one kernel for 16 <= R <= 32, one for R > 32) and
- * on a VALU kernel below 16 rows; fp32 and head_dim 64 run on a general
- * VALU kernel.
+ * Engines (problem->engine). SS_ENGINE_AUTO runs bf16 with head_dim 128 on
+ * the matrix cores: one MFMA kernel for up to 32 rows per KV head
+ * (R = n_queries * G, padded to a 16-row tile) and one for more rows; fp32
+ * and head_dim 64 run on a VALU kernel. On gfx950 the padded MFMA kernel
+ * stays bound by HBM down to a single row, ahead of the VALU kernels, so
+ * AUTO never picks VALU for bf16 / head_dim 128. SS_ENGINE_VALU forces the
+ * VALU kernels (a small-row kernel below 16 rows); SS_ENGINE_MFMA is
+ * SS_ERR_UNSUPPORTED outside bf16 / head_dim 128.
  * Errors: SS_ERR_INVALID_ARG for null pointers, non-positive sizes, slots
  * out of range, bad alignment; SS_ERR_UNSUPPORTED for head_dim outside
  * {64, 128}; SS_ERR_HIP if the launch fails.

@@ -45,7 +45,11 @@ int32_t check_problem(const ss_problem_t* p) {
         return fail(SS_ERR_INVALID_ARG, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)", p->n_q_heads,
                     p->n_kv_heads);
     if (p->dtype != SS_F32 && p->dtype != SS_BF16) return fail(SS_ERR_INVALID_ARG, "unknown dtype %d", p->dtype);
-    if (!isfinite(p->scale)) return fail(SS_ERR_INVALID_ARG, "scale must be finite");
+    if (!isfinite(p->scale) || !(p->scale > 0.f)) return fail(SS_ERR_INVALID_ARG, "scale must be finite and positive");
+    if (p->engine != SS_ENGINE_AUTO && p->engine != SS_ENGINE_VALU && p->engine != SS_ENGINE_MFMA)
+        return fail(SS_ERR_INVALID_ARG, "unknown engine %d", p->engine);
+    if (p->engine == SS_ENGINE_MFMA && !(p->dtype == SS_BF16 && p->head_dim == 128))
+        return fail(SS_ERR_UNSUPPORTED, "the MFMA engine needs bf16 and head_dim 128");
     if (p->head_dim != 64 && p->head_dim != 128)
         return fail(SS_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", p->head_dim);
     if (p->batch > 65535) return fail(SS_ERR_UNSUPPORTED, "batch above 65535");
@@ -79,17 +83,20 @@ int32_t check_state(const ss_state_t* s, const char* name) {
     return SS_OK;
 }
 
-// Which chunk kernel serves a problem. bf16 with head_dim 128: the MFMA
-// kernel when the rows of one KV head fill one or two 16-row tiles, the
-// wide-row MFMA kernel above 32 rows, the small-row VALU kernel below 16 rows
-// (the rows do not fill an MFMA tile). fp32 and head_dim 64 run on the
-// general VALU kernel.
+// Which chunk kernel serves a problem. AUTO: bf16 with head_dim 128 runs on
+// the matrix cores (rows up to 32 on the MFMA kernel, padded to a 16-row
+// tile; more rows on the wide-row MFMA kernel). Measured on gfx950, the
+// padded MFMA kernel stays HBM-bound down to a single row per KV head, while
+// the VALU kernels are bound by vector and LDS issue, so AUTO keeps VALU for
+// fp32 and head_dim 64. VALU forces the vector kernels (the small-row kernel
+// below 16 rows of bf16 / head_dim 128).
 enum class ChunkEngine { kValu, kValuSmall, kMfma, kMfmaWide };
 
 ChunkEngine chunk_engine(const ss_problem_t* p) {
     const int rows = p->n_queries * (p->n_q_heads / p->n_kv_heads);
-    if (p->dtype != SS_BF16 || p->head_dim != 128) return ChunkEngine::kValu;
-    if (rows < 16) return ChunkEngine::kValuSmall;
+    const bool mfma_ok = p->dtype == SS_BF16 && p->head_dim == 128;
+    if (p->engine == SS_ENGINE_VALU || !mfma_ok)
+        return (mfma_ok && rows < 16) ? ChunkEngine::kValuSmall : ChunkEngine::kValu;
     return rows <= 32 ? ChunkEngine::kMfma : ChunkEngine::kMfmaWide;
 }
 

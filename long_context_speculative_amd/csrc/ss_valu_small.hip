@@ -18,8 +18,8 @@
 //            row and tile in the common case);
 //   P V      V goes to a per-wave LDS tile; lane l then owns output features
 //            2l, 2l+1 and accumulates p[row][key] * V[key][2l..2l+1] over the
-//            tile's keys (fp32 FMAs, the weights read from LDS as a
-//            broadcast).
+//            tile's keys, two keys per v_dot2_f32_bf16 (the bf16 weights are
+//            read from LDS as a broadcast; l sums the same rounded weights).
 // The 4 waves' states are merged through LDS at the end.
 
 #include "ss_common.h"
@@ -43,7 +43,7 @@ struct SmallSmem {
     union {
         struct {
             uint16_t v[kWaves][kTile][kVRow];  // per-wave V tile
-            float p[kWaves][RMAX][kTile];      // per-wave softmax weights
+            uint32_t p[kWaves][RMAX][kTile / 2];  // per-wave bf16 weight pairs (keys 2j, 2j+1)
         } t;
         struct {
             float o[kWaves - 1][RMAX][D];
@@ -171,25 +171,41 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_valu_small_kernel(ChunkPara
                 o0[r] *= alpha;
                 o1[r] *= alpha;
             }
-            const float pr = exp2_hw(fmaf(sc[r], c, -m_ref[r]));
+            // bf16 weight; the pair (p[key], p[key + 1]) is packed by the lane
+            // of the even key and stored for the P V products.
+            const __bf16 pb = (__bf16)exp2_hw(fmaf(sc[r], c, -m_ref[r]));
+            const uint32_t pbits = __builtin_bit_cast(uint16_t, pb);
+            const uint32_t pnext = __shfl_down(pbits, 2);
             if (half == 0) {
-                sm.u.t.p[w][r][kk] = pr;
-                l_part[r] += pr;
+                l_part[r] += (float)pb;
+                if ((kk & 1) == 0) sm.u.t.p[w][r][kk >> 1] = pbits | (pnext << 16);
             }
         }
         wave_sync();
 
-        // P V: lane owns features 2*lane, 2*lane + 1.
-#pragma unroll 4
-        for (int k = 0; k < kTile; ++k) {
-            const uint32_t vv = *reinterpret_cast<const uint32_t*>(&sm.u.t.v[w][k][2 * lane]);
-            const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xffff0000u);
+        // P V: lane owns features 2*lane, 2*lane + 1; two keys per v_dot2.
+#pragma unroll 2
+        for (int k = 0; k < kTile; k += 8) {
+            uint32_t va[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) va[j] = *reinterpret_cast<const uint32_t*>(&sm.u.t.v[w][k + j][2 * lane]);
+            uint32_t x0[4], x1[4];  // (V[k][2l], V[k+1][2l]) and (V[k][2l+1], V[k+1][2l+1]) per key pair
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t a = va[2 * j], bb = va[2 * j + 1];
+                x0[j] = (a & 0xffffu) | (bb << 16);
+                x1[j] = (a >> 16) | (bb & 0xffff0000u);
+            }
 #pragma unroll
             for (int r = 0; r < RMAX; ++r) {
                 if (r >= R) continue;
-                const float pk = sm.u.t.p[w][r][k];
-                o0[r] = fmaf(pk, v0, o0[r]);
-                o1[r] = fmaf(pk, v1, o1[r]);
+                const u32x4 pp = *reinterpret_cast<const u32x4*>(&sm.u.t.p[w][r][k >> 1]);
+                const uint32_t pw[4] = {pp.x, pp.y, pp.z, pp.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    o0[r] = dot2(pw[j], x0[j], o0[r]);
+                    o1[r] = dot2(pw[j], x1[j], o1[r]);
+                }
             }
         }
         wave_sync();

@@ -36,17 +36,21 @@ def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int) -> int:
     return max(1, units // (2 * cus))
 
 
-def _problem(cfg) -> ss.Problem:
+ENGINES = {"auto": ss.SS_ENGINE_AUTO, "valu": ss.SS_ENGINE_VALU, "mfma": ss.SS_ENGINE_MFMA}
+
+
+def _problem(cfg, engine="auto") -> ss.Problem:
     return ss.make_problem(cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_queries,
-                           cfg.torch_dtype, cfg.scale)
+                           cfg.torch_dtype, cfg.scale, ENGINES[engine])
 
 
 class ResidentRound:
-    def __init__(self, inp: VerifyInputs, device="cuda", chunk_len=None, chunks_per_slot=1):
-        """chunks_per_slot: an integer, or "auto" (auto_chunks_per_slot)."""
+    def __init__(self, inp: VerifyInputs, device="cuda", chunk_len=None, chunks_per_slot=1, engine="auto"):
+        """chunks_per_slot: an integer, or "auto" (auto_chunks_per_slot).
+        engine: "auto", "valu" or "mfma" (ss_problem_t.engine)."""
         cfg = inp.cfg
         self.cfg = cfg
-        self.problem = _problem(cfg)
+        self.problem = _problem(cfg, engine)
         self.chunk_len = chunk_len or cfg.chunk_len
         if chunks_per_slot == "auto":
             chunks_per_slot = auto_chunks_per_slot(cfg, inp.hist_len, self.chunk_len, device_cus(device))

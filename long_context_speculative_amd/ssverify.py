@@ -24,6 +24,10 @@ SS_ERR_HIP = -3
 SS_F32 = 0
 SS_BF16 = 1
 
+SS_ENGINE_AUTO = 0
+SS_ENGINE_VALU = 1
+SS_ENGINE_MFMA = 2
+
 EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chunk", "ss_verify_candidates",
             "ss_merge_states", "ss_stream_history", "ss_stream_timings", "ss_tree_mask_host", "ss_slot_tokens_host")
 
@@ -37,7 +41,7 @@ class SSError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("n_queries", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("engine", ctypes.c_int32)]
 
 
 class KVView(ctypes.Structure):
@@ -107,10 +111,10 @@ def _stream(stream) -> Optional[int]:
 # struct builders
 # ---------------------------------------------------------------------------
 
-def make_problem(batch, n_q_heads, n_kv_heads, head_dim, n_queries, dtype, scale) -> Problem:
+def make_problem(batch, n_q_heads, n_kv_heads, head_dim, n_queries, dtype, scale, engine=SS_ENGINE_AUTO) -> Problem:
     if isinstance(dtype, torch.dtype):
         dtype = SS_F32 if dtype == torch.float32 else SS_BF16
-    return Problem(batch, n_q_heads, n_kv_heads, head_dim, n_queries, dtype, scale)
+    return Problem(batch, n_q_heads, n_kv_heads, head_dim, n_queries, dtype, scale, engine)
 
 
 def make_view(k: torch.Tensor, v: torch.Tensor, stride_b: int, stride_h: int, stride_t: int, max_len: int,

@@ -38,7 +38,8 @@ def test_abi_version_matches_header():
 
 
 def _problem(**kw):
-    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_queries=6, dtype=ss.SS_BF16, scale=0.088)
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, n_queries=6, dtype=ss.SS_BF16, scale=0.088,
+                engine=ss.SS_ENGINE_AUTO)
     base.update(kw)
     return ss.Problem(**base)
 
@@ -82,6 +83,9 @@ def _state(n_slots=4):
     ("slot_overflow", ss.SS_ERR_INVALID_ARG),
     ("bad_cps", ss.SS_ERR_INVALID_ARG),
     ("bad_stride", ss.SS_ERR_INVALID_ARG),
+    ("bad_engine", ss.SS_ERR_INVALID_ARG),
+    ("mfma_fp32", ss.SS_ERR_UNSUPPORTED),
+    ("negative_scale", ss.SS_ERR_INVALID_ARG),
 ])
 def test_verify_chunk_rejects(case, code):
     L = ss.lib()
@@ -110,6 +114,12 @@ def test_verify_chunk_rejects(case, code):
         args["cps"] = 0
     if case == "bad_stride":
         view = _view(stride_t=100)
+    if case == "bad_engine":
+        p = _problem(engine=7)
+    if case == "mfma_fp32":
+        p = _problem(engine=ss.SS_ENGINE_MFMA, dtype=ss.SS_F32)
+    if case == "negative_scale":
+        p = _problem(scale=-0.1)
     rc = L.ss_verify_chunk(ctypes.byref(p), q, ctypes.byref(view), args["chunk_len"], args["chunk_begin"],
                            args["n_chunks"], args["cps"], ctypes.byref(st.struct), args["slot_begin"], None)
     assert rc == code

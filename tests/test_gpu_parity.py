@@ -117,10 +117,24 @@ def test_round_small(name):
         check_mask(rnd, inp)
 
 
+@pytest.mark.parametrize("name", ["valu_r4", "bf16_small_rows", "valu_r12_ragged", "valu_r15", "c2_small"])
+def test_forced_valu_engine(name):
+    """The VALU engine (SS_ENGINE_VALU) on bf16 shapes: the small-row kernel
+    below 16 rows, the general VALU kernel above."""
+    cfg = SMALL[name]
+    log(f"[valu engine] {name}: rows={cfg.rows}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, engine="valu")
+    rnd.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+
+
 @pytest.mark.parametrize("width", [2, 4, 6, 8])
 def test_verification_widths(width):
-    """Verification widths q in {2, 4, 6, 8} under 4-way GQA: 8 rows per KV
-    head run on the small-row VALU kernel, 16..32 rows on the MFMA kernel."""
+    """Verification widths q in {2, 4, 6, 8} under 4-way GQA (8 to 32 rows per
+    KV head) on the default engine."""
     cfg = C["c2_qwen3_8b"].with_(batch=3, n_queries=width, hist_len=2500, chunk_len=1024)
     log(f"[width] q={width} rows={cfg.rows}")
     inp = wl.make_inputs(cfg)
