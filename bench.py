@@ -83,23 +83,35 @@ def source_hash(cfg, engine="auto") -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(cfg):
+def read_traffic(cfg, split):
     """HBM bytes per chunk-kernel launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source; else None."""
+    summary, if it was taken on the current kernel source with the same
+    history cut; else None."""
     path = os.path.join(ROOT, "profiles", f"chunk_kernel_{cfg.name}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_split = re.search(r"history_split:\s*(\w+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != source_hash(cfg):
+        return None
+    if (m_split.group(1) if m_split else "chunks") != split:
         return None
     return float(m_bytes.group(1))
 
 
-def time_resident(cfg, steps, warmup, cps=1, engine="auto"):
+def make_round(cfg, inp, cps="auto", engine="auto", split="balanced"):
+    """The resident round in the launch configuration the benchmark times
+    (rounds.BENCH_RESIDENT unless overridden)."""
+    kw = dict(rounds.BENCH_RESIDENT)
+    kw.update(chunks_per_slot=cps, split=split)
+    return rounds.ResidentRound(inp, engine=engine, **kw)
+
+
+def time_resident(cfg, steps, warmup, cps="auto", engine="auto", split="balanced"):
     inp = wl.make_inputs(cfg)
-    rnd = rounds.ResidentRound(inp, chunks_per_slot=cps, engine=engine)
+    rnd = make_round(cfg, inp, cps, engine, split)
     del inp
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -191,7 +203,7 @@ def cpu_baseline(cfg, budget_s=15.0):
             "query_tokens_per_s": slices / (cfg.batch * cfg.n_kv_heads) * cfg.batch * cfg.n_queries / done}
 
 
-def counters_pass(cfg, cps=1, engine="auto"):
+def counters_pass(cfg, cps="auto", engine="auto", split="balanced"):
     """One calibration kernel of known traffic (torch.neg over 2^30 bytes of
     bf16: reads 1 GiB, writes 1 GiB), then one step of the workload."""
     src = torch.randn(1 << 29, device="cuda").to(torch.bfloat16)
@@ -202,7 +214,7 @@ def counters_pass(cfg, cps=1, engine="auto"):
     del src, dst
     torch.cuda.empty_cache()
     inp = wl.make_inputs(cfg)
-    rnd = rounds.ResidentRound(inp, chunks_per_slot=cps, engine=engine)
+    rnd = make_round(cfg, inp, cps, engine, split)
     del inp
     torch.cuda.synchronize()
     rnd.run()
@@ -210,6 +222,7 @@ def counters_pass(cfg, cps=1, engine="auto"):
     torch.cuda.synchronize()
     hist_len = np.full(cfg.batch, cfg.hist_len) if not cfg.ragged else rnd.hist_len.cpu().numpy()
     print(json.dumps({"counters_pass": cfg.name, "calibration_bytes": 1 << 30, "chunks_per_slot": cps,
+                      "split": rnd.split, "history_slots": rnd.n_hist_slots,
                       "chunk_kernel_algorithmic_bytes": chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)}),
           flush=True)
 
@@ -222,6 +235,8 @@ def main():
     ap.add_argument("--workload", default="c2_qwen3_8b", choices=[k for k in wl.CONFIGS if not wl.CONFIGS[k].streamed])
     ap.add_argument("--chunks-per-slot", type=int, default=0,
                     help="chunks merged per state slot (0: automatic, about two work-groups per compute unit)")
+    ap.add_argument("--split", default=rounds.BENCH_RESIDENT["split"], choices=["balanced", "chunks"],
+                    help="history cut: ss_verify_history's balanced cut, or ss_verify_chunk over fixed chunks")
     ap.add_argument("--engine", default="auto", choices=list(rounds.ENGINES),
                     help="chunk-kernel engine (ss_problem_t.engine)")
     ap.add_argument("--queries", type=int, default=0, help="override the workload's queries per request")
@@ -244,20 +259,22 @@ def main():
         cfg = cfg.with_(n_queries=args.queries, name=f"{cfg.name}_q{args.queries}")
     cps = args.chunks_per_slot or "auto"
     if args.counters:
-        counters_pass(cfg, cps, args.engine)
+        counters_pass(cfg, cps, args.engine, args.split)
         return
-    rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup, cps, args.engine)
+    rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup, cps, args.engine, args.split)
     cps = rnd.cps
+    kernel = "ss_verify_history" if rnd.split == "balanced" else "ss_verify_chunk"
+    hist_slots = rnd.n_hist_slots
     hist_b, cand_b = kv_bytes(cfg, hist_len)
     gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9
     alg = chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)
-    traffic = read_traffic(cfg) if args.engine == "auto" else None
+    traffic = read_traffic(cfg, rnd.split) if args.engine == "auto" else None
     if cfg.rows > 32:
         # wide row groups: the chunk kernel is bound by the matrix cores
         flops = chunk_kernel_flops(cfg, hist_len)
         roof = {"bound": "mfma", "achieved": round(flops / (ms_chunk * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(flops / (ms_chunk * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None if traffic is None else int(traffic), "kernel": "ss_verify_chunk",
+                "traffic": None if traffic is None else int(traffic), "kernel": kernel,
                 "ms_per_launch": round(ms_chunk, 4), "algorithmic_flops_per_launch": flops,
                 "algorithmic_bytes_per_launch": alg,
                 "hbm_GBps_algorithmic": round(alg / (ms_chunk * 1e-3) / 1e9, 2)}
@@ -265,7 +282,7 @@ def main():
         achieved = alg / (ms_chunk * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic),
-                "kernel": "ss_verify_chunk", "ms_per_launch": round(ms_chunk, 4), "algorithmic_bytes_per_launch": alg}
+                "kernel": kernel, "ms_per_launch": round(ms_chunk, 4), "algorithmic_bytes_per_launch": alg}
     del rnd
     torch.cuda.empty_cache()
 
@@ -286,7 +303,8 @@ def main():
                                f"d={cfg.head_dim}, history={cfg.hist_len} ({'ragged' if cfg.ragged else 'uniform'}),"
                                f" chunk={cfg.chunk_len}, q={cfg.n_queries}, mask={cfg.mask}",
                    "batch": cfg.batch, "history_tokens": cfg.hist_len, "queries": cfg.n_queries,
-                   "chunks_per_slot": cps, "engine": args.engine},
+                   "split": args.split, "history_slots": hist_slots,
+                   "chunks_per_slot": cps if args.split == "chunks" else None, "engine": args.engine},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(cfg.batch * cfg.n_queries / (ms_step * 1e-3), 1),
         "roofline": roof,

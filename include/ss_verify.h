@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 2
+#define SS_ABI_VERSION 3
 
 /* status codes */
 #define SS_OK 0
@@ -165,6 +165,37 @@ SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const
                                ss_stream_t stream);
 
 /*
+ * ss_verify_history -- the state of every request's whole resident history
+ * [0, len_b), cut where the load balances best (section 4.2: the history
+ * serves the whole query group, and by Eq. 9 the merged result does not
+ * depend on where it is cut).
+ *
+ *   q, hist     as ss_verify_chunk; len_b = req_len[b] (or max_len),
+ *               clamped to [0, max_len]
+ *   n_slots     slots per (request, KV head) the call may use, >= 1; the
+ *               call writes exactly slots [slot_begin, slot_begin + n_slots)
+ *               of every row, the ones it does not need as empty states
+ * With the narrow MFMA kernel (AUTO or MFMA engine, bf16, head_dim 128,
+ * R <= 32):
+ *   - ragged lengths (hist->req_len given) and n_slots >= 2: the streams
+ *     (request, KV head) are laid end to end, each padded to a multiple of
+ *     128 tokens, and cut into equal ranges, one per work-group of a single
+ *     full wave of the device; a stream is cut into at most n_slots pieces
+ *     (the ranges grow when n_slots is too small for an even cut);
+ *   - uniform lengths (req_len NULL): every stream is cut into
+ *     P = min(n_slots, max(1, W / (B * Hkv))) equal chunks, W the
+ *     work-groups of one full wave, i.e. n_slots = W / (B * Hkv) gives one
+ *     chunk per work-group.
+ * Other engines, and ragged lengths with n_slots = 1, cut every request
+ * into n_slots chunks of ceil(max_len / n_slots) tokens. Chunks are rounded
+ * up to a multiple of 128 tokens and run as ss_verify_chunk with
+ * chunks_per_slot 1; chunks past a request's end are empty slots.
+ * Errors: as ss_verify_chunk.
+ */
+SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                 int32_t n_slots, const ss_state_t* out, int32_t slot_begin, ss_stream_t stream);
+
+/*
  * ss_verify_candidates -- the state of the GPU-resident candidate region
  * (section 4.2: the GPU region attended under a mask by each query's
  * position), written to one slot.
@@ -252,10 +283,20 @@ SS_API int32_t ss_stream_timings(int32_t n_chunks, float* copy_begin, float* cop
  *   (1 << i). parents and out are host arrays of n entries.
  * ss_slot_tokens_host: the token range [*t0, *t1) that slot s of a chunk call
  *   covers for a request of len tokens.
+ * ss_history_plan_host: the balanced cut of ss_verify_history for host
+ *   lengths lens[batch] (clamped to [0, max_len]) over n_wg work-groups and
+ *   n_slots >= 2 slots. For every slot (b, g, k) of
+ *   plan[batch][n_kv_heads][n_slots][4] it stores {work-group, t0, t1,
+ *   writes}: the work-group that writes it, the token range it covers
+ *   (t0 = t1 = -1 for a slot filled with the empty state) and how many
+ *   times the cut writes it (1 in a correct cut; slots start at
+ *   {-1, -1, -1, 0}). *piece_len receives the tokens per work-group.
  */
 SS_API int32_t ss_tree_mask_host(const int32_t* parents, int32_t n, uint64_t* out);
 SS_API int32_t ss_slot_tokens_host(int32_t len, int32_t chunk_len, int32_t chunk_begin, int32_t n_chunks,
                                    int32_t chunks_per_slot, int32_t s, int64_t* t0, int64_t* t1);
+SS_API int32_t ss_history_plan_host(const int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t max_len,
+                                    int32_t n_wg, int32_t n_slots, int64_t* plan, int64_t* piece_len);
 
 #ifdef __cplusplus
 }

@@ -221,6 +221,43 @@ extern "C" SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const voi
     return ok();
 }
 
+extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                            int32_t n_slots, const ss_state_t* out, int32_t slot_begin,
+                                            ss_stream_t stream) {
+    if (!hist) return fail(SS_ERR_INVALID_ARG, "history view is NULL");
+    if (n_slots < 1) return fail(SS_ERR_INVALID_ARG, "n_slots must be at least 1");
+    // validation first (the chunk length does not change its outcome)
+    int32_t rc = validate_chunk(problem, q, hist, kPlanAlign, 0, n_slots, 1, out, slot_begin);
+    if (rc) return rc;
+    const bool narrow = chunk_engine(problem) == ChunkEngine::kMfma;
+    const int64_t streams = (int64_t)problem->batch * problem->n_kv_heads;
+    // Pieces per stream of a cut by fixed chunks: n_slots, or for uniform
+    // lengths on the narrow kernel as many as fill one wave of work-groups.
+    int64_t pieces = n_slots;
+    if (narrow && !hist->req_len) {
+        int wgs = 0;
+        hipError_t e = mfma_wave_work_groups(problem->n_queries * (problem->n_q_heads / problem->n_kv_heads), &wgs);
+        if (e != hipSuccess) return fail(SS_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+        pieces = wgs / streams;
+        if (pieces < 1) pieces = 1;
+        if (pieces > n_slots) pieces = n_slots;
+    }
+    int64_t chunk = ((int64_t)hist->max_len + pieces - 1) / pieces;
+    chunk = (chunk + kPlanAlign - 1) / kPlanAlign * kPlanAlign;
+    if (chunk < kPlanAlign) chunk = kPlanAlign;
+    if (chunk > 0x7fffffff) chunk = 0x7fffffff;
+    ChunkParams c = make_chunk_params(problem, q, hist, (int32_t)chunk, 0, n_slots, 1, out, slot_begin);
+    hipError_t e;
+    if (narrow && hist->req_len && n_slots >= 2) {
+        c.plan_slots = n_slots;
+        e = launch_history_mfma(c, problem->head_dim, static_cast<hipStream_t>(stream));
+    } else {
+        e = enqueue_chunk(problem, c, static_cast<hipStream_t>(stream));
+    }
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "history kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 extern "C" SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, const void* q, const ss_kv_view_t* cand,
                                                const int32_t* parents, uint64_t* mask_out, const ss_state_t* out,
                                                int32_t slot, ss_stream_t stream) {
@@ -413,5 +450,63 @@ extern "C" SS_API int32_t ss_slot_tokens_host(int32_t len, int32_t chunk_len, in
     if (len < 0 || chunk_len <= 0 || chunk_begin < 0 || n_chunks < 0 || chunks_per_slot <= 0 || s < 0)
         return fail(SS_ERR_INVALID_ARG, "invalid chunk arguments");
     slot_tokens(len, chunk_len, chunk_begin, n_chunks, chunks_per_slot, s, t0, t1);
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_history_plan_host(const int32_t* lens, int32_t batch, int32_t n_kv_heads, int32_t max_len,
+                                               int32_t n_wg, int32_t n_slots, int64_t* plan, int64_t* piece_len) {
+    if (!lens || !plan || !piece_len) return fail(SS_ERR_INVALID_ARG, "lens, plan or piece_len is NULL");
+    if (batch <= 0 || n_kv_heads <= 0 || max_len < 0 || n_wg <= 0 || n_slots < 2)
+        return fail(SS_ERR_INVALID_ARG, "invalid plan arguments");
+    auto len_of = [&](int32_t b) { return clamp_len(lens[b], max_len); };
+    int64_t total = 0, pad_max = 0;
+    for (int32_t b = 0; b < batch; ++b) {
+        const int64_t pad = plan_pad(len_of(b));
+        total += pad;
+        if (pad > pad_max) pad_max = pad;
+    }
+    total *= n_kv_heads;
+    const int64_t L = plan_piece_len(total, pad_max, n_wg, n_slots);
+    *piece_len = L;
+    const int64_t n_entries = (int64_t)batch * n_kv_heads * n_slots;
+    for (int64_t i = 0; i < n_entries; ++i) {
+        plan[4 * i + 0] = plan[4 * i + 1] = plan[4 * i + 2] = -1;
+        plan[4 * i + 3] = 0;
+    }
+    for (int64_t w = 0; w < n_wg; ++w) {
+        // The same start rule as the kernel's wave scan, as a plain loop.
+        const int64_t lo = w * L;
+        int32_t b_first = batch;
+        int64_t line = 0, start = 0;
+        for (int32_t b = 0; b < batch; ++b) {
+            const int64_t span = (int64_t)n_kv_heads * plan_pad(len_of(b));
+            if (start + span > lo || start >= lo) {
+                b_first = b;
+                line = start;
+                break;
+            }
+            start += span;
+        }
+        PlanCursor cur{b_first, 0, line};
+        PlanPiece pc;
+        while (plan_next(len_of, batch, n_kv_heads, L, total, n_slots, w, cur, pc)) {
+            int64_t* e = plan + 4 * (((int64_t)pc.b * n_kv_heads + pc.g) * n_slots);
+            if (pc.k >= n_slots) {
+                e[4 * (n_slots - 1) + 3] += 1000;  // a piece beyond the slots: flagged
+                continue;
+            }
+            if (pc.k >= 0) {
+                e[4 * pc.k + 0] = w;
+                e[4 * pc.k + 1] = pc.t0;
+                e[4 * pc.k + 2] = pc.t1;
+                e[4 * pc.k + 3] += 1;
+            }
+            for (int32_t j = pc.k + 1; j < pc.fill_end; ++j) {
+                e[4 * j + 0] = w;
+                e[4 * j + 1] = e[4 * j + 2] = -1;
+                e[4 * j + 3] += 1;
+            }
+        }
+    }
     return ok();
 }

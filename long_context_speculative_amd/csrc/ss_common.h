@@ -31,6 +31,104 @@ __host__ __device__ inline void slot_tokens(int32_t len, int32_t chunk_len, int3
     *t1 = b;
 }
 
+// Balanced split of the resident history (ss_verify_history). Eq. (9) of
+// SpecStream section 4.2 makes the merged result independent of where the
+// history is cut, so the cuts are placed for an even load: the streams
+// (request b, KV head g) are laid end to end on one line, b-major, each
+// padded to a multiple of kPlanAlign tokens, and work-group w of n_wg takes
+// the line positions [w*L, (w+1)*L). L is the larger of total/n_wg and
+// pad_max/(n_slots-1), rounded up to kPlanAlign, so that no stream is cut
+// into more than n_slots pieces. Piece k of a stream that starts at line
+// position o is its part inside work-group floor(o/L)+k's range; it goes to
+// slot k, and the owner of a stream's last piece fills the slots after it
+// with empty states. A request of length 0 has no pieces: the work-group
+// whose range holds its line position (the last busy one if that is past the
+// end) fills all its slots with empty states.
+constexpr int kPlanAlign = 128;
+
+__host__ __device__ inline int32_t clamp_len(int32_t len, int32_t max_len) {
+    return len < 0 ? 0 : (len > max_len ? max_len : len);
+}
+
+__host__ __device__ inline int64_t plan_pad(int32_t len) {
+    return ((int64_t)len + kPlanAlign - 1) / kPlanAlign * kPlanAlign;
+}
+
+// Tokens per work-group; n_slots >= 2, n_wg >= 1.
+__host__ __device__ inline int64_t plan_piece_len(int64_t total, int64_t pad_max, int32_t n_wg, int32_t n_slots) {
+    const int64_t even = (total + n_wg - 1) / n_wg;
+    const int64_t cap = (pad_max + n_slots - 2) / (n_slots - 1);
+    int64_t len = even > cap ? even : cap;
+    if (len < kPlanAlign) len = kPlanAlign;
+    return (len + kPlanAlign - 1) / kPlanAlign * kPlanAlign;
+}
+
+// Last work-group with a non-empty range (0 when the line is empty).
+__host__ __device__ inline int64_t plan_last_wg(int64_t total, int64_t piece_len) {
+    return total > 0 ? (total - 1) / piece_len : 0;
+}
+
+// Where a work-group is in its walk over the line: request b, KV head g of
+// that request, and the line position of the request's first stream.
+struct PlanCursor {
+    int32_t b;
+    int32_t g;
+    int64_t line;
+};
+
+// One piece: compute the state of tokens [t0, t1) of stream (b, g) into
+// slot k (k = -1: nothing to compute), then store empty states in slots
+// k+1 .. fill_end-1.
+struct PlanPiece {
+    int32_t b, g, k, fill_end;
+    int64_t t0, t1;
+};
+
+// Next piece of work-group w after cursor c; false when w owns no more. The
+// walk starts at the first request whose streams end after w*L, or that
+// starts at or after it, with c = {that request, 0, its line position}.
+template <class LenFn>
+__host__ __device__ inline bool plan_next(const LenFn& len_of, int32_t batch, int32_t n_kv_heads, int64_t piece_len,
+                                          int64_t total, int32_t n_slots, int64_t w, PlanCursor& c, PlanPiece& out) {
+    const int64_t lo = w * piece_len, hi = lo + piece_len;
+    const int64_t w_last = plan_last_wg(total, piece_len);
+    if (w > w_last) return false;
+    while (c.b < batch) {
+        if (c.line >= hi && w != w_last) return false;
+        const int32_t len = len_of(c.b);
+        const int64_t pad = plan_pad(len);
+        if (pad == 0) {
+            const int64_t at = c.line / piece_len;
+            if ((at < w_last ? at : w_last) == w && c.g < n_kv_heads) {
+                out = PlanPiece{c.b, c.g, -1, n_slots, 0, 0};
+                ++c.g;
+                return true;
+            }
+        } else {
+            while (c.g < n_kv_heads) {
+                const int64_t o = c.line + (int64_t)c.g * pad;
+                // streams only start later from here on: none reaches w's range
+                if (o >= hi) return false;
+                const int32_t g = c.g++;
+                if (o + pad <= lo) continue;
+                const int32_t k = (int32_t)(w - o / piece_len);
+                const int32_t n_pieces = (int32_t)((o + pad - 1) / piece_len - o / piece_len + 1);
+                int64_t t0 = lo - o, t1 = hi - o;
+                if (t0 < 0) t0 = 0;
+                if (t1 > pad) t1 = pad;
+                if (t0 > len) t0 = len;
+                if (t1 > len) t1 = len;
+                out = PlanPiece{c.b, g, k, k == n_pieces - 1 ? n_slots : k + 1, t0, t1};
+                return true;
+            }
+        }
+        c.line += (int64_t)n_kv_heads * pad;
+        ++c.b;
+        c.g = 0;
+    }
+    return false;
+}
+
 // Ancestor visibility bits of a candidate tree (node i sees itself and its
 // ancestors). Parent pointers that do not point strictly backwards are read
 // as roots, so the walk is always in bounds.
@@ -64,6 +162,7 @@ struct ChunkParams {
     float* l;
     int32_t slot_begin;
     int32_t row_blocks;  // VALU kernels: rows are split into blocks of kValuRows
+    int32_t plan_slots;  // balanced history split: slots per stream (>= 2)
 };
 
 struct CandParams {
@@ -100,6 +199,12 @@ constexpr int kValuRows = 32;
 // Launchers (defined in the kernel translation units).
 hipError_t launch_chunk_valu(const ChunkParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
+// Balanced split of the whole resident history over one full wave of
+// work-groups (narrow MFMA kernel); p.plan_slots slots from p.slot_begin.
+hipError_t launch_history_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
+// Work-groups of the narrow MFMA kernels that one full wave of the current
+// device holds (resident work-groups per CU times CUs).
+hipError_t mfma_wave_work_groups(int rows, int* n);
 hipError_t launch_chunk_mfma_wide(const ChunkParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_chunk_valu_small(const ChunkParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_candidates(const CandParams& p, int dtype, int head_dim, hipStream_t stream);

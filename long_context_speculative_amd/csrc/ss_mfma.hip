@@ -63,26 +63,21 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-template <int D, int NRT>
-__global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) {
+// State of tokens [t0, t1) of stream (at.b(), at.g()) for every row of the
+// KV head, written to slot at.slot(). `at` is asked again at each use, so
+// that a caller can keep these indices out of registers during the key loop.
+// Uses the work-group's LDS; callers that run several pieces in a row
+// separate them with a barrier.
+template <int D, int NRT, class At>
+__device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT>& sm, const At& at, int64_t t0,
+                                           int64_t t1) {
     constexpr int NS = D / 32;   // feature steps of 32 for S = K Q^T
     constexpr int NXT = D / 16;  // 16-feature output tiles for O^T = V^T P^T
-    __shared__ MfmaSmem<D, NRT> sm;
-
-    // KV head fastest: the heads of one (slot, request) are dispatched
-    // together, so with token-major layouts they stream the same rows.
-    const int g = blockIdx.x % p.n_kv_heads;
-    const int s = blockIdx.x / p.n_kv_heads;
-    const int b = blockIdx.z;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
 
-    int32_t len = p.req_len ? p.req_len[b] : p.max_len;
-    len = min(max(len, 0), p.max_len);
-    int64_t t0, t1;
-    slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
-
-    const int64_t base = (p.req_offset ? p.req_offset[b] : (int64_t)b * p.stride_b) + (int64_t)g * p.stride_h;
+    const int64_t base = (p.req_offset ? p.req_offset[at.b()] : (int64_t)at.b() * p.stride_b) +
+                         (int64_t)at.g() * p.stride_h;
     const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(p.k) + base;
     const uint16_t* __restrict__ vp = static_cast<const uint16_t*>(p.v) + base;
     const int64_t st = p.stride_t;
@@ -93,8 +88,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) 
     for (int rt = 0; rt < NRT; ++rt) {
         const int r = l16 + 16 * rt;
         if (r < p.rows) {
-            const int i = r / p.group, h = g * p.group + r % p.group;
-            const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + ((int64_t)(b * p.n_queries + i) * p.n_q_heads + h) * D;
+            const int i = r / p.group, h = at.g() * p.group + r % p.group;
+            const uint16_t* qrow =
+                static_cast<const uint16_t*>(p.q) + ((int64_t)(at.b() * p.n_queries + i) * p.n_q_heads + h) * D;
 #pragma unroll
             for (int k = 0; k < NS; ++k) qf[rt][k] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 32 * k + 8 * q4));
         } else {
@@ -280,44 +276,204 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) 
         }
     }
     __syncthreads();
-    if (w != 0) return;
+    if (w == 0) {
+        for (int ww = 0; ww < kWaves - 1; ++ww) {
+            float a0[NRT], a1[NRT];
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const float mw = sm.u.mg.m[ww][l16 + 16 * rt];
+                const float lw = sm.u.mg.l[ww][l16 + 16 * rt];
+                const float m_new = fmaxf(m_run[rt], mw);
+                a0[rt] = (m_run[rt] == -INFINITY) ? 0.f : exp2_hw(m_run[rt] - m_new);
+                a1[rt] = (mw == -INFINITY) ? 0.f : exp2_hw(mw - m_new);
+                l_run[rt] = a0[rt] * l_run[rt] + a1[rt] * lw;
+                m_run[rt] = m_new;
+            }
+            int idx = 0;
+#pragma unroll
+            for (int xt = 0; xt < NXT; ++xt)
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        o[xt][rt][j] = a0[rt] * o[xt][rt][j] + a1[rt] * sm.u.mg.acc[ww][idx++][lane];
+                    }
+        }
 
-    for (int ww = 0; ww < kWaves - 1; ++ww) {
-        float a0[NRT], a1[NRT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            const float mw = sm.u.mg.m[ww][l16 + 16 * rt];
-            const float lw = sm.u.mg.l[ww][l16 + 16 * rt];
-            const float m_new = fmaxf(m_run[rt], mw);
-            a0[rt] = (m_run[rt] == -INFINITY) ? 0.f : exp2_hw(m_run[rt] - m_new);
-            a1[rt] = (mw == -INFINITY) ? 0.f : exp2_hw(mw - m_new);
-            l_run[rt] = a0[rt] * l_run[rt] + a1[rt] * lw;
-            m_run[rt] = m_new;
+            const int r = l16 + 16 * rt;
+            if (r >= p.rows) continue;
+            const int i = r / p.group, h = at.g() * p.group + r % p.group;
+            const int64_t row = (((int64_t)at.slot() * p.batch + at.b()) * p.n_queries + i) * p.n_q_heads + h;
+            if (q4 == 0) {
+                p.m[row] = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
+                p.l[row] = l_run[rt];
+            }
+#pragma unroll
+            for (int xt = 0; xt < NXT; ++xt)
+                *reinterpret_cast<floatx4*>(p.acc + row * D + 16 * xt + 4 * q4) = o[xt][rt];
         }
-        int idx = 0;
-#pragma unroll
-        for (int xt = 0; xt < NXT; ++xt)
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    o[xt][rt][j] = a0[rt] * o[xt][rt][j] + a1[rt] * sm.u.mg.acc[ww][idx++][lane];
-                }
     }
+}
 
-#pragma unroll
-    for (int rt = 0; rt < NRT; ++rt) {
-        const int r = l16 + 16 * rt;
-        if (r >= p.rows) continue;
-        const int i = r / p.group, h = g * p.group + r % p.group;
-        const int64_t row = (((int64_t)(p.slot_begin + s) * p.batch + b) * p.n_queries + i) * p.n_q_heads + h;
-        if (q4 == 0) {
-            p.m[row] = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
-            p.l[row] = l_run[rt];
+// Empty states (m = -inf, l = 0, acc = 0) for every row of stream (b, g) in
+// slots [s0, s1).
+template <int D>
+__device__ __forceinline__ void store_empty(const ChunkParams& p, int b, int g, int s0, int s1) {
+    constexpr int kVec = D / 4;
+    for (int slot = s0; slot < s1; ++slot) {
+        const int64_t base = ((int64_t)slot * p.batch + b) * p.n_queries;
+        for (int idx = threadIdx.x; idx < p.rows * kVec; idx += kThreads) {
+            const int r = idx / kVec, x = idx % kVec;
+            const int i = r / p.group, h = g * p.group + r % p.group;
+            const int64_t row = (base + i) * p.n_q_heads + h;
+            *reinterpret_cast<floatx4*>(p.acc + row * D + 4 * x) = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (x == 0) {
+                p.m[row] = -INFINITY;
+                p.l[row] = 0.f;
+            }
         }
+    }
+}
+
+// Piece indices of the chunk kernel: from the work-group's position.
+struct GridAt {
+    const ChunkParams& p;
+    // KV head fastest: the heads of one (slot, request) are dispatched
+    // together, so with token-major layouts they stream the same rows.
+    __device__ int g() const { return blockIdx.x % p.n_kv_heads; }
+    __device__ int b() const { return blockIdx.z; }
+    __device__ int slot() const { return p.slot_begin + (int)(blockIdx.x / p.n_kv_heads); }
+};
+
+// Piece indices of the history kernel: re-read from the LDS copy of the
+// current piece at every use.
+struct LdsAt {
+    const ChunkParams& p;
+    const volatile PlanPiece* pc;
+    __device__ int g() const { return __builtin_amdgcn_readfirstlane(pc->g); }
+    __device__ int b() const { return __builtin_amdgcn_readfirstlane(pc->b); }
+    __device__ int slot() const { return p.slot_begin + __builtin_amdgcn_readfirstlane(pc->k); }
+};
+
+template <int D, int NRT>
+__global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) {
+    __shared__ MfmaSmem<D, NRT> sm;
+    const int s = blockIdx.x / p.n_kv_heads;
+    const int b = blockIdx.z;
+    const int32_t len = clamp_len(p.req_len ? p.req_len[b] : p.max_len, p.max_len);
+    int64_t t0, t1;
+    slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
+    mfma_piece<D, NRT>(p, sm, GridAt{p}, t0, t1);
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// One step of the walk, kept out of line: it runs on one lane between
+// pieces, and inlined its 64-bit arithmetic would hold registers that the
+// key loop needs.
+__device__ __noinline__ int32_t plan_step(const int32_t* req_len, int32_t max_len, int32_t batch, int32_t n_kv_heads,
+                                          int64_t piece_len, int64_t total, int32_t n_slots, int64_t w,
+                                          PlanCursor* cursor, PlanPiece* out) {
+    auto len_of = [&](int32_t b) { return clamp_len(req_len ? req_len[b] : max_len, max_len); };
+    PlanCursor c = *cursor;
+    PlanPiece pc;
+    const bool more = plan_next(len_of, batch, n_kv_heads, piece_len, total, n_slots, w, c, pc);
+    *cursor = c;
+    if (more) *out = pc;
+    return more ? 1 : 0;
+}
+
+// The whole resident history of every request, cut into balanced pieces
+// (the line split of plan_next) over gridDim.x work-groups.
+template <int D, int NRT>
+__global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p) {
+    __shared__ MfmaSmem<D, NRT> sm;
+    const int lane = threadIdx.x & 63;
+    auto len_of = [&](int32_t b) { return clamp_len(p.req_len ? p.req_len[b] : p.max_len, p.max_len); };
+
+    // Line length and longest padded stream; every wave computes the same.
+    int64_t total = 0, pad_max = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int b = b0 + lane;
+        int64_t sum = b < p.batch ? plan_pad(len_of(b)) : 0, mx = sum;
 #pragma unroll
-        for (int xt = 0; xt < NXT; ++xt)
-            *reinterpret_cast<floatx4*>(p.acc + row * D + 16 * xt + 4 * q4) = o[xt][rt];
+        for (int off = 32; off > 0; off >>= 1) {
+            sum += __shfl_xor(sum, off);
+            mx = max(mx, (int64_t)__shfl_xor(mx, off));
+        }
+        total += sum;
+        pad_max = max(pad_max, mx);
+    }
+    total = uniform64(total * p.n_kv_heads);
+    pad_max = uniform64(pad_max);
+    const int64_t piece_len = plan_piece_len(total, pad_max, (int32_t)gridDim.x, p.plan_slots);
+    const int64_t w = blockIdx.x;
+    if (w > plan_last_wg(total, piece_len)) return;
+    const int64_t lo = w * piece_len;
+
+    // First request whose streams end after lo, or that starts at or after it.
+    int32_t b_first = p.batch;
+    int64_t line = 0, carry = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int b = b0 + lane;
+        const int64_t span = b < p.batch ? (int64_t)p.n_kv_heads * plan_pad(len_of(b)) : 0;
+        int64_t incl = span;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        const int64_t start = carry + incl - span;
+        const uint64_t hit = __ballot(b < p.batch && (start + span > lo || start >= lo));
+        if (hit) {
+            const int first = __ffsll((unsigned long long)hit) - 1;
+            b_first = b0 + first;
+            line = __shfl(start, first);
+            break;
+        }
+        carry += __shfl(incl, 63);
+    }
+    line = uniform64(line);
+    b_first = __builtin_amdgcn_readfirstlane(b_first);
+
+    // The walk runs on one lane with its cursor in LDS, so nothing of it is
+    // held in registers across a piece.
+    __shared__ PlanCursor cursor;
+    __shared__ PlanPiece piece;
+    __shared__ int32_t has_piece;
+    if (threadIdx.x == 0) cursor = PlanCursor{b_first, 0, line};
+    for (;;) {
+        __syncthreads();  // the previous piece is done with LDS; the cursor is visible
+        if (threadIdx.x == 0)
+            has_piece = plan_step(p.req_len, p.max_len, p.batch, p.n_kv_heads, piece_len, total, p.plan_slots, w,
+                                  &cursor, const_cast<PlanPiece*>(&piece));
+        __syncthreads();
+        if (!__builtin_amdgcn_readfirstlane(has_piece)) break;
+        // Re-read the arguments for every piece: held across the loop they
+        // would take scalar registers the key loop needs. (The host pass
+        // only checks this body; the kernarg segment exists on the device.)
+#if defined(__HIP_DEVICE_COMPILE__)
+        const __attribute__((address_space(4))) ChunkParams* args =
+            (const __attribute__((address_space(4))) ChunkParams*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(args));
+        const ChunkParams pa = *args;
+#else
+        const ChunkParams& pa = p;
+#endif
+        const volatile PlanPiece* pc = &piece;
+        const int32_t k = __builtin_amdgcn_readfirstlane(pc->k);
+        if (k >= pa.plan_slots) break;  // cannot happen with plan_piece_len; never write past the slots
+        if (k >= 0) mfma_piece<D, NRT>(pa, sm, LdsAt{pa, pc}, uniform64(pc->t0), uniform64(pc->t1));
+        const int32_t b = __builtin_amdgcn_readfirstlane(pc->b);
+        const int32_t g = __builtin_amdgcn_readfirstlane(pc->g);
+        const int32_t s0 = __builtin_amdgcn_readfirstlane(pc->k) + 1;
+        store_empty<D>(pa, b, g, pa.slot_begin + s0, pa.slot_begin + __builtin_amdgcn_readfirstlane(pc->fill_end));
     }
 }
 
@@ -330,12 +486,56 @@ hipError_t launch_t(const ChunkParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// One full wave of work-groups: resident work-groups per CU times CUs,
+// queried once per device.
+constexpr int kMaxDevices = 64;
+
+template <int D, int NRT>
+hipError_t wave_wgs_t(int* out) {
+    static int wave_wgs[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int n = __atomic_load_n(&wave_wgs[dev], __ATOMIC_RELAXED);
+    if (n <= 0) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, history_mfma_kernel<D, NRT>, kThreads, 0);
+        if (e != hipSuccess) return e;
+        n = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+        __atomic_store_n(&wave_wgs[dev], n, __ATOMIC_RELAXED);
+    }
+    *out = n;
+    return hipSuccess;
+}
+
+template <int D, int NRT>
+hipError_t launch_hist_t(const ChunkParams& p, hipStream_t stream) {
+    int n = 0;
+    hipError_t e = wave_wgs_t<D, NRT>(&n);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((history_mfma_kernel<D, NRT>), dim3(n), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 // The V staging map gives each of 16 lanes 8 features of a key: head_dim 128.
 hipError_t launch_chunk_mfma(const ChunkParams& p, int head_dim, hipStream_t stream) {
     if (head_dim != 128 || p.rows > 32) return hipErrorInvalidValue;
     return p.rows > 16 ? launch_t<128, 2>(p, stream) : launch_t<128, 1>(p, stream);
+}
+
+hipError_t mfma_wave_work_groups(int rows, int* n) {
+    if (rows > 32) return hipErrorInvalidValue;
+    return rows > 16 ? wave_wgs_t<128, 2>(n) : wave_wgs_t<128, 1>(n);
+}
+
+hipError_t launch_history_mfma(const ChunkParams& p, int head_dim, hipStream_t stream) {
+    if (head_dim != 128 || p.rows > 32 || p.plan_slots < 2) return hipErrorInvalidValue;
+    return p.rows > 16 ? launch_hist_t<128, 2>(p, stream) : launch_hist_t<128, 1>(p, stream);
 }
 
 }  // namespace ssv

@@ -1,8 +1,9 @@
 """One verification round on the GPU, composed from the C-ABI calls.
 
 ResidentRound: history resident in HBM -> ss_verify_candidates into slot 0,
-ss_verify_chunk over every chunk into slots 1.., ss_merge_states -> O, lse
-(ragged rounds fold only the slots each request's history reaches).
+the history into slots 1.. (ss_verify_chunk over fixed chunks, or
+ss_verify_history's balanced cut), ss_merge_states -> O, lse (ragged chunked
+rounds fold only the slots each request's history reaches).
 StreamedRound: history in pinned host memory -> ss_stream_history on a copy
 and a compute stream, then candidates and merge on the compute stream.
 
@@ -36,6 +37,28 @@ def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int) -> int:
     return max(1, units // (2 * cus))
 
 
+def auto_history_slots(cfg, hist_len, cus: int) -> int:
+    """Slots per stream for ss_verify_history. Ragged lengths: enough that
+    the longest stream does not force ranges longer than an even share of
+    one wave of work-groups (two per compute unit), plus one for the range
+    boundaries. Uniform lengths: one chunk per work-group of that wave. Wide
+    row groups use the fixed cut of 4 chunks per slot."""
+    pads = [-(-int(n) // 128) * 128 for n in hist_len]
+    pad_max = max(pads, default=0)
+    if cfg.rows > 32:
+        return max(1, -(-pad_max // (4 * cfg.chunk_len)))
+    if not cfg.ragged:
+        return max(1, 2 * cus // (cfg.batch * cfg.n_kv_heads))
+    total = sum(pads) * cfg.n_kv_heads
+    if total == 0:
+        return 2
+    return max(2, -(-pad_max * 2 * cus // total) + 2)
+
+
+# Launch configuration of the resident round that the benchmark times.
+BENCH_RESIDENT = dict(split="balanced", chunks_per_slot="auto", history_slots="auto")
+
+
 ENGINES = {"auto": ss.SS_ENGINE_AUTO, "valu": ss.SS_ENGINE_VALU, "mfma": ss.SS_ENGINE_MFMA}
 
 
@@ -45,13 +68,21 @@ def _problem(cfg, engine="auto") -> ss.Problem:
 
 
 class ResidentRound:
-    def __init__(self, inp: VerifyInputs, device="cuda", chunk_len=None, chunks_per_slot=1, engine="auto"):
-        """chunks_per_slot: an integer, or "auto" (auto_chunks_per_slot).
+    def __init__(self, inp: VerifyInputs, device="cuda", chunk_len=None, chunks_per_slot=1, engine="auto",
+                 split="chunks", history_slots="auto"):
+        """split: "chunks" (ss_verify_chunk over chunks of chunk_len, merged
+        chunks_per_slot at a time) or "balanced" (ss_verify_history with
+        history_slots slots per stream).
+        chunks_per_slot: an integer, or "auto" (auto_chunks_per_slot).
+        history_slots: an integer >= 1, or "auto" (auto_history_slots).
         engine: "auto", "valu" or "mfma" (ss_problem_t.engine)."""
         cfg = inp.cfg
         self.cfg = cfg
         self.problem = _problem(cfg, engine)
         self.chunk_len = chunk_len or cfg.chunk_len
+        if split not in ("chunks", "balanced"):
+            raise ValueError(f"unknown split {split!r}")
+        self.split = split
         if chunks_per_slot == "auto":
             chunks_per_slot = auto_chunks_per_slot(cfg, inp.hist_len, self.chunk_len, device_cus(device))
         self.cps = chunks_per_slot
@@ -77,11 +108,16 @@ class ResidentRound:
         if inp.parents is not None:
             self.parents = torch.as_tensor(inp.parents, dtype=torch.int32, device=device).contiguous()
         self.n_chunks = math.ceil(self.max_len / self.chunk_len)
-        self.n_hist_slots = math.ceil(self.n_chunks / self.cps)
+        if split == "balanced":
+            if history_slots == "auto":
+                history_slots = auto_history_slots(cfg, inp.hist_len, device_cus(device))
+            self.n_hist_slots = int(history_slots)
+        else:
+            self.n_hist_slots = math.ceil(self.n_chunks / self.cps)
         # slot 0: candidate region; slots 1 .. n_hist_slots: history
         self.state = ss.StateBuffers(self.problem, self.n_hist_slots + 1, device)
         self.slots_per_req = None
-        if cfg.ragged:
+        if cfg.ragged and split == "chunks":
             per_slot = self.chunk_len * self.cps
             counts = [1 + math.ceil(int(n) / per_slot) for n in inp.hist_len]
             self.slots_per_req = torch.tensor(counts, dtype=torch.int32, device=device)
@@ -91,6 +127,9 @@ class ResidentRound:
         self.lse = torch.empty((cfg.batch, cfg.n_queries, cfg.n_q_heads), dtype=torch.float32, device=device)
 
     def chunks(self, stream=None):
+        if self.split == "balanced":    # writes every history slot, even with no history
+            ss.ss_verify_history(self.problem, self.q, self.hist_view, self.n_hist_slots, self.state, 1, stream)
+            return
         if self.n_chunks == 0:          # no history at all: nothing to enqueue
             return
         ss.ss_verify_chunk(self.problem, self.q, self.hist_view, self.chunk_len, 0, self.n_chunks, self.cps,

@@ -28,8 +28,9 @@ SS_ENGINE_AUTO = 0
 SS_ENGINE_VALU = 1
 SS_ENGINE_MFMA = 2
 
-EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chunk", "ss_verify_candidates",
-            "ss_merge_states", "ss_stream_history", "ss_stream_timings", "ss_tree_mask_host", "ss_slot_tokens_host")
+EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chunk", "ss_verify_history",
+            "ss_verify_candidates", "ss_merge_states", "ss_stream_history", "ss_stream_timings", "ss_tree_mask_host",
+            "ss_slot_tokens_host", "ss_history_plan_host")
 
 
 class SSError(RuntimeError):
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.ss_state_bytes.argtypes = [P(Problem), I32]
         L.ss_verify_chunk.restype = I32
         L.ss_verify_chunk.argtypes = [P(Problem), VP, P(KVView), I32, I32, I32, I32, P(State), I32, VP]
+        L.ss_verify_history.restype = I32
+        L.ss_verify_history.argtypes = [P(Problem), VP, P(KVView), I32, P(State), I32, VP]
         L.ss_verify_candidates.restype = I32
         L.ss_verify_candidates.argtypes = [P(Problem), VP, P(KVView), VP, VP, P(State), I32, VP]
         L.ss_merge_states.restype = I32
@@ -86,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.ss_tree_mask_host.argtypes = [VP, I32, VP]
         L.ss_slot_tokens_host.restype = I32
         L.ss_slot_tokens_host.argtypes = [I32, I32, I32, I32, I32, I32, P(I64), P(I64)]
+        L.ss_history_plan_host.restype = I32
+        L.ss_history_plan_host.argtypes = [VP, I32, I32, I32, I32, I32, VP, P(I64)]
         _lib = L
     return _lib
 
@@ -178,6 +183,12 @@ def ss_verify_chunk(problem: Problem, q: torch.Tensor, hist: KVView, chunk_len: 
                                  n_chunks, chunks_per_slot, ctypes.byref(out.struct), slot_begin, _stream(stream)))
 
 
+def ss_verify_history(problem: Problem, q: torch.Tensor, hist: KVView, n_slots: int, out: StateBuffers,
+                      slot_begin: int, stream=None) -> None:
+    _check(lib().ss_verify_history(ctypes.byref(problem), q.data_ptr(), ctypes.byref(hist), n_slots,
+                                   ctypes.byref(out.struct), slot_begin, _stream(stream)))
+
+
 def ss_verify_candidates(problem: Problem, q: torch.Tensor, cand: KVView, parents: Optional[torch.Tensor],
                          mask_out: Optional[torch.Tensor], out: StateBuffers, slot: int, stream=None) -> None:
     _check(lib().ss_verify_candidates(ctypes.byref(problem), q.data_ptr(), ctypes.byref(cand), _ptr(parents),
@@ -219,3 +230,16 @@ def ss_slot_tokens_host(length: int, chunk_len: int, chunk_begin: int, n_chunks:
     _check(lib().ss_slot_tokens_host(length, chunk_len, chunk_begin, n_chunks, chunks_per_slot, s,
                                      ctypes.byref(t0), ctypes.byref(t1)))
     return t0.value, t1.value
+
+
+def ss_history_plan_host(lens, n_kv_heads: int, max_len: int, n_wg: int, n_slots: int):
+    """The balanced cut of ss_verify_history: (plan, piece_len) with plan an
+    int64 array [batch][n_kv_heads][n_slots][4] of {work-group, t0, t1,
+    writes}."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(lens, dtype=np.int32))
+    plan = np.empty((len(lens), n_kv_heads, n_slots, 4), dtype=np.int64)
+    piece = ctypes.c_int64()
+    _check(lib().ss_history_plan_host(lens.ctypes.data, len(lens), n_kv_heads, max_len, n_wg, n_slots,
+                                      plan.ctypes.data, ctypes.byref(piece)))
+    return plan, piece.value

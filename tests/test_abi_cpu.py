@@ -190,3 +190,95 @@ def test_slot_tokens_host_tile_history():
     # a sub-range of chunks
     assert ss.ss_slot_tokens_host(1000, 64, 3, 5, 2, 1) == (5 * 64, 7 * 64)
     assert ss.ss_slot_tokens_host(1000, 64, 3, 5, 2, 2) == (7 * 64, 8 * 64)
+
+
+def _check_plan(lens, hkv, max_len, n_wg, n_slots):
+    """Invariants of the balanced cut of ss_verify_history: every slot of
+    every stream is written exactly once; the computed pieces of a stream
+    come first and tile [0, len) in order; the rest are empty fills; no
+    work-group outside the grid is used, and no work-group gets more than
+    piece_len (padded) tokens or more than its share plus one alignment
+    step."""
+    plan, piece_len = ss.ss_history_plan_host(lens, hkv, max_len, n_wg, n_slots)
+    lens_c = np.clip(np.asarray(lens, dtype=np.int64), 0, max_len)
+    pad = -(-lens_c // 128) * 128
+    total = int(pad.sum()) * hkv
+    assert piece_len % 128 == 0 and piece_len >= 128
+    # the cut grows past an even share only to respect the slot budget
+    even = -(-total // n_wg)
+    cap = -(-int(pad.max(initial=0)) // (n_slots - 1))
+    assert piece_len < max(even, cap, 128) + 128
+    assert (plan[..., 3] == 1).all(), "a slot written zero or several times"
+    load = {}
+    for b, n in enumerate(lens_c):
+        for g in range(hkv):
+            e = plan[b, g]
+            computed = [k for k in range(n_slots) if e[k, 1] >= 0]
+            assert computed == list(range(len(computed)))
+            if n == 0:
+                assert not computed
+                continue
+            assert computed, "a non-empty stream without pieces"
+            assert e[0, 1] == 0 and e[computed[-1], 2] == n
+            for k in computed[1:]:
+                assert e[k, 1] == e[k - 1, 2]
+            for k in computed:
+                wg = int(e[k, 0])
+                assert 0 <= wg < n_wg
+                # padded extent of the piece inside the work-group's range
+                t0, t1 = int(e[k, 1]), int(e[k, 2])
+                end = int(pad[b]) if k == computed[-1] else t1
+                load[wg] = load.get(wg, 0) + (end - t0)
+            # consecutive pieces go to consecutive work-groups
+            wgs = [int(e[k, 0]) for k in computed]
+            assert wgs == list(range(wgs[0], wgs[0] + len(wgs)))
+    assert all(v <= piece_len for v in load.values())
+    return plan, piece_len
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_history_plan_host_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    batch = int(rng.choice([1, 3, 32, 70, 200]))
+    hkv = int(rng.choice([1, 2, 8]))
+    max_len = int(rng.choice([1, 127, 1000, 65536]))
+    lens = rng.integers(0, max_len + 1, size=batch)
+    lens[rng.random(batch) < 0.2] = 0
+    n_wg = int(rng.choice([1, 7, 64, 512]))
+    n_slots = int(rng.choice([2, 3, 5, 16]))
+    _check_plan(lens, hkv, max_len, n_wg, n_slots)
+
+
+def test_history_plan_host_cases():
+    # uniform lengths: equal ranges, one stream per pair of work-groups
+    plan, L = _check_plan([32768] * 16, 8, 32768, 256, 4)
+    assert L == 16384 and int(plan[..., 0].max()) == 255
+    # the ragged long-history shape: every work-group gets an even share
+    lens = workloads.draw_lengths(workloads.CONFIGS["c3_internlm25_7b_ragged"]).astype(np.int64)
+    plan, L = _check_plan(lens, 8, int(max(lens)), 512, 6)
+    assert L == -(-(-(-lens // 128) * 128).sum() * 8 // 512 // 128) * 128
+    # a slot budget too small for an even cut widens the ranges
+    plan, L = _check_plan([100000], 1, 100000, 512, 2)
+    assert L >= 100096 // 1 and (plan[0, 0, :, 1] >= 0).sum() <= 2
+    # only empty requests: all slots filled empty by work-group 0
+    plan, L = _check_plan([0, 0, 0], 4, 10, 8, 3)
+    assert (plan[..., 0] == 0).all() and (plan[..., 1] == -1).all()
+    # lengths past max_len are clamped, negative ones read as empty
+    _check_plan([5000, -3, 10**6], 2, 4096, 16, 4)
+    with pytest.raises(ss.SSError):
+        ss.ss_history_plan_host([10], 1, 10, 4, 1)
+
+
+def test_verify_history_rejects():
+    L = ss.lib()
+    p = _problem()
+    view = _view(max_len=1000)
+    rc = L.ss_verify_history(ctypes.byref(p), 4096, ctypes.byref(view), 0, ctypes.byref(_state(4).struct), 0, None)
+    assert rc == ss.SS_ERR_INVALID_ARG            # n_slots < 1
+    rc = L.ss_verify_history(ctypes.byref(p), 4096, ctypes.byref(view), 4, ctypes.byref(_state(4).struct), 1, None)
+    assert rc == ss.SS_ERR_INVALID_ARG            # slots [1, 5) of 4
+    rc = L.ss_verify_history(ctypes.byref(p), None, ctypes.byref(view), 2, ctypes.byref(_state(4).struct), 0, None)
+    assert rc == ss.SS_ERR_INVALID_ARG
+    rc = L.ss_verify_history(ctypes.byref(_problem(head_dim=96)), 4096, ctypes.byref(view), 2,
+                             ctypes.byref(_state(4).struct), 0, None)
+    assert rc == ss.SS_ERR_UNSUPPORTED
