@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 3
+#define SS_ABI_VERSION 4
 
 /* status codes */
 #define SS_OK 0
@@ -168,13 +168,18 @@ SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const
  * ss_verify_history -- the state of every request's whole resident history
  * [0, len_b), cut where the load balances best (section 4.2: the history
  * serves the whole query group, and by Eq. 9 the merged result does not
- * depend on where it is cut).
+ * depend on where it is cut), optionally together with the candidate region.
  *
  *   q, hist     as ss_verify_chunk; len_b = req_len[b] (or max_len),
  *               clamped to [0, max_len]
- *   n_slots     slots per (request, KV head) the call may use, >= 1; the
- *               call writes exactly slots [slot_begin, slot_begin + n_slots)
- *               of every row, the ones it does not need as empty states
+ *   cand        NULL, or the candidate keys/values as in
+ *               ss_verify_candidates (cand->max_len == n_queries <= 64);
+ *               then the call's slots hold history and candidates together
+ *   parents, mask_out  as ss_verify_candidates (used only with cand)
+ *   n_slots     slots per (request, KV head) the call may use, >= 1 (>= 2
+ *               with cand outside the narrow MFMA kernel); the call writes
+ *               exactly slots [slot_begin, slot_begin + n_slots) of every
+ *               row, the ones it does not need as empty states
  * With the narrow MFMA kernel (AUTO or MFMA engine, bf16, head_dim 128,
  * R <= 32):
  *   - ragged lengths (hist->req_len given) and n_slots >= 2: the streams
@@ -190,9 +195,14 @@ SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const
  * into n_slots chunks of ceil(max_len / n_slots) tokens. Chunks are rounded
  * up to a multiple of 128 tokens and run as ss_verify_chunk with
  * chunks_per_slot 1; chunks past a request's end are empty slots.
- * Errors: as ss_verify_chunk.
+ * Candidates: the narrow MFMA kernel attends them as one more masked key
+ * tile of the work-group that holds a stream's first piece (no extra launch,
+ * no extra slot); other engines run ss_verify_candidates into slot_begin
+ * and cut the history into the remaining n_slots - 1 slots.
+ * Errors: as ss_verify_chunk and ss_verify_candidates.
  */
 SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                 const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
                                  int32_t n_slots, const ss_state_t* out, int32_t slot_begin, ss_stream_t stream);
 
 /*

@@ -221,58 +221,22 @@ extern "C" SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const voi
     return ok();
 }
 
-extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
-                                            int32_t n_slots, const ss_state_t* out, int32_t slot_begin,
-                                            ss_stream_t stream) {
-    if (!hist) return fail(SS_ERR_INVALID_ARG, "history view is NULL");
-    if (n_slots < 1) return fail(SS_ERR_INVALID_ARG, "n_slots must be at least 1");
-    // validation first (the chunk length does not change its outcome)
-    int32_t rc = validate_chunk(problem, q, hist, kPlanAlign, 0, n_slots, 1, out, slot_begin);
-    if (rc) return rc;
-    const bool narrow = chunk_engine(problem) == ChunkEngine::kMfma;
-    const int64_t streams = (int64_t)problem->batch * problem->n_kv_heads;
-    // Pieces per stream of a cut by fixed chunks: n_slots, or for uniform
-    // lengths on the narrow kernel as many as fill one wave of work-groups.
-    int64_t pieces = n_slots;
-    if (narrow && !hist->req_len) {
-        int wgs = 0;
-        hipError_t e = mfma_wave_work_groups(problem->n_queries * (problem->n_q_heads / problem->n_kv_heads), &wgs);
-        if (e != hipSuccess) return fail(SS_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
-        pieces = wgs / streams;
-        if (pieces < 1) pieces = 1;
-        if (pieces > n_slots) pieces = n_slots;
-    }
-    int64_t chunk = ((int64_t)hist->max_len + pieces - 1) / pieces;
-    chunk = (chunk + kPlanAlign - 1) / kPlanAlign * kPlanAlign;
-    if (chunk < kPlanAlign) chunk = kPlanAlign;
-    if (chunk > 0x7fffffff) chunk = 0x7fffffff;
-    ChunkParams c = make_chunk_params(problem, q, hist, (int32_t)chunk, 0, n_slots, 1, out, slot_begin);
-    hipError_t e;
-    if (narrow && hist->req_len && n_slots >= 2) {
-        c.plan_slots = n_slots;
-        e = launch_history_mfma(c, problem->head_dim, static_cast<hipStream_t>(stream));
-    } else {
-        e = enqueue_chunk(problem, c, static_cast<hipStream_t>(stream));
-    }
-    if (e != hipSuccess) return fail(SS_ERR_HIP, "history kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
-}
+namespace {
 
-extern "C" SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, const void* q, const ss_kv_view_t* cand,
-                                               const int32_t* parents, uint64_t* mask_out, const ss_state_t* out,
-                                               int32_t slot, ss_stream_t stream) {
-    int32_t rc = check_problem(problem);
+// Validation of a candidate view for a problem (shared by the two calls
+// that take one).
+int32_t check_cand(const ss_problem_t* problem, const ss_kv_view_t* cand) {
+    int32_t rc = check_view(problem, cand, "candidate");
     if (rc) return rc;
-    if (!q) return fail(SS_ERR_INVALID_ARG, "q is NULL");
-    if (!aligned16(q)) return fail(SS_ERR_INVALID_ARG, "q must be 16-byte aligned");
-    if ((rc = check_view(problem, cand, "candidate"))) return rc;
-    if ((rc = check_state(out, "output"))) return rc;
     if (problem->n_queries > 64) return fail(SS_ERR_UNSUPPORTED, "more than 64 candidates per request");
     if (cand->max_len != problem->n_queries)
         return fail(SS_ERR_INVALID_ARG, "candidate max_len (%d) must equal n_queries (%d)", cand->max_len,
                     problem->n_queries);
-    if (slot < 0 || slot >= out->n_slots) return fail(SS_ERR_INVALID_ARG, "slot %d outside [0, %d)", slot, out->n_slots);
+    return SS_OK;
+}
 
+CandParams make_cand_params(const ss_problem_t* problem, const void* q, const ss_kv_view_t* cand,
+                            const int32_t* parents, uint64_t* mask_out, const ss_state_t* out, int32_t slot) {
     CandParams c{};
     c.q = q;
     c.k = cand->k;
@@ -295,7 +259,84 @@ extern "C" SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, cons
     c.l = out->l;
     c.slot = slot;
     c.row_blocks = cand_row_blocks(c.rows);
-    hipError_t e = launch_candidates(c, problem->dtype, problem->head_dim, static_cast<hipStream_t>(stream));
+    return c;
+}
+
+}  // namespace
+
+extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                            const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
+                                            int32_t n_slots, const ss_state_t* out, int32_t slot_begin,
+                                            ss_stream_t stream) {
+    if (!hist) return fail(SS_ERR_INVALID_ARG, "history view is NULL");
+    if (n_slots < 1) return fail(SS_ERR_INVALID_ARG, "n_slots must be at least 1");
+    // validation first (the chunk length does not change its outcome)
+    int32_t rc = validate_chunk(problem, q, hist, kPlanAlign, 0, n_slots, 1, out, slot_begin);
+    if (rc) return rc;
+    if (cand && (rc = check_cand(problem, cand))) return rc;
+    const bool narrow = chunk_engine(problem) == ChunkEngine::kMfma;
+    if (cand && !narrow && n_slots < 2)
+        return fail(SS_ERR_INVALID_ARG, "with candidates this engine needs n_slots >= 2");
+    // Slots of the history cut by fixed chunks (other engines with
+    // candidates give the first slot to the candidate region).
+    const int32_t hist_slots = (cand && !narrow) ? n_slots - 1 : n_slots;
+    const int32_t hist_begin = (cand && !narrow) ? slot_begin + 1 : slot_begin;
+    const int64_t streams = (int64_t)problem->batch * problem->n_kv_heads;
+    // Pieces per stream of a cut by fixed chunks: hist_slots, or for uniform
+    // lengths on the narrow kernel as many as fill one wave of work-groups.
+    int64_t pieces = hist_slots;
+    if (narrow && !hist->req_len) {
+        int wgs = 0;
+        hipError_t e = mfma_wave_work_groups(problem->n_queries * (problem->n_q_heads / problem->n_kv_heads), &wgs);
+        if (e != hipSuccess) return fail(SS_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+        pieces = wgs / streams;
+        if (pieces < 1) pieces = 1;
+        if (pieces > hist_slots) pieces = hist_slots;
+    }
+    int64_t chunk = ((int64_t)hist->max_len + pieces - 1) / pieces;
+    chunk = (chunk + kPlanAlign - 1) / kPlanAlign * kPlanAlign;
+    if (chunk < kPlanAlign) chunk = kPlanAlign;
+    if (chunk > 0x7fffffff) chunk = 0x7fffffff;
+    ChunkParams c = make_chunk_params(problem, q, hist, (int32_t)chunk, 0, hist_slots, 1, out, hist_begin);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (cand && narrow) {
+        c.with_cand = 1;
+        c.ck = cand->k;
+        c.cv = cand->v;
+        c.c_stride_b = cand->stride_b;
+        c.c_stride_h = cand->stride_h;
+        c.c_stride_t = cand->stride_t;
+        c.c_req_offset = cand->req_offset;
+        c.parents = parents;
+        c.mask_out = mask_out;
+    } else if (cand) {
+        e = launch_candidates(make_cand_params(problem, q, cand, parents, mask_out, out, slot_begin), problem->dtype,
+                              problem->head_dim, s);
+        if (e != hipSuccess) return fail(SS_ERR_HIP, "candidate kernel launch failed: %s", hipGetErrorString(e));
+    }
+    if (narrow && hist->req_len && hist_slots >= 2) {
+        c.plan_slots = hist_slots;
+        e = launch_history_mfma(c, problem->head_dim, s);
+    } else {
+        e = enqueue_chunk(problem, c, s);
+    }
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "history kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, const void* q, const ss_kv_view_t* cand,
+                                               const int32_t* parents, uint64_t* mask_out, const ss_state_t* out,
+                                               int32_t slot, ss_stream_t stream) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if (!q) return fail(SS_ERR_INVALID_ARG, "q is NULL");
+    if (!aligned16(q)) return fail(SS_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if ((rc = check_cand(problem, cand))) return rc;
+    if ((rc = check_state(out, "output"))) return rc;
+    if (slot < 0 || slot >= out->n_slots) return fail(SS_ERR_INVALID_ARG, "slot %d outside [0, %d)", slot, out->n_slots);
+    hipError_t e = launch_candidates(make_cand_params(problem, q, cand, parents, mask_out, out, slot), problem->dtype,
+                                     problem->head_dim, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SS_ERR_HIP, "candidate kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

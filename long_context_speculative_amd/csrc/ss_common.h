@@ -163,6 +163,15 @@ struct ChunkParams {
     int32_t slot_begin;
     int32_t row_blocks;  // VALU kernels: rows are split into blocks of kValuRows
     int32_t plan_slots;  // balanced history split: slots per stream (>= 2)
+    // Candidate region folded into each stream's first piece (narrow MFMA
+    // kernels, ss_verify_history only): with_cand != 0.
+    int32_t with_cand;
+    const void* ck;
+    const void* cv;
+    int64_t c_stride_b, c_stride_h, c_stride_t;
+    const int64_t* c_req_offset;
+    const int32_t* parents;
+    uint64_t* mask_out;
 };
 
 struct CandParams {

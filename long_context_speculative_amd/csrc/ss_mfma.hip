@@ -43,6 +43,7 @@ constexpr int kVtRow = 36;     // bf16 per transposed-V row: 32 keys + 4 pad (72
 template <int D, int NRT>
 struct MfmaSmem {
     static constexpr int kAccRegs = (D / 16) * NRT * 4;  // accumulator floats per lane
+    uint64_t cbits[32];  // candidate visibility bits (at most 32 candidates here)
     union {
         uint16_t vt[kWaves][D][kVtRow];
         struct {
@@ -64,13 +65,14 @@ __device__ __forceinline__ void wave_sync() {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // State of tokens [t0, t1) of stream (at.b(), at.g()) for every row of the
-// KV head, written to slot at.slot(). `at` is asked again at each use, so
+// KV head, and with `cand` also of the request's candidate rows under their
+// mask, written to slot at.slot(). `at` is asked again at each use, so
 // that a caller can keep these indices out of registers during the key loop.
 // Uses the work-group's LDS; callers that run several pieces in a row
 // separate them with a barrier.
 template <int D, int NRT, class At>
 __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT>& sm, const At& at, int64_t t0,
-                                           int64_t t1) {
+                                           int64_t t1, bool cand) {
     constexpr int NS = D / 32;   // feature steps of 32 for S = K Q^T
     constexpr int NXT = D / 16;  // 16-feature output tiles for O^T = V^T P^T
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -119,41 +121,39 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
     // Loads address a tile as a uniform base (scalar registers) plus a 32-bit
     // per-lane offset. Keys past the range are clamped to its last key so
     // every load stays in bounds; their scores are masked below.
-    const int sti = (int)st;
     // K fragment: keys 16*kt + l16 of the tile, features 32*k + 8*q4 .. +7.
-    auto load_k = [&](int64_t tk, u32x4(&dst)[2][NS]) {
-        const uint16_t* tb = kp + tk * st;
-        const int last = (int)min((int64_t)kTile, t1 - tk) - 1;
+    auto load_k_at = [&](const uint16_t* tb, int stride, int last, u32x4(&dst)[2][NS]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-            const int off = min(16 * kt + l16, last) * sti + 8 * q4;
+            const int off = min(16 * kt + l16, last) * stride + 8 * q4;
 #pragma unroll
             for (int k = 0; k < NS; ++k) dst[kt][k] = *reinterpret_cast<const u32x4*>(tb + off + 32 * k);
         }
     };
     // V rows 4*kg + e (kg = q4 + 4*h), features 8*l16 .. +7.
-    auto load_v = [&](int64_t tk, u32x4(&dst)[2][4]) {
-        const uint16_t* tb = vp + tk * st;
-        const int last = (int)min((int64_t)kTile, t1 - tk) - 1;
+    auto load_v_at = [&](const uint16_t* tb, int stride, int last, u32x4(&dst)[2][4]) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int off = min(4 * (q4 + 4 * h) + e, last) * sti + 8 * l16;
+                const int off = min(4 * (q4 + 4 * h) + e, last) * stride + 8 * l16;
                 dst[h][e] = *reinterpret_cast<const u32x4*>(tb + off);
             }
     };
+    const int sti = (int)st;
+    auto load_k = [&](int64_t tk, u32x4(&dst)[2][NS]) {
+        load_k_at(kp + tk * st, sti, (int)min((int64_t)kTile, t1 - tk) - 1, dst);
+    };
+    auto load_v = [&](int64_t tk, u32x4(&dst)[2][4]) {
+        load_v_at(vp + tk * st, sti, (int)min((int64_t)kTile, t1 - tk) - 1, dst);
+    };
 
-    u32x4 kf[2][NS], vr[2][4];
-    int tau = w;
-    if (tau < n_tiles) {
-        load_k(t0 + (int64_t)kTile * tau, kf);
-        load_v(t0 + (int64_t)kTile * tau, vr);
-    }
-    for (; tau < n_tiles; tau += kWaves) {
-        const int64_t tk = t0 + (int64_t)kTile * tau;
-
-        // Stage V(tau) transposed: vt[x][key] holds 4 keys per 8-byte word.
+    // One tile: the first `valid` keys, and of those only the ones whose bit
+    // is set in vis[rt] (per lane row) when `masked`. after_stage runs once
+    // V is in LDS (its registers are free), after_s once S^T has read K.
+    auto consume = [&](u32x4(&kf)[2][NS], u32x4(&vr)[2][4], int valid, bool masked, const uint32_t(&vis)[NRT],
+                       auto after_stage, auto after_s) {
+        // Stage V transposed: vt[x][key] holds 4 keys per 8-byte word.
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int kg = q4 + 4 * h;
@@ -167,11 +167,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
                 *reinterpret_cast<u32x2*>(&vt[x + 1][4 * kg]) = hi;
             }
         }
-
-        // Prefetch the wave's next tile into the registers just consumed:
-        // V right away (staged above), K once the S^T products have read it.
-        const bool more = tau + kWaves < n_tiles;
-        if (more) load_v(tk + kTile * kWaves, vr);
+        after_stage();
 
         // S^T = K Q^T
         floatx4 sc[2][NRT];
@@ -185,10 +181,10 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
                     a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[kt][k]), qf[rt][k], a, 0, 0, 0);
                 sc[kt][rt] = a;
             }
-        if (more) load_k(tk + kTile * kWaves, kf);
+        after_s();
 
-        // Scale to base 2, mask keys past the range, tile max per row.
-        const int valid = (int)min((int64_t)kTile, t1 - tk);
+        // Scale to base 2, mask keys past the range (and hidden candidates),
+        // tile max per row.
         bool grow = false;
         float alpha[NRT];
 #pragma unroll
@@ -199,7 +195,8 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int key = 16 * kt + 4 * q4 + j;
-                    const float v = key < valid ? sc[kt][rt][j] * c : -INFINITY;
+                    const bool seen = key < valid && (!masked || ((vis[rt] >> key) & 1u));
+                    const float v = seen ? sc[kt][rt][j] * c : -INFINITY;
                     sc[kt][rt][j] = v;
                     mx = fmaxf(mx, v);
                 }
@@ -221,7 +218,10 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
 
         // P = 2^(S - m) in bf16 (B operand of the PV product); l sums the
         // rounded weights so numerator and denominator use the same values.
-        bf16x8 pf[NRT];
+        // The masked (candidate) tile also carries the rounding remainder as
+        // a second bf16 operand: a row that sees only a few candidates would
+        // otherwise feel the 2^-9 weight rounding at full strength.
+        bf16x8 pf[NRT], pr[NRT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             float ls = 0.f;
@@ -229,9 +229,16 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const __bf16 pb = (__bf16)exp2_hw(sc[kt][rt][j] - m_run[rt]);
+                    const float pv = exp2_hw(sc[kt][rt][j] - m_run[rt]);
+                    const __bf16 pb = (__bf16)pv;
                     pf[rt][4 * kt + j] = pb;
-                    ls += (float)pb;
+                    if (masked) {
+                        const __bf16 rb = (__bf16)(pv - (float)pb);
+                        pr[rt][4 * kt + j] = rb;
+                        ls += (float)pb + (float)rb;
+                    } else {
+                        ls += (float)pb;
+                    }
                 }
             l_run[rt] += ls;
         }
@@ -245,9 +252,53 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
             const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 16 + 4 * q4);
             const bf16x8 a = as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[xt][rt], 0, 0, 0);
+            for (int rt = 0; rt < NRT; ++rt) {
+                o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[xt][rt], 0, 0, 0);
+                if (masked) o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pr[rt], o[xt][rt], 0, 0, 0);
+            }
         }
         wave_sync();
+    };
+
+    const uint32_t no_vis[NRT] = {};
+    u32x4 kf[2][NS], vr[2][4];
+    int tau = w;
+    if (tau < n_tiles) {
+        load_k(t0 + (int64_t)kTile * tau, kf);
+        load_v(t0 + (int64_t)kTile * tau, vr);
+    }
+    for (; tau < n_tiles; tau += kWaves) {
+        const int64_t tk = t0 + (int64_t)kTile * tau;
+        // Prefetch the wave's next tile into the registers just consumed:
+        // V right away (staged), K once the S^T products have read it.
+        const bool more = tau + kWaves < n_tiles;
+        consume(kf, vr, (int)min((int64_t)kTile, t1 - tk), false, no_vis,
+                [&] { if (more) load_v(tk + kTile * kWaves, vr); },
+                [&] { if (more) load_k(tk + kTile * kWaves, kf); });
+    }
+
+    // The candidate region (section 4.2: the GPU-resident rows under each
+    // query's mask) as one more masked tile of wave 0: n_queries <= 32 keys.
+    if (cand && w == 0) {
+        const int n = p.n_queries;
+        if (lane == 0) {
+            for (int i = 0; i < n; ++i)
+                sm.cbits[i] = p.parents ? tree_bits_step(sm.cbits, i, p.parents[(int64_t)at.b() * n + i])
+                                        : chain_bits(i);
+        }
+        wave_sync();
+        if (p.mask_out && at.g() == 0 && lane < n) p.mask_out[(int64_t)at.b() * n + lane] = sm.cbits[lane];
+        uint32_t vis[NRT];
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            const int r = l16 + 16 * rt;
+            vis[rt] = r < p.rows ? (uint32_t)sm.cbits[r / p.group] : ~0u;  // padded rows see all (discarded)
+        }
+        const int64_t cbase = (p.c_req_offset ? p.c_req_offset[at.b()] : (int64_t)at.b() * p.c_stride_b) +
+                              (int64_t)at.g() * p.c_stride_h;
+        load_k_at(static_cast<const uint16_t*>(p.ck) + cbase, (int)p.c_stride_t, n - 1, kf);
+        load_v_at(static_cast<const uint16_t*>(p.cv) + cbase, (int)p.c_stride_t, n - 1, vr);
+        consume(kf, vr, n, true, vis, [] {}, [] {});
     }
 
     // Full row sums: the 4 lane groups hold disjoint keys of the same rows.
@@ -354,7 +405,7 @@ struct LdsAt {
     const volatile PlanPiece* pc;
     __device__ int g() const { return __builtin_amdgcn_readfirstlane(pc->g); }
     __device__ int b() const { return __builtin_amdgcn_readfirstlane(pc->b); }
-    __device__ int slot() const { return p.slot_begin + __builtin_amdgcn_readfirstlane(pc->k); }
+    __device__ int slot() const { return p.slot_begin + max(__builtin_amdgcn_readfirstlane(pc->k), 0); }
 };
 
 template <int D, int NRT>
@@ -365,7 +416,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) 
     const int32_t len = clamp_len(p.req_len ? p.req_len[b] : p.max_len, p.max_len);
     int64_t t0, t1;
     slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
-    mfma_piece<D, NRT>(p, sm, GridAt{p}, t0, t1);
+    mfma_piece<D, NRT>(p, sm, GridAt{p}, t0, t1, p.with_cand && s == 0);
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
@@ -469,10 +520,13 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
         const volatile PlanPiece* pc = &piece;
         const int32_t k = __builtin_amdgcn_readfirstlane(pc->k);
         if (k >= pa.plan_slots) break;  // cannot happen with plan_piece_len; never write past the slots
-        if (k >= 0) mfma_piece<D, NRT>(pa, sm, LdsAt{pa, pc}, uniform64(pc->t0), uniform64(pc->t1));
+        // The candidate region joins each stream's first piece; a stream
+        // without history gets it alone in slot 0 (t0 = t1 = 0).
+        const bool cand = pa.with_cand && k <= 0;
+        if (k >= 0 || cand) mfma_piece<D, NRT>(pa, sm, LdsAt{pa, pc}, uniform64(pc->t0), uniform64(pc->t1), cand);
         const int32_t b = __builtin_amdgcn_readfirstlane(pc->b);
         const int32_t g = __builtin_amdgcn_readfirstlane(pc->g);
-        const int32_t s0 = __builtin_amdgcn_readfirstlane(pc->k) + 1;
+        const int32_t s0 = max(__builtin_amdgcn_readfirstlane(pc->k), cand ? 0 : -1) + 1;
         store_empty<D>(pa, b, g, pa.slot_begin + s0, pa.slot_begin + __builtin_amdgcn_readfirstlane(pc->fill_end));
     }
 }

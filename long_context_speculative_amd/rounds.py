@@ -3,7 +3,8 @@
 ResidentRound: history resident in HBM -> ss_verify_candidates into slot 0,
 the history into slots 1.. (ss_verify_chunk over fixed chunks, or
 ss_verify_history's balanced cut), ss_merge_states -> O, lse (ragged chunked
-rounds fold only the slots each request's history reaches).
+rounds fold only the slots each request's history reaches). With the
+candidate region fused, one ss_verify_history call writes all slots.
 StreamedRound: history in pinned host memory -> ss_stream_history on a copy
 and a compute stream, then candidates and merge on the compute stream.
 
@@ -55,8 +56,14 @@ def auto_history_slots(cfg, hist_len, cus: int) -> int:
     return max(2, -(-pad_max * 2 * cus // total) + 2)
 
 
+def narrow_mfma(cfg, engine="auto") -> bool:
+    """Whether the library runs this shape on its narrow MFMA kernels (the
+    ones that can fold the candidate region into the history launch)."""
+    return engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim == 128 and cfg.rows <= 32
+
+
 # Launch configuration of the resident round that the benchmark times.
-BENCH_RESIDENT = dict(split="balanced", chunks_per_slot="auto", history_slots="auto")
+BENCH_RESIDENT = dict(split="balanced", chunks_per_slot="auto", history_slots="auto", fuse_candidates="auto")
 
 
 ENGINES = {"auto": ss.SS_ENGINE_AUTO, "valu": ss.SS_ENGINE_VALU, "mfma": ss.SS_ENGINE_MFMA}
@@ -69,10 +76,13 @@ def _problem(cfg, engine="auto") -> ss.Problem:
 
 class ResidentRound:
     def __init__(self, inp: VerifyInputs, device="cuda", chunk_len=None, chunks_per_slot=1, engine="auto",
-                 split="chunks", history_slots="auto"):
+                 split="chunks", history_slots="auto", fuse_candidates=False):
         """split: "chunks" (ss_verify_chunk over chunks of chunk_len, merged
         chunks_per_slot at a time) or "balanced" (ss_verify_history with
         history_slots slots per stream).
+        fuse_candidates (balanced split only): True, False or "auto" (when
+        the narrow MFMA kernel serves the shape): pass the candidate region
+        to ss_verify_history instead of a separate ss_verify_candidates.
         chunks_per_slot: an integer, or "auto" (auto_chunks_per_slot).
         history_slots: an integer >= 1, or "auto" (auto_history_slots).
         engine: "auto", "valu" or "mfma" (ss_problem_t.engine)."""
@@ -108,14 +118,23 @@ class ResidentRound:
         if inp.parents is not None:
             self.parents = torch.as_tensor(inp.parents, dtype=torch.int32, device=device).contiguous()
         self.n_chunks = math.ceil(self.max_len / self.chunk_len)
+        if fuse_candidates == "auto":
+            fuse_candidates = narrow_mfma(cfg, engine)
+        self.fused = bool(fuse_candidates) and split == "balanced"
         if split == "balanced":
             if history_slots == "auto":
                 history_slots = auto_history_slots(cfg, inp.hist_len, device_cus(device))
             self.n_hist_slots = int(history_slots)
         else:
             self.n_hist_slots = math.ceil(self.n_chunks / self.cps)
-        # slot 0: candidate region; slots 1 .. n_hist_slots: history
-        self.state = ss.StateBuffers(self.problem, self.n_hist_slots + 1, device)
+        if self.fused:
+            # one call writes every slot; outside the narrow kernel it gives
+            # the first to the candidate region
+            self.n_call_slots = self.n_hist_slots + (0 if narrow_mfma(cfg, engine) else 1)
+            self.state = ss.StateBuffers(self.problem, self.n_call_slots, device)
+        else:
+            # slot 0: candidate region; slots 1 .. n_hist_slots: history
+            self.state = ss.StateBuffers(self.problem, self.n_hist_slots + 1, device)
         self.slots_per_req = None
         if cfg.ragged and split == "chunks":
             per_slot = self.chunk_len * self.cps
@@ -127,8 +146,13 @@ class ResidentRound:
         self.lse = torch.empty((cfg.batch, cfg.n_queries, cfg.n_q_heads), dtype=torch.float32, device=device)
 
     def chunks(self, stream=None):
+        if self.fused:                  # history and candidates, every slot written
+            ss.ss_verify_history(self.problem, self.q, self.hist_view, self.cand_view, self.parents, self.mask_out,
+                                 self.n_call_slots, self.state, 0, stream)
+            return
         if self.split == "balanced":    # writes every history slot, even with no history
-            ss.ss_verify_history(self.problem, self.q, self.hist_view, self.n_hist_slots, self.state, 1, stream)
+            ss.ss_verify_history(self.problem, self.q, self.hist_view, None, None, None, self.n_hist_slots,
+                                 self.state, 1, stream)
             return
         if self.n_chunks == 0:          # no history at all: nothing to enqueue
             return
@@ -136,6 +160,8 @@ class ResidentRound:
                            self.state, 1, stream)
 
     def candidates(self, stream=None):
+        if self.fused:                  # done inside the history launch
+            return
         ss.ss_verify_candidates(self.problem, self.q, self.cand_view, self.parents, self.mask_out, self.state,
                                 0, stream)
 

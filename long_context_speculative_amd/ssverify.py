@@ -76,7 +76,7 @@ def lib() -> ctypes.CDLL:
         L.ss_verify_chunk.restype = I32
         L.ss_verify_chunk.argtypes = [P(Problem), VP, P(KVView), I32, I32, I32, I32, P(State), I32, VP]
         L.ss_verify_history.restype = I32
-        L.ss_verify_history.argtypes = [P(Problem), VP, P(KVView), I32, P(State), I32, VP]
+        L.ss_verify_history.argtypes = [P(Problem), VP, P(KVView), P(KVView), VP, VP, I32, P(State), I32, VP]
         L.ss_verify_candidates.restype = I32
         L.ss_verify_candidates.argtypes = [P(Problem), VP, P(KVView), VP, VP, P(State), I32, VP]
         L.ss_merge_states.restype = I32
@@ -183,10 +183,12 @@ def ss_verify_chunk(problem: Problem, q: torch.Tensor, hist: KVView, chunk_len: 
                                  n_chunks, chunks_per_slot, ctypes.byref(out.struct), slot_begin, _stream(stream)))
 
 
-def ss_verify_history(problem: Problem, q: torch.Tensor, hist: KVView, n_slots: int, out: StateBuffers,
-                      slot_begin: int, stream=None) -> None:
-    _check(lib().ss_verify_history(ctypes.byref(problem), q.data_ptr(), ctypes.byref(hist), n_slots,
-                                   ctypes.byref(out.struct), slot_begin, _stream(stream)))
+def ss_verify_history(problem: Problem, q: torch.Tensor, hist: KVView, cand: Optional[KVView],
+                      parents: Optional[torch.Tensor], mask_out: Optional[torch.Tensor], n_slots: int,
+                      out: StateBuffers, slot_begin: int, stream=None) -> None:
+    _check(lib().ss_verify_history(ctypes.byref(problem), q.data_ptr(), ctypes.byref(hist),
+                                   None if cand is None else ctypes.byref(cand), _ptr(parents), _ptr(mask_out),
+                                   n_slots, ctypes.byref(out.struct), slot_begin, _stream(stream)))
 
 
 def ss_verify_candidates(problem: Problem, q: torch.Tensor, cand: KVView, parents: Optional[torch.Tensor],

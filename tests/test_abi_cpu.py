@@ -273,12 +273,17 @@ def test_verify_history_rejects():
     L = ss.lib()
     p = _problem()
     view = _view(max_len=1000)
-    rc = L.ss_verify_history(ctypes.byref(p), 4096, ctypes.byref(view), 0, ctypes.byref(_state(4).struct), 0, None)
-    assert rc == ss.SS_ERR_INVALID_ARG            # n_slots < 1
-    rc = L.ss_verify_history(ctypes.byref(p), 4096, ctypes.byref(view), 4, ctypes.byref(_state(4).struct), 1, None)
-    assert rc == ss.SS_ERR_INVALID_ARG            # slots [1, 5) of 4
-    rc = L.ss_verify_history(ctypes.byref(p), None, ctypes.byref(view), 2, ctypes.byref(_state(4).struct), 0, None)
-    assert rc == ss.SS_ERR_INVALID_ARG
-    rc = L.ss_verify_history(ctypes.byref(_problem(head_dim=96)), 4096, ctypes.byref(view), 2,
-                             ctypes.byref(_state(4).struct), 0, None)
-    assert rc == ss.SS_ERR_UNSUPPORTED
+    def call(problem, q, n_slots, n_state, slot_begin, cand=None):
+        return L.ss_verify_history(ctypes.byref(problem), q, ctypes.byref(view),
+                                   None if cand is None else ctypes.byref(cand), None, None, n_slots,
+                                   ctypes.byref(_state(n_state).struct), slot_begin, None)
+    assert call(p, 4096, 0, 4, 0) == ss.SS_ERR_INVALID_ARG             # n_slots < 1
+    assert call(p, 4096, 4, 4, 1) == ss.SS_ERR_INVALID_ARG             # slots [1, 5) of 4
+    assert call(p, None, 2, 4, 0) == ss.SS_ERR_INVALID_ARG             # no q
+    assert call(_problem(head_dim=96), 4096, 2, 4, 0) == ss.SS_ERR_UNSUPPORTED
+    # candidate views are checked like ss_verify_candidates'
+    assert call(p, 4096, 2, 4, 0, cand=_view(max_len=5)) == ss.SS_ERR_INVALID_ARG    # max_len != n_queries
+    assert call(p, 4096, 2, 4, 0, cand=_view(max_len=6, k=4098)) == ss.SS_ERR_INVALID_ARG
+    assert call(_problem(n_queries=65), 4096, 2, 4, 0, cand=_view(max_len=65)) == ss.SS_ERR_UNSUPPORTED
+    # outside the narrow MFMA kernel the candidates need a slot of their own
+    assert call(_problem(engine=ss.SS_ENGINE_VALU), 4096, 1, 4, 0, cand=_view(max_len=6)) == ss.SS_ERR_INVALID_ARG

@@ -374,6 +374,28 @@ def test_history_balanced(name):
     _check_history_slots(rnd, inp)
 
 
+@pytest.mark.parametrize("name", list(BALANCED))
+def test_history_fused_candidates(name):
+    """ss_verify_history with the candidate region: folded into each stream's
+    first piece on the narrow MFMA kernel, in a slot of its own elsewhere."""
+    base, n_slots = BALANCED[name]
+    cfg = SMALL[base]
+    if n_slots < 2 and not rounds.narrow_mfma(cfg):
+        pytest.skip("candidates need a slot of their own outside the narrow kernel")
+    log(f"[fused] {name}: rows={cfg.rows} slots={n_slots}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, split="balanced", history_slots=n_slots, fuse_candidates=True)
+    for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
+        t.fill_(float("nan"))
+    rnd.mask_out.fill_(-1)
+    rnd.run()
+    torch.cuda.synchronize()
+    assert not torch.isnan(rnd.state.m).any() and not torch.isnan(rnd.state.acc).any()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
+
+
 def test_history_balanced_many_requests_and_empties():
     """More requests than a wavefront has lanes (the start search spans
     several blocks), empty requests between and at the end, lengths off the
@@ -388,28 +410,35 @@ def test_history_balanced_many_requests_and_empties():
     inp.hist_len[7] = 1
     inp.hist_len[8] = 128
     inp.hist_len[9] = 129
+    o_ref, lse_ref = oracle_round(inp)
     for n_slots in (2, 3, 9):
-        log(f"[history] 70 requests, slots={n_slots}")
-        rnd = rounds.ResidentRound(inp, split="balanced", history_slots=n_slots)
+        for fuse in (False, True):
+            log(f"[history] 70 requests, slots={n_slots}, candidates fused={fuse}")
+            rnd = rounds.ResidentRound(inp, split="balanced", history_slots=n_slots, fuse_candidates=fuse)
+            for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
+                t.fill_(float("nan"))
+            rnd.run()
+            torch.cuda.synchronize()
+            compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+            check_mask(rnd, inp)
+            if not fuse:
+                _check_history_slots(rnd, inp)
+            else:
+                assert not torch.isnan(rnd.state.m).any() and not torch.isnan(rnd.state.acc).any()
+    # no history at all: every history slot is empty, the result is the
+    # candidate region alone
+    inp.hist_len[:] = 0
+    o_ref, lse_ref = oracle_round(inp)
+    for fuse in (False, True):
+        rnd = rounds.ResidentRound(inp, split="balanced", history_slots=3, fuse_candidates=fuse)
         for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
             t.fill_(float("nan"))
         rnd.run()
         torch.cuda.synchronize()
-        o_ref, lse_ref = oracle_round(inp)
+        assert np.isneginf(rnd.state.m[1:].cpu().numpy()).all()
+        assert (rnd.state.l[1:] == 0).all() and (rnd.state.acc[1:] == 0).all()
         compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
-        _check_history_slots(rnd, inp)
-    # no history at all: every history slot is empty, the result is the
-    # candidate region alone
-    inp.hist_len[:] = 0
-    rnd = rounds.ResidentRound(inp, split="balanced", history_slots=3)
-    for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
-        t.fill_(float("nan"))
-    rnd.run()
-    torch.cuda.synchronize()
-    assert np.isneginf(rnd.state.m[1:].cpu().numpy()).all()
-    assert (rnd.state.l[1:] == 0).all() and (rnd.state.acc[1:] == 0).all()
-    o_ref, lse_ref = oracle_round(inp)
-    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+        check_mask(rnd, inp)
 
 
 def test_invalid_call_enqueues_nothing():
