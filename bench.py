@@ -3,18 +3,20 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one pass of the whole resident hot path over one batch of
-synthetic input already in HBM: ss_verify_chunk over every history chunk,
-ss_verify_candidates (mask build + masked attention) and ss_merge_states.
-The default workload is the Qwen3-8B-like layer: 16 requests, 32 query heads
-over 8 KV heads, head_dim 128, 32768 committed bf16 tokens in chunks of 4096,
-6 queries (5 drafts + 1) under a causal candidate mask.
+synthetic input already in HBM: ss_verify_history over every request's
+committed history (with the candidate region folded into the same launch
+where the narrow MFMA kernel serves the shape, else ss_verify_candidates
+after it) and ss_merge_states. The default workload is the Qwen3-8B-like
+layer: 16 requests, 32 query heads over 8 KV heads, head_dim 128, 32768
+committed bf16 tokens each, 6 queries (5 drafts + 1) under a causal
+candidate mask.
 
 Prints ONE JSON line. value = effective KV GB/s = (history + candidate K/V
-bytes) / time per step. Also reported: verified query-tokens/s, the chunk
-kernel's roofline (algorithmic bytes per launch / its event-timed launch
-duration), the streamed path on the streamed workload (host-link GB/s against
-a plain pinned H2D copy of the same bytes), and the fp64 CPU oracle timed on
-a bounded sample of the same workload.
+bytes) / time per step. Also reported: verified query-tokens/s, the history
+launch's roofline (algorithmic bytes, or FLOPs for wide row groups, per
+launch / its event-timed duration), the streamed path on the streamed
+workload (host-link GB/s against a plain pinned H2D copy of the same bytes),
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 
 from __future__ import annotations
@@ -60,13 +62,21 @@ def kv_bytes(cfg, hist_len) -> tuple[int, int]:
     return int(np.asarray(hist_len, dtype=np.int64).sum()) * row, cfg.batch * cfg.n_queries * row
 
 
-def chunk_kernel_bytes(cfg, hist_len, n_slots) -> int:
-    """Algorithmic bytes of one chunk-kernel launch: the history K and V once,
-    Q once, and the state slots written (acc + m + l, fp32)."""
-    hist, _ = kv_bytes(cfg, hist_len)
+def chunk_kernel_bytes(cfg, hist_len, n_slots, with_cand=False) -> int:
+    """Algorithmic bytes of one history-kernel launch: the history K and V
+    once, Q once, the state slots written (acc + m + l, fp32), and the
+    candidate K and V when the launch also attends the candidate region."""
+    hist, cand = kv_bytes(cfg, hist_len)
     q = cfg.batch * cfg.n_queries * cfg.n_q_heads * cfg.head_dim * cfg.elem_bytes
     states = n_slots * cfg.batch * cfg.n_queries * cfg.n_q_heads * (cfg.head_dim + 2) * 4
-    return hist + q + states
+    return hist + q + states + (cand if with_cand else 0)
+
+
+def launch_bytes(cfg, hist_len, rnd) -> int:
+    """Algorithmic bytes of the timed history launch of a resident round."""
+    if rnd.fused:
+        return chunk_kernel_bytes(cfg, hist_len, rnd.n_call_slots, with_cand=True)
+    return chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)
 
 
 def chunk_kernel_flops(cfg, hist_len) -> int:
@@ -83,10 +93,10 @@ def source_hash(cfg, engine="auto") -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(cfg, split):
+def read_traffic(cfg, split, fused):
     """HBM bytes per chunk-kernel launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source with the same
-    history cut; else None."""
+    history cut and candidate placement; else None."""
     path = os.path.join(ROOT, "profiles", f"chunk_kernel_{cfg.name}_counters.md")
     if not os.path.exists(path):
         return None
@@ -94,9 +104,12 @@ def read_traffic(cfg, split):
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     m_split = re.search(r"history_split:\s*(\w+)", text)
+    m_fused = re.search(r"fused_candidates:\s*(\w+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != source_hash(cfg):
         return None
     if (m_split.group(1) if m_split else "chunks") != split:
+        return None
+    if (m_fused.group(1) == "True" if m_fused else False) != fused:
         return None
     return float(m_bytes.group(1))
 
@@ -110,27 +123,33 @@ def make_round(cfg, inp, cps="auto", engine="auto", split="balanced"):
 
 
 def time_resident(cfg, steps, warmup, cps="auto", engine="auto", split="balanced"):
+    """Step time over `steps` timed steps (events only at the two ends, so no
+    marker sits between the launches), then the history launch's own
+    duration from HIP events around each launch over another `steps` steps
+    on the same stream."""
     inp = wl.make_inputs(cfg)
     rnd = make_round(cfg, inp, cps, engine, split)
     del inp
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         rnd.run()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_begin.record(stream)
+    for _ in range(steps):
+        rnd.run()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_begin.elapsed_time(t_end) / steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for k in range(steps):
         ev[k][0].record(stream)
         rnd.chunks()
         ev[k][1].record(stream)
         rnd.candidates()
         rnd.merge()
-    t_end.record(stream)
     torch.cuda.synchronize()
-    ms_step = t_begin.elapsed_time(t_end) / steps
     ms_chunk = sum(a.elapsed_time(b) for a, b in ev) / steps
     hist_len = np.full(cfg.batch, cfg.hist_len) if not cfg.ragged else rnd.hist_len.cpu().numpy()
     return rnd, hist_len, ms_step, ms_chunk
@@ -223,7 +242,8 @@ def counters_pass(cfg, cps="auto", engine="auto", split="balanced"):
     hist_len = np.full(cfg.batch, cfg.hist_len) if not cfg.ragged else rnd.hist_len.cpu().numpy()
     print(json.dumps({"counters_pass": cfg.name, "calibration_bytes": 1 << 30, "chunks_per_slot": cps,
                       "split": rnd.split, "history_slots": rnd.n_hist_slots,
-                      "chunk_kernel_algorithmic_bytes": chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)}),
+                      "fused_candidates": rnd.fused,
+                      "chunk_kernel_algorithmic_bytes": launch_bytes(cfg, hist_len, rnd)}),
           flush=True)
 
 
@@ -267,8 +287,9 @@ def main():
     hist_slots = rnd.n_hist_slots
     hist_b, cand_b = kv_bytes(cfg, hist_len)
     gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9
-    alg = chunk_kernel_bytes(cfg, hist_len, rnd.n_hist_slots)
-    traffic = read_traffic(cfg, rnd.split) if args.engine == "auto" else None
+    alg = launch_bytes(cfg, hist_len, rnd)
+    fused = rnd.fused
+    traffic = read_traffic(cfg, rnd.split, rnd.fused) if args.engine == "auto" else None
     if cfg.rows > 32:
         # wide row groups: the chunk kernel is bound by the matrix cores
         flops = chunk_kernel_flops(cfg, hist_len)
@@ -303,7 +324,7 @@ def main():
                                f"d={cfg.head_dim}, history={cfg.hist_len} ({'ragged' if cfg.ragged else 'uniform'}),"
                                f" chunk={cfg.chunk_len}, q={cfg.n_queries}, mask={cfg.mask}",
                    "batch": cfg.batch, "history_tokens": cfg.hist_len, "queries": cfg.n_queries,
-                   "split": args.split, "history_slots": hist_slots,
+                   "split": args.split, "history_slots": hist_slots, "fused_candidates": fused,
                    "chunks_per_slot": cps if args.split == "chunks" else None, "engine": args.engine},
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(cfg.batch * cfg.n_queries / (ms_step * 1e-3), 1),
