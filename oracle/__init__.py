@@ -7,11 +7,15 @@ passage of SpecStream ("Resource-Efficient Speculative Decoding for
 Long-Context LLM Serving", section 4.2) or of the Speculative Streaming post it
 follows.
 
+`tiering` follows section 4.1 of the same paper (Eq. 4-5: which committed
+history migrates to the host, and when).
+
 Pins: every function here is checked by tests that do not reuse its code
 (pure-Python brute force, a library SDPA cross-check, the worked mask example
 printed in the Speculative Streaming post, closed forms and invariants).
 """
 
+from . import tiering  # noqa: F401
 from .verify_attention import (  # noqa: F401
     NEG_INF,
     attention_reference,
