@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 4
+#define SS_ABI_VERSION 5
 
 /* status codes */
 #define SS_OK 0
@@ -251,7 +251,12 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
  *
  *   host_kv      pinned host, chunk-major [n_chunks][2][B][Hkv][C][d]
  *                (K block then V block of each chunk, one contiguous copy
- *                per chunk); every request holds n_chunks * C tokens
+ *                per chunk)
+ *   req_len      device int32 [B] or NULL: request b's history is its first
+ *                req_len[b] tokens (chunk j then holds
+ *                clamp(req_len[b] - j*C, 0, C) of them; the rest of the
+ *                chunk is copied but not attended); NULL: every request
+ *                holds n_chunks * C tokens
  *   staging      device buffer of n_buf chunks (n_buf >= 1, each
  *                2*B*Hkv*C*d elements)
  *   out          chunk j's state goes to slot slot_begin + j
@@ -269,8 +274,8 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
  * Errors: as ss_verify_chunk; SS_ERR_INVALID_ARG if the streams are equal.
  */
 SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, const void* host_kv,
-                                 int32_t chunk_len, int32_t n_chunks, void* staging, int32_t n_buf,
-                                 const ss_state_t* out, int32_t slot_begin, ss_stream_t copy_stream,
+                                 const int32_t* req_len, int32_t chunk_len, int32_t n_chunks, void* staging,
+                                 int32_t n_buf, const ss_state_t* out, int32_t slot_begin, ss_stream_t copy_stream,
                                  ss_stream_t compute_stream, int32_t record_timings);
 
 /*
@@ -283,6 +288,43 @@ SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, con
  */
 SS_API int32_t ss_stream_timings(int32_t n_chunks, float* copy_begin, float* copy_end, float* compute_begin,
                                  float* compute_end);
+
+/*
+ * Commit-aware KV tiering (SpecStream section 4.1). A request's target KV is
+ * split at 0 <= H <= C <= L (Eq. 4): Sealed History [0, H) in a pinned host
+ * store (chunk-major, as ss_stream_history reads it), Active Tail [H, C) and
+ * Speculative Frontier [C, L) on the GPU. Committed KV migrates to the host
+ * in blocks of g tokens once more than T committed tokens sit on the GPU;
+ * rejected candidates are reclaimed on the GPU only, since [C', L) never
+ * meets [0, H).
+ *
+ * ss_tier_migration_end: Eq. (5), E = max(H, g * floor(max(0, C - T) / g)).
+ *   Host only. SS_ERR_INVALID_ARG unless 0 <= H <= C, g > 0, T >= 0.
+ *
+ * ss_tier_migrate: enqueue on `stream` the device-to-host copies of the
+ *   committed rows [begin[b], end[b]) of every request from the GPU tail
+ *   into the host store. tail: device view whose row 0 of request b is token
+ *   tail_first[b] (req_offset must be NULL, rows contiguous: stride_t =
+ *   head_dim); host_kv: pinned [n_chunks][2][B][Hkv][chunk_len][d]; token t
+ *   lands in chunk t / chunk_len, row t % chunk_len. begin, end, tail_first
+ *   are host arrays [B]. The caller moves H to end[b] only after the stream
+ *   has passed the copies (an event), as section 4.1 requires.
+ *   SS_ERR_INVALID_ARG if a range leaves the tail view or the store.
+ *
+ * ss_kv_copy_rows: enqueue on `stream` the device copies of rows
+ *   [src_row[b], src_row[b] + n_rows[b]) of src into rows [dst_row[b], ...)
+ *   of dst, K and V, every KV head (host arrays [B]; views with req_offset
+ *   NULL and contiguous rows). Moves accepted candidates into the tail and
+ *   compacts the tail after a migration (into a second buffer: source and
+ *   destination must not overlap).
+ */
+SS_API int32_t ss_tier_migration_end(int64_t h, int64_t c, int64_t tail, int64_t gran, int64_t* e);
+SS_API int32_t ss_tier_migrate(const ss_problem_t* problem, const ss_kv_view_t* tail, const int64_t* tail_first,
+                               const int64_t* begin, const int64_t* end, void* host_kv, int32_t chunk_len,
+                               int32_t n_chunks, ss_stream_t stream);
+SS_API int32_t ss_kv_copy_rows(const ss_problem_t* problem, const ss_kv_view_t* src, const int64_t* src_row,
+                               const ss_kv_view_t* dst, const int64_t* dst_row, const int64_t* n_rows,
+                               ss_stream_t stream);
 
 /*
  * Host-side helpers that expose the integer rules the kernels apply. They run

@@ -367,9 +367,10 @@ extern "C" SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_
 }
 
 extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, const void* host_kv,
-                                            int32_t chunk_len, int32_t n_chunks, void* staging, int32_t n_buf,
-                                            const ss_state_t* out, int32_t slot_begin, ss_stream_t copy_stream,
-                                            ss_stream_t compute_stream, int32_t record_timings) {
+                                            const int32_t* req_len, int32_t chunk_len, int32_t n_chunks,
+                                            void* staging, int32_t n_buf, const ss_state_t* out, int32_t slot_begin,
+                                            ss_stream_t copy_stream, ss_stream_t compute_stream,
+                                            int32_t record_timings) {
     int32_t rc = check_problem(problem);
     if (rc) return rc;
     if (!q || !host_kv || !staging) return fail(SS_ERR_INVALID_ARG, "q, host_kv or staging is NULL");
@@ -440,7 +441,9 @@ extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const v
         if (record_timings) SS_TRY(hipEventRecord(ev.t_comp0[j], ks));
         view.k = buf;
         view.v = buf + half * es;
+        view.req_len = req_len;  // request b holds clamp(req_len[b] - j*C, 0, C) tokens of this chunk
         ChunkParams c = make_chunk_params(problem, q, &view, chunk_len, 0, 1, 1, out, slot_begin + j);
+        if (req_len) c.len_offset = (int64_t)j * chunk_len;
         SS_TRY(enqueue_chunk(problem, c, ks));
         if (record_timings) SS_TRY(hipEventRecord(ev.t_comp1[j], ks));
         SS_TRY(hipEventRecord(ev.freed[bi], ks));
@@ -473,6 +476,101 @@ extern "C" SS_API int32_t ss_stream_timings(int32_t n_chunks, float* copy_begin,
             e = hipEventElapsedTime(&t, ev.t_copy0[0], it.ev);
             if (e != hipSuccess) return fail(SS_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
             it.out[j] = t;
+        }
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Commit-aware KV tiering (section 4.1): the migration endpoint rule and the
+// row copies that move committed KV between the GPU tail and the host store.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+// A per-request row range of a view whose addresses the host can compute:
+// no device offsets, contiguous feature rows.
+int32_t check_row_view(const ss_problem_t* p, const ss_kv_view_t* v, const char* name) {
+    int32_t rc = check_view(p, v, name);
+    if (rc) return rc;
+    if (v->req_offset) return fail(SS_ERR_INVALID_ARG, "%s view: row copies need req_offset NULL", name);
+    if (v->stride_t != p->head_dim) return fail(SS_ERR_INVALID_ARG, "%s view: rows must be contiguous", name);
+    return SS_OK;
+}
+
+}  // namespace
+
+extern "C" SS_API int32_t ss_tier_migration_end(int64_t h, int64_t c, int64_t tail, int64_t gran, int64_t* e) {
+    if (!e) return fail(SS_ERR_INVALID_ARG, "e is NULL");
+    if (gran <= 0 || tail < 0) return fail(SS_ERR_INVALID_ARG, "granularity must be positive, tail non-negative");
+    if (h < 0 || h > c) return fail(SS_ERR_INVALID_ARG, "need 0 <= H <= C (H=%lld, C=%lld)", (long long)h, (long long)c);
+    const int64_t old = c - tail > 0 ? c - tail : 0;
+    const int64_t end = gran * (old / gran);
+    *e = end > h ? end : h;
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_kv_copy_rows(const ss_problem_t* problem, const ss_kv_view_t* src, const int64_t* src_row,
+                                          const ss_kv_view_t* dst, const int64_t* dst_row, const int64_t* n_rows,
+                                          ss_stream_t stream) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if ((rc = check_row_view(problem, src, "source")) || (rc = check_row_view(problem, dst, "destination"))) return rc;
+    if (!src_row || !dst_row || !n_rows) return fail(SS_ERR_INVALID_ARG, "row arrays must not be NULL");
+    for (int32_t b = 0; b < problem->batch; ++b) {
+        if (n_rows[b] < 0 || src_row[b] < 0 || dst_row[b] < 0 || src_row[b] + n_rows[b] > src->max_len ||
+            dst_row[b] + n_rows[b] > dst->max_len)
+            return fail(SS_ERR_INVALID_ARG, "request %d: rows outside the views", b);
+    }
+    const int64_t es = elem_size(problem), d = problem->head_dim;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int32_t b = 0; b < problem->batch; ++b) {
+        if (n_rows[b] == 0) continue;
+        for (int kv = 0; kv < 2; ++kv) {
+            const char* s0 = static_cast<const char*>(kv ? src->v : src->k) +
+                             (b * src->stride_b + src_row[b] * src->stride_t) * es;
+            char* d0 = static_cast<char*>(const_cast<void*>(kv ? dst->v : dst->k)) +
+                       (b * dst->stride_b + dst_row[b] * dst->stride_t) * es;
+            hipError_t e = hipMemcpy2DAsync(d0, dst->stride_h * es, s0, src->stride_h * es, n_rows[b] * d * es,
+                                            problem->n_kv_heads, hipMemcpyDeviceToDevice, st);
+            if (e != hipSuccess) return fail(SS_ERR_HIP, "row copy failed: %s", hipGetErrorString(e));
+        }
+    }
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_tier_migrate(const ss_problem_t* problem, const ss_kv_view_t* tail,
+                                          const int64_t* tail_first, const int64_t* begin, const int64_t* end,
+                                          void* host_kv, int32_t chunk_len, int32_t n_chunks, ss_stream_t stream) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if ((rc = check_row_view(problem, tail, "tail"))) return rc;
+    if (!tail_first || !begin || !end || !host_kv) return fail(SS_ERR_INVALID_ARG, "NULL argument");
+    if (chunk_len <= 0 || n_chunks < 0) return fail(SS_ERR_INVALID_ARG, "invalid chunk geometry");
+    const int64_t cap = (int64_t)chunk_len * n_chunks;
+    for (int32_t b = 0; b < problem->batch; ++b) {
+        if (begin[b] < tail_first[b] || end[b] < begin[b] || end[b] > cap ||
+            end[b] - tail_first[b] > tail->max_len)
+            return fail(SS_ERR_INVALID_ARG, "request %d: range [%lld, %lld) outside the tail or the host store", b,
+                        (long long)begin[b], (long long)end[b]);
+    }
+    const int64_t es = elem_size(problem), d = problem->head_dim, hkv = problem->n_kv_heads;
+    const int64_t B = problem->batch, C = chunk_len;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    for (int32_t b = 0; b < problem->batch; ++b) {
+        for (int64_t t = begin[b]; t < end[b];) {
+            const int64_t j = t / C, r = t % C;
+            const int64_t n = (end[b] - t) < (C - r) ? (end[b] - t) : (C - r);  // rows within chunk j
+            for (int kv = 0; kv < 2; ++kv) {
+                const char* s0 = static_cast<const char*>(kv ? tail->v : tail->k) +
+                                 (b * tail->stride_b + (t - tail_first[b]) * tail->stride_t) * es;
+                // chunk-major host store [J][2][B][Hkv][C][d]
+                char* d0 = static_cast<char*>(host_kv) + ((((j * 2 + kv) * B + b) * hkv) * C + r) * d * es;
+                hipError_t e = hipMemcpy2DAsync(d0, C * d * es, s0, tail->stride_h * es, n * d * es, hkv,
+                                                hipMemcpyDeviceToHost, st);
+                if (e != hipSuccess) return fail(SS_ERR_HIP, "migration copy failed: %s", hipGetErrorString(e));
+            }
+            t += n;
         }
     }
     return ok();

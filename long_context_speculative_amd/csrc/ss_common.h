@@ -163,6 +163,10 @@ struct ChunkParams {
     int32_t slot_begin;
     int32_t row_blocks;  // VALU kernels: rows are split into blocks of kValuRows
     int32_t plan_slots;  // balanced history split: slots per stream (>= 2)
+    // Tokens of each request that lie before the view's first row (a staging
+    // chunk of a longer history): the chunk kernels see request b as
+    // clamp(req_len[b] - len_offset, 0, max_len) tokens long.
+    int64_t len_offset;
     // Candidate region folded into each stream's first piece (narrow MFMA
     // kernels, ss_verify_history only): with_cand != 0.
     int32_t with_cand;
@@ -201,6 +205,12 @@ struct MergeParams {
     float* o;
     float* lse;
 };
+
+// Length of request b as the chunk kernels see it (see len_offset).
+__host__ __device__ inline int32_t chunk_view_len(const ChunkParams& p, int32_t b) {
+    const int64_t n = (p.req_len ? (int64_t)p.req_len[b] : (int64_t)p.max_len) - p.len_offset;
+    return (int32_t)(n < 0 ? 0 : (n > p.max_len ? p.max_len : n));
+}
 
 // Rows per work-group in the VALU kernels.
 constexpr int kValuRows = 32;

@@ -84,8 +84,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     const int lane = tid & 63, w = tid >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
 
-    int32_t len = p.req_len ? p.req_len[b] : p.max_len;
-    len = min(max(len, 0), p.max_len);
+    const int32_t len = chunk_view_len(p, b);
     int64_t t0, t1;
     slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
 

@@ -139,8 +139,7 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(ChunkParams p) {
     const int r0 = rb * kValuRows;
     const int nr = min(kValuRows, p.rows - r0);
 
-    int32_t len = p.req_len ? p.req_len[b] : p.max_len;
-    len = min(max(len, 0), p.max_len);
+    const int32_t len = chunk_view_len(p, b);
     int64_t t0, t1;
     slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
 

@@ -75,8 +75,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_valu_small_kernel(ChunkPara
     const int kk = lane >> 1, half = lane & 1;
     const int R = p.rows;
 
-    int32_t len = p.req_len ? p.req_len[b] : p.max_len;
-    len = min(max(len, 0), p.max_len);
+    const int32_t len = chunk_view_len(p, b);
     int64_t t0, t1;
     slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
 

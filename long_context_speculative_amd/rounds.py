@@ -214,3 +214,166 @@ class StreamedRound:
                                 self.n_chunks, cs)
         ss.ss_merge_states(self.problem, self.state, None, self.o, self.lse, cs)
         torch.cuda.current_stream().wait_stream(cs)
+
+
+class TieredRound:
+    """Commit-aware KV tiering around the verification round (SpecStream
+    section 4.1, Eq. 4-5), one request per batch row:
+
+      Sealed History [0, H_b)   pinned host store, chunk-major
+                                [J][2][B][Hkv][C][d]; streamed every round
+                                (ss_stream_history with per-request lengths)
+      Active Tail [H_b, C_b)    device tail buffer, row 0 = token H_b
+      Speculative Frontier      the round's candidate rows (device)
+
+    verify() runs one round: streamed sealed history into slots [0, J),
+    the tail with the candidate region folded in (ss_verify_history) into
+    the following slots, then the merge. commit() moves the accepted
+    candidates into the tail (the rest is simply not kept: rollback stays on
+    the GPU). migrate() applies Eq. (5) through the library, copies [H_b,
+    E_b) to the host store on the copy stream and, ordered after those
+    copies, compacts the tail into the second tail buffer; H_b becomes E_b.
+    """
+
+    def __init__(self, cfg, hist_k, hist_v, tail_target=512, gran=256, chunk_len=512, max_tokens=None,
+                 q_max=None, device="cuda", n_buf=2, tail_slots=2):
+        """hist_k, hist_v: per-request CPU tensors [Hkv][N_b][d] of the
+        initial committed history (cfg.torch_dtype)."""
+        self.cfg = cfg
+        self.problem = _problem(cfg)
+        self.device = device
+        b_, hkv, d = cfg.batch, cfg.n_kv_heads, cfg.head_dim
+        dt = cfg.torch_dtype
+        self.tail_target, self.gran, self.chunk_len = tail_target, gran, chunk_len
+        self.n_buf, self.tail_slots = n_buf, tail_slots
+        q_max = q_max or cfg.n_queries
+        lens = [int(k.shape[1]) for k in hist_k]
+        max_tokens = max_tokens or (max(lens) + 64 * q_max)
+        self.n_chunks_cap = -(-max_tokens // chunk_len)
+        # tail capacity: T + g of committed rows after migration stays below
+        # T + g; one round adds at most q_max
+        self.cap = -(-(tail_target + 2 * gran + q_max) // 128) * 128
+        chunk_elems = 2 * b_ * hkv * chunk_len * d
+        self.host_kv = torch.zeros((self.n_chunks_cap, chunk_elems), dtype=dt, pin_memory=True)
+        self.staging = torch.empty((n_buf, chunk_elems), dtype=dt, device=device)
+        self.tails = [(torch.zeros((b_, hkv, self.cap, d), dtype=dt, device=device),
+                       torch.zeros((b_, hkv, self.cap, d), dtype=dt, device=device)) for _ in range(2)]
+        self.cur = 0
+        self.copy_stream = torch.cuda.Stream(device=device)
+        self.compute_stream = torch.cuda.Stream(device=device)
+        self.state = ss.StateBuffers(self.problem, self.n_chunks_cap + tail_slots, device)
+        self.o = torch.empty((b_, cfg.n_queries, cfg.n_q_heads, d), dtype=torch.float32, device=device)
+        self.lse = torch.empty((b_, cfg.n_queries, cfg.n_q_heads), dtype=torch.float32, device=device)
+        self.mask_out = torch.zeros((b_, cfg.n_queries), dtype=torch.int64, device=device)
+
+        # Initial placement: the whole committed history goes to the device
+        # once, Eq. (5) decides what is sealed, the sealed part is migrated to
+        # the host store and the rest becomes the tail.
+        n0 = max(max(lens), 1)
+        full_k = torch.zeros((b_, hkv, n0, d), dtype=dt)
+        full_v = torch.zeros((b_, hkv, n0, d), dtype=dt)
+        for b in range(b_):
+            full_k[b, :, :lens[b]] = hist_k[b]
+            full_v[b, :, :lens[b]] = hist_v[b]
+        full_k, full_v = full_k.to(device), full_v.to(device)
+        full = self._view(full_k, full_v, n0)
+        self.H = [0] * b_
+        self.C = list(lens)
+        ends = [ss.ss_tier_migration_end(0, c, tail_target, gran) for c in self.C]
+        stream = torch.cuda.current_stream()
+        ss.ss_tier_migrate(self.problem, full, [0] * b_, [0] * b_, ends, self.host_kv, chunk_len,
+                           self.n_chunks_cap, stream)
+        ss.ss_kv_copy_rows(self.problem, full, ends, self.tail_view(), [0] * b_,
+                           [c - e for c, e in zip(self.C, ends)], stream)
+        torch.cuda.synchronize()
+        self.H = ends
+        self._check_capacity()
+
+    # ---- views --------------------------------------------------------------
+    def _view(self, k, v, rows, req_len=None):
+        b_, hkv, cap, d = k.shape
+        return ss.make_view(k, v, hkv * cap * d, cap * d, d, rows, None, req_len)
+
+    def tail_view(self, req_len=None):
+        k, v = self.tails[self.cur]
+        return self._view(k, v, self.cap, req_len)
+
+    def _check_capacity(self):
+        for h, c in zip(self.H, self.C):
+            if not (0 <= h <= c and c - h <= self.cap):
+                raise RuntimeError(f"tail of {c - h} rows exceeds the buffer ({self.cap})")
+
+    # ---- one round ----------------------------------------------------------
+    def verify(self, q, k_cand, v_cand, parents=None):
+        """q [B][nq][Hq][d], k_cand/v_cand [B][Hkv][nq][d] (device). Result in
+        self.o / self.lse once the current stream has caught up."""
+        cfg = self.cfg
+        cs = self.compute_stream
+        cs.wait_stream(torch.cuda.current_stream())
+        self.q = q
+        self.cand_view = ss.head_major_view(k_cand, v_cand)
+        self.k_cand, self.v_cand = k_cand, v_cand
+        self.sealed_len = torch.tensor(self.H, dtype=torch.int32, device=self.device)
+        self.tail_len = torch.tensor([c - h for c, h in zip(self.C, self.H)], dtype=torch.int32,
+                                     device=self.device)
+        n_chunks = -(-max(self.H) // self.chunk_len)
+        n_slots = n_chunks + self.tail_slots
+        st = ss.StateBuffers.__new__(ss.StateBuffers)
+        st.acc, st.m, st.l, st.n_slots = self.state.acc, self.state.m, self.state.l, n_slots
+        st.struct = ss.State(self.state.acc.data_ptr(), self.state.m.data_ptr(), self.state.l.data_ptr(), n_slots)
+        if n_chunks:
+            ss.ss_stream_history(self.problem, q, self.host_kv, self.chunk_len, n_chunks, self.staging, self.n_buf,
+                                 st, 0, self.copy_stream, cs, req_len=self.sealed_len)
+        ss.ss_verify_history(self.problem, q, self.tail_view(self.tail_len), self.cand_view, parents,
+                             self.mask_out, self.tail_slots, st, n_chunks, cs)
+        ss.ss_merge_states(self.problem, st, None, self.o, self.lse, cs)
+        torch.cuda.current_stream().wait_stream(cs)
+        return self.o, self.lse
+
+    def commit(self, accepted):
+        """accepted[b]: how many of request b's candidates (a prefix) the
+        target accepted. Their KV joins the tail; the rest is dropped."""
+        src_rows = [0] * self.cfg.batch
+        dst_rows = [c - h for c, h in zip(self.C, self.H)]
+        cand = ss.head_major_view(self.k_cand, self.v_cand)
+        ss.ss_kv_copy_rows(self.problem, cand, src_rows, self.tail_view(), dst_rows, list(accepted),
+                           torch.cuda.current_stream())
+        self.C = [c + int(a) for c, a in zip(self.C, accepted)]
+        self._check_capacity()
+
+    def migrate(self):
+        """Eq. (5) for every request; [H_b, E_b) goes to the host store, then
+        the tail is compacted so that row 0 is token E_b. Returns E."""
+        ends = [ss.ss_tier_migration_end(h, c, self.tail_target, self.gran) for h, c in zip(self.H, self.C)]
+        if all(e == h for e, h in zip(ends, self.H)):
+            return ends
+        cur = torch.cuda.current_stream()
+        self.copy_stream.wait_stream(cur)
+        ss.ss_tier_migrate(self.problem, self.tail_view(), self.H, self.H, ends, self.host_kv, self.chunk_len,
+                           self.n_chunks_cap, self.copy_stream)
+        # the sealed range is reclaimed on the GPU only after its copy landed
+        cur.wait_stream(self.copy_stream)
+        nxt = 1 - self.cur
+        k, v = self.tails[nxt]
+        ss.ss_kv_copy_rows(self.problem, self.tail_view(), [e - h for e, h in zip(ends, self.H)],
+                           self._view(k, v, self.cap), [0] * self.cfg.batch,
+                           [c - e for c, e in zip(self.C, ends)], cur)
+        self.cur = nxt
+        self.H = ends
+        return ends
+
+    # ---- inspection (tests) -------------------------------------------------
+    def sealed_rows(self, b, which):
+        """Host-store rows [0, H_b) of request b: CPU tensor [Hkv][H_b][d]."""
+        cfg = self.cfg
+        j = -(-self.H[b] // self.chunk_len)
+        kv = 0 if which == "k" else 1
+        blocks = self.host_kv[:j].view(j, 2, cfg.batch, cfg.n_kv_heads, self.chunk_len, cfg.head_dim)
+        rows = blocks[:, kv, b].permute(1, 0, 2, 3).reshape(cfg.n_kv_heads, j * self.chunk_len, cfg.head_dim)
+        return rows[:, :self.H[b]]
+
+    def tail_rows(self, b, which):
+        """Device tail rows [H_b, C_b) of request b, on the CPU."""
+        k, v = self.tails[self.cur]
+        t = k if which == "k" else v
+        return t[b, :, :self.C[b] - self.H[b]].cpu()

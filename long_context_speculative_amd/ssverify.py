@@ -30,7 +30,8 @@ SS_ENGINE_MFMA = 2
 
 EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chunk", "ss_verify_history",
             "ss_verify_candidates", "ss_merge_states", "ss_stream_history", "ss_stream_timings", "ss_tree_mask_host",
-            "ss_slot_tokens_host", "ss_history_plan_host")
+            "ss_slot_tokens_host", "ss_history_plan_host", "ss_tier_migration_end", "ss_tier_migrate",
+            "ss_kv_copy_rows")
 
 
 class SSError(RuntimeError):
@@ -82,7 +83,7 @@ def lib() -> ctypes.CDLL:
         L.ss_merge_states.restype = I32
         L.ss_merge_states.argtypes = [P(Problem), P(State), VP, VP, VP, VP]
         L.ss_stream_history.restype = I32
-        L.ss_stream_history.argtypes = [P(Problem), VP, VP, I32, I32, VP, I32, P(State), I32, VP, VP, I32]
+        L.ss_stream_history.argtypes = [P(Problem), VP, VP, VP, I32, I32, VP, I32, P(State), I32, VP, VP, I32]
         L.ss_stream_timings.restype = I32
         L.ss_stream_timings.argtypes = [I32, VP, VP, VP, VP]
         L.ss_tree_mask_host.restype = I32
@@ -91,6 +92,12 @@ def lib() -> ctypes.CDLL:
         L.ss_slot_tokens_host.argtypes = [I32, I32, I32, I32, I32, I32, P(I64), P(I64)]
         L.ss_history_plan_host.restype = I32
         L.ss_history_plan_host.argtypes = [VP, I32, I32, I32, I32, I32, VP, P(I64)]
+        L.ss_tier_migration_end.restype = I32
+        L.ss_tier_migration_end.argtypes = [I64, I64, I64, I64, P(I64)]
+        L.ss_tier_migrate.restype = I32
+        L.ss_tier_migrate.argtypes = [P(Problem), P(KVView), VP, VP, VP, VP, I32, I32, VP]
+        L.ss_kv_copy_rows.restype = I32
+        L.ss_kv_copy_rows.argtypes = [P(Problem), P(KVView), VP, P(KVView), VP, VP, VP]
         _lib = L
     return _lib
 
@@ -205,9 +212,9 @@ def ss_merge_states(problem: Problem, states: StateBuffers, slots_per_req: Optio
 
 def ss_stream_history(problem: Problem, q: torch.Tensor, host_kv: torch.Tensor, chunk_len: int, n_chunks: int,
                       staging: torch.Tensor, n_buf: int, out: StateBuffers, slot_begin: int, copy_stream,
-                      compute_stream, record_timings: bool = False) -> None:
-    _check(lib().ss_stream_history(ctypes.byref(problem), q.data_ptr(), host_kv.data_ptr(), chunk_len, n_chunks,
-                                   staging.data_ptr(), n_buf, ctypes.byref(out.struct), slot_begin,
+                      compute_stream, record_timings: bool = False, req_len: Optional[torch.Tensor] = None) -> None:
+    _check(lib().ss_stream_history(ctypes.byref(problem), q.data_ptr(), host_kv.data_ptr(), _ptr(req_len), chunk_len,
+                                   n_chunks, staging.data_ptr(), n_buf, ctypes.byref(out.struct), slot_begin,
                                    _stream(copy_stream), _stream(compute_stream), int(bool(record_timings))))
 
 
@@ -245,3 +252,27 @@ def ss_history_plan_host(lens, n_kv_heads: int, max_len: int, n_wg: int, n_slots
     _check(lib().ss_history_plan_host(lens.ctypes.data, len(lens), n_kv_heads, max_len, n_wg, n_slots,
                                       plan.ctypes.data, ctypes.byref(piece)))
     return plan, piece.value
+
+
+def _i64(values):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(values, dtype=np.int64))
+
+
+def ss_tier_migration_end(h: int, c: int, tail: int, gran: int) -> int:
+    e = ctypes.c_int64()
+    _check(lib().ss_tier_migration_end(h, c, tail, gran, ctypes.byref(e)))
+    return e.value
+
+
+def ss_tier_migrate(problem: Problem, tail: KVView, tail_first, begin, end, host_kv: torch.Tensor, chunk_len: int,
+                    n_chunks: int, stream=None) -> None:
+    a, b_, e = _i64(tail_first), _i64(begin), _i64(end)
+    _check(lib().ss_tier_migrate(ctypes.byref(problem), ctypes.byref(tail), a.ctypes.data, b_.ctypes.data,
+                                 e.ctypes.data, host_kv.data_ptr(), chunk_len, n_chunks, _stream(stream)))
+
+
+def ss_kv_copy_rows(problem: Problem, src: KVView, src_row, dst: KVView, dst_row, n_rows, stream=None) -> None:
+    a, b_, n = _i64(src_row), _i64(dst_row), _i64(n_rows)
+    _check(lib().ss_kv_copy_rows(ctypes.byref(problem), ctypes.byref(src), a.ctypes.data, ctypes.byref(dst),
+                                 b_.ctypes.data, n.ctypes.data, _stream(stream)))

@@ -140,10 +140,10 @@ def test_candidates_and_stream_reject():
                                 ctypes.byref(_state(2).struct), 2, None)
     assert rc == ss.SS_ERR_INVALID_ARG          # slot out of range
     # equal copy and compute streams
-    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, 64, 4, 8192, 2, ctypes.byref(_state(4).struct), 0,
+    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, None, 64, 4, 8192, 2, ctypes.byref(_state(4).struct), 0,
                              None, None, 0)
     assert rc == ss.SS_ERR_INVALID_ARG
-    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, 64, 5, 8192, 2, ctypes.byref(_state(4).struct), 0,
+    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, None, 64, 5, 8192, 2, ctypes.byref(_state(4).struct), 0,
                              1, 2, 0)
     assert rc == ss.SS_ERR_INVALID_ARG          # 5 chunks, 4 slots
     rc = L.ss_merge_states(ctypes.byref(p), ctypes.byref(_state().struct), None, None, 4096, None)
@@ -287,3 +287,51 @@ def test_verify_history_rejects():
     assert call(_problem(n_queries=65), 4096, 2, 4, 0, cand=_view(max_len=65)) == ss.SS_ERR_UNSUPPORTED
     # outside the narrow MFMA kernel the candidates need a slot of their own
     assert call(_problem(engine=ss.SS_ENGINE_VALU), 4096, 1, 4, 0, cand=_view(max_len=6)) == ss.SS_ERR_INVALID_ARG
+
+
+def test_tier_migration_end_matches_oracle():
+    """The library's Eq. (5) against the oracle's, bit for bit, and against
+    the hand-worked cases."""
+    from oracle import tiering
+    rng = np.random.default_rng(11)
+    for _ in range(2000):
+        g = int(rng.choice([1, 128, 256, 4096]))
+        t = int(rng.choice([0, 512, 3000]))
+        h = g * int(rng.integers(0, 50))
+        c = h + int(rng.integers(0, 30 * g + t))
+        assert ss.ss_tier_migration_end(h, c, t, g) == tiering.migration_end(h, c, t, g)
+    path = os.path.join(ROOT, "tests", "golden", "tiering_eq5_cases.txt")
+    for line in open(path):
+        line = line.split("#", 1)[0].split()
+        if line:
+            h, c, t, g, e = (int(x) for x in line)
+            assert ss.ss_tier_migration_end(h, c, t, g) == e
+    for bad in ((5, 4, 0, 1), (-1, 4, 0, 1), (0, 4, 0, 0), (0, 4, -1, 1)):
+        with pytest.raises(ss.SSError):
+            ss.ss_tier_migration_end(*bad)
+
+
+def test_tier_copies_reject():
+    L = ss.lib()
+    p = _problem(batch=2)
+    tail = ss.KVView(4096, 8192, 2 * 1024 * 128, 1024 * 128, 128, None, None, 1024)
+    rows = lambda *v: (ctypes.c_int64 * 2)(*v)
+    host = 65536
+    ok = L.ss_tier_migrate(ctypes.byref(p), ctypes.byref(tail), rows(100, 100), rows(100, 300), rows(100, 300),
+                           host, 512, 4, None)
+    assert ok == ss.SS_OK                       # empty and in-range: nothing enqueued, nothing rejected
+    # a range that leaves the tail view, one before the tail's first row, one past the host store
+    assert L.ss_tier_migrate(ctypes.byref(p), ctypes.byref(tail), rows(0, 0), rows(0, 0), rows(1025, 0), host, 4096,
+                             4, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_tier_migrate(ctypes.byref(p), ctypes.byref(tail), rows(50, 0), rows(40, 0), rows(60, 0), host, 512,
+                             4, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_tier_migrate(ctypes.byref(p), ctypes.byref(tail), rows(0, 0), rows(0, 0), rows(0, 2049), host, 512,
+                             4, None) == ss.SS_ERR_INVALID_ARG
+    # views must be addressable from the host with contiguous rows
+    bad = ss.KVView(4096, 8192, 2 * 1024 * 128, 1024 * 128, 256, None, None, 1024)
+    assert L.ss_tier_migrate(ctypes.byref(p), ctypes.byref(bad), rows(0, 0), rows(0, 0), rows(1, 1), host, 512, 4,
+                             None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_kv_copy_rows(ctypes.byref(p), ctypes.byref(tail), rows(0, 0), ctypes.byref(tail), rows(1000, 0),
+                             rows(30, 0), None) == ss.SS_ERR_INVALID_ARG      # past the destination rows
+    assert L.ss_kv_copy_rows(ctypes.byref(p), ctypes.byref(tail), rows(0, 0), ctypes.byref(tail), rows(0, 0),
+                             rows(-1, 0), None) == ss.SS_ERR_INVALID_ARG
