@@ -281,11 +281,18 @@ class TieredRound:
         self.C = list(lens)
         ends = [ss.ss_tier_migration_end(0, c, tail_target, gran) for c in self.C]
         stream = torch.cuda.current_stream()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
         ss.ss_tier_migrate(self.problem, full, [0] * b_, [0] * b_, ends, self.host_kv, chunk_len,
                            self.n_chunks_cap, stream)
+        ev1.record(stream)
         ss.ss_kv_copy_rows(self.problem, full, ends, self.tail_view(), [0] * b_,
                            [c - e for c, e in zip(self.C, ends)], stream)
         torch.cuda.synchronize()
+        # the bulk migration of the initial history (device to host)
+        self.init_migrate_ms = ev0.elapsed_time(ev1)
+        self.init_migrated_bytes = 2 * sum(ends) * hkv * d * cfg.elem_bytes
         self.H = ends
         self._check_capacity()
 
