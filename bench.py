@@ -170,7 +170,7 @@ def time_streamed(cfg, reps=3):
         walls.append(time.perf_counter() - t0)
     from long_context_speculative_amd import ssverify as ss
     c0, c1, k0, k1 = ss.ss_stream_timings(srd.n_chunks)
-    bubble = sum(max(0.0, c1[j] - k1[j - 1]) for j in range(1, srd.n_chunks))
+    bubble = rounds.exposed_wait((c0, c1, k0, k1))
     # plain pinned H2D copy of the same bytes, same chunking, one stream
     dst = srd.staging
     torch.cuda.synchronize()
@@ -194,6 +194,46 @@ def time_streamed(cfg, reps=3):
         "chunk_copy_ms_mean": float(np.mean([c1[j] - c0[j] for j in range(srd.n_chunks)])),
         "query_tokens_per_s": cfg.batch * cfg.n_queries / wall,
     }
+
+
+def time_layered(cfg, n_layers=4, hist_len=16384, rest_dim=8192, rest_reps=2, reps=3):
+    """Cross-layer prefetch and grouped transfers (SpecStream section 4.2):
+    n_layers layers of the streamed workload's shape (history cut to
+    hist_len tokens per layer), each followed on the compute stream by a
+    stand-in for the rest of the layer (bf16 matrix products), with the
+    staging ring continued across layers (the next layer's chunks are copied
+    while the current one finishes) or restarted per layer."""
+    lcfg = cfg.with_(hist_len=hist_len)
+    inputs = [wl.make_inputs(lcfg.with_(seed=lcfg.seed + 100 * i)) for i in range(n_layers)]
+    lr = rounds.LayeredStreamedRound(inputs, n_buf=2, chunks_per_copy=2, rest_dim=rest_dim, rest_reps=rest_reps)
+    del inputs
+    out = {"workload": f"{n_layers} layers of {cfg.name} with {hist_len} history tokens each, "
+                       f"rest of layer = {rest_reps} bf16 {rest_dim}^2 matrix products",
+           "chunks_per_copy": 2, "n_buf": 2}
+    for prefetch in (False, True):
+        lr.run(prefetch=prefetch)
+        torch.cuda.synchronize()
+        walls = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            lr.run(prefetch=prefetch, record_timings=True)
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t0)
+        key = "prefetch" if prefetch else "no_prefetch"
+        out[key] = {"ms_per_round": min(walls) * 1e3,
+                    "exposed_wait_ms_per_layer": [round(w, 3) for w in lr.layer_waits()]}
+    # the rest-of-layer stand-in alone
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(lr.layers[0].compute_stream):
+        x = lr.rest_a
+        for _ in range(rest_reps * n_layers):
+            x = torch.mm(x, lr.rest_b)
+    torch.cuda.synchronize()
+    out["rest_of_layers_ms"] = (time.perf_counter() - t0) * 1e3
+    out["round_speedup_from_prefetch"] = out["no_prefetch"]["ms_per_round"] / out["prefetch"]["ms_per_round"]
+    return out
 
 
 def time_tiered(cfg, n_rounds=4, tail=512, gran=2048):
@@ -395,6 +435,8 @@ def main():
         out["streamed"] = time_streamed(wl.CONFIGS["c5_streamed"])
         torch.cuda.empty_cache()
         out["tiered"] = time_tiered(wl.CONFIGS["c5_streamed"])
+        torch.cuda.empty_cache()
+        out["layered"] = time_layered(wl.CONFIGS["c5_streamed"])
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg)

@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 5
+#define SS_ABI_VERSION 6
 
 /* status codes */
 #define SS_OK 0
@@ -59,6 +59,10 @@ extern "C" {
 /* element types */
 #define SS_F32 0
 #define SS_BF16 1
+
+/* ss_stream_history flags */
+#define SS_STREAM_TIMINGS 1  /* record per-chunk events for ss_stream_timings     */
+#define SS_STREAM_CONTINUE 2 /* continue the previous call's staging ring          */
 
 /* chunk-kernel engines (ss_problem_t.engine) */
 #define SS_ENGINE_AUTO 0 /* measured choice, see ss_verify_chunk                 */
@@ -247,47 +251,60 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
  * ss_stream_history -- streamed verification over a history held in pinned
  * host memory (section 4.2, pipelined KV transfers: staging buffers, a
  * transfer stream and a compute stream; each chunk is attended as soon as it
- * has landed).
+ * has landed; adjacent chunks grouped into one transfer; the next layer's
+ * history fetched while the current layer finishes).
  *
  *   host_kv      pinned host, chunk-major [n_chunks][2][B][Hkv][C][d]
- *                (K block then V block of each chunk, one contiguous copy
- *                per chunk)
+ *                (K block then V block of each chunk)
  *   req_len      device int32 [B] or NULL: request b's history is its first
  *                req_len[b] tokens (chunk j then holds
  *                clamp(req_len[b] - j*C, 0, C) of them; the rest of the
  *                chunk is copied but not attended); NULL: every request
  *                holds n_chunks * C tokens
- *   staging      device buffer of n_buf chunks (n_buf >= 1, each
- *                2*B*Hkv*C*d elements)
+ *   chunks_per_copy  adjacent chunks moved by one copy (>= 1): a staging
+ *                buffer holds that many chunks
+ *   staging      device buffer of n_buf staging buffers (n_buf >= 1, each
+ *                chunks_per_copy * 2*B*Hkv*C*d elements)
  *   out          chunk j's state goes to slot slot_begin + j
  *   copy_stream, compute_stream  must differ; the copies run on the first,
  *                the chunk kernels on the second
- *   record_timings  nonzero: per-chunk copy and compute events are recorded
- *                for ss_stream_timings
- * For chunk j: the copy stream waits until the compute that last used
- * staging buffer j % n_buf has finished, copies chunk j into it and marks it
- * arrived; the compute stream waits for that mark, runs ss_verify_chunk on
- * the buffer and marks the buffer free. Before the first copy the copy
- * stream waits for all work already enqueued on the compute stream. The
+ *   flags        SS_STREAM_TIMINGS: record per-chunk events (ss_stream_timings).
+ *                SS_STREAM_CONTINUE: the staging ring (same staging pointer,
+ *                n_buf and buffer size) continues from the previous call on
+ *                this device: each copy waits only until the last kernel that
+ *                read its buffer is done, not for the compute stream's earlier
+ *                work, so it may run while the compute stream still finishes
+ *                the previous layer (cross-layer prefetch). The caller must
+ *                not touch the staging buffers between such calls.
+ * Per copy group: the copy stream waits until the chunks that last used the
+ * staging buffer have been attended, copies the group, marks it arrived; the
+ * compute stream waits for that mark, runs ss_verify_chunk on each of its
+ * chunks and marks the buffer free. Without SS_STREAM_CONTINUE the first
+ * copy also waits for all work already enqueued on the compute stream. The
  * call returns without synchronising; candidates and merge may follow on
  * the compute stream.
- * Errors: as ss_verify_chunk; SS_ERR_INVALID_ARG if the streams are equal.
+ * Errors: as ss_verify_chunk; SS_ERR_INVALID_ARG if the streams are equal,
+ * on unknown flags, or on SS_STREAM_CONTINUE with a different ring.
  */
 SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, const void* host_kv,
-                                 const int32_t* req_len, int32_t chunk_len, int32_t n_chunks, void* staging,
-                                 int32_t n_buf, const ss_state_t* out, int32_t slot_begin, ss_stream_t copy_stream,
-                                 ss_stream_t compute_stream, int32_t record_timings);
+                                 const int32_t* req_len, int32_t chunk_len, int32_t n_chunks,
+                                 int32_t chunks_per_copy, void* staging, int32_t n_buf, const ss_state_t* out,
+                                 int32_t slot_begin, ss_stream_t copy_stream, ss_stream_t compute_stream,
+                                 int32_t flags);
 
 /*
- * ss_stream_timings -- per-chunk event times of the last ss_stream_history
- * call on this process that recorded timings, in milliseconds from the
- * start of the first copy. Call after synchronising both streams.
- * n_chunks must equal that call's n_chunks. Any output pointer may be NULL.
- * The exposed wait (compute bubble) of chunk j is
+ * ss_stream_timings -- per-chunk event times of a timed ss_stream_history
+ * call on this device: back = 0 the latest, 1 the one before, ... (the last
+ * 64 are kept). Milliseconds from the compute stream's frontier when that
+ * call was made (negative when a continued ring fetched the chunk before
+ * the compute stream got there). Call after synchronising both streams.
+ * n_chunks must equal that call's n_chunks; chunks of one copy group share
+ * its copy times. Any output pointer may be NULL. The exposed wait of the
+ * call is max(0, copy_end[0]) + sum over j >= 1 of
  * max(0, copy_end[j] - compute_end[j-1]).
  */
-SS_API int32_t ss_stream_timings(int32_t n_chunks, float* copy_begin, float* copy_end, float* compute_begin,
-                                 float* compute_end);
+SS_API int32_t ss_stream_timings(int32_t back, int32_t n_chunks, float* copy_begin, float* copy_end,
+                                 float* compute_begin, float* compute_end);
 
 /*
  * Commit-aware KV tiering (SpecStream section 4.1). A request's target KV is

@@ -167,12 +167,28 @@ hipError_t enqueue_chunk(const ss_problem_t* p, const ChunkParams& c, hipStream_
 // Event pool of the streaming pipeline (one per device, reused across calls).
 // ---------------------------------------------------------------------------
 
+// Timing events of one streaming call; times are read relative to `start`,
+// the compute stream's frontier when the call was made.
+struct TimingSet {
+    hipEvent_t start = nullptr;
+    std::vector<hipEvent_t> copy0, copy1;  // per copy group
+    std::vector<hipEvent_t> comp0, comp1;  // per chunk
+    int32_t n_chunks = -1, group = 1;
+};
+
+constexpr int kTimingRing = 64;  // timed calls kept per device
+
 struct StreamEvents {
     int device = -1;
     std::vector<hipEvent_t> arrived, freed;  // per staging buffer, no timing
     hipEvent_t start = nullptr;              // compute-stream frontier at call start
-    std::vector<hipEvent_t> t_copy0, t_copy1, t_comp0, t_comp1;  // timing events
-    int32_t timed_chunks = -1;
+    // Staging ring as the last call left it, for SS_STREAM_CONTINUE.
+    const void* staging = nullptr;
+    int64_t buf_bytes = 0;
+    int32_t n_buf = 0, next_buf = 0;
+    std::vector<char> used;                  // buffer has a recorded `freed`
+    TimingSet timing[kTimingRing];
+    int64_t timed_calls = 0;
 };
 
 std::mutex g_ev_mutex;
@@ -368,25 +384,28 @@ extern "C" SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_
 
 extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, const void* host_kv,
                                             const int32_t* req_len, int32_t chunk_len, int32_t n_chunks,
-                                            void* staging, int32_t n_buf, const ss_state_t* out, int32_t slot_begin,
-                                            ss_stream_t copy_stream, ss_stream_t compute_stream,
-                                            int32_t record_timings) {
+                                            int32_t chunks_per_copy, void* staging, int32_t n_buf,
+                                            const ss_state_t* out, int32_t slot_begin, ss_stream_t copy_stream,
+                                            ss_stream_t compute_stream, int32_t flags) {
     int32_t rc = check_problem(problem);
     if (rc) return rc;
     if (!q || !host_kv || !staging) return fail(SS_ERR_INVALID_ARG, "q, host_kv or staging is NULL");
     if (!aligned16(q) || !aligned16(staging)) return fail(SS_ERR_INVALID_ARG, "q and staging must be 16-byte aligned");
     if ((rc = check_state(out, "output"))) return rc;
-    if (chunk_len <= 0 || n_chunks < 0 || n_buf <= 0)
-        return fail(SS_ERR_INVALID_ARG, "chunk_len and n_buf must be positive, n_chunks non-negative");
+    if (chunk_len <= 0 || n_chunks < 0 || n_buf <= 0 || chunks_per_copy <= 0)
+        return fail(SS_ERR_INVALID_ARG, "chunk_len, chunks_per_copy and n_buf must be positive, n_chunks non-negative");
     if (slot_begin < 0 || (int64_t)slot_begin + n_chunks > out->n_slots)
         return fail(SS_ERR_INVALID_ARG, "slots [%d, %d) exceed n_slots %d", slot_begin, slot_begin + n_chunks,
                     out->n_slots);
     if (copy_stream == compute_stream) return fail(SS_ERR_INVALID_ARG, "copy and compute streams must differ");
-    if (n_chunks == 0) return ok();
+    if (flags & ~(SS_STREAM_TIMINGS | SS_STREAM_CONTINUE)) return fail(SS_ERR_INVALID_ARG, "unknown flags %d", flags);
+    const bool timed = flags & SS_STREAM_TIMINGS;
+    const bool cont = flags & SS_STREAM_CONTINUE;
 
     const int64_t es = elem_size(problem);
     const int64_t half = (int64_t)problem->batch * problem->n_kv_heads * chunk_len * problem->head_dim;
     const int64_t chunk_bytes = 2 * half * es;
+    const int64_t buf_bytes = chunk_bytes * chunks_per_copy;
     hipStream_t cs = static_cast<hipStream_t>(copy_stream);
     hipStream_t ks = static_cast<hipStream_t>(compute_stream);
 
@@ -397,18 +416,36 @@ extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const v
     std::lock_guard<std::mutex> lock(g_ev_mutex);
     if ((int)g_events.size() <= dev) g_events.resize(dev + 1);
     StreamEvents& ev = g_events[dev];
+    if (cont && !(ev.staging == staging && ev.n_buf == n_buf && ev.buf_bytes == buf_bytes))
+        return fail(SS_ERR_INVALID_ARG, "SS_STREAM_CONTINUE needs the previous call's staging ring");
+    if (n_chunks == 0) return ok();
     ev.device = dev;
     const unsigned sync_flags = hipEventDisableTiming;
     if ((e = grow(ev.arrived, n_buf, sync_flags)) != hipSuccess || (e = grow(ev.freed, n_buf, sync_flags)) != hipSuccess)
         return fail(SS_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
     if (!ev.start && (e = hipEventCreateWithFlags(&ev.start, sync_flags)) != hipSuccess)
         return fail(SS_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
-    if (record_timings) {
-        if ((e = grow(ev.t_copy0, n_chunks, hipEventDefault)) != hipSuccess ||
-            (e = grow(ev.t_copy1, n_chunks, hipEventDefault)) != hipSuccess ||
-            (e = grow(ev.t_comp0, n_chunks, hipEventDefault)) != hipSuccess ||
-            (e = grow(ev.t_comp1, n_chunks, hipEventDefault)) != hipSuccess)
+    const int64_t n_groups = (n_chunks + chunks_per_copy - 1) / chunks_per_copy;
+    TimingSet* ts = nullptr;
+    if (timed) {
+        ts = &ev.timing[ev.timed_calls % kTimingRing];
+        if (!ts->start && (e = hipEventCreateWithFlags(&ts->start, hipEventDefault)) != hipSuccess)
             return fail(SS_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+        if ((e = grow(ts->copy0, n_groups, hipEventDefault)) != hipSuccess ||
+            (e = grow(ts->copy1, n_groups, hipEventDefault)) != hipSuccess ||
+            (e = grow(ts->comp0, n_chunks, hipEventDefault)) != hipSuccess ||
+            (e = grow(ts->comp1, n_chunks, hipEventDefault)) != hipSuccess)
+            return fail(SS_ERR_HIP, "event creation failed: %s", hipGetErrorString(e));
+    }
+    if (!cont) {
+        // A fresh ring: the first copies may overwrite staging buffers that
+        // earlier compute work still reads, so they wait for everything
+        // already on the compute stream.
+        ev.staging = staging;
+        ev.n_buf = n_buf;
+        ev.buf_bytes = buf_bytes;
+        ev.next_buf = 0;
+        ev.used.assign(n_buf, 0);
     }
 
     ss_kv_view_t view{};
@@ -416,6 +453,7 @@ extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const v
     view.stride_h = (int64_t)chunk_len * problem->head_dim;
     view.stride_t = problem->head_dim;
     view.max_len = chunk_len;
+    view.req_len = req_len;  // request b holds clamp(req_len[b] - j*C, 0, C) tokens of chunk j
 
 #define SS_TRY(call)                                                                              \
     do {                                                                                          \
@@ -423,57 +461,73 @@ extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const v
         if (err_ != hipSuccess) return fail(SS_ERR_HIP, "%s: %s", #call, hipGetErrorString(err_)); \
     } while (0)
 
-    // The first copy may overwrite staging buffers that earlier compute work
-    // still reads: order it after everything already on the compute stream.
     SS_TRY(hipEventRecord(ev.start, ks));
-    SS_TRY(hipStreamWaitEvent(cs, ev.start, 0));
-    for (int32_t j = 0; j < n_chunks; ++j) {
-        const int32_t bi = j % n_buf;
-        char* buf = static_cast<char*>(staging) + (int64_t)bi * chunk_bytes;
-        const char* src = static_cast<const char*>(host_kv) + (int64_t)j * chunk_bytes;
-        if (j >= n_buf) SS_TRY(hipStreamWaitEvent(cs, ev.freed[bi], 0));
-        if (record_timings) SS_TRY(hipEventRecord(ev.t_copy0[j], cs));
-        SS_TRY(hipMemcpyAsync(buf, src, chunk_bytes, hipMemcpyHostToDevice, cs));
-        if (record_timings) SS_TRY(hipEventRecord(ev.t_copy1[j], cs));
+    if (timed) SS_TRY(hipEventRecord(ts->start, ks));
+    // Continuing a ring: every buffer waits only for its own last reader
+    // (its `freed` mark), so the copies run ahead of whatever else the
+    // compute stream does in between: the next layer's history is fetched
+    // while the current layer finishes.
+    if (!cont) SS_TRY(hipStreamWaitEvent(cs, ev.start, 0));
+    for (int64_t gi = 0; gi < n_groups; ++gi) {
+        const int32_t bi = (int32_t)((ev.next_buf + gi) % n_buf);
+        const int64_t j0 = gi * chunks_per_copy;
+        const int64_t nj = (n_chunks - j0) < chunks_per_copy ? (n_chunks - j0) : chunks_per_copy;
+        char* buf = static_cast<char*>(staging) + (int64_t)bi * buf_bytes;
+        const char* src = static_cast<const char*>(host_kv) + j0 * chunk_bytes;
+        if (ev.used[bi]) SS_TRY(hipStreamWaitEvent(cs, ev.freed[bi], 0));
+        if (timed) SS_TRY(hipEventRecord(ts->copy0[gi], cs));
+        SS_TRY(hipMemcpyAsync(buf, src, nj * chunk_bytes, hipMemcpyHostToDevice, cs));
+        if (timed) SS_TRY(hipEventRecord(ts->copy1[gi], cs));
         SS_TRY(hipEventRecord(ev.arrived[bi], cs));
 
         SS_TRY(hipStreamWaitEvent(ks, ev.arrived[bi], 0));
-        if (record_timings) SS_TRY(hipEventRecord(ev.t_comp0[j], ks));
-        view.k = buf;
-        view.v = buf + half * es;
-        view.req_len = req_len;  // request b holds clamp(req_len[b] - j*C, 0, C) tokens of this chunk
-        ChunkParams c = make_chunk_params(problem, q, &view, chunk_len, 0, 1, 1, out, slot_begin + j);
-        if (req_len) c.len_offset = (int64_t)j * chunk_len;
-        SS_TRY(enqueue_chunk(problem, c, ks));
-        if (record_timings) SS_TRY(hipEventRecord(ev.t_comp1[j], ks));
+        for (int64_t c = 0; c < nj; ++c) {
+            const int64_t j = j0 + c;
+            if (timed) SS_TRY(hipEventRecord(ts->comp0[j], ks));
+            view.k = buf + c * chunk_bytes;
+            view.v = buf + c * chunk_bytes + half * es;
+            ChunkParams p = make_chunk_params(problem, q, &view, chunk_len, 0, 1, 1, out, slot_begin + (int32_t)j);
+            if (req_len) p.len_offset = j * chunk_len;
+            SS_TRY(enqueue_chunk(problem, p, ks));
+            if (timed) SS_TRY(hipEventRecord(ts->comp1[j], ks));
+        }
         SS_TRY(hipEventRecord(ev.freed[bi], ks));
+        ev.used[bi] = 1;
     }
 #undef SS_TRY
-    ev.timed_chunks = record_timings ? n_chunks : -1;
+    ev.next_buf = (int32_t)((ev.next_buf + n_groups) % n_buf);
+    if (timed) {
+        ts->n_chunks = n_chunks;
+        ts->group = chunks_per_copy;
+        ++ev.timed_calls;
+    }
     return ok();
 }
 
-extern "C" SS_API int32_t ss_stream_timings(int32_t n_chunks, float* copy_begin, float* copy_end,
+extern "C" SS_API int32_t ss_stream_timings(int32_t back, int32_t n_chunks, float* copy_begin, float* copy_end,
                                             float* compute_begin, float* compute_end) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(SS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
     std::lock_guard<std::mutex> lock(g_ev_mutex);
-    if ((int)g_events.size() <= dev || g_events[dev].timed_chunks < 0)
-        return fail(SS_ERR_INVALID_ARG, "no timed streaming call on this device");
+    if ((int)g_events.size() <= dev) return fail(SS_ERR_INVALID_ARG, "no timed streaming call on this device");
     StreamEvents& ev = g_events[dev];
-    if (n_chunks != ev.timed_chunks)
-        return fail(SS_ERR_INVALID_ARG, "n_chunks %d differs from the timed call's %d", n_chunks, ev.timed_chunks);
+    if (back < 0 || back >= kTimingRing || back >= ev.timed_calls)
+        return fail(SS_ERR_INVALID_ARG, "no timed streaming call %d calls back", back);
+    const TimingSet& ts = ev.timing[(ev.timed_calls - 1 - back) % kTimingRing];
+    if (n_chunks != ts.n_chunks)
+        return fail(SS_ERR_INVALID_ARG, "n_chunks %d differs from the timed call's %d", n_chunks, ts.n_chunks);
     for (int32_t j = 0; j < n_chunks; ++j) {
-        float t;
+        const int32_t gi = j / ts.group;
         struct {
             float* out;
             hipEvent_t ev;
-        } items[4] = {{copy_begin, ev.t_copy0[j]}, {copy_end, ev.t_copy1[j]}, {compute_begin, ev.t_comp0[j]},
-                      {compute_end, ev.t_comp1[j]}};
+        } items[4] = {{copy_begin, ts.copy0[gi]}, {copy_end, ts.copy1[gi]}, {compute_begin, ts.comp0[j]},
+                      {compute_end, ts.comp1[j]}};
         for (auto& it : items) {
             if (!it.out) continue;
-            e = hipEventElapsedTime(&t, ev.t_copy0[0], it.ev);
+            float t;
+            e = hipEventElapsedTime(&t, ts.start, it.ev);
             if (e != hipSuccess) return fail(SS_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
             it.out[j] = t;
         }

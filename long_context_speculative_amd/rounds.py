@@ -176,7 +176,7 @@ class ResidentRound:
 
 
 class StreamedRound:
-    def __init__(self, inp: VerifyInputs, device="cuda", n_buf=2, chunk_len=None):
+    def __init__(self, inp: VerifyInputs, device="cuda", n_buf=2, chunk_len=None, chunks_per_copy=1):
         cfg = inp.cfg
         self.cfg = cfg
         self.problem = _problem(cfg)
@@ -186,11 +186,13 @@ class StreamedRound:
             raise ValueError("streamed rounds need one history length, a multiple of the chunk length")
         self.n_chunks = n // self.chunk_len
         self.n_buf = n_buf
+        self.chunks_per_copy = chunks_per_copy
         b_, hkv, d = cfg.batch, cfg.n_kv_heads, cfg.head_dim
         self.chunk_elems = 2 * b_ * hkv * self.chunk_len * d
         self.host_kv = torch.empty((self.n_chunks, self.chunk_elems), dtype=cfg.torch_dtype, pin_memory=True)
         to_chunk_major(inp.k_hist, inp.v_hist, self.chunk_len, self.host_kv)
-        self.staging = torch.empty((n_buf, self.chunk_elems), dtype=cfg.torch_dtype, device=device)
+        self.staging = torch.empty((n_buf, chunks_per_copy * self.chunk_elems), dtype=cfg.torch_dtype,
+                                   device=device)
         self.q = inp.q.to(device)
         self.k_cand = inp.k_cand.to(device)
         self.v_cand = inp.v_cand.to(device)
@@ -209,11 +211,75 @@ class StreamedRound:
         cs = self.compute_stream
         cs.wait_stream(torch.cuda.current_stream())
         ss.ss_stream_history(self.problem, self.q, self.host_kv, self.chunk_len, self.n_chunks, self.staging,
-                             self.n_buf, self.state, 0, self.copy_stream, cs, record_timings)
+                             self.n_buf, self.state, 0, self.copy_stream, cs, record_timings,
+                             chunks_per_copy=self.chunks_per_copy)
         ss.ss_verify_candidates(self.problem, self.q, self.cand_view, self.parents, None, self.state,
                                 self.n_chunks, cs)
         ss.ss_merge_states(self.problem, self.state, None, self.o, self.lse, cs)
         torch.cuda.current_stream().wait_stream(cs)
+
+
+def exposed_wait(timings) -> float:
+    """The compute stream's wait for data in one streaming call, in ms: the
+    first chunk's arrival after the call, then every chunk that lands after
+    the previous chunk's attention finished (SpecStream section 3.2's
+    compute bubble)."""
+    c0, c1, k0, k1 = timings
+    return max(0.0, c1[0]) + sum(max(0.0, c1[j] - k1[j - 1]) for j in range(1, len(c1)))
+
+
+class LayeredStreamedRound:
+    """A verification round through L layers, each with its own host-resident
+    history (SpecStream section 4.2: the target reads each layer's history
+    layer by layer). Between layers the compute stream runs the rest of the
+    layer (output projection and feed-forward), stood in for here by a
+    square bf16 matrix product chain of a chosen size. With prefetch the
+    staging ring continues across layers (SS_STREAM_CONTINUE), so the next
+    layer's first chunks are copied while the current layer finishes."""
+
+    def __init__(self, inputs, device="cuda", n_buf=2, chunks_per_copy=1, rest_dim=4096, rest_reps=4):
+        self.layers = [StreamedRound.__new__(StreamedRound) for _ in inputs]
+        first = StreamedRound(inputs[0], device, n_buf, None, chunks_per_copy)
+        self.layers[0] = first
+        for i, inp in enumerate(inputs[1:], 1):
+            lay = StreamedRound.__new__(StreamedRound)
+            lay.__dict__.update(first.__dict__)     # same geometry, staging ring and streams
+            lay.host_kv = torch.empty_like(first.host_kv, pin_memory=True)
+            to_chunk_major(inp.k_hist, inp.v_hist, lay.chunk_len, lay.host_kv)
+            lay.q = inp.q.to(device)
+            lay.k_cand = inp.k_cand.to(device)
+            lay.v_cand = inp.v_cand.to(device)
+            lay.cand_view = ss.head_major_view(lay.k_cand, lay.v_cand)
+            lay.parents = None if inp.parents is None else torch.as_tensor(inp.parents, dtype=torch.int32,
+                                                                           device=device).contiguous()
+            lay.state = ss.StateBuffers(first.problem, first.n_chunks + 1, device)
+            lay.o = torch.empty_like(first.o)
+            lay.lse = torch.empty_like(first.lse)
+            self.layers[i] = lay
+        self.rest_a = torch.randn((rest_dim, rest_dim), device=device).to(torch.bfloat16)
+        self.rest_b = torch.randn((rest_dim, rest_dim), device=device).to(torch.bfloat16)
+        self.rest_reps = rest_reps
+
+    def run(self, prefetch=True, record_timings=False):
+        first = self.layers[0]
+        cs = first.compute_stream
+        cs.wait_stream(torch.cuda.current_stream())
+        for i, lay in enumerate(self.layers):
+            ss.ss_stream_history(lay.problem, lay.q, lay.host_kv, lay.chunk_len, lay.n_chunks, lay.staging,
+                                 lay.n_buf, lay.state, 0, lay.copy_stream, cs, record_timings,
+                                 chunks_per_copy=lay.chunks_per_copy, continue_ring=prefetch and i > 0)
+            ss.ss_verify_candidates(lay.problem, lay.q, lay.cand_view, lay.parents, None, lay.state, lay.n_chunks, cs)
+            ss.ss_merge_states(lay.problem, lay.state, None, lay.o, lay.lse, cs)
+            with torch.cuda.stream(cs):       # the rest of the layer
+                x = self.rest_a
+                for _ in range(self.rest_reps):
+                    x = torch.mm(x, self.rest_b)
+        torch.cuda.current_stream().wait_stream(cs)
+
+    def layer_waits(self):
+        """Exposed wait of every layer of the last timed run, in ms."""
+        n = len(self.layers)
+        return [exposed_wait(ss.ss_stream_timings(self.layers[i].n_chunks, back=n - 1 - i)) for i in range(n)]
 
 
 class TieredRound:

@@ -24,6 +24,9 @@ SS_ERR_HIP = -3
 SS_F32 = 0
 SS_BF16 = 1
 
+SS_STREAM_TIMINGS = 1
+SS_STREAM_CONTINUE = 2
+
 SS_ENGINE_AUTO = 0
 SS_ENGINE_VALU = 1
 SS_ENGINE_MFMA = 2
@@ -83,9 +86,9 @@ def lib() -> ctypes.CDLL:
         L.ss_merge_states.restype = I32
         L.ss_merge_states.argtypes = [P(Problem), P(State), VP, VP, VP, VP]
         L.ss_stream_history.restype = I32
-        L.ss_stream_history.argtypes = [P(Problem), VP, VP, VP, I32, I32, VP, I32, P(State), I32, VP, VP, I32]
+        L.ss_stream_history.argtypes = [P(Problem), VP, VP, VP, I32, I32, I32, VP, I32, P(State), I32, VP, VP, I32]
         L.ss_stream_timings.restype = I32
-        L.ss_stream_timings.argtypes = [I32, VP, VP, VP, VP]
+        L.ss_stream_timings.argtypes = [I32, I32, VP, VP, VP, VP]
         L.ss_tree_mask_host.restype = I32
         L.ss_tree_mask_host.argtypes = [VP, I32, VP]
         L.ss_slot_tokens_host.restype = I32
@@ -212,16 +215,19 @@ def ss_merge_states(problem: Problem, states: StateBuffers, slots_per_req: Optio
 
 def ss_stream_history(problem: Problem, q: torch.Tensor, host_kv: torch.Tensor, chunk_len: int, n_chunks: int,
                       staging: torch.Tensor, n_buf: int, out: StateBuffers, slot_begin: int, copy_stream,
-                      compute_stream, record_timings: bool = False, req_len: Optional[torch.Tensor] = None) -> None:
+                      compute_stream, record_timings: bool = False, req_len: Optional[torch.Tensor] = None,
+                      chunks_per_copy: int = 1, continue_ring: bool = False) -> None:
+    flags = (SS_STREAM_TIMINGS if record_timings else 0) | (SS_STREAM_CONTINUE if continue_ring else 0)
     _check(lib().ss_stream_history(ctypes.byref(problem), q.data_ptr(), host_kv.data_ptr(), _ptr(req_len), chunk_len,
-                                   n_chunks, staging.data_ptr(), n_buf, ctypes.byref(out.struct), slot_begin,
-                                   _stream(copy_stream), _stream(compute_stream), int(bool(record_timings))))
+                                   n_chunks, chunks_per_copy, staging.data_ptr(), n_buf, ctypes.byref(out.struct),
+                                   slot_begin, _stream(copy_stream), _stream(compute_stream), flags))
 
 
-def ss_stream_timings(n_chunks: int):
-    """Per-chunk (copy_begin, copy_end, compute_begin, compute_end) in ms."""
+def ss_stream_timings(n_chunks: int, back: int = 0):
+    """Per-chunk (copy_begin, copy_end, compute_begin, compute_end) in ms from
+    the compute stream's frontier at the timed call `back` calls ago."""
     bufs = [(ctypes.c_float * n_chunks)() for _ in range(4)]
-    _check(lib().ss_stream_timings(n_chunks, *[ctypes.addressof(b) for b in bufs]))
+    _check(lib().ss_stream_timings(back, n_chunks, *[ctypes.addressof(b) for b in bufs]))
     return [list(b) for b in bufs]
 
 

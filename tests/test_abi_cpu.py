@@ -140,12 +140,18 @@ def test_candidates_and_stream_reject():
                                 ctypes.byref(_state(2).struct), 2, None)
     assert rc == ss.SS_ERR_INVALID_ARG          # slot out of range
     # equal copy and compute streams
-    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, None, 64, 4, 8192, 2, ctypes.byref(_state(4).struct), 0,
+    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, None, 64, 4, 1, 8192, 2, ctypes.byref(_state(4).struct), 0,
                              None, None, 0)
     assert rc == ss.SS_ERR_INVALID_ARG
-    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, None, 64, 5, 8192, 2, ctypes.byref(_state(4).struct), 0,
+    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, None, 64, 5, 1, 8192, 2, ctypes.byref(_state(4).struct), 0,
                              1, 2, 0)
     assert rc == ss.SS_ERR_INVALID_ARG          # 5 chunks, 4 slots
+    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, None, 64, 4, 0, 8192, 2, ctypes.byref(_state(4).struct), 0,
+                             1, 2, 0)
+    assert rc == ss.SS_ERR_INVALID_ARG          # chunks_per_copy 0
+    rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, None, 64, 4, 1, 8192, 2, ctypes.byref(_state(4).struct), 0,
+                             1, 2, 4)
+    assert rc == ss.SS_ERR_INVALID_ARG          # unknown flag
     rc = L.ss_merge_states(ctypes.byref(p), ctypes.byref(_state().struct), None, None, 4096, None)
     assert rc == ss.SS_ERR_INVALID_ARG
 

@@ -291,12 +291,12 @@ def test_closed_forms_on_gpu():
     assert np.abs(rnd.o.cpu().numpy()[0][:, sel[2]] - inp.v_hist[0, 1, t].float().numpy()).max() < 5e-3
 
 
-@pytest.mark.parametrize("n_buf", [1, 2, 3])
-def test_streamed_matches_resident_and_oracle(n_buf):
+@pytest.mark.parametrize("n_buf,per_copy", [(1, 1), (2, 1), (3, 1), (2, 3), (1, 2)])
+def test_streamed_matches_resident_and_oracle(n_buf, per_copy):
     cfg = SMALL["c5_small"].with_(hist_len=8 * 256, chunk_len=256)
-    log(f"[streamed] n_buf {n_buf}")
+    log(f"[streamed] n_buf {n_buf}, chunks per copy {per_copy}")
     inp = wl.make_inputs(cfg)
-    srd = rounds.StreamedRound(inp, n_buf=n_buf)
+    srd = rounds.StreamedRound(inp, n_buf=n_buf, chunks_per_copy=per_copy)
     srd.run(record_timings=True)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle_round(inp)
@@ -308,137 +308,33 @@ def test_streamed_matches_resident_and_oracle(n_buf):
     c0, c1, k0, k1 = ss.ss_stream_timings(srd.n_chunks)
     for j in range(srd.n_chunks):
         assert c0[j] <= c1[j] <= k0[j] + 1e-3 and k0[j] <= k1[j]     # compute starts after its chunk landed
+        if j % per_copy:                                              # one copy per group of chunks
+            assert c0[j] == c0[j - 1] and c1[j] == c1[j - 1]
+    assert rounds.exposed_wait((c0, c1, k0, k1)) >= 0
 
 
-BALANCED = {
-    "c3_small_s2": ("c3_small", 2),
-    "c3_small_s6": ("c3_small", 6),
-    "c3_small_token_s3": ("c3_small_token", 3),
-    "c2_small_s3": ("c2_small", 3),
-    "rows16_s4": ("bf16_rows16", 4),
-    "rows4_mfma_s2": ("valu_r4", 2),
-    "rows32_g8_s5": ("bf16_rows32_g8", 5),
-    # cuts by fixed chunks: fp32 (VALU), wide rows, one slot
-    "c1_fallback_s3": ("c1", 3),
-    "wide_fallback_s3": ("wide_r96_ragged", 3),
-    "c2_one_slot": ("c2_small", 1),
-}
-
-
-def _history_only(inp):
-    """The oracle's state of each request's whole history (one slot)."""
-    cfg = inp.cfg
-    n = max(int(inp.hist_len.max()), 1)
-    return oracle.chunk_slot_states(inp.q.float().numpy(), inp.hist_per_request("k"), inp.hist_per_request("v"),
-                                    inp.hist_len, n, 0, 1, 1, cfg.scale)
-
-
-def _check_history_slots(rnd, inp):
-    """Folding the history slots (1 ..) alone gives the history-only result:
-    every slot was written (the state was pre-filled with NaN) and together
-    they cover each request's history exactly once."""
-    cfg = inp.cfg
-    m, l, acc = _history_only(inp)
-    o_ref, lse_ref = oracle.merge_slots(m, l, acc)
-    hs = slice(1, 1 + rnd.n_hist_slots)
-    gm = rnd.state.m[hs].double().cpu().numpy()
-    gl = rnd.state.l[hs].double().cpu().numpy()
-    gacc = rnd.state.acc[hs].double().cpu().numpy()
-    assert not np.isnan(gm).any() and not np.isnan(gl).any() and not np.isnan(gacc).any()
-    o, lse = oracle.merge_slots(gm, gl, gacc)
-    # requests without history: lse = -inf and O = 0 on both sides
-    empty = np.isneginf(lse_ref)
-    assert np.array_equal(np.isneginf(lse), empty)
-    assert (o[empty] == 0).all()
-    tol = TOL[cfg.dtype]
-    eo = np.abs(o - o_ref).max()
-    el = np.abs(lse[~empty] - lse_ref[~empty]).max() if (~empty).any() else 0.0
-    log(f"  history slots: max|dO| = {eo:.3e}, max|dlse| = {el:.3e} (tol {tol})")
-    assert eo <= tol and el <= tol, (eo, el)
-
-
-@pytest.mark.parametrize("name", list(BALANCED))
-def test_history_balanced(name):
-    base, n_slots = BALANCED[name]
-    cfg = SMALL[base]
-    log(f"[history] {name}: rows={cfg.rows} slots={n_slots}")
-    inp = wl.make_inputs(cfg)
-    rnd = rounds.ResidentRound(inp, split="balanced", history_slots=n_slots)
-    for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
-        t.fill_(float("nan"))
-    rnd.run()
-    torch.cuda.synchronize()
-    o_ref, lse_ref = oracle_round(inp)
-    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
-    check_mask(rnd, inp)
-    _check_history_slots(rnd, inp)
-
-
-@pytest.mark.parametrize("name", list(BALANCED))
-def test_history_fused_candidates(name):
-    """ss_verify_history with the candidate region: folded into each stream's
-    first piece on the narrow MFMA kernel, in a slot of its own elsewhere."""
-    base, n_slots = BALANCED[name]
-    cfg = SMALL[base]
-    if n_slots < 2 and not rounds.narrow_mfma(cfg):
-        pytest.skip("candidates need a slot of their own outside the narrow kernel")
-    log(f"[fused] {name}: rows={cfg.rows} slots={n_slots}")
-    inp = wl.make_inputs(cfg)
-    rnd = rounds.ResidentRound(inp, split="balanced", history_slots=n_slots, fuse_candidates=True)
-    for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
-        t.fill_(float("nan"))
-    rnd.mask_out.fill_(-1)
-    rnd.run()
-    torch.cuda.synchronize()
-    assert not torch.isnan(rnd.state.m).any() and not torch.isnan(rnd.state.acc).any()
-    o_ref, lse_ref = oracle_round(inp)
-    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
-    check_mask(rnd, inp)
-
-
-def test_history_balanced_many_requests_and_empties():
-    """More requests than a wavefront has lanes (the start search spans
-    several blocks), empty requests between and at the end, lengths off the
-    128-token alignment. Lengths are drawn from [400, 2000] apart from the
-    planted ones: with only a few visible keys the bf16 weights of the P V
-    product alone move O by up to about 3e-3 (2^-9 relative on weights that
-    a handful of keys dominate), which the 2e-3 bar does not allow for."""
-    cfg = SMALL["c3_small"].with_(batch=70, hist_len=2000, ragged_lo=400, chunk_len=256)
-    inp = wl.make_inputs(cfg)
-    inp.hist_len = inp.hist_len.copy()
-    inp.hist_len[[0, 5, 6, 40, 68, 69]] = 0
-    inp.hist_len[7] = 1
-    inp.hist_len[8] = 128
-    inp.hist_len[9] = 129
-    o_ref, lse_ref = oracle_round(inp)
-    for n_slots in (2, 3, 9):
-        for fuse in (False, True):
-            log(f"[history] 70 requests, slots={n_slots}, candidates fused={fuse}")
-            rnd = rounds.ResidentRound(inp, split="balanced", history_slots=n_slots, fuse_candidates=fuse)
-            for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
-                t.fill_(float("nan"))
-            rnd.run()
-            torch.cuda.synchronize()
-            compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
-            check_mask(rnd, inp)
-            if not fuse:
-                _check_history_slots(rnd, inp)
-            else:
-                assert not torch.isnan(rnd.state.m).any() and not torch.isnan(rnd.state.acc).any()
-    # no history at all: every history slot is empty, the result is the
-    # candidate region alone
-    inp.hist_len[:] = 0
-    o_ref, lse_ref = oracle_round(inp)
-    for fuse in (False, True):
-        rnd = rounds.ResidentRound(inp, split="balanced", history_slots=3, fuse_candidates=fuse)
-        for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
-            t.fill_(float("nan"))
-        rnd.run()
+@pytest.mark.parametrize("n_buf,per_copy", [(1, 1), (2, 1), (2, 2), (3, 1)])
+def test_layered_stream_with_prefetch(n_buf, per_copy):
+    """Three layers, each with its own host-resident history, the staging
+    ring continued across layers (cross-layer prefetch) or restarted per
+    layer: every layer's result matches the oracle, and chunks are attended
+    only after they landed."""
+    base = SMALL["c5_small"].with_(hist_len=6 * 256, chunk_len=256)
+    inputs = [wl.make_inputs(base.with_(seed=base.seed + 10 * i)) for i in range(3)]
+    lr = rounds.LayeredStreamedRound(inputs, n_buf=n_buf, chunks_per_copy=per_copy, rest_dim=512, rest_reps=2)
+    refs = [oracle_round(inp) for inp in inputs]
+    for prefetch in (True, False, True):
+        log(f"[layered] n_buf {n_buf}, chunks per copy {per_copy}, prefetch {prefetch}")
+        for lay in lr.layers:
+            lay.o.fill_(float("nan"))
+        lr.run(prefetch=prefetch, record_timings=True)
         torch.cuda.synchronize()
-        assert np.isneginf(rnd.state.m[1:].cpu().numpy()).all()
-        assert (rnd.state.l[1:] == 0).all() and (rnd.state.acc[1:] == 0).all()
-        compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
-        check_mask(rnd, inp)
+        for lay, (o_ref, lse_ref) in zip(lr.layers, refs):
+            compare(base, lay.o.cpu().numpy(), lay.lse.cpu().numpy(), o_ref, lse_ref)
+        for i, lay in enumerate(lr.layers):
+            c0, c1, k0, k1 = ss.ss_stream_timings(lay.n_chunks, back=len(lr.layers) - 1 - i)
+            assert all(c1[j] <= k0[j] + 1e-3 for j in range(lay.n_chunks))
+        log(f"  exposed waits (ms): {[round(w, 3) for w in lr.layer_waits()]}")
 
 
 def test_invalid_call_enqueues_nothing():
