@@ -8,14 +8,16 @@ Long-Context LLM Serving", section 4.2) or of the Speculative Streaming post it
 follows.
 
 `tiering` follows section 4.1 of the same paper (Eq. 4-5: which committed
-history migrates to the host, and when).
+history migrates to the host, and when). `sparse` reads the block importance
+statistics and block-sparse verification of the SparseSpec-L and Dustin
+abstracts on the same pages.
 
 Pins: every function here is checked by tests that do not reuse its code
 (pure-Python brute force, a library SDPA cross-check, the worked mask example
 printed in the Speculative Streaming post, closed forms and invariants).
 """
 
-from . import tiering  # noqa: F401
+from . import sparse, tiering  # noqa: F401
 from .verify_attention import (  # noqa: F401
     NEG_INF,
     attention_reference,
