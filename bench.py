@@ -236,6 +236,48 @@ def time_layered(cfg, n_layers=4, hist_len=16384, rest_dim=8192, rest_reps=2, re
     return out
 
 
+def time_sparse(cfg, block_len=512, k=16, reps=20):
+    """Block statistics and block-sparse verification on the resident
+    workload: the full round with one state slot per block, the per-head
+    importance and top-k selection, and the sparse round over the kept
+    blocks; the sparse result is compared with the full one on the GPU."""
+    inp = wl.make_inputs(cfg)
+    sr = rounds.SparseRound(inp, block_len, k)
+    del inp
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    ms_full = timed(sr.full)
+    ms_select = timed(sr.select)
+    ms_sparse = timed(sr.sparse)
+    torch.cuda.synchronize()
+    o_full, o_sparse = sr.full_round.o, sr.o
+    kept = (sr.selected >= 0).sum().item() / (cfg.batch * cfg.n_kv_heads)
+    hist_b, cand_b = kv_bytes(cfg, np.full(cfg.batch, cfg.hist_len))
+    kept_b = hist_b * kept / sr.n_blocks
+    return {
+        "workload": f"{cfg.name}, blocks of {block_len} tokens, {k} of {sr.n_blocks} kept per (request, KV head)",
+        "full_round_block_slots_ms": ms_full,
+        "importance_and_select_ms": ms_select,
+        "sparse_round_ms": ms_sparse,
+        "sparse_kept_KV_GBps": (kept_b + cand_b) / (ms_sparse * 1e-3) / 1e9,
+        "speedup_vs_full_round": ms_full / ms_sparse,
+        "max_abs_O_sparse_vs_full": float((o_sparse - o_full).abs().max().item()),
+        "mean_abs_O_sparse_vs_full": float((o_sparse - o_full).abs().mean().item()),
+    }
+
+
 def time_tiered(cfg, n_rounds=4, tail=512, gran=2048):
     """Commit-aware tiering (SpecStream section 4.1) on the streamed
     workload's shape: every request starts with its whole committed history,
@@ -431,6 +473,9 @@ def main():
         "query_tokens_per_s": round(cfg.batch * cfg.n_queries / (ms_step * 1e-3), 1),
         "roofline": roof,
     }
+    if args.workload == "c2_qwen3_8b" and not args.no_streamed:
+        out["sparse"] = time_sparse(cfg)
+        torch.cuda.empty_cache()
     if not args.no_streamed:
         out["streamed"] = time_streamed(wl.CONFIGS["c5_streamed"])
         torch.cuda.empty_cache()

@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 6
+#define SS_ABI_VERSION 7
 
 /* status codes */
 #define SS_OK 0
@@ -305,6 +305,40 @@ SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, con
  */
 SS_API int32_t ss_stream_timings(int32_t back, int32_t n_chunks, float* copy_begin, float* copy_end,
                                  float* compute_begin, float* compute_end);
+
+/*
+ * Block statistics and block-sparse verification: the per-block softmax
+ * statistics of a full verification round recycled as a per-head importance
+ * signal (the SparseSpec-L abstract on the pages), and verification of the
+ * history blocks that signal selects (the Dustin abstract). A block is a
+ * chunk of block_len tokens; with one state slot per block (ss_verify_chunk,
+ * chunks_per_slot 1) the mass that row r puts on block j is
+ * l_j(r) * exp(m_j(r) - lse(r)).
+ *
+ * ss_verify_chunk_gathered: as ss_verify_chunk with chunks_per_slot 1, but
+ *   slot slot_begin + s of (request b, KV head g) holds chunk
+ *   chunk_idx[(b * Hkv + g) * n_sel + s] of that request (device int32
+ *   [B][Hkv][n_sel]; < 0 or past the request's end: an empty slot). The
+ *   selection may differ per KV head.
+ * ss_block_importance: importance[b][g][j] = max over the rows r of KV head
+ *   g of l_j(r) * exp(m_j(r) - lse(r)), block j's state in slot
+ *   slot_begin + j of `states`, lse [B][q][Hq] the round's final lse
+ *   (ss_merge_states). Rows with l = 0 or lse = -inf contribute 0. Device
+ *   arrays; float32.
+ * ss_select_blocks: out[b][g][0..k) = the k blocks of largest importance
+ *   among request b's ceil(len_b / block_len) blocks (len_b = req_len[b], or
+ *   max_len when req_len is NULL; clamped to [0, max_len]), ties to the lower
+ *   index, listed in increasing order, padded with -1. n_blocks <= 8192
+ *   (SS_ERR_UNSUPPORTED above). Device arrays.
+ */
+SS_API int32_t ss_verify_chunk_gathered(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                        int32_t chunk_len, const int32_t* chunk_idx, int32_t n_sel,
+                                        const ss_state_t* out, int32_t slot_begin, ss_stream_t stream);
+SS_API int32_t ss_block_importance(const ss_problem_t* problem, const ss_state_t* states, int32_t slot_begin,
+                                   int32_t n_blocks, const float* lse, float* importance, ss_stream_t stream);
+SS_API int32_t ss_select_blocks(const ss_problem_t* problem, const float* importance, int32_t n_blocks,
+                                const int32_t* req_len, int32_t max_len, int32_t block_len, int32_t k, int32_t* out,
+                                ss_stream_t stream);
 
 /*
  * Commit-aware KV tiering (SpecStream section 4.1). A request's target KV is

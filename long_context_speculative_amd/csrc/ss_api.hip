@@ -536,6 +536,76 @@ extern "C" SS_API int32_t ss_stream_timings(int32_t back, int32_t n_chunks, floa
 }
 
 // ---------------------------------------------------------------------------
+// Block statistics and block-sparse verification (SparseSpec-L's recycled
+// attention statistics, Dustin's sparse verification).
+// ---------------------------------------------------------------------------
+
+extern "C" SS_API int32_t ss_verify_chunk_gathered(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                                   int32_t chunk_len, const int32_t* chunk_idx, int32_t n_sel,
+                                                   const ss_state_t* out, int32_t slot_begin, ss_stream_t stream) {
+    int32_t rc = validate_chunk(problem, q, hist, chunk_len, 0, n_sel, 1, out, slot_begin);
+    if (rc) return rc;
+    if (!chunk_idx) return fail(SS_ERR_INVALID_ARG, "chunk_idx is NULL");
+    if (n_sel == 0) return ok();
+    ChunkParams c = make_chunk_params(problem, q, hist, chunk_len, 0, n_sel, 1, out, slot_begin);
+    c.chunk_idx = chunk_idx;
+    c.n_sel = n_sel;
+    hipError_t e = enqueue_chunk(problem, c, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "chunk kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_block_importance(const ss_problem_t* problem, const ss_state_t* states, int32_t slot_begin,
+                                              int32_t n_blocks, const float* lse, float* importance,
+                                              ss_stream_t stream) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if ((rc = check_state(states, "block"))) return rc;
+    if (!lse || !importance) return fail(SS_ERR_INVALID_ARG, "lse or importance is NULL");
+    if (n_blocks < 0 || slot_begin < 0 || (int64_t)slot_begin + n_blocks > states->n_slots)
+        return fail(SS_ERR_INVALID_ARG, "blocks [%d, %d) outside the %d slots", slot_begin, slot_begin + n_blocks,
+                    states->n_slots);
+    ImportanceParams p{};
+    p.m = states->m;
+    p.l = states->l;
+    p.slot_begin = slot_begin;
+    p.batch = problem->batch;
+    p.n_q_heads = problem->n_q_heads;
+    p.n_kv_heads = problem->n_kv_heads;
+    p.n_queries = problem->n_queries;
+    p.n_blocks = n_blocks;
+    p.lse = lse;
+    p.importance = importance;
+    hipError_t e = launch_importance(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "importance kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" SS_API int32_t ss_select_blocks(const ss_problem_t* problem, const float* importance, int32_t n_blocks,
+                                           const int32_t* req_len, int32_t max_len, int32_t block_len, int32_t k,
+                                           int32_t* out, ss_stream_t stream) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if (!importance || !out) return fail(SS_ERR_INVALID_ARG, "importance or out is NULL");
+    if (n_blocks < 1 || k < 1 || block_len < 1 || max_len < 0)
+        return fail(SS_ERR_INVALID_ARG, "n_blocks, k and block_len must be positive, max_len non-negative");
+    if (n_blocks > kMaxSelectBlocks) return fail(SS_ERR_UNSUPPORTED, "more than %d blocks", kMaxSelectBlocks);
+    SelectParams p{};
+    p.importance = importance;
+    p.batch = problem->batch;
+    p.n_kv_heads = problem->n_kv_heads;
+    p.n_blocks = n_blocks;
+    p.k = k;
+    p.block_len = block_len;
+    p.max_len = max_len;
+    p.req_len = req_len;
+    p.out = out;
+    hipError_t e = launch_select(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "selection kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
 // Commit-aware KV tiering (section 4.1): the migration endpoint rule and the
 // row copies that move committed KV between the GPU tail and the host store.
 // ---------------------------------------------------------------------------

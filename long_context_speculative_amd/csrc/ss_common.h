@@ -167,6 +167,11 @@ struct ChunkParams {
     // chunk of a longer history): the chunk kernels see request b as
     // clamp(req_len[b] - len_offset, 0, max_len) tokens long.
     int64_t len_offset;
+    // Gathered chunks: slot s of (request b, KV head g) holds chunk
+    // chunk_idx[(b * n_kv_heads + g) * n_sel + s] (< 0: an empty slot);
+    // NULL: the contiguous chunk range of slot_tokens.
+    const int32_t* chunk_idx;
+    int32_t n_sel;
     // Candidate region folded into each stream's first piece (narrow MFMA
     // kernels, ss_verify_history only): with_cand != 0.
     int32_t with_cand;
@@ -212,6 +217,42 @@ __host__ __device__ inline int32_t chunk_view_len(const ChunkParams& p, int32_t 
     return (int32_t)(n < 0 ? 0 : (n > p.max_len ? p.max_len : n));
 }
 
+// Token range of slot s of (request b, KV head g) in a chunk call: the
+// contiguous chunk range, or the listed chunk of a gathered call.
+__host__ __device__ inline void piece_tokens(const ChunkParams& p, int32_t len, int32_t b, int32_t g, int32_t s,
+                                             int64_t* t0, int64_t* t1) {
+    if (!p.chunk_idx) {
+        slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, t0, t1);
+        return;
+    }
+    const int32_t c = p.chunk_idx[((int64_t)b * p.n_kv_heads + g) * p.n_sel + s];
+    int64_t a = c < 0 ? (int64_t)len : (int64_t)c * p.chunk_len;
+    int64_t e = a + p.chunk_len;
+    if (a > len) a = len;
+    if (e > len) e = len;
+    *t0 = a;
+    *t1 = e;
+}
+
+struct ImportanceParams {
+    const float* m;
+    const float* l;
+    int32_t slot_begin;  // block j's state is in slot slot_begin + j
+    int32_t batch, n_q_heads, n_kv_heads, n_queries, n_blocks;
+    const float* lse;    // [B][q][Hq]
+    float* importance;   // [B][Hkv][n_blocks]
+};
+
+struct SelectParams {
+    const float* importance;  // [B][Hkv][n_blocks]
+    int32_t batch, n_kv_heads, n_blocks, k, block_len, max_len;
+    const int32_t* req_len;
+    int32_t* out;             // [B][Hkv][k]
+};
+
+// Blocks the selection kernel holds in LDS.
+constexpr int kMaxSelectBlocks = 8192;
+
 // Rows per work-group in the VALU kernels.
 constexpr int kValuRows = 32;
 
@@ -230,5 +271,7 @@ hipError_t launch_candidates(const CandParams& p, int dtype, int head_dim, hipSt
 // Row blocks of the candidate kernel for `rows` rows per KV head.
 int cand_row_blocks(int rows);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
+hipError_t launch_importance(const ImportanceParams& p, hipStream_t stream);
+hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 
 }  // namespace ssv

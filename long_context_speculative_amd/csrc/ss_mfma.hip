@@ -412,10 +412,11 @@ template <int D, int NRT>
 __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) {
     __shared__ MfmaSmem<D, NRT> sm;
     const int s = blockIdx.x / p.n_kv_heads;
+    const int g = blockIdx.x % p.n_kv_heads;
     const int b = blockIdx.z;
     const int32_t len = chunk_view_len(p, b);
     int64_t t0, t1;
-    slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
+    piece_tokens(p, len, b, g, s, &t0, &t1);
     mfma_piece<D, NRT>(p, sm, GridAt{p}, t0, t1, p.with_cand && s == 0);
 }
 

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
 
     const int32_t len = chunk_view_len(p, b);
     int64_t t0, t1;
-    slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
+    piece_tokens(p, len, b, g, s, &t0, &t1);
 
     const int64_t base = (p.req_offset ? p.req_offset[b] : (int64_t)b * p.stride_b) + (int64_t)g * p.stride_h;
     const uint16_t* __restrict__ kp = static_cast<const uint16_t*>(p.k) + base;

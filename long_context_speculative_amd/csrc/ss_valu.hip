@@ -141,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void chunk_valu_kernel(ChunkParams p) {
 
     const int32_t len = chunk_view_len(p, b);
     int64_t t0, t1;
-    slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
+    piece_tokens(p, len, b, g, s, &t0, &t1);
 
     load_rows<T, D>(sm.q, static_cast<const T*>(p.q), b, g, r0, nr, p.n_queries, p.n_q_heads, p.group);
     const int64_t base = (p.req_offset ? p.req_offset[b] : (int64_t)b * p.stride_b) + (int64_t)g * p.stride_h;

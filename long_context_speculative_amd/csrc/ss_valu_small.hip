@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_valu_small_kernel(ChunkPara
 
     const int32_t len = chunk_view_len(p, b);
     int64_t t0, t1;
-    slot_tokens(len, p.chunk_len, p.chunk_begin, p.n_chunks, p.cps, s, &t0, &t1);
+    piece_tokens(p, len, b, g, s, &t0, &t1);
 
     // Query rows of this KV head into LDS (rows past R are zero).
     for (int e = tid; e < RMAX * (D / 8); e += kThreads) {

@@ -450,3 +450,52 @@ class TieredRound:
         k, v = self.tails[self.cur]
         t = k if which == "k" else v
         return t[b, :, :self.C[b] - self.H[b]].cpu()
+
+
+class SparseRound:
+    """Block statistics and block-sparse verification on a resident history
+    (the SparseSpec-L and Dustin abstracts on the pages, over SpecStream's
+    block-wise states):
+
+      full()    verification with one state slot per block of block_len
+                tokens (ss_verify_chunk, chunks_per_slot 1), the candidate
+                region in slot 0, merge -> O, lse of the full round;
+      select()  per-(request, KV head) importance of every block
+                (ss_block_importance) and the k most important blocks
+                (ss_select_blocks);
+      sparse()  verification of the selected blocks only
+                (ss_verify_chunk_gathered) with the candidate region, merge.
+    """
+
+    def __init__(self, inp: VerifyInputs, block_len: int, k: int, device="cuda", engine="auto"):
+        self.full_round = ResidentRound(inp, device, chunk_len=block_len, chunks_per_slot=1, engine=engine)
+        fr = self.full_round
+        cfg = inp.cfg
+        self.cfg, self.problem, self.block_len, self.k = cfg, fr.problem, block_len, k
+        self.n_blocks = fr.n_chunks
+        b_, hkv = cfg.batch, cfg.n_kv_heads
+        self.importance = torch.zeros((b_, hkv, max(self.n_blocks, 1)), dtype=torch.float32, device=device)
+        self.selected = torch.full((b_, hkv, k), -1, dtype=torch.int32, device=device)
+        self.len_dev = fr.hist_len if cfg.ragged else None
+        self.state = ss.StateBuffers(self.problem, k + 1, device)
+        self.o = torch.empty_like(fr.o)
+        self.lse = torch.empty_like(fr.lse)
+
+    def full(self, stream=None):
+        self.full_round.run(stream)
+
+    def select(self, stream=None):
+        fr = self.full_round
+        if self.n_blocks == 0:
+            self.selected.fill_(-1)
+            return
+        ss.ss_block_importance(self.problem, fr.state, 1, self.n_blocks, fr.lse, self.importance, stream)
+        ss.ss_select_blocks(self.problem, self.importance, self.len_dev, fr.max_len, self.block_len, self.k,
+                            self.selected, stream)
+
+    def sparse(self, stream=None):
+        fr = self.full_round
+        ss.ss_verify_chunk_gathered(self.problem, fr.q, fr.hist_view, self.block_len, self.selected, self.state, 1,
+                                    stream)
+        ss.ss_verify_candidates(self.problem, fr.q, fr.cand_view, fr.parents, None, self.state, 0, stream)
+        ss.ss_merge_states(self.problem, self.state, None, self.o, self.lse, stream)

@@ -34,7 +34,7 @@ SS_ENGINE_MFMA = 2
 EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chunk", "ss_verify_history",
             "ss_verify_candidates", "ss_merge_states", "ss_stream_history", "ss_stream_timings", "ss_tree_mask_host",
             "ss_slot_tokens_host", "ss_history_plan_host", "ss_tier_migration_end", "ss_tier_migrate",
-            "ss_kv_copy_rows")
+            "ss_kv_copy_rows", "ss_verify_chunk_gathered", "ss_block_importance", "ss_select_blocks")
 
 
 class SSError(RuntimeError):
@@ -101,6 +101,12 @@ def lib() -> ctypes.CDLL:
         L.ss_tier_migrate.argtypes = [P(Problem), P(KVView), VP, VP, VP, VP, I32, I32, VP]
         L.ss_kv_copy_rows.restype = I32
         L.ss_kv_copy_rows.argtypes = [P(Problem), P(KVView), VP, P(KVView), VP, VP, VP]
+        L.ss_verify_chunk_gathered.restype = I32
+        L.ss_verify_chunk_gathered.argtypes = [P(Problem), VP, P(KVView), I32, VP, I32, P(State), I32, VP]
+        L.ss_block_importance.restype = I32
+        L.ss_block_importance.argtypes = [P(Problem), P(State), I32, I32, VP, VP, VP]
+        L.ss_select_blocks.restype = I32
+        L.ss_select_blocks.argtypes = [P(Problem), VP, I32, VP, I32, I32, I32, VP, VP]
         _lib = L
     return _lib
 
@@ -282,3 +288,24 @@ def ss_kv_copy_rows(problem: Problem, src: KVView, src_row, dst: KVView, dst_row
     a, b_, n = _i64(src_row), _i64(dst_row), _i64(n_rows)
     _check(lib().ss_kv_copy_rows(ctypes.byref(problem), ctypes.byref(src), a.ctypes.data, ctypes.byref(dst),
                                  b_.ctypes.data, n.ctypes.data, _stream(stream)))
+
+
+def ss_verify_chunk_gathered(problem: Problem, q: torch.Tensor, hist: KVView, chunk_len: int, chunk_idx: torch.Tensor,
+                             out: StateBuffers, slot_begin: int, stream=None) -> None:
+    """chunk_idx: device int32 [B][Hkv][n_sel]."""
+    _check(lib().ss_verify_chunk_gathered(ctypes.byref(problem), q.data_ptr(), ctypes.byref(hist), chunk_len,
+                                          chunk_idx.data_ptr(), chunk_idx.shape[-1], ctypes.byref(out.struct),
+                                          slot_begin, _stream(stream)))
+
+
+def ss_block_importance(problem: Problem, states: StateBuffers, slot_begin: int, n_blocks: int, lse: torch.Tensor,
+                        importance: torch.Tensor, stream=None) -> None:
+    _check(lib().ss_block_importance(ctypes.byref(problem), ctypes.byref(states.struct), slot_begin, n_blocks,
+                                     lse.data_ptr(), importance.data_ptr(), _stream(stream)))
+
+
+def ss_select_blocks(problem: Problem, importance: torch.Tensor, req_len: Optional[torch.Tensor], max_len: int,
+                     block_len: int, k: int, out: torch.Tensor, stream=None) -> None:
+    """importance: device float32 [B][Hkv][n_blocks]; out: device int32 [B][Hkv][k]."""
+    _check(lib().ss_select_blocks(ctypes.byref(problem), importance.data_ptr(), importance.shape[-1], _ptr(req_len),
+                                  max_len, block_len, k, out.data_ptr(), _stream(stream)))
