@@ -54,7 +54,7 @@ def chunk_kernel_sources(cfg, engine="auto"):
         main = "ss_mfma.hip"
     else:
         main = "ss_mfma_wide.hip"
-    return [CSRC + main, CSRC + "ss_common.h"]
+    return [CSRC + main, CSRC + "ss_common.h", "long_context_speculative_amd/build.py"]
 
 
 def kv_bytes(cfg, hist_len) -> tuple[int, int]:

@@ -28,7 +28,8 @@
 //     2^8 over it (weights then stay <= 256; the rescale is rare);
 //   - row groups beyond the first re-read the chunk; all row groups of one
 //     (slot, KV head, request) are placed on the same XCD (work-group ids 8
-//     apart, dispatched back to back) so the re-read hits that XCD's L2.
+//     apart, dispatched back to back) so the re-read hits that XCD's L2, and
+//     eight consecutive (slot, KV head) units spread over the eight XCDs.
 
 #include <type_traits>
 
@@ -72,13 +73,16 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     static_assert(kPieces % T == 0, "tile pieces must divide evenly");
     __shared__ WideSmem sm;
 
-    // Work-group -> (slot, row group): row groups of one slot are 8 ids apart.
+    // Work-group -> (unit u = (slot, KV head), row group): eight consecutive
+    // units go to the eight XCDs (dispatch is round-robin over them), and the
+    // row groups of one unit are 8 ids apart, so they share that XCD's L2.
     const int x = blockIdx.x;
     const int x_hi = x / (8 * row_groups), rem = x % (8 * row_groups);
     const int rg = rem / 8;
-    const int s = x_hi * 8 + rem % 8;
-    if (s >= p.n_items) return;
-    const int g = blockIdx.y;
+    const int u = x_hi * 8 + rem % 8;
+    if (u >= p.n_items * p.n_kv_heads) return;
+    const int s = u % p.n_items;
+    const int g = u / p.n_items;
     const int b = blockIdx.z;
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -333,9 +337,10 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
 template <int NW>
 hipError_t launch_wide_t(const ChunkParams& p, hipStream_t stream) {
     const int row_groups = (p.rows + 32 * NW - 1) / (32 * NW);
-    const int64_t gx = (int64_t)((p.n_items + 7) / 8) * 8 * row_groups;
+    const int64_t units = (int64_t)p.n_items * p.n_kv_heads;
+    const int64_t gx = (units + 7) / 8 * 8 * row_groups;
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
-    dim3 grid((unsigned)gx, p.n_kv_heads, p.batch);
+    dim3 grid((unsigned)gx, 1, p.batch);
     hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW>), grid, dim3(64 * NW), 0, stream, p, row_groups);
     return hipGetLastError();
 }
