@@ -337,6 +337,137 @@ def test_layered_stream_with_prefetch(n_buf, per_copy):
         log(f"  exposed waits (ms): {[round(w, 3) for w in lr.layer_waits()]}")
 
 
+BALANCED = {
+    "c3_small_s2": ("c3_small", 2),
+    "c3_small_s6": ("c3_small", 6),
+    "c3_small_token_s3": ("c3_small_token", 3),
+    "c2_small_s3": ("c2_small", 3),
+    "rows16_s4": ("bf16_rows16", 4),
+    "rows4_mfma_s2": ("valu_r4", 2),
+    "rows32_g8_s5": ("bf16_rows32_g8", 5),
+    # cuts by fixed chunks: fp32 (VALU), wide rows, one slot
+    "c1_fallback_s3": ("c1", 3),
+    "wide_fallback_s3": ("wide_r96_ragged", 3),
+    "c2_one_slot": ("c2_small", 1),
+}
+
+
+def _history_only(inp):
+    """The oracle's state of each request's whole history (one slot)."""
+    cfg = inp.cfg
+    n = max(int(inp.hist_len.max()), 1)
+    return oracle.chunk_slot_states(inp.q.float().numpy(), inp.hist_per_request("k"), inp.hist_per_request("v"),
+                                    inp.hist_len, n, 0, 1, 1, cfg.scale)
+
+
+def _check_history_slots(rnd, inp):
+    """Folding the history slots (1 ..) alone gives the history-only result:
+    every slot was written (the state was pre-filled with NaN) and together
+    they cover each request's history exactly once."""
+    cfg = inp.cfg
+    m, l, acc = _history_only(inp)
+    o_ref, lse_ref = oracle.merge_slots(m, l, acc)
+    hs = slice(1, 1 + rnd.n_hist_slots)
+    gm = rnd.state.m[hs].double().cpu().numpy()
+    gl = rnd.state.l[hs].double().cpu().numpy()
+    gacc = rnd.state.acc[hs].double().cpu().numpy()
+    assert not np.isnan(gm).any() and not np.isnan(gl).any() and not np.isnan(gacc).any()
+    o, lse = oracle.merge_slots(gm, gl, gacc)
+    # requests without history: lse = -inf and O = 0 on both sides
+    empty = np.isneginf(lse_ref)
+    assert np.array_equal(np.isneginf(lse), empty)
+    assert (o[empty] == 0).all()
+    tol = TOL[cfg.dtype]
+    eo = np.abs(o - o_ref).max()
+    el = np.abs(lse[~empty] - lse_ref[~empty]).max() if (~empty).any() else 0.0
+    log(f"  history slots: max|dO| = {eo:.3e}, max|dlse| = {el:.3e} (tol {tol})")
+    assert eo <= tol and el <= tol, (eo, el)
+
+
+@pytest.mark.parametrize("name", list(BALANCED))
+def test_history_balanced(name):
+    base, n_slots = BALANCED[name]
+    cfg = SMALL[base]
+    log(f"[history] {name}: rows={cfg.rows} slots={n_slots}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, split="balanced", history_slots=n_slots)
+    for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
+        t.fill_(float("nan"))
+    rnd.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
+    _check_history_slots(rnd, inp)
+
+
+@pytest.mark.parametrize("name", list(BALANCED))
+def test_history_fused_candidates(name):
+    """ss_verify_history with the candidate region: folded into each stream's
+    first piece on the narrow MFMA kernel, in a slot of its own elsewhere."""
+    base, n_slots = BALANCED[name]
+    cfg = SMALL[base]
+    if n_slots < 2 and not rounds.narrow_mfma(cfg):
+        pytest.skip("candidates need a slot of their own outside the narrow kernel")
+    log(f"[fused] {name}: rows={cfg.rows} slots={n_slots}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, split="balanced", history_slots=n_slots, fuse_candidates=True)
+    for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
+        t.fill_(float("nan"))
+    rnd.mask_out.fill_(-1)
+    rnd.run()
+    torch.cuda.synchronize()
+    assert not torch.isnan(rnd.state.m).any() and not torch.isnan(rnd.state.acc).any()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
+
+
+def test_history_balanced_many_requests_and_empties():
+    """More requests than a wavefront has lanes (the start search spans
+    several blocks), empty requests between and at the end, lengths off the
+    128-token alignment. Lengths are drawn from [400, 2000] apart from the
+    planted ones: with only a few visible keys the bf16 weights of the P V
+    product alone move O by up to about 3e-3 (2^-9 relative on weights that
+    a handful of keys dominate), which the 2e-3 bar does not allow for."""
+    cfg = SMALL["c3_small"].with_(batch=70, hist_len=2000, ragged_lo=400, chunk_len=256)
+    inp = wl.make_inputs(cfg)
+    inp.hist_len = inp.hist_len.copy()
+    inp.hist_len[[0, 5, 6, 40, 68, 69]] = 0
+    inp.hist_len[7] = 1
+    inp.hist_len[8] = 128
+    inp.hist_len[9] = 129
+    o_ref, lse_ref = oracle_round(inp)
+    for n_slots in (2, 3, 9):
+        for fuse in (False, True):
+            log(f"[history] 70 requests, slots={n_slots}, candidates fused={fuse}")
+            rnd = rounds.ResidentRound(inp, split="balanced", history_slots=n_slots, fuse_candidates=fuse)
+            for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
+                t.fill_(float("nan"))
+            rnd.run()
+            torch.cuda.synchronize()
+            compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+            check_mask(rnd, inp)
+            if not fuse:
+                _check_history_slots(rnd, inp)
+            else:
+                assert not torch.isnan(rnd.state.m).any() and not torch.isnan(rnd.state.acc).any()
+    # no history at all: every history slot is empty, the result is the
+    # candidate region alone
+    inp.hist_len[:] = 0
+    o_ref, lse_ref = oracle_round(inp)
+    for fuse in (False, True):
+        rnd = rounds.ResidentRound(inp, split="balanced", history_slots=3, fuse_candidates=fuse)
+        for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
+            t.fill_(float("nan"))
+        rnd.run()
+        torch.cuda.synchronize()
+        assert np.isneginf(rnd.state.m[1:].cpu().numpy()).all()
+        assert (rnd.state.l[1:] == 0).all() and (rnd.state.acc[1:] == 0).all()
+        compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+        check_mask(rnd, inp)
+
+
 def test_invalid_call_enqueues_nothing():
     cfg = SMALL["c2_small"]
     inp = wl.make_inputs(cfg)
