@@ -236,6 +236,30 @@ def time_layered(cfg, n_layers=4, hist_len=16384, rest_dim=8192, rest_reps=2, re
     return out
 
 
+def read_probe(n_bytes=2 << 30, reps=10):
+    """Same-run HBM read reference (ss_read_probe): the history kernels' load
+    shape over n_bytes, with one wave of work-groups (their launch shape)
+    and with four per CU."""
+    from long_context_speculative_amd import ssverify as ss
+    cus = rounds.device_cus()
+    src = torch.ones(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    out = {"bytes": n_bytes}
+    for name, wgs in (("one_wave_GBps", 2 * cus), ("four_per_cu_GBps", 8 * cus)):
+        ss.ss_read_probe(src, wgs, sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            ss.ss_read_probe(src, wgs, sink)
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = round(n_bytes / (a.elapsed_time(b) / reps * 1e-3) / 1e9, 1)
+    del src
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_sparse(cfg, block_len=512, k=16, reps=20):
     """Block statistics and block-sparse verification on the resident
     workload: the full round with one state slot per block, the per-head
@@ -449,6 +473,9 @@ def main():
                 "kernel": kernel, "ms_per_launch": round(ms_chunk, 4), "algorithmic_bytes_per_launch": alg}
     del rnd
     torch.cuda.empty_cache()
+    probe = read_probe()
+    if roof["bound"] == "hbm":
+        roof["frac_of_read_probe"] = round(roof["achieved"] / max(probe["one_wave_GBps"], probe["four_per_cu_GBps"]), 4)
 
     out = {
         "metric": "verification-attn effective KV GB/s (% of HBM peak) + verified query-tokens/s",
@@ -472,6 +499,7 @@ def main():
         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "query_tokens_per_s": round(cfg.batch * cfg.n_queries / (ms_step * 1e-3), 1),
         "roofline": roof,
+        "hbm_read_probe": probe,
     }
     if args.workload == "c2_qwen3_8b" and not args.no_streamed:
         out["sparse"] = time_sparse(cfg)

@@ -378,6 +378,17 @@ SS_API int32_t ss_kv_copy_rows(const ss_problem_t* problem, const ss_kv_view_t* 
                                ss_stream_t stream);
 
 /*
+ * ss_read_probe -- measurement reference, not part of the method: a kernel
+ * that reads bytes (a multiple of 16) from the device buffer src with the
+ * history kernels' load shape (16-byte loads, eight in flight per lane), each
+ * of n_work_groups work-groups streaming one contiguous span. sink: device
+ * uint32 [256], written only for one particular data value. The benchmark
+ * reports the history kernels' bandwidth against this one.
+ */
+SS_API int32_t ss_read_probe(const void* src, int64_t bytes, int32_t n_work_groups, uint32_t* sink,
+                             ss_stream_t stream);
+
+/*
  * Host-side helpers that expose the integer rules the kernels apply. They run
  * on the CPU, touch no device, and are the same code the kernels compile.
  *

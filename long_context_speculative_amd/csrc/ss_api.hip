@@ -700,6 +700,16 @@ extern "C" SS_API int32_t ss_tier_migrate(const ss_problem_t* problem, const ss_
     return ok();
 }
 
+extern "C" SS_API int32_t ss_read_probe(const void* src, int64_t bytes, int32_t n_work_groups, uint32_t* sink,
+                                        ss_stream_t stream) {
+    if (!src || !sink) return fail(SS_ERR_INVALID_ARG, "src or sink is NULL");
+    if (!aligned16(src) || bytes < 16 || n_work_groups <= 0)
+        return fail(SS_ERR_INVALID_ARG, "src must be 16-byte aligned, bytes >= 16, n_work_groups > 0");
+    hipError_t e = launch_read_probe(src, bytes, n_work_groups, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "read probe launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 extern "C" SS_API int32_t ss_tree_mask_host(const int32_t* parents, int32_t n, uint64_t* out) {
     if (!parents || !out) return fail(SS_ERR_INVALID_ARG, "parents or out is NULL");
     if (n < 0 || n > 64) return fail(SS_ERR_INVALID_ARG, "n must be in [0, 64]");

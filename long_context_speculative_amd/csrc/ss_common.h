@@ -272,6 +272,7 @@ hipError_t launch_candidates(const CandParams& p, int dtype, int head_dim, hipSt
 int cand_row_blocks(int rows);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_importance(const ImportanceParams& p, hipStream_t stream);
+hipError_t launch_read_probe(const void* src, int64_t bytes, int32_t n_wg, uint32_t* sink, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 
 }  // namespace ssv

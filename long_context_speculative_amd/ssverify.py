@@ -34,7 +34,8 @@ SS_ENGINE_MFMA = 2
 EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chunk", "ss_verify_history",
             "ss_verify_candidates", "ss_merge_states", "ss_stream_history", "ss_stream_timings", "ss_tree_mask_host",
             "ss_slot_tokens_host", "ss_history_plan_host", "ss_tier_migration_end", "ss_tier_migrate",
-            "ss_kv_copy_rows", "ss_verify_chunk_gathered", "ss_block_importance", "ss_select_blocks")
+            "ss_kv_copy_rows", "ss_verify_chunk_gathered", "ss_block_importance", "ss_select_blocks",
+            "ss_read_probe")
 
 
 class SSError(RuntimeError):
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.ss_block_importance.argtypes = [P(Problem), P(State), I32, I32, VP, VP, VP]
         L.ss_select_blocks.restype = I32
         L.ss_select_blocks.argtypes = [P(Problem), VP, I32, VP, I32, I32, I32, VP, VP]
+        L.ss_read_probe.restype = I32
+        L.ss_read_probe.argtypes = [VP, I64, I32, VP, VP]
         _lib = L
     return _lib
 
@@ -309,3 +312,9 @@ def ss_select_blocks(problem: Problem, importance: torch.Tensor, req_len: Option
     """importance: device float32 [B][Hkv][n_blocks]; out: device int32 [B][Hkv][k]."""
     _check(lib().ss_select_blocks(ctypes.byref(problem), importance.data_ptr(), importance.shape[-1], _ptr(req_len),
                                   max_len, block_len, k, out.data_ptr(), _stream(stream)))
+
+
+def ss_read_probe(src: torch.Tensor, n_work_groups: int, sink: torch.Tensor, stream=None) -> None:
+    """Reads all of src (a 16-byte multiple) with n_work_groups contiguous spans."""
+    _check(lib().ss_read_probe(src.data_ptr(), src.numel() * src.element_size(), n_work_groups, sink.data_ptr(),
+                               _stream(stream)))
