@@ -512,3 +512,39 @@ def test_full_size_sampled(name):
         log(f"[full] {name}: oracle slice b={b} g={g}")
         o_ref, lse_ref = oracle_round(inp, requests=[b], kv_heads=[g])
         compare(cfg, o, lse, o_ref, lse_ref, rows_of(cfg, b, g))
+
+
+# ---------------------------------------------------------------------------
+# size extremes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["one_request_1m_tokens", "many_short_requests", "max_candidates_tree"])
+def test_size_extremes(name):
+    """One request with a million committed tokens (the balanced cut splits
+    its streams over the whole device), 1024 requests with short ragged
+    histories, and the largest candidate region (64 tree nodes under 8-way
+    GQA: 512 rows), each in the benchmark's launch configuration; sampled
+    (request, KV head) slices against the oracle."""
+    if name == "one_request_1m_tokens":
+        cfg = C["c2_qwen3_8b"].with_(batch=1, hist_len=1 << 20, chunk_len=4096)
+        picks = [(0, 0), (0, 5)]
+    elif name == "many_short_requests":
+        cfg = C["c3_internlm25_7b_ragged"].with_(batch=1024, hist_len=600, ragged_lo=300, chunk_len=256)
+        picks = [(0, 0), (511, 3), (1023, 7)]
+    else:
+        cfg = C["c4_tree_72b"].with_(batch=2, hist_len=3000, chunk_len=1024)
+        picks = [(0, 0), (1, 7)]
+    log(f"[extremes] {name}: generating")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, **rounds.BENCH_RESIDENT)
+    log(f"[extremes] {name}: {rnd.n_hist_slots} history slots, running")
+    rnd.run()
+    torch.cuda.synchronize()
+    o = rnd.o.cpu().numpy()
+    lse = rnd.lse.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    check_mask(rnd, inp)
+    for b, g in picks:
+        log(f"[extremes] {name}: oracle slice b={b} g={g}")
+        o_ref, lse_ref = oracle_round(inp, requests=[b], kv_heads=[g])
+        compare(cfg, o, lse, o_ref, lse_ref, rows_of(cfg, b, g))
