@@ -262,11 +262,16 @@ def read_probe(n_bytes=2 << 30, reps=10):
 
 def time_sparse(cfg, block_len=512, k=16, reps=20):
     """Block statistics and block-sparse verification on the resident
-    workload: the full round with one state slot per block, the per-head
-    importance and top-k selection, and the sparse round over the kept
-    blocks; the sparse result is compared with the full one on the GPU."""
+    workload, with the importance signal taken two ways: from a full round
+    with one state slot per block (ss_verify_chunk), and from the block
+    statistics that the benchmarked full round (balanced cut, candidates
+    fused) records as it goes. Then the per-head top-k selection and the
+    sparse round over the kept blocks; the sparse result is compared with
+    the full one on the GPU."""
     inp = wl.make_inputs(cfg)
-    sr = rounds.SparseRound(inp, block_len, k)
+    modes = {"block_slots": rounds.SparseRound(inp, block_len, k),
+             "stats": rounds.SparseRound(inp, block_len, k, stats=True)}
+    plain = rounds.ResidentRound(inp, **rounds.BENCH_RESIDENT)
     del inp
     stream = torch.cuda.current_stream()
 
@@ -282,24 +287,31 @@ def time_sparse(cfg, block_len=512, k=16, reps=20):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    ms_full = timed(sr.full)
-    ms_select = timed(sr.select)
-    ms_sparse = timed(sr.sparse)
-    torch.cuda.synchronize()
-    o_full, o_sparse = sr.full_round.o, sr.o
-    kept = (sr.selected >= 0).sum().item() / (cfg.batch * cfg.n_kv_heads)
+    ms_plain = timed(plain.run)
     hist_b, cand_b = kv_bytes(cfg, np.full(cfg.batch, cfg.hist_len))
-    kept_b = hist_b * kept / sr.n_blocks
-    return {
-        "workload": f"{cfg.name}, blocks of {block_len} tokens, {k} of {sr.n_blocks} kept per (request, KV head)",
-        "full_round_block_slots_ms": ms_full,
-        "importance_and_select_ms": ms_select,
-        "sparse_round_ms": ms_sparse,
-        "sparse_kept_KV_GBps": (kept_b + cand_b) / (ms_sparse * 1e-3) / 1e9,
-        "speedup_vs_full_round": ms_full / ms_sparse,
-        "max_abs_O_sparse_vs_full": float((o_sparse - o_full).abs().max().item()),
-        "mean_abs_O_sparse_vs_full": float((o_sparse - o_full).abs().mean().item()),
-    }
+    out = {"full_round_plain_ms": ms_plain}
+    for name, sr in modes.items():
+        ms_full = timed(sr.full)
+        ms_select = timed(sr.select)
+        ms_sparse = timed(sr.sparse)
+        torch.cuda.synchronize()
+        o_full, o_sparse = sr.full_round.o, sr.o
+        kept = (sr.selected >= 0).sum().item() / (cfg.batch * cfg.n_kv_heads)
+        kept_b = hist_b * kept / sr.n_blocks
+        out["workload"] = (f"{cfg.name}, blocks of {block_len} tokens, {k} of {sr.n_blocks} kept per "
+                           f"(request, KV head)")
+        out[name] = {
+            "full_round_ms": ms_full,
+            "importance_and_select_ms": ms_select,
+            "sparse_round_ms": ms_sparse,
+            "sparse_kept_KV_GBps": (kept_b + cand_b) / (ms_sparse * 1e-3) / 1e9,
+            "speedup_vs_plain_full_round": ms_plain / ms_sparse,
+            "max_abs_O_sparse_vs_full": float((o_sparse - o_full).abs().max().item()),
+            "mean_abs_O_sparse_vs_full": float((o_sparse - o_full).abs().mean().item()),
+        }
+    out["stats_recording_overhead"] = out["stats"]["full_round_ms"] / ms_plain - 1.0
+    out["selected_blocks_agree"] = bool(torch.equal(modes["stats"].selected, modes["block_slots"].selected))
+    return out
 
 
 def time_tiered(cfg, n_rounds=4, tail=512, gran=2048):

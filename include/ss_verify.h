@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 7
+#define SS_ABI_VERSION 8
 
 /* status codes */
 #define SS_OK 0
@@ -122,6 +122,20 @@ typedef struct ss_state {
     float* l;
     int32_t n_slots;
 } ss_state_t;
+
+/*
+ * Block statistics recorded by ss_verify_history as a by-product of full
+ * verification: for every row and block j of block_len history tokens, the
+ * online-softmax state (m, l) of the block's keys (in parts whose Eq. 8 fold
+ * is the block's state). buf holds ss_block_stats_bytes(problem, n_blocks)
+ * bytes (caller-owned, device; layout internal, read by
+ * ss_block_importance_stats); blocks past n_blocks are not recorded.
+ */
+typedef struct ss_block_stats {
+    void* buf;
+    int32_t block_len; /* a positive multiple of 128 */
+    int32_t n_blocks;
+} ss_block_stats_t;
 
 /* ABI version this library implements (SS_ABI_VERSION). */
 SS_API int32_t ss_abi_version(void);
@@ -203,11 +217,16 @@ SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const
  * tile of the work-group that holds a stream's first piece (no extra launch,
  * no extra slot); other engines run ss_verify_candidates into slot_begin
  * and cut the history into the remaining n_slots - 1 slots.
+ * stats: NULL, or record block statistics (narrow MFMA kernel only,
+ *   SS_ERR_UNSUPPORTED otherwise): the buffer is first filled with empty
+ *   states, then the cut is aligned to block_len (no block is split between
+ *   two pieces), and every piece records the (m, l) of its blocks.
  * Errors: as ss_verify_chunk and ss_verify_candidates.
  */
 SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
                                  const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
-                                 int32_t n_slots, const ss_state_t* out, int32_t slot_begin, ss_stream_t stream);
+                                 const ss_block_stats_t* stats, int32_t n_slots, const ss_state_t* out,
+                                 int32_t slot_begin, ss_stream_t stream);
 
 /*
  * ss_verify_candidates -- the state of the GPU-resident candidate region
@@ -336,6 +355,12 @@ SS_API int32_t ss_verify_chunk_gathered(const ss_problem_t* problem, const void*
                                         const ss_state_t* out, int32_t slot_begin, ss_stream_t stream);
 SS_API int32_t ss_block_importance(const ss_problem_t* problem, const ss_state_t* states, int32_t slot_begin,
                                    int32_t n_blocks, const float* lse, float* importance, ss_stream_t stream);
+/* Bytes of a block-statistics buffer for n_blocks blocks, or a negative status. */
+SS_API int64_t ss_block_stats_bytes(const ss_problem_t* problem, int32_t n_blocks);
+/* As ss_block_importance, from block statistics recorded by ss_verify_history
+ * (importance [B][Hkv][stats->n_blocks]). */
+SS_API int32_t ss_block_importance_stats(const ss_problem_t* problem, const ss_block_stats_t* stats,
+                                         const float* lse, float* importance, ss_stream_t stream);
 SS_API int32_t ss_select_blocks(const ss_problem_t* problem, const float* importance, int32_t n_blocks,
                                 const int32_t* req_len, int32_t max_len, int32_t block_len, int32_t k, int32_t* out,
                                 ss_stream_t stream);

@@ -151,6 +151,7 @@ ChunkParams make_chunk_params(const ss_problem_t* p, const void* q, const ss_kv_
     c.l = out->l;
     c.slot_begin = slot_begin;
     c.row_blocks = (c.rows + kValuRows - 1) / kValuRows;
+    c.plan_align = kPlanAlign;
     return c;
 }
 
@@ -282,8 +283,8 @@ CandParams make_cand_params(const ss_problem_t* problem, const void* q, const ss
 
 extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
                                             const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
-                                            int32_t n_slots, const ss_state_t* out, int32_t slot_begin,
-                                            ss_stream_t stream) {
+                                            const ss_block_stats_t* stats, int32_t n_slots, const ss_state_t* out,
+                                            int32_t slot_begin, ss_stream_t stream) {
     if (!hist) return fail(SS_ERR_INVALID_ARG, "history view is NULL");
     if (n_slots < 1) return fail(SS_ERR_INVALID_ARG, "n_slots must be at least 1");
     // validation first (the chunk length does not change its outcome)
@@ -293,6 +294,12 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
     const bool narrow = chunk_engine(problem) == ChunkEngine::kMfma;
     if (cand && !narrow && n_slots < 2)
         return fail(SS_ERR_INVALID_ARG, "with candidates this engine needs n_slots >= 2");
+    if (stats) {
+        if (!narrow) return fail(SS_ERR_UNSUPPORTED, "block statistics need the narrow MFMA kernel");
+        if (!stats->buf || stats->block_len <= 0 || stats->block_len % kPlanAlign || stats->n_blocks <= 0)
+            return fail(SS_ERR_INVALID_ARG, "block statistics: buffer, a positive multiple of %d tokens, blocks",
+                        kPlanAlign);
+    }
     // Slots of the history cut by fixed chunks (other engines with
     // candidates give the first slot to the candidate region).
     const int32_t hist_slots = (cand && !narrow) ? n_slots - 1 : n_slots;
@@ -310,12 +317,23 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
         if (pieces > hist_slots) pieces = hist_slots;
     }
     int64_t chunk = ((int64_t)hist->max_len + pieces - 1) / pieces;
-    chunk = (chunk + kPlanAlign - 1) / kPlanAlign * kPlanAlign;
-    if (chunk < kPlanAlign) chunk = kPlanAlign;
-    if (chunk > 0x7fffffff) chunk = 0x7fffffff;
+    const int64_t align = stats ? stats->block_len : kPlanAlign;  // blocks never straddle two pieces
+    chunk = (chunk + align - 1) / align * align;
+    if (chunk < align) chunk = align;
+    if (chunk > 0x7fffffff) return fail(SS_ERR_UNSUPPORTED, "history too long for %d slots", hist_slots);
     ChunkParams c = make_chunk_params(problem, q, hist, (int32_t)chunk, 0, hist_slots, 1, out, hist_begin);
+    c.plan_align = (int32_t)align;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
+    if (stats) {
+        c.stats = static_cast<float*>(stats->buf);
+        c.stats_block = stats->block_len;
+        c.stats_blocks = stats->n_blocks;
+        const int64_t pairs = (int64_t)kStatsQuarters * problem->batch * problem->n_queries * problem->n_q_heads *
+                              stats->n_blocks;
+        e = launch_stats_fill(c.stats, pairs, s);
+        if (e != hipSuccess) return fail(SS_ERR_HIP, "statistics fill failed: %s", hipGetErrorString(e));
+    }
     if (cand && narrow) {
         c.with_cand = 1;
         c.ck = cand->k;
@@ -577,6 +595,35 @@ extern "C" SS_API int32_t ss_block_importance(const ss_problem_t* problem, const
     p.lse = lse;
     p.importance = importance;
     hipError_t e = launch_importance(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "importance kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+extern "C" SS_API int64_t ss_block_stats_bytes(const ss_problem_t* problem, int32_t n_blocks) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if (n_blocks <= 0) return fail(SS_ERR_INVALID_ARG, "n_blocks must be positive");
+    ok();
+    return (int64_t)kStatsQuarters * problem->batch * problem->n_queries * problem->n_q_heads * n_blocks * 2 *
+           (int64_t)sizeof(float);
+}
+
+extern "C" SS_API int32_t ss_block_importance_stats(const ss_problem_t* problem, const ss_block_stats_t* stats,
+                                                    const float* lse, float* importance, ss_stream_t stream) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if (!stats || !stats->buf || stats->n_blocks <= 0 || !lse || !importance)
+        return fail(SS_ERR_INVALID_ARG, "statistics, lse or importance missing");
+    StatsImportanceParams p{};
+    p.ml = static_cast<const float2*>(stats->buf);
+    p.batch = problem->batch;
+    p.n_q_heads = problem->n_q_heads;
+    p.n_kv_heads = problem->n_kv_heads;
+    p.n_queries = problem->n_queries;
+    p.n_blocks = stats->n_blocks;
+    p.lse = lse;
+    p.importance = importance;
+    hipError_t e = launch_importance_stats(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SS_ERR_HIP, "importance kernel launch failed: %s", hipGetErrorString(e));
     return ok();
 }

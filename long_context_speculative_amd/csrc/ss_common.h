@@ -50,17 +50,20 @@ __host__ __device__ inline int32_t clamp_len(int32_t len, int32_t max_len) {
     return len < 0 ? 0 : (len > max_len ? max_len : len);
 }
 
-__host__ __device__ inline int64_t plan_pad(int32_t len) {
-    return ((int64_t)len + kPlanAlign - 1) / kPlanAlign * kPlanAlign;
+__host__ __device__ inline int64_t plan_pad(int32_t len, int32_t align = kPlanAlign) {
+    return ((int64_t)len + align - 1) / align * align;
 }
 
 // Tokens per work-group; n_slots >= 2, n_wg >= 1.
-__host__ __device__ inline int64_t plan_piece_len(int64_t total, int64_t pad_max, int32_t n_wg, int32_t n_slots) {
+// (align: a multiple of kPlanAlign; block statistics align the cut to their
+// blocks so that no block is shared by two pieces.)
+__host__ __device__ inline int64_t plan_piece_len(int64_t total, int64_t pad_max, int32_t n_wg, int32_t n_slots,
+                                                  int32_t align = kPlanAlign) {
     const int64_t even = (total + n_wg - 1) / n_wg;
     const int64_t cap = (pad_max + n_slots - 2) / (n_slots - 1);
     int64_t len = even > cap ? even : cap;
-    if (len < kPlanAlign) len = kPlanAlign;
-    return (len + kPlanAlign - 1) / kPlanAlign * kPlanAlign;
+    if (len < align) len = align;
+    return (len + align - 1) / align * align;
 }
 
 // Last work-group with a non-empty range (0 when the line is empty).
@@ -89,14 +92,15 @@ struct PlanPiece {
 // starts at or after it, with c = {that request, 0, its line position}.
 template <class LenFn>
 __host__ __device__ inline bool plan_next(const LenFn& len_of, int32_t batch, int32_t n_kv_heads, int64_t piece_len,
-                                          int64_t total, int32_t n_slots, int64_t w, PlanCursor& c, PlanPiece& out) {
+                                          int64_t total, int32_t n_slots, int64_t w, PlanCursor& c, PlanPiece& out,
+                                          int32_t align = kPlanAlign) {
     const int64_t lo = w * piece_len, hi = lo + piece_len;
     const int64_t w_last = plan_last_wg(total, piece_len);
     if (w > w_last) return false;
     while (c.b < batch) {
         if (c.line >= hi && w != w_last) return false;
         const int32_t len = len_of(c.b);
-        const int64_t pad = plan_pad(len);
+        const int64_t pad = plan_pad(len, align);
         if (pad == 0) {
             const int64_t at = c.line / piece_len;
             if ((at < w_last ? at : w_last) == w && c.g < n_kv_heads) {
@@ -181,6 +185,13 @@ struct ChunkParams {
     const int64_t* c_req_offset;
     const int32_t* parents;
     uint64_t* mask_out;
+    // Block statistics (history kernels of the narrow MFMA engine): per wave
+    // quarter w, row and block j of stats_block tokens, the state (m, l) of
+    // the keys of block j that wave w attended; stats[((((w * B + b) * q + i)
+    // * Hq + h) * stats_blocks + j) * 2 + {0: m, 1: l}]. NULL: none.
+    float* stats;
+    int32_t stats_block, stats_blocks;
+    int32_t plan_align;  // balanced cut: stream padding and piece alignment
 };
 
 struct CandParams {
@@ -250,6 +261,16 @@ struct SelectParams {
     int32_t* out;             // [B][Hkv][k]
 };
 
+struct StatsImportanceParams {
+    const float2* ml;   // block statistics, four wave quarters (ChunkParams::stats layout)
+    int32_t batch, n_q_heads, n_kv_heads, n_queries, n_blocks;
+    const float* lse;   // [B][q][Hq]
+    float* importance;  // [B][Hkv][n_blocks]
+};
+
+// Wave quarters of the block statistics (the narrow MFMA kernels' waves).
+constexpr int kStatsQuarters = 4;
+
 // Blocks the selection kernel holds in LDS.
 constexpr int kMaxSelectBlocks = 8192;
 
@@ -274,5 +295,7 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_importance(const ImportanceParams& p, hipStream_t stream);
 hipError_t launch_read_probe(const void* src, int64_t bytes, int32_t n_wg, uint32_t* sink, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
+hipError_t launch_stats_fill(float* ml, int64_t n_pairs, hipStream_t stream);
+hipError_t launch_importance_stats(const StatsImportanceParams& p, hipStream_t stream);
 
 }  // namespace ssv

@@ -36,6 +36,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
+static_assert(kWaves == kStatsQuarters, "block statistics keep one quarter per wave");
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;      // keys per wave iteration
 constexpr int kVtRow = 36;     // bf16 per transposed-V row: 32 keys + 4 pad (72 bytes)
@@ -70,7 +71,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast
 // that a caller can keep these indices out of registers during the key loop.
 // Uses the work-group's LDS; callers that run several pieces in a row
 // separate them with a barrier.
-template <int D, int NRT, class At>
+template <int D, int NRT, bool STATS, class At>
 __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT>& sm, const At& at, int64_t t0,
                                            int64_t t1, bool cand) {
     constexpr int NS = D / 32;   // feature steps of 32 for S = K Q^T
@@ -148,6 +149,31 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
         load_v_at(vp + tk * st, sti, (int)min((int64_t)kTile, t1 - tk) - 1, dst);
     };
 
+    // Block statistics: the running state of the keys of the current block
+    // (stats_block tokens) that this wave attends, written out when the
+    // wave moves to the next block: reference maximum m_run, and this
+    // lane's share bl of the sum of the (bf16) weights.
+    float bl[NRT];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) bl[rt] = 0.f;
+    int64_t blk_cur = -1;
+    auto flush_block = [&](int64_t blk) {
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) {
+            float lsum = bl[rt];
+            lsum += __shfl_xor(lsum, 16);
+            lsum += __shfl_xor(lsum, 32);
+            const int r = l16 + 16 * rt;
+            if (q4 == 0 && r < p.rows && blk < p.stats_blocks) {
+                const int i = r / p.group, h = at.g() * p.group + r % p.group;
+                const int64_t e = ((((int64_t)w * p.batch + at.b()) * p.n_queries + i) * p.n_q_heads + h) *
+                                  p.stats_blocks + blk;
+                *reinterpret_cast<float2*>(p.stats + 2 * e) =
+                    make_float2(m_run[rt] == -INFINITY ? -INFINITY : m_run[rt] * kLn2, lsum);
+            }
+        }
+    };
+
     // One tile: the first `valid` keys, and of those only the ones whose bit
     // is set in vis[rt] (per lane row) when `masked`. after_stage runs once
     // V is in LDS (its registers are free), after_s once S^T has read K.
@@ -211,6 +237,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
                 l_run[rt] *= alpha[rt];
+                if constexpr (STATS) bl[rt] *= alpha[rt];
 #pragma unroll
                 for (int xt = 0; xt < NXT; ++xt) o[xt][rt] *= alpha[rt];
             }
@@ -241,6 +268,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
                     }
                 }
             l_run[rt] += ls;
+            if constexpr (STATS) bl[rt] += masked ? 0.f : ls;
         }
 
         wave_sync();
@@ -272,9 +300,22 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
         // Prefetch the wave's next tile into the registers just consumed:
         // V right away (staged), K once the S^T products have read it.
         const bool more = tau + kWaves < n_tiles;
+        if constexpr (STATS) {
+            const int64_t blk = tk / p.stats_block;
+            if (blk != blk_cur) {
+                if (blk_cur >= 0) flush_block(blk_cur);
+                blk_cur = blk;
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt) bl[rt] = 0.f;
+            }
+        }
         consume(kf, vr, (int)min((int64_t)kTile, t1 - tk), false, no_vis,
                 [&] { if (more) load_v(tk + kTile * kWaves, vr); },
                 [&] { if (more) load_k(tk + kTile * kWaves, kf); });
+    }
+
+    if constexpr (STATS) {
+        if (blk_cur >= 0) flush_block(blk_cur);
     }
 
     // The candidate region (section 4.2: the GPU-resident rows under each
@@ -408,7 +449,7 @@ struct LdsAt {
     __device__ int slot() const { return p.slot_begin + max(__builtin_amdgcn_readfirstlane(pc->k), 0); }
 };
 
-template <int D, int NRT>
+template <int D, int NRT, bool STATS>
 __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) {
     __shared__ MfmaSmem<D, NRT> sm;
     const int s = blockIdx.x / p.n_kv_heads;
@@ -417,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) 
     const int32_t len = chunk_view_len(p, b);
     int64_t t0, t1;
     piece_tokens(p, len, b, g, s, &t0, &t1);
-    mfma_piece<D, NRT>(p, sm, GridAt{p}, t0, t1, p.with_cand && s == 0);
+    mfma_piece<D, NRT, STATS>(p, sm, GridAt{p}, t0, t1, p.with_cand && s == 0);
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
@@ -431,11 +472,11 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 // key loop needs.
 __device__ __noinline__ int32_t plan_step(const int32_t* req_len, int32_t max_len, int32_t batch, int32_t n_kv_heads,
                                           int64_t piece_len, int64_t total, int32_t n_slots, int64_t w,
-                                          PlanCursor* cursor, PlanPiece* out) {
+                                          PlanCursor* cursor, PlanPiece* out, int32_t align) {
     auto len_of = [&](int32_t b) { return clamp_len(req_len ? req_len[b] : max_len, max_len); };
     PlanCursor c = *cursor;
     PlanPiece pc;
-    const bool more = plan_next(len_of, batch, n_kv_heads, piece_len, total, n_slots, w, c, pc);
+    const bool more = plan_next(len_of, batch, n_kv_heads, piece_len, total, n_slots, w, c, pc, align);
     *cursor = c;
     if (more) *out = pc;
     return more ? 1 : 0;
@@ -443,7 +484,7 @@ __device__ __noinline__ int32_t plan_step(const int32_t* req_len, int32_t max_le
 
 // The whole resident history of every request, cut into balanced pieces
 // (the line split of plan_next) over gridDim.x work-groups.
-template <int D, int NRT>
+template <int D, int NRT, bool STATS>
 __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p) {
     __shared__ MfmaSmem<D, NRT> sm;
     const int lane = threadIdx.x & 63;
@@ -453,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
     int64_t total = 0, pad_max = 0;
     for (int b0 = 0; b0 < p.batch; b0 += 64) {
         const int b = b0 + lane;
-        int64_t sum = b < p.batch ? plan_pad(len_of(b)) : 0, mx = sum;
+        int64_t sum = b < p.batch ? plan_pad(len_of(b), p.plan_align) : 0, mx = sum;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
             sum += __shfl_xor(sum, off);
@@ -464,7 +505,7 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
     }
     total = uniform64(total * p.n_kv_heads);
     pad_max = uniform64(pad_max);
-    const int64_t piece_len = plan_piece_len(total, pad_max, (int32_t)gridDim.x, p.plan_slots);
+    const int64_t piece_len = plan_piece_len(total, pad_max, (int32_t)gridDim.x, p.plan_slots, p.plan_align);
     const int64_t w = blockIdx.x;
     if (w > plan_last_wg(total, piece_len)) return;
     const int64_t lo = w * piece_len;
@@ -474,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
     int64_t line = 0, carry = 0;
     for (int b0 = 0; b0 < p.batch; b0 += 64) {
         const int b = b0 + lane;
-        const int64_t span = b < p.batch ? (int64_t)p.n_kv_heads * plan_pad(len_of(b)) : 0;
+        const int64_t span = b < p.batch ? (int64_t)p.n_kv_heads * plan_pad(len_of(b), p.plan_align) : 0;
         int64_t incl = span;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -504,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
         __syncthreads();  // the previous piece is done with LDS; the cursor is visible
         if (threadIdx.x == 0)
             has_piece = plan_step(p.req_len, p.max_len, p.batch, p.n_kv_heads, piece_len, total, p.plan_slots, w,
-                                  &cursor, const_cast<PlanPiece*>(&piece));
+                                  &cursor, const_cast<PlanPiece*>(&piece), p.plan_align);
         __syncthreads();
         if (!__builtin_amdgcn_readfirstlane(has_piece)) break;
         // Re-read the arguments for every piece: held across the loop they
@@ -524,7 +565,8 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
         // The candidate region joins each stream's first piece; a stream
         // without history gets it alone in slot 0 (t0 = t1 = 0).
         const bool cand = pa.with_cand && k <= 0;
-        if (k >= 0 || cand) mfma_piece<D, NRT>(pa, sm, LdsAt{pa, pc}, uniform64(pc->t0), uniform64(pc->t1), cand);
+        if (k >= 0 || cand)
+            mfma_piece<D, NRT, STATS>(pa, sm, LdsAt{pa, pc}, uniform64(pc->t0), uniform64(pc->t1), cand);
         const int32_t b = __builtin_amdgcn_readfirstlane(pc->b);
         const int32_t g = __builtin_amdgcn_readfirstlane(pc->g);
         const int32_t s0 = max(__builtin_amdgcn_readfirstlane(pc->k), cand ? 0 : -1) + 1;
@@ -537,7 +579,10 @@ hipError_t launch_t(const ChunkParams& p, hipStream_t stream) {
     const int64_t gx = (int64_t)p.n_items * p.n_kv_heads;
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     dim3 grid((unsigned)gx, 1, p.batch);
-    hipLaunchKernelGGL((chunk_mfma_kernel<D, NRT>), grid, dim3(kThreads), 0, stream, p);
+    if (p.stats)
+        hipLaunchKernelGGL((chunk_mfma_kernel<D, NRT, true>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((chunk_mfma_kernel<D, NRT, false>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -557,7 +602,7 @@ hipError_t wave_wgs_t(int* out) {
         int cus = 0, per_cu = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, history_mfma_kernel<D, NRT>, kThreads, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, history_mfma_kernel<D, NRT, false>, kThreads, 0);
         if (e != hipSuccess) return e;
         n = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
         __atomic_store_n(&wave_wgs[dev], n, __ATOMIC_RELAXED);
@@ -571,7 +616,10 @@ hipError_t launch_hist_t(const ChunkParams& p, hipStream_t stream) {
     int n = 0;
     hipError_t e = wave_wgs_t<D, NRT>(&n);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((history_mfma_kernel<D, NRT>), dim3(n), dim3(kThreads), 0, stream, p);
+    if (p.stats)
+        hipLaunchKernelGGL((history_mfma_kernel<D, NRT, true>), dim3(n), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((history_mfma_kernel<D, NRT, false>), dim3(n), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

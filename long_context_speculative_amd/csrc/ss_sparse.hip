@@ -11,6 +11,8 @@
 //
 // importance_kernel: one thread per (request, KV head, block); the rows of
 // the head are read from the block's slot and the final lse.
+// importance_stats_kernel: the same mass from the block statistics the
+// history kernels record as a by-product (four wave quarters per block).
 // select_kernel: one work-group per (request, KV head); every block's rank
 // (more important first, ties to the lower index) is counted against all
 // others in LDS, the k best are written in increasing index order, padded
@@ -80,7 +82,59 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p) {
     for (int s = kept + threadIdx.x; s < p.k; s += kThreads) p.out[((int64_t)b * p.n_kv_heads + g) * p.k + s] = -1;
 }
 
+// Empty states (m = -inf, l = 0) in every entry of a block-statistics buffer.
+__global__ __launch_bounds__(kThreads) void stats_fill_kernel(float2* __restrict__ ml, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+        ml[i] = make_float2(-INFINITY, 0.f);
+}
+
+// Importance from block statistics: the four wave quarters of a block fold
+// into its mass l * exp(m - lse) per row, maximised over the KV head's rows.
+__global__ __launch_bounds__(kThreads) void importance_stats_kernel(StatsImportanceParams p) {
+    const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t total = (int64_t)p.batch * p.n_kv_heads * p.n_blocks;
+    if (id >= total) return;
+    const int j = (int)(id % p.n_blocks);
+    const int g = (int)((id / p.n_blocks) % p.n_kv_heads);
+    const int b = (int)(id / ((int64_t)p.n_blocks * p.n_kv_heads));
+    const int group = p.n_q_heads / p.n_kv_heads;
+    const int rows = p.n_queries * group;
+    const int64_t quarter = (int64_t)p.batch * p.n_queries * p.n_q_heads * p.n_blocks;
+    float best = 0.f;
+    for (int r = 0; r < rows; ++r) {
+        const int i = r / group, h = g * group + r % group;
+        const int64_t out_row = ((int64_t)b * p.n_queries + i) * p.n_q_heads + h;
+        const float lse = p.lse[out_row];
+        if (!(lse > -INFINITY)) continue;
+        float mass = 0.f;
+        for (int w = 0; w < kStatsQuarters; ++w) {
+            const float2 ml = p.ml[w * quarter + out_row * p.n_blocks + j];
+            if (ml.y > 0.f) mass += ml.y * __builtin_amdgcn_exp2f((ml.x - lse) * kLog2e);
+        }
+        best = fmaxf(best, mass);
+    }
+    p.importance[id] = best;
+}
+
 }  // namespace
+
+hipError_t launch_stats_fill(float* ml, int64_t n_pairs, hipStream_t stream) {
+    if (n_pairs <= 0) return hipSuccess;
+    int64_t blocks = (n_pairs + kThreads - 1) / kThreads;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(stats_fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       reinterpret_cast<float2*>(ml), n_pairs);
+    return hipGetLastError();
+}
+
+hipError_t launch_importance_stats(const StatsImportanceParams& p, hipStream_t stream) {
+    const int64_t total = (int64_t)p.batch * p.n_kv_heads * p.n_blocks;
+    const int64_t blocks = (total + kThreads - 1) / kThreads;
+    if (blocks == 0) return hipSuccess;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(importance_stats_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_importance(const ImportanceParams& p, hipStream_t stream) {
     const int64_t total = (int64_t)p.batch * p.n_kv_heads * p.n_blocks;

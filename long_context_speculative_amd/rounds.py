@@ -141,6 +141,7 @@ class ResidentRound:
             counts = [1 + math.ceil(int(n) / per_slot) for n in inp.hist_len]
             self.slots_per_req = torch.tensor(counts, dtype=torch.int32, device=device)
         self.mask_out = torch.zeros((cfg.batch, cfg.n_queries), dtype=torch.int64, device=device)
+        self.stats = None               # a BlockStatsBuffer: balanced split records block statistics
         self.o = torch.empty((cfg.batch, cfg.n_queries, cfg.n_q_heads, cfg.head_dim), dtype=torch.float32,
                              device=device)
         self.lse = torch.empty((cfg.batch, cfg.n_queries, cfg.n_q_heads), dtype=torch.float32, device=device)
@@ -148,11 +149,11 @@ class ResidentRound:
     def chunks(self, stream=None):
         if self.fused:                  # history and candidates, every slot written
             ss.ss_verify_history(self.problem, self.q, self.hist_view, self.cand_view, self.parents, self.mask_out,
-                                 self.n_call_slots, self.state, 0, stream)
+                                 self.n_call_slots, self.state, 0, stream, stats=self.stats)
             return
         if self.split == "balanced":    # writes every history slot, even with no history
             ss.ss_verify_history(self.problem, self.q, self.hist_view, None, None, None, self.n_hist_slots,
-                                 self.state, 1, stream)
+                                 self.state, 1, stream, stats=self.stats)
             return
         if self.n_chunks == 0:          # no history at all: nothing to enqueue
             return
@@ -457,22 +458,34 @@ class SparseRound:
     (the SparseSpec-L and Dustin abstracts on the pages, over SpecStream's
     block-wise states):
 
-      full()    verification with one state slot per block of block_len
-                tokens (ss_verify_chunk, chunks_per_slot 1), the candidate
-                region in slot 0, merge -> O, lse of the full round;
+      full()    the full round -> O, lse. With stats=False: one state slot
+                per block of block_len tokens (ss_verify_chunk,
+                chunks_per_slot 1), the candidate region in slot 0, merge.
+                With stats=True: the resident round as benchmarked (balanced
+                cut, candidates fused) recording block statistics as it goes
+                (narrow MFMA kernel, block_len a multiple of 128);
       select()  per-(request, KV head) importance of every block
-                (ss_block_importance) and the k most important blocks
-                (ss_select_blocks);
+                (ss_block_importance from the block slots, or
+                ss_block_importance_stats from the statistics) and the k most
+                important blocks (ss_select_blocks);
       sparse()  verification of the selected blocks only
                 (ss_verify_chunk_gathered) with the candidate region, merge.
     """
 
-    def __init__(self, inp: VerifyInputs, block_len: int, k: int, device="cuda", engine="auto"):
-        self.full_round = ResidentRound(inp, device, chunk_len=block_len, chunks_per_slot=1, engine=engine)
-        fr = self.full_round
+    def __init__(self, inp: VerifyInputs, block_len: int, k: int, device="cuda", engine="auto", stats=False):
         cfg = inp.cfg
+        self.use_stats = bool(stats)
+        if self.use_stats:
+            if not narrow_mfma(cfg, engine):
+                raise ValueError("block statistics need the narrow MFMA kernel")
+            self.full_round = ResidentRound(inp, device, chunk_len=block_len, engine=engine, **BENCH_RESIDENT)
+        else:
+            self.full_round = ResidentRound(inp, device, chunk_len=block_len, chunks_per_slot=1, engine=engine)
+        fr = self.full_round
         self.cfg, self.problem, self.block_len, self.k = cfg, fr.problem, block_len, k
         self.n_blocks = fr.n_chunks
+        if self.use_stats and self.n_blocks > 0:
+            fr.stats = ss.BlockStatsBuffer(self.problem, block_len, self.n_blocks, device)
         b_, hkv = cfg.batch, cfg.n_kv_heads
         self.importance = torch.zeros((b_, hkv, max(self.n_blocks, 1)), dtype=torch.float32, device=device)
         self.selected = torch.full((b_, hkv, k), -1, dtype=torch.int32, device=device)
@@ -489,7 +502,10 @@ class SparseRound:
         if self.n_blocks == 0:
             self.selected.fill_(-1)
             return
-        ss.ss_block_importance(self.problem, fr.state, 1, self.n_blocks, fr.lse, self.importance, stream)
+        if self.use_stats:
+            ss.ss_block_importance_stats(self.problem, fr.stats, fr.lse, self.importance, stream)
+        else:
+            ss.ss_block_importance(self.problem, fr.state, 1, self.n_blocks, fr.lse, self.importance, stream)
         ss.ss_select_blocks(self.problem, self.importance, self.len_dev, fr.max_len, self.block_len, self.k,
                             self.selected, stream)
 

@@ -35,7 +35,7 @@ EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chun
             "ss_verify_candidates", "ss_merge_states", "ss_stream_history", "ss_stream_timings", "ss_tree_mask_host",
             "ss_slot_tokens_host", "ss_history_plan_host", "ss_tier_migration_end", "ss_tier_migrate",
             "ss_kv_copy_rows", "ss_verify_chunk_gathered", "ss_block_importance", "ss_select_blocks",
-            "ss_read_probe")
+            "ss_read_probe", "ss_block_stats_bytes", "ss_block_importance_stats")
 
 
 class SSError(RuntimeError):
@@ -54,6 +54,10 @@ class KVView(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
                 ("stride_h", ctypes.c_int64), ("stride_t", ctypes.c_int64), ("req_offset", ctypes.c_void_p),
                 ("req_len", ctypes.c_void_p), ("max_len", ctypes.c_int32)]
+
+
+class BlockStats(ctypes.Structure):
+    _fields_ = [("buf", ctypes.c_void_p), ("block_len", ctypes.c_int32), ("n_blocks", ctypes.c_int32)]
 
 
 class State(ctypes.Structure):
@@ -81,7 +85,8 @@ def lib() -> ctypes.CDLL:
         L.ss_verify_chunk.restype = I32
         L.ss_verify_chunk.argtypes = [P(Problem), VP, P(KVView), I32, I32, I32, I32, P(State), I32, VP]
         L.ss_verify_history.restype = I32
-        L.ss_verify_history.argtypes = [P(Problem), VP, P(KVView), P(KVView), VP, VP, I32, P(State), I32, VP]
+        L.ss_verify_history.argtypes = [P(Problem), VP, P(KVView), P(KVView), VP, VP, P(BlockStats), I32,
+                                        P(State), I32, VP]
         L.ss_verify_candidates.restype = I32
         L.ss_verify_candidates.argtypes = [P(Problem), VP, P(KVView), VP, VP, P(State), I32, VP]
         L.ss_merge_states.restype = I32
@@ -106,6 +111,10 @@ def lib() -> ctypes.CDLL:
         L.ss_verify_chunk_gathered.argtypes = [P(Problem), VP, P(KVView), I32, VP, I32, P(State), I32, VP]
         L.ss_block_importance.restype = I32
         L.ss_block_importance.argtypes = [P(Problem), P(State), I32, I32, VP, VP, VP]
+        L.ss_block_stats_bytes.restype = I64
+        L.ss_block_stats_bytes.argtypes = [P(Problem), I32]
+        L.ss_block_importance_stats.restype = I32
+        L.ss_block_importance_stats.argtypes = [P(Problem), P(BlockStats), VP, VP, VP]
         L.ss_select_blocks.restype = I32
         L.ss_select_blocks.argtypes = [P(Problem), VP, I32, VP, I32, I32, I32, VP, VP]
         L.ss_read_probe.restype = I32
@@ -204,10 +213,12 @@ def ss_verify_chunk(problem: Problem, q: torch.Tensor, hist: KVView, chunk_len: 
 
 def ss_verify_history(problem: Problem, q: torch.Tensor, hist: KVView, cand: Optional[KVView],
                       parents: Optional[torch.Tensor], mask_out: Optional[torch.Tensor], n_slots: int,
-                      out: StateBuffers, slot_begin: int, stream=None) -> None:
+                      out: StateBuffers, slot_begin: int, stream=None, stats: Optional["BlockStatsBuffer"] = None
+                      ) -> None:
     _check(lib().ss_verify_history(ctypes.byref(problem), q.data_ptr(), ctypes.byref(hist),
                                    None if cand is None else ctypes.byref(cand), _ptr(parents), _ptr(mask_out),
-                                   n_slots, ctypes.byref(out.struct), slot_begin, _stream(stream)))
+                                   None if stats is None else ctypes.byref(stats.struct), n_slots,
+                                   ctypes.byref(out.struct), slot_begin, _stream(stream)))
 
 
 def ss_verify_candidates(problem: Problem, q: torch.Tensor, cand: KVView, parents: Optional[torch.Tensor],
@@ -305,6 +316,28 @@ def ss_block_importance(problem: Problem, states: StateBuffers, slot_begin: int,
                         importance: torch.Tensor, stream=None) -> None:
     _check(lib().ss_block_importance(ctypes.byref(problem), ctypes.byref(states.struct), slot_begin, n_blocks,
                                      lse.data_ptr(), importance.data_ptr(), _stream(stream)))
+
+
+def ss_block_stats_bytes(problem: Problem, n_blocks: int) -> int:
+    r = lib().ss_block_stats_bytes(ctypes.byref(problem), n_blocks)
+    _check(int(r) if r < 0 else 0)
+    return int(r)
+
+
+class BlockStatsBuffer:
+    """Device buffer for the block statistics ss_verify_history records."""
+
+    def __init__(self, problem: Problem, block_len: int, n_blocks: int, device="cuda"):
+        n = ss_block_stats_bytes(problem, n_blocks)
+        self.buf = torch.empty(n // 4, dtype=torch.float32, device=device)
+        self.struct = BlockStats(self.buf.data_ptr(), block_len, n_blocks)
+        self.block_len, self.n_blocks = block_len, n_blocks
+
+
+def ss_block_importance_stats(problem: Problem, stats: BlockStatsBuffer, lse: torch.Tensor, importance: torch.Tensor,
+                              stream=None) -> None:
+    _check(lib().ss_block_importance_stats(ctypes.byref(problem), ctypes.byref(stats.struct), lse.data_ptr(),
+                                           importance.data_ptr(), _stream(stream)))
 
 
 def ss_select_blocks(problem: Problem, importance: torch.Tensor, req_len: Optional[torch.Tensor], max_len: int,

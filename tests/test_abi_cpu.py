@@ -279,9 +279,10 @@ def test_verify_history_rejects():
     L = ss.lib()
     p = _problem()
     view = _view(max_len=1000)
-    def call(problem, q, n_slots, n_state, slot_begin, cand=None):
+    def call(problem, q, n_slots, n_state, slot_begin, cand=None, stats=None):
         return L.ss_verify_history(ctypes.byref(problem), q, ctypes.byref(view),
-                                   None if cand is None else ctypes.byref(cand), None, None, n_slots,
+                                   None if cand is None else ctypes.byref(cand), None, None,
+                                   None if stats is None else ctypes.byref(stats), n_slots,
                                    ctypes.byref(_state(n_state).struct), slot_begin, None)
     assert call(p, 4096, 0, 4, 0) == ss.SS_ERR_INVALID_ARG             # n_slots < 1
     assert call(p, 4096, 4, 4, 1) == ss.SS_ERR_INVALID_ARG             # slots [1, 5) of 4
@@ -293,6 +294,28 @@ def test_verify_history_rejects():
     assert call(_problem(n_queries=65), 4096, 2, 4, 0, cand=_view(max_len=65)) == ss.SS_ERR_UNSUPPORTED
     # outside the narrow MFMA kernel the candidates need a slot of their own
     assert call(_problem(engine=ss.SS_ENGINE_VALU), 4096, 1, 4, 0, cand=_view(max_len=6)) == ss.SS_ERR_INVALID_ARG
+    # block statistics: narrow MFMA kernel only, block_len a positive multiple of 128, a buffer
+    assert call(_problem(engine=ss.SS_ENGINE_VALU), 4096, 2, 4, 0,
+                stats=ss.BlockStats(4096, 128, 8)) == ss.SS_ERR_UNSUPPORTED
+    assert call(p, 4096, 2, 4, 0, stats=ss.BlockStats(4096, 100, 8)) == ss.SS_ERR_INVALID_ARG
+    assert call(p, 4096, 2, 4, 0, stats=ss.BlockStats(4096, 0, 8)) == ss.SS_ERR_INVALID_ARG
+    assert call(p, 4096, 2, 4, 0, stats=ss.BlockStats(4096, 256, 0)) == ss.SS_ERR_INVALID_ARG
+    assert call(p, 4096, 2, 4, 0, stats=ss.BlockStats(None, 256, 8)) == ss.SS_ERR_INVALID_ARG
+
+
+def test_block_stats_bytes_and_rejects():
+    p = _problem()
+    # four wave quarters x rows x blocks x (m, l) floats
+    rows = p.batch * p.n_queries * p.n_q_heads
+    assert ss.ss_block_stats_bytes(p, 8) == 4 * rows * 8 * 2 * 4
+    with pytest.raises(ss.SSError):
+        ss.ss_block_stats_bytes(p, 0)
+    L = ss.lib()
+    st = ss.BlockStats(4096, 256, 8)
+    assert L.ss_block_importance_stats(ctypes.byref(p), None, 4096, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_block_importance_stats(ctypes.byref(p), ctypes.byref(st), None, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_block_importance_stats(ctypes.byref(p), ctypes.byref(ss.BlockStats(4096, 256, 0)), 4096, 4096,
+                                       None) == ss.SS_ERR_INVALID_ARG
 
 
 def test_tier_migration_end_matches_oracle():

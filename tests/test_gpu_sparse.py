@@ -113,3 +113,73 @@ def test_gathered_chunks_invalid_entries():
                     assert np.isneginf(m[s, b][:, hs]).all() and (l[s, b][:, hs] == 0).all()
                 else:
                     assert np.abs(m[s, b][:, hs] - ref_m[j, b][:, hs]).max() <= 2e-3
+
+
+STATS_CASES = {
+    # uniform lengths: ss_verify_history's equal-chunk cut, chunks rounded to blocks
+    "c2_like_256": (C["c2_qwen3_8b"].with_(batch=2, hist_len=3000), 256, 4),
+    "c2_like_128": (C["c2_qwen3_8b"].with_(batch=2, hist_len=2900), 128, 5),
+    # ragged lengths: the balanced line cut, aligned to blocks
+    "ragged_128": (C["c3_internlm25_7b_ragged"].with_(batch=4, hist_len=2500, ragged_lo=300), 128, 6),
+    "ragged_512": (C["c3_internlm25_7b_ragged"].with_(batch=3, hist_len=9000, ragged_lo=700), 512, 4),
+    "tree_g8": (C["c4_tree_72b"].with_(batch=2, n_queries=4, hist_len=1100), 128, 3),
+}
+
+
+@pytest.mark.parametrize("name", list(STATS_CASES))
+def test_block_statistics_of_the_full_round(name):
+    """Importance from the statistics the full round records as it goes:
+    against the fp64 oracle within the bf16-weight bound, against the
+    importance read from per-block state slots, and the full round's O and
+    lse unchanged by the recording (bit for bit where the cut is the same)."""
+    cfg, block_len, k = STATS_CASES[name]
+    log(f"[stats] {name}: rows={cfg.rows}, block {block_len}, k {k}")
+    inp = wl.make_inputs(cfg)
+    sr = rounds.SparseRound(inp, block_len, k, stats=True)
+    sr.full()
+    sr.select()
+    slots = rounds.SparseRound(inp, block_len, k)
+    slots.full()
+    slots.select()
+    plain = rounds.ResidentRound(inp, **rounds.BENCH_RESIDENT)
+    plain.run()
+    torch.cuda.synchronize()
+    q = inp.q.float().numpy()
+    kh, vh = inp.hist_per_request("k"), inp.hist_per_request("v")
+    kc = inp.k_cand.float().numpy()
+    vis = cand_vis(inp)
+    imp_ref = sparse.block_importance(q, kh, vh, inp.hist_len, kc, vis, cfg.scale, block_len, sr.n_blocks)
+    imp = sr.importance.cpu().numpy().astype(np.float64)
+    d = np.abs(imp - imp_ref)
+    log(f"  stats importance: max|d| {d.max():.2e}, max mass {imp_ref.max():.3f}")
+    assert (d - 2 ** -8 * imp_ref).max() <= 1e-6
+    imp_slots = slots.importance.cpu().numpy().astype(np.float64)
+    assert (np.abs(imp - imp_slots) - 2 ** -7 * imp_slots).max() <= 2e-6
+    sel = sr.selected.cpu().numpy()
+    assert np.array_equal(sel, sparse.select_blocks(imp, inp.hist_len, block_len, k))
+    # the verification result is the round's, recording or not
+    o_ref, lse_ref = oracle.attention_reference(q, kh, vh, inp.hist_len, kc, inp.v_cand.float().numpy(), vis,
+                                                cfg.scale)
+    o, lse = sr.full_round.o.cpu().numpy(), sr.full_round.lse.cpu().numpy()
+    assert np.abs(o - o_ref).max() <= TOL[cfg.dtype] and np.abs(lse - lse_ref).max() <= TOL[cfg.dtype]
+    if block_len == 128:
+        assert torch.equal(sr.full_round.o, plain.o) and torch.equal(sr.full_round.lse, plain.lse)
+
+
+def test_block_statistics_fewer_blocks_than_history():
+    """Blocks past the buffer's n_blocks are not recorded; the recorded ones
+    match those of a buffer that covers the whole history."""
+    cfg = C["c3_internlm25_7b_ragged"].with_(batch=3, hist_len=4000, ragged_lo=1500)
+    inp = wl.make_inputs(cfg)
+    rr = rounds.ResidentRound(inp, **rounds.BENCH_RESIDENT)
+    full_blocks = -(-rr.max_len // 256)
+    imps = []
+    for nb in (full_blocks, 5):
+        rr.stats = ss.BlockStatsBuffer(rr.problem, 256, nb)
+        rr.run()
+        imp = torch.full((cfg.batch, cfg.n_kv_heads, nb), -1.0, device="cuda")
+        ss.ss_block_importance_stats(rr.problem, rr.stats, rr.lse, imp)
+        torch.cuda.synchronize()
+        imps.append(imp.cpu())
+    assert torch.equal(imps[1], imps[0][..., :5])
+    assert (imps[0] >= 0).all() and (imps[0][..., :5] > 0).any()
