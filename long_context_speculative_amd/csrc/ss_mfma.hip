@@ -39,6 +39,7 @@ constexpr int kWaves = 4;
 static_assert(kWaves == kStatsQuarters, "block statistics keep one quarter per wave");
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;      // keys per wave iteration
+static_assert(kPlanAlign % (kTile * kWaves) == 0, "a block holds a whole step of every wave");
 constexpr int kVtRow = 36;     // bf16 per transposed-V row: 32 keys + 4 pad (72 bytes)
 
 template <int D, int NRT>
@@ -152,25 +153,30 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
     // Block statistics: the running state of the keys of the current block
     // (stats_block tokens) that this wave attends, written out when the
     // wave moves to the next block: reference maximum m_run, and this
-    // lane's share bl of the sum of the (bf16) weights.
+    // lane's share bl of the sum of the (bf16) weights. Entry layout
+    // [wave][request][KV head][block][row of the head], so that one store
+    // (lane group q4 writes row tile q4) covers consecutive rows.
     float bl[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) bl[rt] = 0.f;
-    int64_t blk_cur = -1;
+    int64_t blk_cur = -1, blk_end = -1;  // current block and the token that ends it
     auto flush_block = [&](int64_t blk) {
+        float mv = -INFINITY, lv = 0.f;
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             float lsum = bl[rt];
             lsum += __shfl_xor(lsum, 16);
             lsum += __shfl_xor(lsum, 32);
-            const int r = l16 + 16 * rt;
-            if (q4 == 0 && r < p.rows && blk < p.stats_blocks) {
-                const int i = r / p.group, h = at.g() * p.group + r % p.group;
-                const int64_t e = ((((int64_t)w * p.batch + at.b()) * p.n_queries + i) * p.n_q_heads + h) *
-                                  p.stats_blocks + blk;
-                *reinterpret_cast<float2*>(p.stats + 2 * e) =
-                    make_float2(m_run[rt] == -INFINITY ? -INFINITY : m_run[rt] * kLn2, lsum);
+            if (q4 == rt) {
+                mv = m_run[rt];
+                lv = lsum;
             }
+        }
+        const int r = l16 + 16 * q4;
+        if (q4 < NRT && r < p.rows && blk < p.stats_blocks) {
+            const int64_t e =
+                ((((int64_t)w * p.batch + at.b()) * p.n_kv_heads + at.g()) * p.stats_blocks + blk) * p.rows + r;
+            *reinterpret_cast<float2*>(p.stats + 2 * e) = make_float2(mv == -INFINITY ? -INFINITY : mv * kLn2, lv);
         }
     };
 
@@ -300,17 +306,32 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
         // Prefetch the wave's next tile into the registers just consumed:
         // V right away (staged), K once the S^T products have read it.
         const bool more = tau + kWaves < n_tiles;
+        // Block statistics: a wave steps kTile * kWaves tokens, so at most
+        // one block ends per step; the finished one is written out once V is
+        // staged (bl and m_run still hold it), before the V prefetch.
+        int64_t done_blk = -1;
         if constexpr (STATS) {
-            const int64_t blk = tk / p.stats_block;
-            if (blk != blk_cur) {
-                if (blk_cur >= 0) flush_block(blk_cur);
-                blk_cur = blk;
-#pragma unroll
-                for (int rt = 0; rt < NRT; ++rt) bl[rt] = 0.f;
+            if (tk >= blk_end) {
+                if (blk_cur >= 0) {
+                    done_blk = blk_cur;
+                    ++blk_cur;
+                } else {
+                    blk_cur = tk / p.stats_block;
+                }
+                blk_end = (blk_cur + 1) * p.stats_block;
             }
         }
         consume(kf, vr, (int)min((int64_t)kTile, t1 - tk), false, no_vis,
-                [&] { if (more) load_v(tk + kTile * kWaves, vr); },
+                [&] {
+                    if constexpr (STATS) {
+                        if (done_blk >= 0) {
+                            flush_block(done_blk);
+#pragma unroll
+                            for (int rt = 0; rt < NRT; ++rt) bl[rt] = 0.f;
+                        }
+                    }
+                    if (more) load_v(tk + kTile * kWaves, vr);
+                },
                 [&] { if (more) load_k(tk + kTile * kWaves, kf); });
     }
 

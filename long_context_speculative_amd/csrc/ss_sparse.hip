@@ -12,7 +12,8 @@
 // importance_kernel: one thread per (request, KV head, block); the rows of
 // the head are read from the block's slot and the final lse.
 // importance_stats_kernel: the same mass from the block statistics the
-// history kernels record as a by-product (four wave quarters per block).
+// history kernels record as a by-product (four wave quarters per block,
+// entries [quarter][request][KV head][block][row of the head]).
 // select_kernel: one work-group per (request, KV head); every block's rank
 // (more important first, ties to the lower index) is counted against all
 // others in LDS, the k best are written in increasing index order, padded
@@ -90,30 +91,36 @@ __global__ __launch_bounds__(kThreads) void stats_fill_kernel(float2* __restrict
 
 // Importance from block statistics: the four wave quarters of a block fold
 // into its mass l * exp(m - lse) per row, maximised over the KV head's rows.
+// One wave per (request, KV head, block): lane r + 32 * half takes row r
+// (and rows r + 32, ...) of quarters half and half + 2; entries of
+// consecutive rows are adjacent.
 __global__ __launch_bounds__(kThreads) void importance_stats_kernel(StatsImportanceParams p) {
-    const int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int lane = threadIdx.x % 64;
+    const int64_t unit = (int64_t)blockIdx.x * (kThreads / 64) + threadIdx.x / 64;  // (request, KV head, block)
     const int64_t total = (int64_t)p.batch * p.n_kv_heads * p.n_blocks;
-    if (id >= total) return;
-    const int j = (int)(id % p.n_blocks);
-    const int g = (int)((id / p.n_blocks) % p.n_kv_heads);
-    const int b = (int)(id / ((int64_t)p.n_blocks * p.n_kv_heads));
+    if (unit >= total) return;  // whole waves
+    const int64_t bg = unit / p.n_blocks;
+    const int g = (int)(bg % p.n_kv_heads), b = (int)(bg / p.n_kv_heads);
     const int group = p.n_q_heads / p.n_kv_heads;
     const int rows = p.n_queries * group;
-    const int64_t quarter = (int64_t)p.batch * p.n_queries * p.n_q_heads * p.n_blocks;
+    const int half = lane / 32;
+    const int64_t quarter = total * rows;
     float best = 0.f;
-    for (int r = 0; r < rows; ++r) {
+    for (int r = lane % 32; r < rows; r += 32) {  // same trip count in both halves
         const int i = r / group, h = g * group + r % group;
-        const int64_t out_row = ((int64_t)b * p.n_queries + i) * p.n_q_heads + h;
-        const float lse = p.lse[out_row];
-        if (!(lse > -INFINITY)) continue;
+        const float lse = p.lse[((int64_t)b * p.n_queries + i) * p.n_q_heads + h];
         float mass = 0.f;
-        for (int w = 0; w < kStatsQuarters; ++w) {
-            const float2 ml = p.ml[w * quarter + out_row * p.n_blocks + j];
-            if (ml.y > 0.f) mass += ml.y * __builtin_amdgcn_exp2f((ml.x - lse) * kLog2e);
+        if (lse > -INFINITY) {
+            for (int w = half; w < kStatsQuarters; w += 2) {
+                const float2 ml = p.ml[w * quarter + unit * rows + r];
+                if (ml.y > 0.f) mass += ml.y * __builtin_amdgcn_exp2f((ml.x - lse) * kLog2e);
+            }
         }
+        mass += __shfl_xor(mass, 32);
         best = fmaxf(best, mass);
     }
-    p.importance[id] = best;
+    for (int off = 16; off >= 1; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+    if (lane == 0) p.importance[unit] = best;
 }
 
 }  // namespace
@@ -128,11 +135,11 @@ hipError_t launch_stats_fill(float* ml, int64_t n_pairs, hipStream_t stream) {
 }
 
 hipError_t launch_importance_stats(const StatsImportanceParams& p, hipStream_t stream) {
-    const int64_t total = (int64_t)p.batch * p.n_kv_heads * p.n_blocks;
-    const int64_t blocks = (total + kThreads - 1) / kThreads;
-    if (blocks == 0) return hipSuccess;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(importance_stats_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+    const int64_t units = (int64_t)p.batch * p.n_kv_heads * p.n_blocks;
+    const int64_t wgs = (units + kThreads / 64 - 1) / (kThreads / 64);
+    if (wgs == 0) return hipSuccess;
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(importance_stats_kernel, dim3((unsigned)wgs), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
