@@ -122,14 +122,17 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
 
     // Loads address a tile as a uniform base (scalar registers) plus a 32-bit
     // per-lane offset. Keys past the range are clamped to its last key so
-    // every load stays in bounds; their scores are masked below.
+    // every load stays in bounds; their scores are masked below. K and V are
+    // read once per round (the whole GQA group of a KV head shares one
+    // work-group), so the loads are non-temporal: streamed past the caches'
+    // normal retention, which reads HBM measurably faster on this device.
     // K fragment: keys 16*kt + l16 of the tile, features 32*k + 8*q4 .. +7.
     auto load_k_at = [&](const uint16_t* tb, int stride, int last, u32x4(&dst)[2][NS]) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             const int off = min(16 * kt + l16, last) * stride + 8 * q4;
 #pragma unroll
-            for (int k = 0; k < NS; ++k) dst[kt][k] = *reinterpret_cast<const u32x4*>(tb + off + 32 * k);
+            for (int k = 0; k < NS; ++k) dst[kt][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tb + off + 32 * k));
         }
     };
     // V rows 4*kg + e (kg = q4 + 4*h), features 8*l16 .. +7.
@@ -139,7 +142,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int off = min(4 * (q4 + 4 * h) + e, last) * stride + 8 * l16;
-                dst[h][e] = *reinterpret_cast<const u32x4*>(tb + off);
+                dst[h][e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tb + off));
             }
     };
     const int sti = (int)st;

@@ -1,8 +1,8 @@
 // Same-run HBM read reference of libssverify's measurement: how fast this
 // device streams a buffer it only reads, with the history kernels' load
-// shape (16-byte loads, eight in flight per lane) and either their launch
-// shape (one wave of work-groups, each a contiguous span) or more
-// work-groups. The history kernels' bandwidth is reported against it.
+// shape (16-byte non-temporal loads, eight in flight per lane) and either
+// their launch shape (one wave of work-groups, each a contiguous span) or
+// more work-groups. The history kernels' bandwidth is reported against it.
 
 #include "ss_common.h"
 
@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kThreads) void read_probe_kernel(const u32x4* __res
 #pragma unroll
         for (int j = 0; j < kDepth; ++j) {
             const int64_t k = i + (int64_t)j * kThreads;
-            v[j] = k < end ? src[k] : u32x4{0u, 0u, 0u, 0u};
+            v[j] = k < end ? __builtin_nontemporal_load(&src[k]) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int j = 0; j < kDepth; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
