@@ -351,6 +351,11 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
     }
     if (narrow && hist->req_len && hist_slots >= 2) {
         c.plan_slots = hist_slots;
+        // every slot starts empty; pieces overwrite theirs
+        const int64_t rows = (int64_t)problem->batch * problem->n_queries * problem->n_q_heads;
+        e = launch_state_fill(out->acc, out->m, out->l, (int64_t)hist_begin * rows, (int64_t)hist_slots * rows,
+                              problem->head_dim, s);
+        if (e != hipSuccess) return fail(SS_ERR_HIP, "state fill failed: %s", hipGetErrorString(e));
         e = launch_history_mfma(c, problem->head_dim, s);
     } else {
         e = enqueue_chunk(problem, c, s);

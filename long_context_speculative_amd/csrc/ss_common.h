@@ -40,10 +40,11 @@ __host__ __device__ inline void slot_tokens(int32_t len, int32_t chunk_len, int3
 // pad_max/(n_slots-1), rounded up to kPlanAlign, so that no stream is cut
 // into more than n_slots pieces. Piece k of a stream that starts at line
 // position o is its part inside work-group floor(o/L)+k's range; it goes to
-// slot k, and the owner of a stream's last piece fills the slots after it
-// with empty states. A request of length 0 has no pieces: the work-group
-// whose range holds its line position (the last busy one if that is past the
-// end) fills all its slots with empty states.
+// slot k; the slots after a stream's last piece hold empty states. A request
+// of length 0 has no pieces: the work-group whose range holds its line
+// position (the last busy one if that is past the end) owns its empty slots
+// (and the candidate region when it is folded in). The kernels leave empty
+// slots to a fill before the launch; fill_end records them for the host.
 constexpr int kPlanAlign = 128;
 
 __host__ __device__ inline int32_t clamp_len(int32_t len, int32_t max_len) {
@@ -186,9 +187,10 @@ struct ChunkParams {
     const int32_t* parents;
     uint64_t* mask_out;
     // Block statistics (history kernels of the narrow MFMA engine): per wave
-    // quarter w, row and block j of stats_block tokens, the state (m, l) of
-    // the keys of block j that wave w attended; stats[((((w * B + b) * q + i)
-    // * Hq + h) * stats_blocks + j) * 2 + {0: m, 1: l}]. NULL: none.
+    // quarter w, row r of KV head g (r = i * group + h % group) and block j
+    // of stats_block tokens, the state (m, l) of the keys of block j that
+    // wave w attended; stats[(((((w * B + b) * Hkv + g) * stats_blocks + j)
+    // * rows + r) * 2 + {0: m, 1: l}]. NULL: none.
     float* stats;
     int32_t stats_block, stats_blocks;
     int32_t plan_align;  // balanced cut: stream padding and piece alignment
@@ -296,6 +298,10 @@ hipError_t launch_importance(const ImportanceParams& p, hipStream_t stream);
 hipError_t launch_read_probe(const void* src, int64_t bytes, int32_t n_wg, uint32_t* sink, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_stats_fill(float* ml, int64_t n_pairs, hipStream_t stream);
+// Empty states (m = -inf, l = 0, acc = 0) in rows [row_begin, row_begin +
+// n_rows) of a state buffer (a row: head_dim accumulators, one m, one l).
+hipError_t launch_state_fill(float* acc, float* m, float* l, int64_t row_begin, int64_t n_rows, int head_dim,
+                             hipStream_t stream);
 hipError_t launch_importance_stats(const StatsImportanceParams& p, hipStream_t stream);
 
 }  // namespace ssv

@@ -44,14 +44,17 @@ constexpr int kVtRow = 36;     // bf16 per transposed-V row: 32 keys + 4 pad (72
 
 template <int D, int NRT>
 struct MfmaSmem {
-    static constexpr int kAccRegs = (D / 16) * NRT * 4;  // accumulator floats per lane
+    // Accumulator floats per lane of the feature tiles one wave owns in the
+    // final merge (wave w owns the 16-feature tiles xt with xt % kWaves == w).
+    static constexpr int kOwnRegs = (D / 16 / kWaves) * NRT * 4;
     uint64_t cbits[32];  // candidate visibility bits (at most 32 candidates here)
     union {
         uint16_t vt[kWaves][D][kVtRow];
         struct {
-            float acc[kWaves - 1][kAccRegs][64];
-            float m[kWaves - 1][16 * NRT];
-            float l[kWaves - 1][16 * NRT];
+            // [owner wave][contributing wave, owner skipped][owned float][lane]
+            float acc[kWaves][kWaves - 1][kOwnRegs][64];
+            float m[kWaves][16 * NRT];
+            float l[kWaves][16 * NRT];
         } mg;
     } u;
 };
@@ -373,82 +376,75 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
         l_run[rt] += __shfl_xor(l_run[rt], 32);
     }
 
-    // Merge the waves' states (Eq. 8) through LDS; wave 0 writes the slot.
-    __syncthreads();
-    if (w > 0) {
-        int idx = 0;
-#pragma unroll
-        for (int xt = 0; xt < NXT; ++xt)
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sm.u.mg.acc[w - 1][idx++][lane] = o[xt][rt][j];
-        if (q4 == 0) {
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                sm.u.mg.m[w - 1][l16 + 16 * rt] = m_run[rt];
-                sm.u.mg.l[w - 1][l16 + 16 * rt] = l_run[rt];
-            }
-        }
-    }
-    __syncthreads();
-    if (w == 0) {
-        for (int ww = 0; ww < kWaves - 1; ++ww) {
-            float a0[NRT], a1[NRT];
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                const float mw = sm.u.mg.m[ww][l16 + 16 * rt];
-                const float lw = sm.u.mg.l[ww][l16 + 16 * rt];
-                const float m_new = fmaxf(m_run[rt], mw);
-                a0[rt] = (m_run[rt] == -INFINITY) ? 0.f : exp2_hw(m_run[rt] - m_new);
-                a1[rt] = (mw == -INFINITY) ? 0.f : exp2_hw(mw - m_new);
-                l_run[rt] = a0[rt] * l_run[rt] + a1[rt] * lw;
-                m_run[rt] = m_new;
-            }
-            int idx = 0;
-#pragma unroll
-            for (int xt = 0; xt < NXT; ++xt)
-#pragma unroll
-                for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        o[xt][rt][j] = a0[rt] * o[xt][rt][j] + a1[rt] * sm.u.mg.acc[ww][idx++][lane];
-                    }
-        }
-
+    // Merge the waves' states (Eq. 8) through LDS, the work split by feature
+    // tiles: every wave publishes its (m, l) and the accumulator tiles that
+    // other waves own, then folds the four partial states of its own tiles
+    // and writes them; wave 0 also writes m and l.
+    static_assert(NXT % kWaves == 0, "feature tiles split evenly over the waves");
+    constexpr int kOwnTile = NRT * 4;  // floats per lane of one owned feature tile
+    __syncthreads();  // every wave is done with the V staging area
+    if (q4 == 0) {
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
-            const int r = l16 + 16 * rt;
-            if (r >= p.rows) continue;
-            const int i = r / p.group, h = at.g() * p.group + r % p.group;
-            const int64_t row = (((int64_t)at.slot() * p.batch + at.b()) * p.n_queries + i) * p.n_q_heads + h;
-            if (q4 == 0) {
-                p.m[row] = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
-                p.l[row] = l_run[rt];
-            }
-#pragma unroll
-            for (int xt = 0; xt < NXT; ++xt)
-                *reinterpret_cast<floatx4*>(p.acc + row * D + 16 * xt + 4 * q4) = o[xt][rt];
+            sm.u.mg.m[w][l16 + 16 * rt] = m_run[rt];
+            sm.u.mg.l[w][l16 + 16 * rt] = l_run[rt];
         }
     }
-}
-
-// Empty states (m = -inf, l = 0, acc = 0) for every row of stream (b, g) in
-// slots [s0, s1).
-template <int D>
-__device__ __forceinline__ void store_empty(const ChunkParams& p, int b, int g, int s0, int s1) {
-    constexpr int kVec = D / 4;
-    for (int slot = s0; slot < s1; ++slot) {
-        const int64_t base = ((int64_t)slot * p.batch + b) * p.n_queries;
-        for (int idx = threadIdx.x; idx < p.rows * kVec; idx += kThreads) {
-            const int r = idx / kVec, x = idx % kVec;
-            const int i = r / p.group, h = g * p.group + r % p.group;
-            const int64_t row = (base + i) * p.n_q_heads + h;
-            *reinterpret_cast<floatx4*>(p.acc + row * D + 4 * x) = floatx4{0.f, 0.f, 0.f, 0.f};
-            if (x == 0) {
-                p.m[row] = -INFINITY;
-                p.l[row] = 0.f;
+#pragma unroll
+    for (int xt = 0; xt < NXT; ++xt) {
+        const int owner = xt % kWaves;
+        if (owner == w) continue;
+        const int slot = w < owner ? w : w - 1;
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sm.u.mg.acc[owner][slot][(xt / kWaves) * kOwnTile + rt * 4 + j][lane] = o[xt][rt][j];
+    }
+    __syncthreads();
+    float a[kWaves][NRT];  // weight of each wave's partial state in the merged one
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        float mw[kWaves], m_tot = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            mw[ww] = sm.u.mg.m[ww][l16 + 16 * rt];
+            m_tot = fmaxf(m_tot, mw[ww]);
+        }
+        float l_tot = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            a[ww][rt] = (mw[ww] == -INFINITY) ? 0.f : exp2_hw(mw[ww] - m_tot);
+            l_tot += a[ww][rt] * sm.u.mg.l[ww][l16 + 16 * rt];
+        }
+        m_run[rt] = m_tot;
+        l_run[rt] = l_tot;
+    }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+        const int r = l16 + 16 * rt;
+        if (r >= p.rows) continue;
+        const int i = r / p.group, h = at.g() * p.group + r % p.group;
+        const int64_t row = (((int64_t)at.slot() * p.batch + at.b()) * p.n_queries + i) * p.n_q_heads + h;
+        if (w == 0 && q4 == 0) {
+            p.m[row] = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
+            p.l[row] = l_run[rt];
+        }
+#pragma unroll
+        for (int xt = 0; xt < NXT; ++xt) {
+            if (xt % kWaves != w) continue;
+            floatx4 v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                float x = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < kWaves; ++ww) {
+                    const float part = ww == w ? o[xt][rt][j]
+                                               : sm.u.mg.acc[w][ww < w ? ww : ww - 1][(xt / kWaves) * kOwnTile + rt * 4 + j][lane];
+                    x += a[ww][rt] * part;
+                }
+                v[j] = x;
             }
+            *reinterpret_cast<floatx4*>(p.acc + row * D + 16 * xt + 4 * q4) = v;
         }
     }
 }
@@ -589,12 +585,11 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
         // The candidate region joins each stream's first piece; a stream
         // without history gets it alone in slot 0 (t0 = t1 = 0).
         const bool cand = pa.with_cand && k <= 0;
+        // Slots without a piece keep the empty states written before the
+        // launch (a separate fill: stores here, behind the key loop's reads,
+        // cost several times their bytes).
         if (k >= 0 || cand)
             mfma_piece<D, NRT, STATS>(pa, sm, LdsAt{pa, pc}, uniform64(pc->t0), uniform64(pc->t1), cand);
-        const int32_t b = __builtin_amdgcn_readfirstlane(pc->b);
-        const int32_t g = __builtin_amdgcn_readfirstlane(pc->g);
-        const int32_t s0 = max(__builtin_amdgcn_readfirstlane(pc->k), cand ? 0 : -1) + 1;
-        store_empty<D>(pa, b, g, pa.slot_begin + s0, pa.slot_begin + __builtin_amdgcn_readfirstlane(pc->fill_end));
     }
 }
 

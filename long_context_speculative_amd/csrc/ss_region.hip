@@ -247,6 +247,20 @@ hipError_t launch_cand_t(const CandParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Empty states over a contiguous range of rows: the slots that the balanced
+// cut leaves without a piece keep them.
+__global__ __launch_bounds__(kThreads) void state_fill_kernel(float4* __restrict__ acc, int64_t n_vec,
+                                                              float* __restrict__ m, float* __restrict__ l,
+                                                              int64_t n_rows) {
+    const int64_t step = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_vec; i += step)
+        acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_rows; i += step) {
+        m[i] = -INFINITY;
+        l[i] = 0.f;
+    }
+}
+
 }  // namespace
 
 int cand_row_blocks(int rows) { return (rows + kRowsPerBlock - 1) / kRowsPerBlock; }
@@ -258,6 +272,18 @@ hipError_t launch_candidates(const CandParams& p, int dtype, int head_dim, hipSt
     }
     if (head_dim == 64) return launch_cand_t<uint16_t, 64>(p, stream);
     return launch_cand_t<uint16_t, 128>(p, stream);
+}
+
+hipError_t launch_state_fill(float* acc, float* m, float* l, int64_t row_begin, int64_t n_rows, int head_dim,
+                             hipStream_t stream) {
+    if (n_rows <= 0) return hipSuccess;
+    const int64_t n_vec = n_rows * head_dim / 4;
+    int64_t blocks = (n_vec + kThreads - 1) / kThreads;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(state_fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       reinterpret_cast<float4*>(acc + row_begin * head_dim), n_vec, m + row_begin, l + row_begin,
+                       n_rows);
+    return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
