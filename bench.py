@@ -238,14 +238,14 @@ def time_layered(cfg, n_layers=4, hist_len=16384, rest_dim=8192, rest_reps=2, re
 
 def read_probe(n_bytes=2 << 30, reps=10):
     """Same-run HBM read reference (ss_read_probe): the history kernels' load
-    shape over n_bytes, with one wave of work-groups (their launch shape)
-    and with four per CU."""
+    shape over n_bytes of N(0,1) bf16 data (like the KV history), with one
+    work-group per CU (their launch shape) and with eight."""
     from long_context_speculative_amd import ssverify as ss
     cus = rounds.device_cus()
-    src = torch.ones(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
+    src = torch.randn(n_bytes // 2, dtype=torch.bfloat16, device="cuda")
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     out = {"bytes": n_bytes}
-    for name, wgs in (("one_wave_GBps", 2 * cus), ("four_per_cu_GBps", 8 * cus)):
+    for name, wgs in (("one_per_cu_GBps", cus), ("eight_per_cu_GBps", 8 * cus)):
         ss.ss_read_probe(src, wgs, sink)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -465,6 +465,9 @@ def main():
     if args.counters:
         counters_pass(cfg, cps, args.engine, args.split)
         return
+    # the read reference first, while the device is in the state the timed
+    # steps start from (after seconds of streaming it reads measurably slower)
+    probe = read_probe()
     rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup, cps, args.engine, args.split)
     cps = rnd.cps
     kernel = "ss_verify_history" if rnd.split == "balanced" else "ss_verify_chunk"
@@ -490,9 +493,8 @@ def main():
                 "kernel": kernel, "ms_per_launch": round(ms_chunk, 4), "algorithmic_bytes_per_launch": alg}
     del rnd
     torch.cuda.empty_cache()
-    probe = read_probe()
     if roof["bound"] == "hbm":
-        roof["frac_of_read_probe"] = round(roof["achieved"] / max(probe["one_wave_GBps"], probe["four_per_cu_GBps"]), 4)
+        roof["frac_of_read_probe"] = round(roof["achieved"] / max(probe["one_per_cu_GBps"], probe["eight_per_cu_GBps"]), 4)
 
     out = {
         "metric": "verification-attn effective KV GB/s (% of HBM peak) + verified query-tokens/s",

@@ -306,7 +306,7 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
     const int32_t hist_begin = (cand && !narrow) ? slot_begin + 1 : slot_begin;
     const int64_t streams = (int64_t)problem->batch * problem->n_kv_heads;
     // Pieces per stream of a cut by fixed chunks: hist_slots, or for uniform
-    // lengths on the narrow kernel as many as fill one wave of work-groups.
+    // lengths on the narrow kernel one work-group per CU.
     int64_t pieces = hist_slots;
     if (narrow && !hist->req_len) {
         int wgs = 0;

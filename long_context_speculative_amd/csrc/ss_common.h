@@ -282,11 +282,11 @@ constexpr int kValuRows = 32;
 // Launchers (defined in the kernel translation units).
 hipError_t launch_chunk_valu(const ChunkParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
-// Balanced split of the whole resident history over one full wave of
-// work-groups (narrow MFMA kernel); p.plan_slots slots from p.slot_begin.
+// Balanced split of the whole resident history over one work-group per CU
+// (narrow MFMA kernel); p.plan_slots slots from p.slot_begin.
 hipError_t launch_history_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
-// Work-groups of the narrow MFMA kernels that one full wave of the current
-// device holds (resident work-groups per CU times CUs).
+// Work-groups of one launch of the narrow MFMA kernels that covers the
+// current device: one per CU.
 hipError_t mfma_wave_work_groups(int rows, int* n);
 hipError_t launch_chunk_mfma_wide(const ChunkParams& p, int head_dim, hipStream_t stream);
 hipError_t launch_chunk_valu_small(const ChunkParams& p, int head_dim, hipStream_t stream);

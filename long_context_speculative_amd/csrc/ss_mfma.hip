@@ -605,8 +605,11 @@ hipError_t launch_t(const ChunkParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// One full wave of work-groups: resident work-groups per CU times CUs,
-// queried once per device.
+// Work-groups of one history launch: one per CU, queried once per device.
+// A CU could hold two of these 4-wave work-groups, but the SIMD arbiter
+// favours the older one: it finishes its range early and leaves the other
+// streaming alone, so the launch ends later than with one work-group (one
+// wave per SIMD) per CU over twice the range.
 constexpr int kMaxDevices = 64;
 
 template <int D, int NRT>
@@ -618,12 +621,10 @@ hipError_t wave_wgs_t(int* out) {
     if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
     int n = __atomic_load_n(&wave_wgs[dev], __ATOMIC_RELAXED);
     if (n <= 0) {
-        int cus = 0, per_cu = 0;
+        int cus = 0;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, history_mfma_kernel<D, NRT, false>, kThreads, 0);
-        if (e != hipSuccess) return e;
-        n = (cus > 0 ? cus : 1) * (per_cu > 0 ? per_cu : 1);
+        n = cus > 0 ? cus : 1;
         __atomic_store_n(&wave_wgs[dev], n, __ATOMIC_RELAXED);
     }
     *out = n;

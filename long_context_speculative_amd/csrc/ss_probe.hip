@@ -1,7 +1,7 @@
 // Same-run HBM read reference of libssverify's measurement: how fast this
 // device streams a buffer it only reads, with the history kernels' load
 // shape (16-byte non-temporal loads, eight in flight per lane) and either
-// their launch shape (one wave of work-groups, each a contiguous span) or
+// their launch shape (one work-group per CU, each a contiguous span) or
 // more work-groups. The history kernels' bandwidth is reported against it.
 
 #include "ss_common.h"

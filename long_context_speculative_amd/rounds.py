@@ -26,34 +26,43 @@ def device_cus(device="cuda") -> int:
     return torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
 
 
-def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int) -> int:
+def wgs_per_cu(cfg, engine="auto") -> int:
+    """Work-groups per compute unit in one launch: one for the narrow MFMA
+    kernels (two co-resident 4-wave work-groups progress unevenly, and the
+    one left alone at the end streams slower), two for the other chunk
+    kernels."""
+    return 1 if narrow_mfma(cfg, engine) else 2
+
+
+def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int, engine="auto") -> int:
     """Chunks merged per state slot for a resident round. Wide row groups
     (compute-bound) take 4. Otherwise the slot count is chosen so that the
-    chunk kernel launches about two work-groups per compute unit (one full
-    wave of work-groups): fewer launches leave units idle, more leave
-    partly filled rounds and cost a state slot each."""
+    chunk kernel launches about one full wave of work-groups (wgs_per_cu
+    per compute unit): fewer launches leave units idle, more leave partly
+    filled rounds and cost a state slot each."""
     if cfg.rows > 32:
         return 4
     units = sum(-(-int(n) // chunk_len) for n in hist_len) * cfg.n_kv_heads
-    return max(1, units // (2 * cus))
+    return max(1, units // (wgs_per_cu(cfg, engine) * cus))
 
 
-def auto_history_slots(cfg, hist_len, cus: int) -> int:
+def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
     """Slots per stream for ss_verify_history. Ragged lengths: enough that
     the longest stream does not force ranges longer than an even share of
-    one wave of work-groups (two per compute unit), plus one for the range
-    boundaries. Uniform lengths: one chunk per work-group of that wave. Wide
-    row groups use the fixed cut of 4 chunks per slot."""
+    one wave of work-groups, plus one for the range boundaries. Uniform
+    lengths: one chunk per work-group of that wave. Wide row groups use the
+    fixed cut of 4 chunks per slot."""
     pads = [-(-int(n) // 128) * 128 for n in hist_len]
     pad_max = max(pads, default=0)
     if cfg.rows > 32:
         return max(1, -(-pad_max // (4 * cfg.chunk_len)))
+    wave = wgs_per_cu(cfg, engine) * cus
     if not cfg.ragged:
-        return max(1, 2 * cus // (cfg.batch * cfg.n_kv_heads))
+        return max(1, wave // (cfg.batch * cfg.n_kv_heads))
     total = sum(pads) * cfg.n_kv_heads
     if total == 0:
         return 2
-    return max(2, -(-pad_max * 2 * cus // total) + 2)
+    return max(2, -(-pad_max * wave // total) + 2)
 
 
 def narrow_mfma(cfg, engine="auto") -> bool:
@@ -94,7 +103,7 @@ class ResidentRound:
             raise ValueError(f"unknown split {split!r}")
         self.split = split
         if chunks_per_slot == "auto":
-            chunks_per_slot = auto_chunks_per_slot(cfg, inp.hist_len, self.chunk_len, device_cus(device))
+            chunks_per_slot = auto_chunks_per_slot(cfg, inp.hist_len, self.chunk_len, device_cus(device), engine)
         self.cps = chunks_per_slot
         self.q = inp.q.to(device)
         self.k_hist = inp.k_hist.to(device)
@@ -123,7 +132,7 @@ class ResidentRound:
         self.fused = bool(fuse_candidates) and split == "balanced"
         if split == "balanced":
             if history_slots == "auto":
-                history_slots = auto_history_slots(cfg, inp.hist_len, device_cus(device))
+                history_slots = auto_history_slots(cfg, inp.hist_len, device_cus(device), engine)
             self.n_hist_slots = int(history_slots)
         else:
             self.n_hist_slots = math.ceil(self.n_chunks / self.cps)
