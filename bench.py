@@ -402,7 +402,19 @@ def cpu_baseline(cfg, budget_s=15.0):
     cores = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
     return {"value": kv / done / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{slices} (request, KV head) slices of {cfg.name}, fp64 NumPy, {done:.1f} s",
-            "query_tokens_per_s": slices / (cfg.batch * cfg.n_kv_heads) * cfg.batch * cfg.n_queries / done}
+            "query_tokens_per_s": slices / (cfg.batch * cfg.n_kv_heads) * cfg.batch * cfg.n_queries / done,
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def counters_pass(cfg, cps="auto", engine="auto", split="balanced"):
@@ -446,6 +458,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true", help="skip the streamed, tiered and layered legs")
     ap.add_argument("--no-sparse", action="store_true", help="skip the block-statistics / sparse leg")
+    ap.add_argument("--streamed-only", action="store_true",
+                    help="run only the streamed leg (c5_streamed) and print its record (for traces of that path)")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection pass: one plain elementwise copy of 1 GiB (the calibration kernel "
                          "of known size), then one step of the workload; prints nothing else")
@@ -458,6 +472,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.streamed_only:
+        print(json.dumps({"streamed": time_streamed(wl.CONFIGS["c5_streamed"])}), flush=True)
+        return
     cfg = wl.CONFIGS[args.workload]
     if args.queries:
         cfg = cfg.with_(n_queries=args.queries, name=f"{cfg.name}_q{args.queries}")

@@ -47,7 +47,6 @@ constexpr int D = 128;
 constexpr int kTile = 32;       // keys per iteration
 constexpr int kRow = D + 8;     // bf16 per staged K row (16-byte pad: 16-byte reads of 16 rows hit 64 banks)
 constexpr int kVRow = D + 16;   // bf16 per staged V row (32-byte pad: 8-byte transposing reads of 8 rows hit 64 banks)
-constexpr int kRT = 2;          // 16-row tiles per wave (32 rows)
 constexpr int kNS = D / 32;     // 32-feature steps of S = K Q^T
 constexpr int kNXT = D / 16;    // 16-feature tiles of O^T
 constexpr float kGrowLog2 = 8.f;  // rescale threshold (log2 units)
@@ -65,8 +64,8 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
         (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
 }
 
-template <int NW>
-__global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams p, int row_groups) {
+template <int NW, int kRT>
+__global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_kernel(ChunkParams p, int row_groups) {
     constexpr int T = 64 * NW;
     constexpr int kPieces = kTile * (D / 8);   // 16-byte pieces per K (or V) tile
     constexpr int kPer = kPieces / T;          // pieces of K and of V per thread
@@ -98,7 +97,8 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     const int64_t st = p.stride_t;
     const int sti = (int)st;
 
-    const int row0 = rg * 32 * NW + 32 * w;  // first row of this wave
+    constexpr int kWaveRows = 16 * kRT;
+    const int row0 = rg * kWaveRows * NW + kWaveRows * w;  // first row of this wave
     const bool active = row0 < p.rows;
 
     bf16x8 qf[kRT][kNS];
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     // features 8*(u % 16) .. +7). Keys past the range are clamped to its last
     // key (finite values; their scores are masked).
     u32x4 pa[2][kPer], pb[2][kPer];
-    auto fetch = [&](int64_t tk, u32x4(&pre)[2][kPer]) {
+    auto fetch = [&](int64_t tk, u32x4(&pre)[2][kPer]) __attribute__((always_inline)) {
         const int last = (int)min((int64_t)kTile, t1 - tk) - 1;
         const uint16_t* kb = kp + tk * st;
         const uint16_t* vb = vp + tk * st;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
             pre[1][j] = *reinterpret_cast<const u32x4*>(vb + off);
         }
     };
-    auto stage = [&](int buf, const u32x4(&pre)[2][kPer]) {
+    auto stage = [&](int buf, const u32x4(&pre)[2][kPer]) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int u = tid + j * T;
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     };
 
     // S^T = K Q^T (raw dot products) of the tile in LDS buffer buf.
-    auto qk = [&](const int buf, const int /*t*/, floatx4(&sc)[2][kRT]) {
+    auto qk = [&](const int buf, const int /*t*/, floatx4(&sc)[2][kRT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     };
     // Row maxima of a tile, in c-scaled log2 units (c > 0, so the max of raw
     // scores picks the max of scaled ones).
-    auto row_max = [&](const floatx4(&sc)[2][kRT], float(&mc)[kRT]) {
+    auto row_max = [&](const floatx4(&sc)[2][kRT], float(&mc)[kRT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
             float mx = fmaxf(fmaxf(fmaxf(sc[0][rt][0], sc[0][rt][1]), fmaxf(sc[0][rt][2], sc[0][rt][3])),
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     };
     // Moves the reference maximum when some row's tile maximum exceeds it by
     // more than 2^8, rescaling the accumulated state (Eq. 8).
-    auto rescale = [&](const float(&mc)[kRT]) {
+    auto rescale = [&](const float(&mc)[kRT]) __attribute__((always_inline)) {
         bool grow = false;
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) grow |= mc[rt] > m_run[rt] + kGrowLog2;
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     // at features 16*xt + 4*(l16 % 4) .. +3 of key 4*q4 + l16 / 4 (and of
     // key 16 + ...); it receives feature 16*xt + l16 of keys 4*q4 .. +3 (and
     // 16 + 4*q4 .. +3): the keys of the P slots it holds.
-    auto softmax_pv = [&](const int buf, const floatx4(&sc)[2][kRT]) {
+    auto softmax_pv = [&](const int buf, const floatx4(&sc)[2][kRT]) __attribute__((always_inline)) {
         bf16x8 pf[kRT];
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     // Main loop: iterations t = 0 .. n_full - 2, unrolled by two (register
     // sets pa / pb, score sets sc_a / sc_b alternate roles).
     auto step = [&](auto compute, int t, int b_cur, floatx4(&sc_cur)[2][kRT], floatx4(&sc_next)[2][kRT],
-                    u32x4(&stage_set)[2][kPer], u32x4(&fetch_set)[2][kPer]) {
+                    u32x4(&stage_set)[2][kPer], u32x4(&fetch_set)[2][kPer]) __attribute__((always_inline)) {
         const int b1 = next_buf(b_cur), b2 = next_buf(b1);
         fetch(tile_start(t + 3), fetch_set);
         if constexpr (decltype(compute)::value) {
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
         if constexpr (decltype(compute)::value) rescale(mc);
         __syncthreads();
     };
-    auto main_loop = [&](auto compute) {
+    auto main_loop = [&](auto compute) __attribute__((always_inline)) {
         int bi = 0;
         for (int t = 0; t + 1 < n_full; t += 2) {
             step(compute, t, bi, sc_a, sc_b, pa, pb);
@@ -334,14 +334,14 @@ __global__ __launch_bounds__(64 * NW, 2) void chunk_mfma_wide_kernel(ChunkParams
     }
 }
 
-template <int NW>
+template <int NW, int kRT>
 hipError_t launch_wide_t(const ChunkParams& p, hipStream_t stream) {
-    const int row_groups = (p.rows + 32 * NW - 1) / (32 * NW);
+    const int row_groups = (p.rows + 16 * kRT * NW - 1) / (16 * kRT * NW);
     const int64_t units = (int64_t)p.n_items * p.n_kv_heads;
     const int64_t gx = (units + 7) / 8 * 8 * row_groups;
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     dim3 grid((unsigned)gx, 1, p.batch);
-    hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW>), grid, dim3(64 * NW), 0, stream, p, row_groups);
+    hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW, kRT>), grid, dim3(64 * NW), 0, stream, p, row_groups);
     return hipGetLastError();
 }
 
@@ -351,8 +351,8 @@ hipError_t launch_chunk_mfma_wide(const ChunkParams& p, int head_dim, hipStream_
     if (head_dim != D || p.rows <= 32) return hipErrorInvalidValue;
     // 32 rows per wave: up to 128 rows in one group of four waves, more rows
     // in groups of eight waves (two per SIMD).
-    if (p.rows <= 128) return launch_wide_t<4>(p, stream);
-    return launch_wide_t<8>(p, stream);
+    if (p.rows <= 128) return launch_wide_t<4, 2>(p, stream);
+    return launch_wide_t<8, 2>(p, stream);
 }
 
 }  // namespace ssv
