@@ -147,6 +147,24 @@ __host__ __device__ inline uint64_t chain_bits(int32_t i) {
     return i >= 63 ? ~(uint64_t)0 : (((uint64_t)1 << (i + 1)) - 1);
 }
 
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48), every lane receiving the result, with the gfx950 lane-swap
+// instructions (plain VALU work) instead of shuffles routed through the LDS
+// crossbar. The sums associate as (x0 + x16) + (x32 + x48) in every lane.
+__device__ __forceinline__ float group4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float group4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // ---------------------------------------------------------------------------
 // Kernel parameter blocks (passed by value).
 // ---------------------------------------------------------------------------

@@ -171,8 +171,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
             float lsum = bl[rt];
-            lsum += __shfl_xor(lsum, 16);
-            lsum += __shfl_xor(lsum, 32);
+            lsum = group4_sum(lsum);
             if (q4 == rt) {
                 mv = m_run[rt];
                 lv = lsum;
@@ -238,8 +237,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
                     sc[kt][rt][j] = v;
                     mx = fmaxf(mx, v);
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = group4_max(mx);
             const float m_new = fmaxf(m_run[rt], mx);
             alpha[rt] = (m_run[rt] == -INFINITY) ? 0.f : exp2_hw(m_run[rt] - m_new);
             grow |= m_new > m_run[rt];
@@ -372,8 +370,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
     // Full row sums: the 4 lane groups hold disjoint keys of the same rows.
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-        l_run[rt] += __shfl_xor(l_run[rt], 16);
-        l_run[rt] += __shfl_xor(l_run[rt], 32);
+        l_run[rt] = group4_sum(l_run[rt]);
     }
 
     // Merge the waves' states (Eq. 8) through LDS, the work split by feature

@@ -178,8 +178,7 @@ __global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_ker
         for (int rt = 0; rt < kRT; ++rt) {
             float mx = fmaxf(fmaxf(fmaxf(sc[0][rt][0], sc[0][rt][1]), fmaxf(sc[0][rt][2], sc[0][rt][3])),
                              fmaxf(fmaxf(sc[1][rt][0], sc[1][rt][1]), fmaxf(sc[1][rt][2], sc[1][rt][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            mx = group4_max(mx);
             mc[rt] = mx * c;
         }
     };
