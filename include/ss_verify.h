@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 8
+#define SS_ABI_VERSION 9
 
 /* status codes */
 #define SS_OK 0
@@ -334,11 +334,15 @@ SS_API int32_t ss_stream_timings(int32_t back, int32_t n_chunks, float* copy_beg
  * chunks_per_slot 1) the mass that row r puts on block j is
  * l_j(r) * exp(m_j(r) - lse(r)).
  *
- * ss_verify_chunk_gathered: as ss_verify_chunk with chunks_per_slot 1, but
- *   slot slot_begin + s of (request b, KV head g) holds chunk
- *   chunk_idx[(b * Hkv + g) * n_sel + s] of that request (device int32
- *   [B][Hkv][n_sel]; < 0 or past the request's end: an empty slot). The
- *   selection may differ per KV head.
+ * ss_verify_chunk_gathered: as ss_verify_chunk over listed chunks: the
+ *   list of (request b, KV head g) is chunk_idx[(b * Hkv + g) * n_sel + e],
+ *   e < n_sel (device int32 [B][Hkv][n_sel]; an entry < 0 or past the
+ *   request's end stands for no keys), and slot slot_begin + s holds entries
+ *   [s * chunks_per_slot, (s + 1) * chunks_per_slot) merged, so
+ *   ceil(n_sel / chunks_per_slot) slots are written. The selection may differ
+ *   per KV head. chunks_per_slot > 1 needs the narrow MFMA engine and at
+ *   most 64 chunks per slot (SS_ERR_UNSUPPORTED otherwise), and chunk_len a
+ *   multiple of 32.
  * ss_block_importance: importance[b][g][j] = max over the rows r of KV head
  *   g of l_j(r) * exp(m_j(r) - lse(r)), block j's state in slot
  *   slot_begin + j of `states`, lse [B][q][Hq] the round's final lse
@@ -352,7 +356,8 @@ SS_API int32_t ss_stream_timings(int32_t back, int32_t n_chunks, float* copy_beg
  */
 SS_API int32_t ss_verify_chunk_gathered(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
                                         int32_t chunk_len, const int32_t* chunk_idx, int32_t n_sel,
-                                        const ss_state_t* out, int32_t slot_begin, ss_stream_t stream);
+                                        int32_t chunks_per_slot, const ss_state_t* out, int32_t slot_begin,
+                                        ss_stream_t stream);
 SS_API int32_t ss_block_importance(const ss_problem_t* problem, const ss_state_t* states, int32_t slot_begin,
                                    int32_t n_blocks, const float* lse, float* importance, ss_stream_t stream);
 /* Bytes of a block-statistics buffer for n_blocks blocks, or a negative status. */

@@ -565,12 +565,20 @@ extern "C" SS_API int32_t ss_stream_timings(int32_t back, int32_t n_chunks, floa
 
 extern "C" SS_API int32_t ss_verify_chunk_gathered(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
                                                    int32_t chunk_len, const int32_t* chunk_idx, int32_t n_sel,
-                                                   const ss_state_t* out, int32_t slot_begin, ss_stream_t stream) {
-    int32_t rc = validate_chunk(problem, q, hist, chunk_len, 0, n_sel, 1, out, slot_begin);
+                                                   int32_t chunks_per_slot, const ss_state_t* out, int32_t slot_begin,
+                                                   ss_stream_t stream) {
+    int32_t rc = validate_chunk(problem, q, hist, chunk_len, 0, n_sel, chunks_per_slot, out, slot_begin);
     if (rc) return rc;
     if (!chunk_idx) return fail(SS_ERR_INVALID_ARG, "chunk_idx is NULL");
+    if (chunks_per_slot > 1) {
+        if (chunk_engine(problem) != ChunkEngine::kMfma)
+            return fail(SS_ERR_UNSUPPORTED, "several gathered chunks per slot need the narrow MFMA engine");
+        if (chunk_len % 32) return fail(SS_ERR_INVALID_ARG, "several gathered chunks per slot need chunk_len %% 32 == 0");
+        if (chunks_per_slot > kMaxGatherPerSlot)
+            return fail(SS_ERR_UNSUPPORTED, "at most %d gathered chunks per slot", kMaxGatherPerSlot);
+    }
     if (n_sel == 0) return ok();
-    ChunkParams c = make_chunk_params(problem, q, hist, chunk_len, 0, n_sel, 1, out, slot_begin);
+    ChunkParams c = make_chunk_params(problem, q, hist, chunk_len, 0, n_sel, chunks_per_slot, out, slot_begin);
     c.chunk_idx = chunk_idx;
     c.n_sel = n_sel;
     hipError_t e = enqueue_chunk(problem, c, static_cast<hipStream_t>(stream));

@@ -293,6 +293,8 @@ constexpr int kStatsQuarters = 4;
 
 // Blocks the selection kernel holds in LDS.
 constexpr int kMaxSelectBlocks = 8192;
+// Listed chunks merged into one slot of a gathered call (narrow MFMA kernel).
+constexpr int kMaxGatherPerSlot = 64;
 
 // Rows per work-group in the VALU kernels.
 constexpr int kValuRows = 32;

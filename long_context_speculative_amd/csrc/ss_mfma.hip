@@ -25,6 +25,8 @@
 // The 4 waves' states are merged with Eq. (8) through LDS at the end and
 // written as the slot's state (m in natural-log units).
 
+#include <type_traits>
+
 #include "ss_common.h"
 
 namespace ssv {
@@ -48,6 +50,7 @@ struct MfmaSmem {
     // final merge (wave w owns the 16-feature tiles xt with xt % kWaves == w).
     static constexpr int kOwnRegs = (D / 16 / kWaves) * NRT * 4;
     uint64_t cbits[32];  // candidate visibility bits (at most 32 candidates here)
+    int32_t gidx[kMaxGatherPerSlot];  // a gathered slot's chunk list
     union {
         uint16_t vt[kWaves][D][kVtRow];
         struct {
@@ -69,15 +72,44 @@ __device__ __forceinline__ void wave_sync() {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// State of tokens [t0, t1) of stream (at.b(), at.g()) for every row of the
+// Key tiles of a piece. ContigTiles: tokens [t0, t1) in tiles of kTile.
+// GatherTiles: the listed chunks of a gathered slot one after the other,
+// chunk_len / kTile tiles each (chunk_len a multiple of kTile); a tile of an
+// entry < 0 or past the request's end has no keys and is skipped.
+struct ContigTiles {
+    int64_t t0, t1;
+    __device__ int n_tiles() const { return (int)((t1 - t0 + kTile - 1) / kTile); }
+    __device__ int64_t tk(int tau) const { return t0 + (int64_t)kTile * tau; }
+    __device__ int valid(int tau) const { return (int)min((int64_t)kTile, t1 - tk(tau)); }
+};
+
+struct GatherTiles {
+    const int32_t* idx;  // the slot's entries, staged in LDS by the kernel
+    int32_t n_entries, chunk_len, len;
+    __device__ int per_chunk() const { return chunk_len / kTile; }
+    __device__ int n_tiles() const { return n_entries * per_chunk(); }
+    // First token of tile tau and its keys (0: an entry < 0 or past the end).
+    __device__ void tile(int tau, int64_t* tk, int* valid) const {
+        const int j = tau / per_chunk();
+        const int32_t c = __builtin_amdgcn_readfirstlane(idx[j]);
+        const int64_t t = (int64_t)c * chunk_len + (int64_t)kTile * (tau - j * per_chunk());
+        const int64_t left = (int64_t)len - t;
+        *valid = c < 0 ? 0 : (int)(left < 0 ? 0 : (left > kTile ? kTile : left));
+        *tk = *valid > 0 ? t : 0;
+    }
+};
+
+// State of the key tiles `tl` of stream (at.b(), at.g()) for every row of the
 // KV head, and with `cand` also of the request's candidate rows under their
 // mask, written to slot at.slot(). `at` is asked again at each use, so
 // that a caller can keep these indices out of registers during the key loop.
 // Uses the work-group's LDS; callers that run several pieces in a row
 // separate them with a barrier.
-template <int D, int NRT, bool STATS, class At>
-__device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT>& sm, const At& at, int64_t t0,
-                                           int64_t t1, bool cand) {
+template <int D, int NRT, bool STATS, class At, class Tiles>
+__device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT>& sm, const At& at, const Tiles& tl,
+                                           bool cand) {
+    constexpr bool kGather = std::is_same<Tiles, GatherTiles>::value;
+    static_assert(!(kGather && STATS), "block statistics cover contiguous pieces only");
     constexpr int NS = D / 32;   // feature steps of 32 for S = K Q^T
     constexpr int NXT = D / 16;  // 16-feature output tiles for O^T = V^T P^T
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -119,8 +151,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
     }
     const float c = p.scale * kLog2e;
 
-    const int64_t n_keys = t1 - t0;
-    const int n_tiles = (int)((n_keys + kTile - 1) / kTile);
+    const int n_tiles = tl.n_tiles();
     uint16_t(*vt)[kVtRow] = sm.u.vt[w];
 
     // Loads address a tile as a uniform base (scalar registers) plus a 32-bit
@@ -149,12 +180,9 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
             }
     };
     const int sti = (int)st;
-    auto load_k = [&](int64_t tk, u32x4(&dst)[2][NS]) {
-        load_k_at(kp + tk * st, sti, (int)min((int64_t)kTile, t1 - tk) - 1, dst);
-    };
-    auto load_v = [&](int64_t tk, u32x4(&dst)[2][4]) {
-        load_v_at(vp + tk * st, sti, (int)min((int64_t)kTile, t1 - tk) - 1, dst);
-    };
+    // Tile tau's loads (tk: its first token, valid > 0: its keys).
+    auto load_k = [&](int64_t tk, int valid, u32x4(&dst)[2][NS]) { load_k_at(kp + tk * st, sti, valid - 1, dst); };
+    auto load_v = [&](int64_t tk, int valid, u32x4(&dst)[2][4]) { load_v_at(vp + tk * st, sti, valid - 1, dst); };
 
     // Block statistics: the running state of the keys of the current block
     // (stats_block tokens) that this wave attends, written out when the
@@ -301,42 +329,70 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
     const uint32_t no_vis[NRT] = {};
     u32x4 kf[2][NS], vr[2][4];
     int tau = w;
-    if (tau < n_tiles) {
-        load_k(t0 + (int64_t)kTile * tau, kf);
-        load_v(t0 + (int64_t)kTile * tau, vr);
-    }
-    for (; tau < n_tiles; tau += kWaves) {
-        const int64_t tk = t0 + (int64_t)kTile * tau;
-        // Prefetch the wave's next tile into the registers just consumed:
-        // V right away (staged), K once the S^T products have read it.
-        const bool more = tau + kWaves < n_tiles;
-        // Block statistics: a wave steps kTile * kWaves tokens, so at most
-        // one block ends per step; the finished one is written out once V is
-        // staged (bl and m_run still hold it), before the V prefetch.
-        int64_t done_blk = -1;
-        if constexpr (STATS) {
-            if (tk >= blk_end) {
-                if (blk_cur >= 0) {
-                    done_blk = blk_cur;
-                    ++blk_cur;
-                } else {
-                    blk_cur = tk / p.stats_block;
-                }
-                blk_end = (blk_cur + 1) * p.stats_block;
-            }
+    if constexpr (!kGather) {
+        const int64_t t0 = tl.t0;
+        if (tau < n_tiles) {
+            load_k(tl.tk(tau), tl.valid(tau), kf);
+            load_v(tl.tk(tau), tl.valid(tau), vr);
         }
-        consume(kf, vr, (int)min((int64_t)kTile, t1 - tk), false, no_vis,
-                [&] {
-                    if constexpr (STATS) {
-                        if (done_blk >= 0) {
-                            flush_block(done_blk);
-#pragma unroll
-                            for (int rt = 0; rt < NRT; ++rt) bl[rt] = 0.f;
-                        }
+        for (; tau < n_tiles; tau += kWaves) {
+            const int64_t tk = t0 + (int64_t)kTile * tau;
+            // Prefetch the wave's next tile into the registers just consumed:
+            // V right away (staged), K once the S^T products have read it.
+            const int nxt = tau + kWaves;
+            const bool more = nxt < n_tiles;
+            // Block statistics: a wave steps kTile * kWaves tokens, so at most
+            // one block ends per step; the finished one is written out once V
+            // is staged (bl and m_run still hold it), before the V prefetch.
+            int64_t done_blk = -1;
+            if constexpr (STATS) {
+                if (tk >= blk_end) {
+                    if (blk_cur >= 0) {
+                        done_blk = blk_cur;
+                        ++blk_cur;
+                    } else {
+                        blk_cur = tk / p.stats_block;
                     }
-                    if (more) load_v(tk + kTile * kWaves, vr);
-                },
-                [&] { if (more) load_k(tk + kTile * kWaves, kf); });
+                    blk_end = (blk_cur + 1) * p.stats_block;
+                }
+            }
+            consume(kf, vr, tl.valid(tau), false, no_vis,
+                    [&] {
+                        if constexpr (STATS) {
+                            if (done_blk >= 0) {
+                                flush_block(done_blk);
+#pragma unroll
+                                for (int rt = 0; rt < NRT; ++rt) bl[rt] = 0.f;
+                            }
+                        }
+                        if (more) load_v(tl.tk(nxt), tl.valid(nxt), vr);
+                    },
+                    [&] { if (more) load_k(tl.tk(nxt), tl.valid(nxt), kf); });
+        }
+    } else {
+        // Gathered chunks: tiles without keys are neither loaded nor
+        // attended (nothing is read outside the listed chunks).
+        int v_cur = 0;
+        int64_t tk_cur = 0;
+        if (tau < n_tiles) tl.tile(tau, &tk_cur, &v_cur);
+        if (v_cur > 0) {
+            load_k(tk_cur, v_cur, kf);
+            load_v(tk_cur, v_cur, vr);
+        }
+        for (; tau < n_tiles; tau += kWaves) {
+            const int nxt = tau + kWaves;
+            int v_nxt = 0;
+            int64_t tk_nxt = 0;
+            if (nxt < n_tiles) tl.tile(nxt, &tk_nxt, &v_nxt);
+            if (v_cur > 0) {
+                consume(kf, vr, v_cur, false, no_vis, [&] { if (v_nxt > 0) load_v(tk_nxt, v_nxt, vr); },
+                        [&] { if (v_nxt > 0) load_k(tk_nxt, v_nxt, kf); });
+            } else if (v_nxt > 0) {
+                load_v(tk_nxt, v_nxt, vr);
+                load_k(tk_nxt, v_nxt, kf);
+            }
+            v_cur = v_nxt;
+        }
     }
 
     if constexpr (STATS) {
@@ -466,16 +522,28 @@ struct LdsAt {
     __device__ int slot() const { return p.slot_begin + max(__builtin_amdgcn_readfirstlane(pc->k), 0); }
 };
 
-template <int D, int NRT, bool STATS>
+template <int D, int NRT, bool STATS, bool GATHER>
 __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) {
     __shared__ MfmaSmem<D, NRT> sm;
     const int s = blockIdx.x / p.n_kv_heads;
     const int g = blockIdx.x % p.n_kv_heads;
     const int b = blockIdx.z;
     const int32_t len = chunk_view_len(p, b);
-    int64_t t0, t1;
-    piece_tokens(p, len, b, g, s, &t0, &t1);
-    mfma_piece<D, NRT, STATS>(p, sm, GridAt{p}, t0, t1, p.with_cand && s == 0);
+    if constexpr (GATHER) {
+        // slot s: entries [s * cps, s * cps + cps) of (b, g)'s list, staged in
+        // LDS (cps <= kMaxGatherPerSlot) so that reading them never waits on
+        // the key loop's outstanding loads
+        const int e0 = s * p.cps;
+        const int ne = min(p.cps, p.n_sel - e0);
+        if ((int)threadIdx.x < ne) sm.gidx[threadIdx.x] = p.chunk_idx[((int64_t)b * p.n_kv_heads + g) * p.n_sel + e0 + threadIdx.x];
+        __syncthreads();
+        const GatherTiles tl{sm.gidx, ne, p.chunk_len, len};
+        mfma_piece<D, NRT, STATS>(p, sm, GridAt{p}, tl, p.with_cand && s == 0);
+    } else {
+        int64_t t0, t1;
+        piece_tokens(p, len, b, g, s, &t0, &t1);
+        mfma_piece<D, NRT, STATS>(p, sm, GridAt{p}, ContigTiles{t0, t1}, p.with_cand && s == 0);
+    }
 }
 
 __device__ __forceinline__ int64_t uniform64(int64_t x) {
@@ -586,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
         // launch (a separate fill: stores here, behind the key loop's reads,
         // cost several times their bytes).
         if (k >= 0 || cand)
-            mfma_piece<D, NRT, STATS>(pa, sm, LdsAt{pa, pc}, uniform64(pc->t0), uniform64(pc->t1), cand);
+            mfma_piece<D, NRT, STATS>(pa, sm, LdsAt{pa, pc}, ContigTiles{uniform64(pc->t0), uniform64(pc->t1)}, cand);
     }
 }
 
@@ -596,9 +664,11 @@ hipError_t launch_t(const ChunkParams& p, hipStream_t stream) {
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     dim3 grid((unsigned)gx, 1, p.batch);
     if (p.stats)
-        hipLaunchKernelGGL((chunk_mfma_kernel<D, NRT, true>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((chunk_mfma_kernel<D, NRT, true, false>), grid, dim3(kThreads), 0, stream, p);
+    else if (p.chunk_idx && p.cps > 1)
+        hipLaunchKernelGGL((chunk_mfma_kernel<D, NRT, false, true>), grid, dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((chunk_mfma_kernel<D, NRT, false>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((chunk_mfma_kernel<D, NRT, false, false>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

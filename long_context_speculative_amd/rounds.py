@@ -478,10 +478,15 @@ class SparseRound:
                 ss_block_importance_stats from the statistics) and the k most
                 important blocks (ss_select_blocks);
       sparse()  verification of the selected blocks only
-                (ss_verify_chunk_gathered) with the candidate region, merge.
+                (ss_verify_chunk_gathered, gather_per_slot selected blocks
+                merged per slot) with the candidate region, merge.
+
+    gather_per_slot: an integer, or "auto": on the narrow MFMA kernel as
+    many as give about one work-group per compute unit, else 1.
     """
 
-    def __init__(self, inp: VerifyInputs, block_len: int, k: int, device="cuda", engine="auto", stats=False):
+    def __init__(self, inp: VerifyInputs, block_len: int, k: int, device="cuda", engine="auto", stats=False,
+                 gather_per_slot="auto"):
         cfg = inp.cfg
         self.use_stats = bool(stats)
         if self.use_stats:
@@ -499,7 +504,14 @@ class SparseRound:
         self.importance = torch.zeros((b_, hkv, max(self.n_blocks, 1)), dtype=torch.float32, device=device)
         self.selected = torch.full((b_, hkv, k), -1, dtype=torch.int32, device=device)
         self.len_dev = fr.hist_len if cfg.ragged else None
-        self.state = ss.StateBuffers(self.problem, k + 1, device)
+        if gather_per_slot == "auto":
+            gather_per_slot = 1
+            if narrow_mfma(cfg, engine) and block_len % 32 == 0:
+                units = k * b_ * hkv
+                gather_per_slot = max(1, min(k, 64, -(-units // (wgs_per_cu(cfg, engine) * device_cus(device)))))
+        self.gather_per_slot = int(gather_per_slot)
+        self.n_sparse_slots = -(-k // self.gather_per_slot)
+        self.state = ss.StateBuffers(self.problem, self.n_sparse_slots + 1, device)
         self.o = torch.empty_like(fr.o)
         self.lse = torch.empty_like(fr.lse)
 
@@ -521,6 +533,6 @@ class SparseRound:
     def sparse(self, stream=None):
         fr = self.full_round
         ss.ss_verify_chunk_gathered(self.problem, fr.q, fr.hist_view, self.block_len, self.selected, self.state, 1,
-                                    stream)
+                                    stream, chunks_per_slot=self.gather_per_slot)
         ss.ss_verify_candidates(self.problem, fr.q, fr.cand_view, fr.parents, None, self.state, 0, stream)
         ss.ss_merge_states(self.problem, self.state, None, self.o, self.lse, stream)

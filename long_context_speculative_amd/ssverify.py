@@ -108,7 +108,7 @@ def lib() -> ctypes.CDLL:
         L.ss_kv_copy_rows.restype = I32
         L.ss_kv_copy_rows.argtypes = [P(Problem), P(KVView), VP, P(KVView), VP, VP, VP]
         L.ss_verify_chunk_gathered.restype = I32
-        L.ss_verify_chunk_gathered.argtypes = [P(Problem), VP, P(KVView), I32, VP, I32, P(State), I32, VP]
+        L.ss_verify_chunk_gathered.argtypes = [P(Problem), VP, P(KVView), I32, VP, I32, I32, P(State), I32, VP]
         L.ss_block_importance.restype = I32
         L.ss_block_importance.argtypes = [P(Problem), P(State), I32, I32, VP, VP, VP]
         L.ss_block_stats_bytes.restype = I64
@@ -305,11 +305,12 @@ def ss_kv_copy_rows(problem: Problem, src: KVView, src_row, dst: KVView, dst_row
 
 
 def ss_verify_chunk_gathered(problem: Problem, q: torch.Tensor, hist: KVView, chunk_len: int, chunk_idx: torch.Tensor,
-                             out: StateBuffers, slot_begin: int, stream=None) -> None:
-    """chunk_idx: device int32 [B][Hkv][n_sel]."""
+                             out: StateBuffers, slot_begin: int, stream=None, chunks_per_slot: int = 1) -> None:
+    """chunk_idx: device int32 [B][Hkv][n_sel]; slot slot_begin + s merges
+    entries [s * chunks_per_slot, (s + 1) * chunks_per_slot)."""
     _check(lib().ss_verify_chunk_gathered(ctypes.byref(problem), q.data_ptr(), ctypes.byref(hist), chunk_len,
-                                          chunk_idx.data_ptr(), chunk_idx.shape[-1], ctypes.byref(out.struct),
-                                          slot_begin, _stream(stream)))
+                                          chunk_idx.data_ptr(), chunk_idx.shape[-1], chunks_per_slot,
+                                          ctypes.byref(out.struct), slot_begin, _stream(stream)))
 
 
 def ss_block_importance(problem: Problem, states: StateBuffers, slot_begin: int, n_blocks: int, lse: torch.Tensor,

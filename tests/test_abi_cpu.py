@@ -303,6 +303,21 @@ def test_verify_history_rejects():
     assert call(p, 4096, 2, 4, 0, stats=ss.BlockStats(None, 256, 8)) == ss.SS_ERR_INVALID_ARG
 
 
+def test_gathered_chunks_per_slot_rejects():
+    L = ss.lib()
+    view = _view(max_len=1000)
+    def call(problem, chunk_len, n_sel, cps, n_state):
+        return L.ss_verify_chunk_gathered(ctypes.byref(problem), 4096, ctypes.byref(view), chunk_len, 4096, n_sel,
+                                          cps, ctypes.byref(_state(n_state).struct), 0, None)
+    assert call(_problem(), 128, 8, 0, 8) == ss.SS_ERR_INVALID_ARG          # chunks_per_slot < 1
+    assert call(_problem(), 128, 8, 4, 1) == ss.SS_ERR_INVALID_ARG          # 2 slots needed
+    assert call(_problem(), 100, 8, 4, 2) == ss.SS_ERR_INVALID_ARG          # chunk_len % 32
+    assert call(_problem(engine=ss.SS_ENGINE_VALU), 128, 8, 4, 2) == ss.SS_ERR_UNSUPPORTED
+    assert call(_problem(), 128, 130, 65, 2) == ss.SS_ERR_UNSUPPORTED      # more than 64 per slot
+    assert L.ss_verify_chunk_gathered(ctypes.byref(_problem()), 4096, ctypes.byref(view), 128, None, 8, 4,
+                                      ctypes.byref(_state(2).struct), 0, None) == ss.SS_ERR_INVALID_ARG
+
+
 def test_block_stats_bytes_and_rejects():
     p = _problem()
     # four wave quarters x rows x blocks x (m, l) floats

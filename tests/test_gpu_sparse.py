@@ -183,3 +183,48 @@ def test_block_statistics_fewer_blocks_than_history():
         imps.append(imp.cpu())
     assert torch.equal(imps[1], imps[0][..., :5])
     assert (imps[0] >= 0).all() and (imps[0][..., :5] > 0).any()
+
+
+GATHER_CASES = {
+    # name: (config, block_len, k, chunks per slot)
+    "c2_like_4": (C["c2_qwen3_8b"].with_(batch=2, hist_len=3000), 256, 6, 4),
+    "ragged_3": (C["c3_internlm25_7b_ragged"].with_(batch=4, hist_len=2500, ragged_lo=300), 128, 7, 3),
+    "tree_g8_all": (C["c4_tree_72b"].with_(batch=2, n_queries=4, hist_len=1100), 128, 5, 5),
+}
+
+
+@pytest.mark.parametrize("name", list(GATHER_CASES))
+def test_gathered_chunks_merged_per_slot(name):
+    """Several selected blocks merged into one slot (one work-group runs
+    them one after the other): against the oracle's attention over the
+    selected blocks, and against one block per slot."""
+    cfg, block_len, k, per = GATHER_CASES[name]
+    log(f"[gather] {name}: rows={cfg.rows}, block {block_len}, k {k}, {per} per slot")
+    inp = wl.make_inputs(cfg)
+    many = rounds.SparseRound(inp, block_len, k, gather_per_slot=per)
+    one = rounds.SparseRound(inp, block_len, k, gather_per_slot=1)
+    for sr in (many, one):
+        sr.full()
+        sr.select()
+    # plant entries without keys: -1 and past the request's end
+    sel = many.selected.clone()
+    sel[:, :, 1] = -1
+    sel[0, 0, 2] = 10_000
+    for sr in (many, one):
+        sr.selected.copy_(sel)
+        for t in (sr.state.acc, sr.state.m, sr.state.l):
+            t.fill_(float("nan"))
+        sr.sparse()
+    torch.cuda.synchronize()
+    assert many.n_sparse_slots == -(-k // per)
+    q = inp.q.float().numpy()
+    kh, vh = inp.hist_per_request("k"), inp.hist_per_request("v")
+    kc, vc = inp.k_cand.float().numpy(), inp.v_cand.float().numpy()
+    o_ref, lse_ref = sparse.gathered_attention(q, kh, vh, inp.hist_len, block_len, sel.cpu().numpy(), kc, vc,
+                                               cand_vis(inp), cfg.scale)
+    eo = np.abs(many.o.cpu().numpy() - o_ref).max()
+    el = np.abs(many.lse.cpu().numpy() - lse_ref).max()
+    log(f"  merged slots: max|dO| {eo:.2e}, max|dlse| {el:.2e}")
+    assert eo <= TOL[cfg.dtype] and el <= TOL[cfg.dtype]
+    assert (many.o - one.o).abs().max().item() <= TOL[cfg.dtype]
+    assert not torch.isnan(many.state.m).any() and not torch.isnan(many.state.acc).any()
