@@ -311,7 +311,7 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
     if (narrow && !hist->req_len) {
         int wgs = 0;
         hipError_t e = mfma_wave_work_groups(problem->n_queries * (problem->n_q_heads / problem->n_kv_heads), &wgs);
-        if (e != hipSuccess) return fail(SS_ERR_HIP, "occupancy query failed: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return fail(SS_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
         pieces = wgs / streams;
         if (pieces < 1) pieces = 1;
         if (pieces > hist_slots) pieces = hist_slots;

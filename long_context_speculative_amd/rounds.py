@@ -37,8 +37,7 @@ def wgs_per_cu(cfg, engine="auto") -> int:
 def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int, engine="auto") -> int:
     """Chunks merged per state slot for a resident round. Wide row groups
     (compute-bound) take 4. Otherwise the slot count is chosen so that the
-    chunk kernel launches about one full wave of work-groups (wgs_per_cu
-    per compute unit): fewer launches leave units idle, more leave partly
+    chunk kernel launches about wgs_per_cu work-groups per compute unit: fewer launches leave units idle, more leave partly
     filled rounds and cost a state slot each."""
     if cfg.rows > 32:
         return 4
@@ -49,7 +48,7 @@ def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int, engine="auto") -> i
 def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
     """Slots per stream for ss_verify_history. Ragged lengths: enough that
     the longest stream does not force ranges longer than an even share of
-    one wave of work-groups, plus one for the range boundaries. Uniform
+    wgs_per_cu work-groups per compute unit, plus one for the range boundaries. Uniform
     lengths: one chunk per work-group of that wave. Wide row groups use the
     fixed cut of 4 chunks per slot."""
     pads = [-(-int(n) // 128) * 128 for n in hist_len]
