@@ -37,8 +37,9 @@ def wgs_per_cu(cfg, engine="auto") -> int:
 def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int, engine="auto") -> int:
     """Chunks merged per state slot for a resident round. Wide row groups
     (compute-bound) take 4. Otherwise the slot count is chosen so that the
-    chunk kernel launches about wgs_per_cu work-groups per compute unit: fewer launches leave units idle, more leave partly
-    filled rounds and cost a state slot each."""
+    chunk kernel launches about wgs_per_cu work-groups per compute unit:
+    fewer leave units idle, more leave partly filled rounds and cost a state
+    slot each."""
     if cfg.rows > 32:
         return 4
     units = sum(-(-int(n) // chunk_len) for n in hist_len) * cfg.n_kv_heads
@@ -47,10 +48,10 @@ def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int, engine="auto") -> i
 
 def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
     """Slots per stream for ss_verify_history. Ragged lengths: enough that
-    the longest stream does not force ranges longer than an even share of
-    wgs_per_cu work-groups per compute unit, plus one for the range boundaries. Uniform
-    lengths: one chunk per work-group of that wave. Wide row groups use the
-    fixed cut of 4 chunks per slot."""
+    the longest stream does not force ranges longer than an even share over
+    the launch (wgs_per_cu work-groups per compute unit), plus one for the
+    range boundaries. Uniform lengths: one chunk per work-group of that
+    launch. Wide row groups use the fixed cut of 4 chunks per slot."""
     pads = [-(-int(n) // 128) * 128 for n in hist_len]
     pad_max = max(pads, default=0)
     if cfg.rows > 32:
