@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 9
+#define SS_ABI_VERSION 10
 
 /* status codes */
 #define SS_OK 0
@@ -129,7 +129,8 @@ typedef struct ss_state {
  * online-softmax state (m, l) of the block's keys (in parts whose Eq. 8 fold
  * is the block's state). buf holds ss_block_stats_bytes(problem, n_blocks)
  * bytes (caller-owned, device; layout internal, read by
- * ss_block_importance_stats); blocks past n_blocks are not recorded.
+ * ss_block_importance_stats; needs no initialisation); blocks past n_blocks
+ * are not recorded, nor blocks past a request's end.
  */
 typedef struct ss_block_stats {
     void* buf;
@@ -218,9 +219,10 @@ SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const
  * no extra slot); other engines run ss_verify_candidates into slot_begin
  * and cut the history into the remaining n_slots - 1 slots.
  * stats: NULL, or record block statistics (narrow MFMA kernel only,
- *   SS_ERR_UNSUPPORTED otherwise): the buffer is first filled with empty
- *   states, then the cut is aligned to block_len (no block is split between
- *   two pieces), and every piece records the (m, l) of its blocks.
+ *   SS_ERR_UNSUPPORTED otherwise): the cut is aligned to block_len (no block
+ *   is split between two pieces) and every piece records the (m, l) of its
+ *   blocks; which entries exist follows from the lengths alone, so
+ *   ss_block_importance_stats takes the same lengths.
  * Errors: as ss_verify_chunk and ss_verify_candidates.
  */
 SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
@@ -363,9 +365,12 @@ SS_API int32_t ss_block_importance(const ss_problem_t* problem, const ss_state_t
 /* Bytes of a block-statistics buffer for n_blocks blocks, or a negative status. */
 SS_API int64_t ss_block_stats_bytes(const ss_problem_t* problem, int32_t n_blocks);
 /* As ss_block_importance, from block statistics recorded by ss_verify_history
- * (importance [B][Hkv][stats->n_blocks]). */
+ * (importance [B][Hkv][stats->n_blocks]); req_len (device int32 [B], or NULL:
+ * every request max_len long) and max_len as in that call's history view.
+ * Blocks past a request's end get importance 0. */
 SS_API int32_t ss_block_importance_stats(const ss_problem_t* problem, const ss_block_stats_t* stats,
-                                         const float* lse, float* importance, ss_stream_t stream);
+                                         const int32_t* req_len, int32_t max_len, const float* lse,
+                                         float* importance, ss_stream_t stream);
 SS_API int32_t ss_select_blocks(const ss_problem_t* problem, const float* importance, int32_t n_blocks,
                                 const int32_t* req_len, int32_t max_len, int32_t block_len, int32_t k, int32_t* out,
                                 ss_stream_t stream);

@@ -329,10 +329,6 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
         c.stats = static_cast<float*>(stats->buf);
         c.stats_block = stats->block_len;
         c.stats_blocks = stats->n_blocks;
-        const int64_t pairs = (int64_t)kStatsQuarters * problem->batch * problem->n_queries * problem->n_q_heads *
-                              stats->n_blocks;
-        e = launch_stats_fill(c.stats, pairs, s);
-        if (e != hipSuccess) return fail(SS_ERR_HIP, "statistics fill failed: %s", hipGetErrorString(e));
     }
     if (cand && narrow) {
         c.with_cand = 1;
@@ -622,11 +618,14 @@ extern "C" SS_API int64_t ss_block_stats_bytes(const ss_problem_t* problem, int3
 }
 
 extern "C" SS_API int32_t ss_block_importance_stats(const ss_problem_t* problem, const ss_block_stats_t* stats,
-                                                    const float* lse, float* importance, ss_stream_t stream) {
+                                                    const int32_t* req_len, int32_t max_len, const float* lse,
+                                                    float* importance, ss_stream_t stream) {
     int32_t rc = check_problem(problem);
     if (rc) return rc;
     if (!stats || !stats->buf || stats->n_blocks <= 0 || !lse || !importance)
         return fail(SS_ERR_INVALID_ARG, "statistics, lse or importance missing");
+    if (stats->block_len <= 0 || stats->block_len % kPlanAlign || max_len < 0)
+        return fail(SS_ERR_INVALID_ARG, "block_len must be a positive multiple of %d, max_len >= 0", kPlanAlign);
     StatsImportanceParams p{};
     p.ml = static_cast<const float2*>(stats->buf);
     p.batch = problem->batch;
@@ -634,6 +633,9 @@ extern "C" SS_API int32_t ss_block_importance_stats(const ss_problem_t* problem,
     p.n_kv_heads = problem->n_kv_heads;
     p.n_queries = problem->n_queries;
     p.n_blocks = stats->n_blocks;
+    p.block_len = stats->block_len;
+    p.req_len = req_len;
+    p.max_len = max_len;
     p.lse = lse;
     p.importance = importance;
     hipError_t e = launch_importance_stats(p, static_cast<hipStream_t>(stream));

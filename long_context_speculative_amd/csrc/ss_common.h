@@ -283,7 +283,9 @@ struct SelectParams {
 
 struct StatsImportanceParams {
     const float2* ml;   // block statistics, four wave quarters (ChunkParams::stats layout)
-    int32_t batch, n_q_heads, n_kv_heads, n_queries, n_blocks;
+    int32_t batch, n_q_heads, n_kv_heads, n_queries, n_blocks, block_len;
+    const int32_t* req_len;  // [B] or NULL: every request max_len long
+    int32_t max_len;
     const float* lse;   // [B][q][Hq]
     float* importance;  // [B][Hkv][n_blocks]
 };
@@ -317,7 +319,6 @@ hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_importance(const ImportanceParams& p, hipStream_t stream);
 hipError_t launch_read_probe(const void* src, int64_t bytes, int32_t n_wg, uint32_t* sink, hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
-hipError_t launch_stats_fill(float* ml, int64_t n_pairs, hipStream_t stream);
 // Empty states (m = -inf, l = 0, acc = 0) in rows [row_begin, row_begin +
 // n_rows) of a state buffer (a row: head_dim accumulators, one m, one l).
 hipError_t launch_state_fill(float* acc, float* m, float* l, int64_t row_begin, int64_t n_rows, int head_dim,

@@ -83,12 +83,6 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p) {
     for (int s = kept + threadIdx.x; s < p.k; s += kThreads) p.out[((int64_t)b * p.n_kv_heads + g) * p.k + s] = -1;
 }
 
-// Empty states (m = -inf, l = 0) in every entry of a block-statistics buffer.
-__global__ __launch_bounds__(kThreads) void stats_fill_kernel(float2* __restrict__ ml, int64_t n) {
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
-        ml[i] = make_float2(-INFINITY, 0.f);
-}
-
 // Importance from block statistics: the four wave quarters of a block fold
 // into its mass l * exp(m - lse) per row, maximised over the KV head's rows.
 // One wave per (request, KV head, block): lane r + 32 * half takes row r
@@ -105,13 +99,20 @@ __global__ __launch_bounds__(kThreads) void importance_stats_kernel(StatsImporta
     const int rows = p.n_queries * group;
     const int half = lane / 32;
     const int64_t quarter = total * rows;
+    // The entries that exist: the pieces are block-aligned and a wave takes
+    // every fourth tile of a piece, so wave w attended block j iff the block
+    // holds more than w tiles of the request's keys.
+    const int32_t len = clamp_len(p.req_len ? p.req_len[b] : p.max_len, p.max_len);
+    const int j = (int)(unit % p.n_blocks);
+    const int64_t keys = (int64_t)len - (int64_t)j * p.block_len;
+    const int tiles = keys <= 0 ? 0 : (int)min((int64_t)kStatsQuarters, (min(keys, (int64_t)p.block_len) + 31) / 32);
     float best = 0.f;
     for (int r = lane % 32; r < rows; r += 32) {  // same trip count in both halves
         const int i = r / group, h = g * group + r % group;
         const float lse = p.lse[((int64_t)b * p.n_queries + i) * p.n_q_heads + h];
         float mass = 0.f;
         if (lse > -INFINITY) {
-            for (int w = half; w < kStatsQuarters; w += 2) {
+            for (int w = half; w < tiles; w += 2) {
                 const float2 ml = p.ml[w * quarter + unit * rows + r];
                 if (ml.y > 0.f) mass += ml.y * __builtin_amdgcn_exp2f((ml.x - lse) * kLog2e);
             }
@@ -124,15 +125,6 @@ __global__ __launch_bounds__(kThreads) void importance_stats_kernel(StatsImporta
 }
 
 }  // namespace
-
-hipError_t launch_stats_fill(float* ml, int64_t n_pairs, hipStream_t stream) {
-    if (n_pairs <= 0) return hipSuccess;
-    int64_t blocks = (n_pairs + kThreads - 1) / kThreads;
-    if (blocks > 4096) blocks = 4096;
-    hipLaunchKernelGGL(stats_fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       reinterpret_cast<float2*>(ml), n_pairs);
-    return hipGetLastError();
-}
 
 hipError_t launch_importance_stats(const StatsImportanceParams& p, hipStream_t stream) {
     const int64_t units = (int64_t)p.batch * p.n_kv_heads * p.n_blocks;

@@ -524,7 +524,8 @@ class SparseRound:
             self.selected.fill_(-1)
             return
         if self.use_stats:
-            ss.ss_block_importance_stats(self.problem, fr.stats, fr.lse, self.importance, stream)
+            ss.ss_block_importance_stats(self.problem, fr.stats, self.len_dev, fr.max_len, fr.lse, self.importance,
+                                         stream)
         else:
             ss.ss_block_importance(self.problem, fr.state, 1, self.n_blocks, fr.lse, self.importance, stream)
         ss.ss_select_blocks(self.problem, self.importance, self.len_dev, fr.max_len, self.block_len, self.k,

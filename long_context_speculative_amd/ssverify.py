@@ -114,7 +114,7 @@ def lib() -> ctypes.CDLL:
         L.ss_block_stats_bytes.restype = I64
         L.ss_block_stats_bytes.argtypes = [P(Problem), I32]
         L.ss_block_importance_stats.restype = I32
-        L.ss_block_importance_stats.argtypes = [P(Problem), P(BlockStats), VP, VP, VP]
+        L.ss_block_importance_stats.argtypes = [P(Problem), P(BlockStats), VP, I32, VP, VP, VP]
         L.ss_select_blocks.restype = I32
         L.ss_select_blocks.argtypes = [P(Problem), VP, I32, VP, I32, I32, I32, VP, VP]
         L.ss_read_probe.restype = I32
@@ -335,10 +335,12 @@ class BlockStatsBuffer:
         self.block_len, self.n_blocks = block_len, n_blocks
 
 
-def ss_block_importance_stats(problem: Problem, stats: BlockStatsBuffer, lse: torch.Tensor, importance: torch.Tensor,
-                              stream=None) -> None:
-    _check(lib().ss_block_importance_stats(ctypes.byref(problem), ctypes.byref(stats.struct), lse.data_ptr(),
-                                           importance.data_ptr(), _stream(stream)))
+def ss_block_importance_stats(problem: Problem, stats: BlockStatsBuffer, req_len: Optional[torch.Tensor], max_len: int,
+                              lse: torch.Tensor, importance: torch.Tensor, stream=None) -> None:
+    """req_len / max_len: the lengths of the history view the statistics were
+    recorded over (req_len device int32 [B], or None: all max_len)."""
+    _check(lib().ss_block_importance_stats(ctypes.byref(problem), ctypes.byref(stats.struct), _ptr(req_len), max_len,
+                                           lse.data_ptr(), importance.data_ptr(), _stream(stream)))
 
 
 def ss_select_blocks(problem: Problem, importance: torch.Tensor, req_len: Optional[torch.Tensor], max_len: int,

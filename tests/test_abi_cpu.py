@@ -327,10 +327,15 @@ def test_block_stats_bytes_and_rejects():
         ss.ss_block_stats_bytes(p, 0)
     L = ss.lib()
     st = ss.BlockStats(4096, 256, 8)
-    assert L.ss_block_importance_stats(ctypes.byref(p), None, 4096, 4096, None) == ss.SS_ERR_INVALID_ARG
-    assert L.ss_block_importance_stats(ctypes.byref(p), ctypes.byref(st), None, 4096, None) == ss.SS_ERR_INVALID_ARG
-    assert L.ss_block_importance_stats(ctypes.byref(p), ctypes.byref(ss.BlockStats(4096, 256, 0)), 4096, 4096,
-                                       None) == ss.SS_ERR_INVALID_ARG
+    def imp(stats, max_len=1000, lse=4096, out=4096):
+        return L.ss_block_importance_stats(ctypes.byref(p), None if stats is None else ctypes.byref(stats), None,
+                                           max_len, lse, out, None)
+    assert imp(None) == ss.SS_ERR_INVALID_ARG
+    assert imp(st, lse=None) == ss.SS_ERR_INVALID_ARG
+    assert imp(st, out=None) == ss.SS_ERR_INVALID_ARG
+    assert imp(ss.BlockStats(4096, 256, 0)) == ss.SS_ERR_INVALID_ARG
+    assert imp(ss.BlockStats(4096, 100, 8)) == ss.SS_ERR_INVALID_ARG       # block_len not a multiple of 128
+    assert imp(st, max_len=-1) == ss.SS_ERR_INVALID_ARG
 
 
 def test_tier_migration_end_matches_oracle():

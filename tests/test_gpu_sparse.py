@@ -168,21 +168,27 @@ def test_block_statistics_of_the_full_round(name):
 
 def test_block_statistics_fewer_blocks_than_history():
     """Blocks past the buffer's n_blocks are not recorded; the recorded ones
-    match those of a buffer that covers the whole history."""
+    match those of a buffer that covers the whole history. The buffer needs
+    no initialisation (it starts as NaN here): the importance reads only the
+    entries the lengths say exist, and blocks past a request's end get 0."""
     cfg = C["c3_internlm25_7b_ragged"].with_(batch=3, hist_len=4000, ragged_lo=1500)
     inp = wl.make_inputs(cfg)
     rr = rounds.ResidentRound(inp, **rounds.BENCH_RESIDENT)
-    full_blocks = -(-rr.max_len // 256)
+    full_blocks = -(-rr.max_len // 256) + 2
     imps = []
     for nb in (full_blocks, 5):
         rr.stats = ss.BlockStatsBuffer(rr.problem, 256, nb)
+        rr.stats.buf.fill_(float("nan"))
         rr.run()
         imp = torch.full((cfg.batch, cfg.n_kv_heads, nb), -1.0, device="cuda")
-        ss.ss_block_importance_stats(rr.problem, rr.stats, rr.lse, imp)
+        ss.ss_block_importance_stats(rr.problem, rr.stats, rr.hist_len, rr.max_len, rr.lse, imp)
         torch.cuda.synchronize()
         imps.append(imp.cpu())
     assert torch.equal(imps[1], imps[0][..., :5])
-    assert (imps[0] >= 0).all() and (imps[0][..., :5] > 0).any()
+    assert torch.isfinite(imps[0]).all() and (imps[0] >= 0).all() and (imps[0][..., :5] > 0).any()
+    for b, n in enumerate(inp.hist_len):
+        nb = -(-int(n) // 256)
+        assert (imps[0][b, :, :nb] > 0).all() and (imps[0][b, :, nb:] == 0).all()
 
 
 GATHER_CASES = {
