@@ -400,7 +400,19 @@ def cpu_baseline(cfg, budget_s=15.0):
     row = 2 * cfg.head_dim * cfg.elem_bytes
     kv = slices * (int(inp.hist_len.max()) + cfg.n_queries) * row
     cores = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+    # the whole tiny fp32 round (c1) on one thread
+    from threadpoolctl import threadpool_limits
+    c1 = wl.CONFIGS["c1_tiny_f32"]
+    inp1 = wl.make_inputs(c1)
+    vis1 = np.stack([oracle.chain_mask(c1.n_queries)] * c1.batch)
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        oracle.attention_reference(inp1.q.float().numpy(), inp1.hist_per_request("k"), inp1.hist_per_request("v"),
+                                   inp1.hist_len, inp1.k_cand.float().numpy(), inp1.v_cand.float().numpy(), vis1,
+                                   c1.scale)
+        c1_ms = (time.perf_counter() - t1) * 1e3
     return {"value": kv / done / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "c1_round_one_thread_ms": round(c1_ms, 3),
             "sample": f"{slices} (request, KV head) slices of {cfg.name}, fp64 NumPy, {done:.1f} s",
             "query_tokens_per_s": slices / (cfg.batch * cfg.n_kv_heads) * cfg.batch * cfg.n_queries / done,
             "cpu_model": cpu_model(), "logical_cpus": os.cpu_count()}
