@@ -11,10 +11,12 @@
 //     16-row MFMA tiles) with its Q^T fragments and O^T accumulator in
 //     registers, small enough for two waves per SIMD, so one wave's softmax
 //     overlaps the other's matrix work;
-//   - key tiles of 32 are copied once per work-group into LDS, K and V both
-//     in their natural [key][feature] layout (rows padded so the reads are
-//     free of bank conflicts), in a ring of three buffers, loads issued three
-//     tiles ahead;
+//   - key tiles of KT (32, or 64 for groups of eight waves) are copied once
+//     per work-group into LDS, K and V both in their natural [key][feature]
+//     layout (rows padded so the reads are free of bank conflicts), in a ring
+//     of three buffers, loads issued three tiles ahead; a 64-key tile halves
+//     the barriers and row-maximum reductions per key (about 5% on a 512-row
+//     group) at 105 KB of LDS, which one eight-wave group per CU affords;
 //   - the loop is software-pipelined: the S products of tile t+1 are issued
 //     next to the softmax and P V of tile t, so matrix and vector work of one
 //     wave overlap, on top of the two waves per SIMD;
@@ -44,16 +46,17 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
-constexpr int kTile = 32;       // keys per iteration
+constexpr int kTile = 32;       // keys per MFMA sub-tile (KT keys per iteration)
 constexpr int kRow = D + 8;     // bf16 per staged K row (16-byte pad: 16-byte reads of 16 rows hit 64 banks)
 constexpr int kVRow = D + 16;   // bf16 per staged V row (32-byte pad: 8-byte transposing reads of 8 rows hit 64 banks)
 constexpr int kNS = D / 32;     // 32-feature steps of S = K Q^T
 constexpr int kNXT = D / 16;    // 16-feature tiles of O^T
 constexpr float kGrowLog2 = 8.f;  // rescale threshold (log2 units)
 
+template <int KT>
 struct WideSmem {
-    uint16_t k[3][kTile][kRow];
-    uint16_t v[3][kTile][kVRow];
+    uint16_t k[3][KT][kRow];
+    uint16_t v[3][KT][kVRow];
 };
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -64,13 +67,16 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
         (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
 }
 
-template <int NW, int kRT>
-__global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_kernel(ChunkParams p, int row_groups) {
+template <int NW, int kRT, int KT>
+__global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk_mfma_wide_kernel(ChunkParams p, int row_groups) {
+    static_assert(KT % kTile == 0, "an iteration is whole sub-tiles");
+    constexpr int kSub = KT / kTile;           // 32-key sub-tiles per iteration
+    constexpr int kKB = 2 * kSub;              // 16-key blocks per iteration
     constexpr int T = 64 * NW;
-    constexpr int kPieces = kTile * (D / 8);   // 16-byte pieces per K (or V) tile
+    constexpr int kPieces = KT * (D / 8);      // 16-byte pieces per K (or V) tile
     constexpr int kPer = kPieces / T;          // pieces of K and of V per thread
     static_assert(kPieces % T == 0, "tile pieces must divide evenly");
-    __shared__ WideSmem sm;
+    __shared__ WideSmem<KT> sm;
 
     // Work-group -> (unit u = (slot, KV head), row group): eight consecutive
     // units go to the eight XCDs (dispatch is round-robin over them), and the
@@ -128,14 +134,14 @@ __global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_ker
     for (int rt = 0; rt < kRT; ++rt) m_run[rt] = -INFINITY;
     const float c = p.scale * kLog2e;
     const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-    const int n_tiles = (int)((t1 - t0 + kTile - 1) / kTile);
+    const int n_tiles = (int)((t1 - t0 + KT - 1) / KT);
 
     // Staging: thread tid copies K and V pieces u = tid + j*T (key u / 16,
     // features 8*(u % 16) .. +7). Keys past the range are clamped to its last
     // key (finite values; their scores are masked).
     u32x4 pa[2][kPer], pb[2][kPer];
     auto fetch = [&](int64_t tk, u32x4(&pre)[2][kPer]) __attribute__((always_inline)) {
-        const int last = (int)min((int64_t)kTile, t1 - tk) - 1;
+        const int last = (int)min((int64_t)KT, t1 - tk) - 1;
         const uint16_t* kb = kp + tk * st;
         const uint16_t* vb = vp + tk * st;
 #pragma unroll
@@ -156,15 +162,15 @@ __global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_ker
     };
 
     // S^T = K Q^T (raw dot products) of the tile in LDS buffer buf.
-    auto qk = [&](const int buf, const int /*t*/, floatx4(&sc)[2][kRT]) __attribute__((always_inline)) {
+    auto qk = [&](const int buf, const int /*t*/, floatx4(&sc)[kKB][kRT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int kt = 0; kt < kKB; ++kt)
 #pragma unroll
             for (int rt = 0; rt < kRT; ++rt) sc[kt][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < kNS; ++k)
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < kKB; ++kt) {
                 const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&sm.k[buf][16 * kt + l16][32 * k + 8 * q4]));
 #pragma unroll
                 for (int rt = 0; rt < kRT; ++rt)
@@ -173,11 +179,15 @@ __global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_ker
     };
     // Row maxima of a tile, in c-scaled log2 units (c > 0, so the max of raw
     // scores picks the max of scaled ones).
-    auto row_max = [&](const floatx4(&sc)[2][kRT], float(&mc)[kRT]) __attribute__((always_inline)) {
+    auto row_max = [&](const floatx4(&sc)[kKB][kRT], float(&mc)[kRT]) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < kRT; ++rt) {
-            float mx = fmaxf(fmaxf(fmaxf(sc[0][rt][0], sc[0][rt][1]), fmaxf(sc[0][rt][2], sc[0][rt][3])),
-                             fmaxf(fmaxf(sc[1][rt][0], sc[1][rt][1]), fmaxf(sc[1][rt][2], sc[1][rt][3])));
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < kKB; kt += 2)
+                mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[kt][rt][0], sc[kt][rt][1]), fmaxf(sc[kt][rt][2], sc[kt][rt][3])),
+                                     fmaxf(fmaxf(sc[kt + 1][rt][0], sc[kt + 1][rt][1]),
+                                           fmaxf(sc[kt + 1][rt][2], sc[kt + 1][rt][3]))));
             mx = group4_max(mx);
             mc[rt] = mx * c;
         }
@@ -200,38 +210,45 @@ __global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_ker
             }
         }
     };
-    // P = 2^(c*S - m) in bf16 (slot j of a lane = key 4*q4 + j, slot 4 + j =
-    // key 16 + 4*q4 + j), then O^T += V^T P^T and l += 1^T P^T from LDS
-    // buffer buf. For the transposing read, lane (group q4, index l16) points
-    // at features 16*xt + 4*(l16 % 4) .. +3 of key 4*q4 + l16 / 4 (and of
-    // key 16 + ...); it receives feature 16*xt + l16 of keys 4*q4 .. +3 (and
-    // 16 + 4*q4 .. +3): the keys of the P slots it holds.
-    auto softmax_pv = [&](const int buf, const floatx4(&sc)[2][kRT]) __attribute__((always_inline)) {
-        bf16x8 pf[kRT];
+    // Per 32-key sub-tile su: P = 2^(c*S - m) in bf16 (slot j of a lane =
+    // key 32*su + 4*q4 + j, slot 4 + j = key 32*su + 16 + 4*q4 + j), then
+    // O^T += V^T P^T and l += 1^T P^T from LDS buffer buf. For the
+    // transposing read, lane (group q4, index l16) points at features
+    // 16*xt + 4*(l16 % 4) .. +3 of key 32*su + 4*q4 + l16 / 4 (and of key
+    // 32*su + 16 + ...); it receives feature 16*xt + l16 of keys
+    // 32*su + 4*q4 .. +3 (and 32*su + 16 + 4*q4 .. +3): the keys of the P
+    // slots it holds.
+    auto softmax_pv = [&](const int buf, const floatx4(&sc)[kKB][kRT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) {
-            const float nm = -m_run[rt];
+        for (int su = 0; su < kSub; ++su) {  // 32-key sub-tiles
+            bf16x8 pf[kRT];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int rt = 0; rt < kRT; ++rt) {
+                const float nm = -m_run[rt];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) pf[rt][4 * kt + j] = (__bf16)exp2_hw(fmaf(sc[kt][rt][j], c, nm));
-        }
-        const uint16_t* vrow0 = &sm.v[buf][4 * q4 + (l16 >> 2)][4 * (l16 & 3)];
-        const uint16_t* vrow1 = vrow0 + 16 * kVRow;
+                for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int rt = 0; rt < kRT; ++rt) ol[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[rt], ol[rt], 0, 0, 0);
-#pragma unroll
-        for (int xt = 0; xt < kNXT; ++xt) {
-            const s16x4 lo = lds_read_tr(vrow0 + 16 * xt);
-            const s16x4 hi = lds_read_tr(vrow1 + 16 * xt);
-            const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    for (int j = 0; j < 4; ++j)
+                        pf[rt][4 * kt + j] = (__bf16)exp2_hw(fmaf(sc[2 * su + kt][rt][j], c, nm));
+            }
+            const uint16_t* vrow0 = &sm.v[buf][kTile * su + 4 * q4 + (l16 >> 2)][4 * (l16 & 3)];
+            const uint16_t* vrow1 = vrow0 + 16 * kVRow;
 #pragma unroll
             for (int rt = 0; rt < kRT; ++rt)
-                o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[xt][rt], 0, 0, 0);
+                ol[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[rt], ol[rt], 0, 0, 0);
+#pragma unroll
+            for (int xt = 0; xt < kNXT; ++xt) {
+                const s16x4 lo = lds_read_tr(vrow0 + 16 * xt);
+                const s16x4 hi = lds_read_tr(vrow1 + 16 * xt);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int rt = 0; rt < kRT; ++rt)
+                    o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[xt][rt], 0, 0, 0);
+            }
         }
     };
 
-    // Software pipeline over the key tiles. Tiles 0 .. n_full-1 hold 32 keys;
+    // Software pipeline over the key tiles. Tiles 0 .. n_full-1 hold KT keys;
     // a last partial tile (the tail) is handled after the loop, so the loop
     // body needs no masking and has no branch: the scheduler can interleave
     // the S(t+1) products with the softmax of tile t.
@@ -244,12 +261,12 @@ __global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_ker
     // part) moves the reference maximum for tile t+1. Tile indices past the
     // last tile are clamped to it: their loads and staging are harmless
     // (the buffer they land in is not read again).
-    const int n_full = (int)((t1 - t0) / kTile);
-    const bool has_tail = (t1 - t0) % kTile != 0;
-    auto tile_start = [&](int t) { return t0 + (int64_t)kTile * min(t, n_tiles - 1); };
+    const int n_full = (int)((t1 - t0) / KT);
+    const bool has_tail = (t1 - t0) % KT != 0;
+    auto tile_start = [&](int t) { return t0 + (int64_t)KT * min(t, n_tiles - 1); };
     auto next_buf = [](int bi) { return bi == 2 ? 0 : bi + 1; };
 
-    floatx4 sc_a[2][kRT], sc_b[2][kRT];
+    floatx4 sc_a[kKB][kRT], sc_b[kKB][kRT];
     float mc[kRT];
     if (n_tiles > 0) {
         fetch(tile_start(0), pa);
@@ -267,7 +284,7 @@ __global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_ker
 
     // Main loop: iterations t = 0 .. n_full - 2, unrolled by two (register
     // sets pa / pb, score sets sc_a / sc_b alternate roles).
-    auto step = [&](auto compute, int t, int b_cur, floatx4(&sc_cur)[2][kRT], floatx4(&sc_next)[2][kRT],
+    auto step = [&](auto compute, int t, int b_cur, floatx4(&sc_cur)[kKB][kRT], floatx4(&sc_next)[kKB][kRT],
                     u32x4(&stage_set)[2][kPer], u32x4(&fetch_set)[2][kPer]) __attribute__((always_inline)) {
         const int b1 = next_buf(b_cur), b2 = next_buf(b1);
         fetch(tile_start(t + 3), fetch_set);
@@ -302,9 +319,9 @@ __global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_ker
         if (has_tail) {
             const int bt = n_full % 3;
             qk(bt, n_full, sc_a);
-            const int valid = (int)(t1 - t0 - (int64_t)kTile * n_full);
+            const int valid = (int)(t1 - t0 - (int64_t)KT * n_full);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < kKB; ++kt)
 #pragma unroll
                 for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
@@ -333,14 +350,14 @@ __global__ __launch_bounds__(64 * NW, kRT == 2 ? 2 : 1) void chunk_mfma_wide_ker
     }
 }
 
-template <int NW, int kRT>
+template <int NW, int kRT, int KT>
 hipError_t launch_wide_t(const ChunkParams& p, hipStream_t stream) {
     const int row_groups = (p.rows + 16 * kRT * NW - 1) / (16 * kRT * NW);
     const int64_t units = (int64_t)p.n_items * p.n_kv_heads;
     const int64_t gx = (units + 7) / 8 * 8 * row_groups;
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     dim3 grid((unsigned)gx, 1, p.batch);
-    hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW, kRT>), grid, dim3(64 * NW), 0, stream, p, row_groups);
+    hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW, kRT, KT>), grid, dim3(64 * NW), 0, stream, p, row_groups);
     return hipGetLastError();
 }
 
@@ -348,10 +365,11 @@ hipError_t launch_wide_t(const ChunkParams& p, hipStream_t stream) {
 
 hipError_t launch_chunk_mfma_wide(const ChunkParams& p, int head_dim, hipStream_t stream) {
     if (head_dim != D || p.rows <= 32) return hipErrorInvalidValue;
-    // 32 rows per wave: up to 128 rows in one group of four waves, more rows
-    // in groups of eight waves (two per SIMD).
-    if (p.rows <= 128) return launch_wide_t<4, 2>(p, stream);
-    return launch_wide_t<8, 2>(p, stream);
+    // 32 rows per wave: up to 128 rows in one group of four waves (32-key
+    // tiles, two groups per CU), more rows in groups of eight waves (two per
+    // SIMD, 64-key tiles, one group per CU).
+    if (p.rows <= 128) return launch_wide_t<4, 2, 32>(p, stream);
+    return launch_wide_t<8, 2, 64>(p, stream);
 }
 
 }  // namespace ssv
