@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 10
+#define SS_ABI_VERSION 11
 
 /* status codes */
 #define SS_OK 0
@@ -196,7 +196,7 @@ SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const
  *               then the call's slots hold history and candidates together
  *   parents, mask_out  as ss_verify_candidates (used only with cand)
  *   n_slots     slots per (request, KV head) the call may use, >= 1 (>= 2
- *               with cand outside the narrow MFMA kernel); the call writes
+ *               with cand on the VALU engines); the call writes
  *               exactly slots [slot_begin, slot_begin + n_slots) of every
  *               row, the ones it does not need as empty states
  * With the narrow MFMA kernel (AUTO or MFMA engine, bf16, head_dim 128,
@@ -214,10 +214,11 @@ SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const
  * into n_slots chunks of ceil(max_len / n_slots) tokens. Chunks are rounded
  * up to a multiple of 128 tokens and run as ss_verify_chunk with
  * chunks_per_slot 1; chunks past a request's end are empty slots.
- * Candidates: the narrow MFMA kernel attends them as one more masked key
- * tile of the work-group that holds a stream's first piece (no extra launch,
- * no extra slot); other engines run ss_verify_candidates into slot_begin
- * and cut the history into the remaining n_slots - 1 slots.
+ * Candidates: the MFMA kernels (narrow and wide-row) attend them as masked
+ * key tiles after the history, in the work-groups that hold a stream's
+ * first piece (no extra launch, no extra slot); the VALU engines run
+ * ss_verify_candidates into slot_begin and cut the history into the
+ * remaining n_slots - 1 slots.
  * stats: NULL, or record block statistics (narrow MFMA kernel only,
  *   SS_ERR_UNSUPPORTED otherwise): the cut is aligned to block_len (no block
  *   is split between two pieces) and every piece records the (m, l) of its

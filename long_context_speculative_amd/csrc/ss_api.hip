@@ -291,8 +291,11 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
     int32_t rc = validate_chunk(problem, q, hist, kPlanAlign, 0, n_slots, 1, out, slot_begin);
     if (rc) return rc;
     if (cand && (rc = check_cand(problem, cand))) return rc;
-    const bool narrow = chunk_engine(problem) == ChunkEngine::kMfma;
-    if (cand && !narrow && n_slots < 2)
+    const ChunkEngine engine = chunk_engine(problem);
+    const bool narrow = engine == ChunkEngine::kMfma;
+    // the MFMA kernels attend the candidates inside the history launch
+    const bool fuse = cand && (narrow || engine == ChunkEngine::kMfmaWide);
+    if (cand && !fuse && n_slots < 2)
         return fail(SS_ERR_INVALID_ARG, "with candidates this engine needs n_slots >= 2");
     if (stats) {
         if (!narrow) return fail(SS_ERR_UNSUPPORTED, "block statistics need the narrow MFMA kernel");
@@ -300,10 +303,10 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
             return fail(SS_ERR_INVALID_ARG, "block statistics: buffer, a positive multiple of %d tokens, blocks",
                         kPlanAlign);
     }
-    // Slots of the history cut by fixed chunks (other engines with
-    // candidates give the first slot to the candidate region).
-    const int32_t hist_slots = (cand && !narrow) ? n_slots - 1 : n_slots;
-    const int32_t hist_begin = (cand && !narrow) ? slot_begin + 1 : slot_begin;
+    // Slots of the history (the VALU engines give the first slot to the
+    // candidate region).
+    const int32_t hist_slots = (cand && !fuse) ? n_slots - 1 : n_slots;
+    const int32_t hist_begin = (cand && !fuse) ? slot_begin + 1 : slot_begin;
     const int64_t streams = (int64_t)problem->batch * problem->n_kv_heads;
     // Pieces per stream of a cut by fixed chunks: hist_slots, or for uniform
     // lengths on the narrow kernel one work-group per CU.
@@ -330,7 +333,7 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
         c.stats_block = stats->block_len;
         c.stats_blocks = stats->n_blocks;
     }
-    if (cand && narrow) {
+    if (fuse) {
         c.with_cand = 1;
         c.ck = cand->k;
         c.cv = cand->v;

@@ -147,6 +147,32 @@ __host__ __device__ inline uint64_t chain_bits(int32_t i) {
     return i >= 63 ? ~(uint64_t)0 : (((uint64_t)1 << (i + 1)) - 1);
 }
 
+// The same tree bits for node `lane` of one wave (n <= 64 nodes, all lanes
+// active), by pointer jumping instead of a walk in node order: after round k
+// a lane holds its own bit and those of its ancestors less than 2^k links
+// up, and points at the ancestor 2^k links up (or at none), so six rounds
+// reach the root of any tree of 64 nodes. The parents are read with one
+// coalesced load; lanes >= n return bits of no meaning.
+__device__ inline uint64_t wave_tree_bits(const int32_t* parents, int32_t n, int32_t lane) {
+    int32_t up = -1;
+    if (lane < n) {
+        up = parents[lane];
+        if (up < 0 || up >= lane) up = -1;
+    }
+    uint64_t bits = (uint64_t)1 << lane;
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+        const int src = up < 0 ? lane : up;
+        const uint32_t lo = __shfl((uint32_t)bits, src), hi = __shfl((uint32_t)(bits >> 32), src);
+        const int32_t up2 = __shfl(up, src);
+        if (up >= 0) {
+            bits |= ((uint64_t)hi << 32) | lo;
+            up = up2;
+        }
+    }
+    return bits;
+}
+
 // Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
 // l^48), every lane receiving the result, with the gfx950 lane-swap
 // instructions (plain VALU work) instead of shuffles routed through the LDS

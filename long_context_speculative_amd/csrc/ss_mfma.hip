@@ -403,13 +403,10 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
     // query's mask) as one more masked tile of wave 0: n_queries <= 32 keys.
     if (cand && w == 0) {
         const int n = p.n_queries;
-        if (lane == 0) {
-            for (int i = 0; i < n; ++i)
-                sm.cbits[i] = p.parents ? tree_bits_step(sm.cbits, i, p.parents[(int64_t)at.b() * n + i])
-                                        : chain_bits(i);
-        }
+        const uint64_t bits = p.parents ? wave_tree_bits(p.parents + (int64_t)at.b() * n, n, lane) : chain_bits(lane);
+        if (lane < n) sm.cbits[lane] = bits;
         wave_sync();
-        if (p.mask_out && at.g() == 0 && lane < n) p.mask_out[(int64_t)at.b() * n + lane] = sm.cbits[lane];
+        if (p.mask_out && at.g() == 0 && lane < n) p.mask_out[(int64_t)at.b() * n + lane] = bits;
         uint32_t vis[NRT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {

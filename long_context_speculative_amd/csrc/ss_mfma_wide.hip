@@ -53,10 +53,14 @@ constexpr int kNS = D / 32;     // 32-feature steps of S = K Q^T
 constexpr int kNXT = D / 16;    // 16-feature tiles of O^T
 constexpr float kGrowLog2 = 8.f;  // rescale threshold (log2 units)
 
+// 16-byte aligned so that the 16-byte staging stores and K reads are single
+// ds_write_b128 / ds_read_b128 (with only the 8-byte alignment of the
+// member types the compiler splits them into pairs of 8-byte accesses).
 template <int KT>
-struct WideSmem {
+struct alignas(16) WideSmem {
     uint16_t k[3][KT][kRow];
     uint16_t v[3][KT][kVRow];
+    uint64_t cbits[64];  // candidate visibility bits (n_queries <= 64)
 };
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -330,6 +334,68 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
             row_max(sc_a, mc);
             rescale(mc);
             softmax_pv(bt, sc_a);
+        }
+    }
+
+    // The candidate region (section 4.2: the GPU-resident rows under each
+    // query's mask), attended after the history by the work-groups of each
+    // stream's first piece as masked key tiles (n_queries <= 64 keys). Every
+    // wave stages; the uniform condition keeps the barriers uniform.
+    if (p.with_cand && s == 0) {
+        const int n = p.n_queries;
+        if (w == 0) {
+            const uint64_t bits = p.parents ? wave_tree_bits(p.parents + (int64_t)b * n, n, lane) : chain_bits(lane);
+            if (lane < n) sm.cbits[lane] = bits;
+            if (p.mask_out && g == 0 && rg == 0 && lane < n) p.mask_out[(int64_t)b * n + lane] = bits;
+        }
+        __syncthreads();  // every wave is done with the ring buffers
+        const int64_t cbase =
+            (p.c_req_offset ? p.c_req_offset[b] : (int64_t)b * p.c_stride_b) + (int64_t)g * p.c_stride_h;
+        const uint16_t* ckp = static_cast<const uint16_t*>(p.ck) + cbase;
+        const uint16_t* cvp = static_cast<const uint16_t*>(p.cv) + cbase;
+        const int cst = (int)p.c_stride_t;
+        for (int c0 = 0; c0 < n; c0 += KT) {
+            const int last = min(KT, n - c0) - 1;  // rows past the region repeat its last one
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int u = tid + j * T;
+                const int off = (c0 + min(u >> 4, last)) * cst + 8 * (u & 15);
+                pa[0][j] = *reinterpret_cast<const u32x4*>(ckp + off);
+                pa[1][j] = *reinterpret_cast<const u32x4*>(cvp + off);
+            }
+            if (c0 > 0) __syncthreads();  // the previous candidate tile is consumed
+            stage(0, pa);
+            __syncthreads();  // the tile and the visibility bits are in LDS
+            if (active) {
+                qk(0, 0, sc_a);
+#pragma unroll
+                for (int rt = 0; rt < kRT; ++rt) {
+                    const int r = row0 + 16 * rt + l16;
+                    const uint64_t vis = r < p.rows ? sm.cbits[r / p.group] : ~(uint64_t)0;  // padded rows: discarded
+#pragma unroll
+                    for (int kt = 0; kt < kKB; ++kt)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int key = c0 + 16 * kt + 4 * q4 + j;
+                            if (key >= n || !((vis >> key) & 1)) sc_a[kt][rt][j] = -INFINITY;
+                        }
+                }
+                row_max(sc_a, mc);
+                rescale(mc);
+                // A row that has seen no key yet and sees none here keeps
+                // the empty state: its weights are 0 against any reference,
+                // so take 0 for this tile and restore -inf afterwards.
+                bool none[kRT];
+#pragma unroll
+                for (int rt = 0; rt < kRT; ++rt) {
+                    none[rt] = m_run[rt] == -INFINITY;
+                    if (none[rt]) m_run[rt] = 0.f;
+                }
+                softmax_pv(0, sc_a);
+#pragma unroll
+                for (int rt = 0; rt < kRT; ++rt)
+                    if (none[rt]) m_run[rt] = -INFINITY;
+            }
         }
     }
 

@@ -66,9 +66,15 @@ def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
 
 
 def narrow_mfma(cfg, engine="auto") -> bool:
-    """Whether the library runs this shape on its narrow MFMA kernels (the
-    ones that can fold the candidate region into the history launch)."""
+    """Whether the library runs this shape on its narrow MFMA kernels."""
     return engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim == 128 and cfg.rows <= 32
+
+
+def mfma_fuses_candidates(cfg, engine="auto") -> bool:
+    """Whether ss_verify_history folds the candidate region into the history
+    launch (the MFMA kernels, narrow and wide-row) instead of giving it a
+    slot of its own."""
+    return engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim == 128
 
 
 # Launch configuration of the resident round that the benchmark times.
@@ -90,8 +96,8 @@ class ResidentRound:
         chunks_per_slot at a time) or "balanced" (ss_verify_history with
         history_slots slots per stream).
         fuse_candidates (balanced split only): True, False or "auto" (when
-        the narrow MFMA kernel serves the shape): pass the candidate region
-        to ss_verify_history instead of a separate ss_verify_candidates.
+        an MFMA kernel serves the shape): pass the candidate region to
+        ss_verify_history instead of a separate ss_verify_candidates.
         chunks_per_slot: an integer, or "auto" (auto_chunks_per_slot).
         history_slots: an integer >= 1, or "auto" (auto_history_slots).
         engine: "auto", "valu" or "mfma" (ss_problem_t.engine)."""
@@ -128,7 +134,7 @@ class ResidentRound:
             self.parents = torch.as_tensor(inp.parents, dtype=torch.int32, device=device).contiguous()
         self.n_chunks = math.ceil(self.max_len / self.chunk_len)
         if fuse_candidates == "auto":
-            fuse_candidates = narrow_mfma(cfg, engine)
+            fuse_candidates = mfma_fuses_candidates(cfg, engine)
         self.fused = bool(fuse_candidates) and split == "balanced"
         if split == "balanced":
             if history_slots == "auto":
@@ -137,9 +143,9 @@ class ResidentRound:
         else:
             self.n_hist_slots = math.ceil(self.n_chunks / self.cps)
         if self.fused:
-            # one call writes every slot; outside the narrow kernel it gives
-            # the first to the candidate region
-            self.n_call_slots = self.n_hist_slots + (0 if narrow_mfma(cfg, engine) else 1)
+            # one call writes every slot; the VALU engines give the first to
+            # the candidate region
+            self.n_call_slots = self.n_hist_slots + (0 if mfma_fuses_candidates(cfg, engine) else 1)
             self.state = ss.StateBuffers(self.problem, self.n_call_slots, device)
         else:
             # slot 0: candidate region; slots 1 .. n_hist_slots: history

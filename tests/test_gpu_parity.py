@@ -404,10 +404,10 @@ def test_history_balanced(name):
 @pytest.mark.parametrize("name", list(BALANCED))
 def test_history_fused_candidates(name):
     """ss_verify_history with the candidate region: folded into each stream's
-    first piece on the narrow MFMA kernel, in a slot of its own elsewhere."""
+    first piece on the MFMA kernels, in a slot of its own on the VALU ones."""
     base, n_slots = BALANCED[name]
     cfg = SMALL[base]
-    if n_slots < 2 and not rounds.narrow_mfma(cfg):
+    if n_slots < 2 and not rounds.mfma_fuses_candidates(cfg):
         pytest.skip("candidates need a slot of their own outside the narrow kernel")
     log(f"[fused] {name}: rows={cfg.rows} slots={n_slots}")
     inp = wl.make_inputs(cfg)
@@ -420,6 +420,59 @@ def test_history_fused_candidates(name):
     assert not torch.isnan(rnd.state.m).any() and not torch.isnan(rnd.state.acc).any()
     o_ref, lse_ref = oracle_round(inp)
     compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
+
+
+@pytest.mark.parametrize("group", [2, 8])
+def test_wide_fused_candidates_forest(group):
+    """The wide-row kernel with the candidate region folded in: 64 candidates
+    forming two trees (node 32 is a second root and nodes 33.. hang below
+    it), requests without history. With 128 rows (32-key tiles) the rows of
+    the second tree see nothing in the first candidate tile and nothing
+    before it, so they stay empty through that tile; with 512 rows (64-key
+    tiles) the candidates are one tile.
+
+    Requests with history take the 2e-3 bar. A request without history
+    averages at most 64 candidate values with bf16 weights: rounding a
+    weight moves it by at most 2^-9 relative, and the denominator sums the
+    same rounded weights, so O moves by at most 2^-9 * max_t |V_t - O| per
+    feature (t over the row's visible candidates; O of order 1 here, so
+    this exceeds 2e-3), and lse by at most ln(1 + 2^-9) < 2e-3."""
+    cfg = C["c3_internlm25_7b_ragged"].with_(batch=4, n_q_heads=2 * group, n_kv_heads=2, n_queries=64,
+                                              hist_len=700, ragged_lo=1, chunk_len=256, mask="tree")
+    log(f"[wide fused forest] rows={cfg.rows}")
+    inp = wl.make_inputs(cfg)
+    inp.hist_len = inp.hist_len.copy()
+    inp.hist_len[[0, 2]] = 0
+    inp.parents = inp.parents.copy()
+    inp.parents[:, 32] = -1
+    inp.parents[:, 33:] = np.arange(32, 63)
+    rnd = rounds.ResidentRound(inp, split="balanced", history_slots=3, fuse_candidates=True)
+    for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
+        t.fill_(float("nan"))
+    rnd.mask_out.fill_(-1)
+    rnd.run()
+    torch.cuda.synchronize()
+    assert not torch.isnan(rnd.state.m).any() and not torch.isnan(rnd.state.acc).any()
+    o_ref, lse_ref = oracle_round(inp)
+    o, lse = rnd.o.cpu().numpy(), rnd.lse.cpu().numpy()
+    tol = TOL[cfg.dtype]
+    assert np.abs(lse - lse_ref).max() <= tol
+    with_hist = np.flatnonzero(inp.hist_len > 0)
+    eo = np.abs(o[with_hist] - o_ref[with_hist]).max()
+    log(f"  with history: max|dO| = {eo:.3e} (tol {tol})")
+    assert eo <= tol
+    vis = cand_visibility(inp)
+    v = inp.v_cand.double().numpy()  # [B][Hkv][n][d]
+    worst = 0.0
+    for b in np.flatnonzero(inp.hist_len == 0):
+        for i in range(cfg.n_queries):
+            for h in range(cfg.n_q_heads):
+                vt = v[b, h // cfg.group][vis[b, i]]  # the row's visible candidate values
+                bound = 2.0 ** -9 * np.abs(vt - o_ref[b, i, h]).max(axis=0) * 1.01 + 1e-5
+                worst = max(worst, (np.abs(o[b, i, h] - o_ref[b, i, h]) / bound).max())
+    log(f"  without history: max |dO| / bf16-weight bound = {worst:.3f}")
+    assert worst <= 1.0
     check_mask(rnd, inp)
 
 
