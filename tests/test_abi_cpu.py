@@ -32,6 +32,28 @@ def test_library_exports_every_declared_call():
     assert set(names) == set(ss.EXPORTED)
 
 
+def test_missing_library_fails_loudly():
+    """Without the built library every call raises; nothing falls back to
+    another implementation (checked in a fresh interpreter, whose binding has
+    not loaded the library yet)."""
+    import subprocess
+    import sys
+    code = (
+        "import sys\n"
+        "from long_context_speculative_amd import ssverify as ss\n"
+        "ss.LIB_PATH = '/nonexistent/libssverify.so'\n"
+        "for call in (ss.ss_abi_version, lambda: ss.ss_tier_migration_end(0, 0, 512, 128)):\n"
+        "    try:\n"
+        "        call()\n"
+        "    except RuntimeError as e:\n"
+        "        assert 'missing' in str(e), e\n"
+        "    else:\n"
+        "        sys.exit('a call returned without the library')\n"
+    )
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
 def test_abi_version_matches_header():
     m = re.search(r"#define\s+SS_ABI_VERSION\s+(\d+)", open(HEADER).read())
     assert ss.ss_abi_version() == int(m.group(1))
