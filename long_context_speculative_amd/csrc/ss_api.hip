@@ -152,6 +152,7 @@ ChunkParams make_chunk_params(const ss_problem_t* p, const void* q, const ss_kv_
     c.slot_begin = slot_begin;
     c.row_blocks = (c.rows + kValuRows - 1) / kValuRows;
     c.plan_align = kPlanAlign;
+    c.full_len = h->max_len;
     return c;
 }
 
@@ -510,6 +511,7 @@ extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const v
             view.v = buf + c * chunk_bytes + half * es;
             ChunkParams p = make_chunk_params(problem, q, &view, chunk_len, 0, 1, 1, out, slot_begin + (int32_t)j);
             if (req_len) p.len_offset = j * chunk_len;
+            p.full_len = (int64_t)n_chunks * chunk_len;
             SS_TRY(enqueue_chunk(problem, p, ks));
             if (timed) SS_TRY(hipEventRecord(ts->comp1[j], ks));
         }

@@ -238,6 +238,9 @@ struct ChunkParams {
     float* stats;
     int32_t stats_block, stats_blocks;
     int32_t plan_align;  // balanced cut: stream padding and piece alignment
+    // Tokens of every request's whole history when req_len is NULL (the view
+    // may show only a part of it, as a staging chunk does).
+    int64_t full_len;
 };
 
 struct CandParams {
@@ -272,6 +275,22 @@ struct MergeParams {
 __host__ __device__ inline int32_t chunk_view_len(const ChunkParams& p, int32_t b) {
     const int64_t n = (p.req_len ? (int64_t)p.req_len[b] : (int64_t)p.max_len) - p.len_offset;
     return (int32_t)(n < 0 ? 0 : (n > p.max_len ? p.max_len : n));
+}
+
+// Softmax weights enter the P V products as bf16. Rounding a weight moves it
+// by up to 2^-8 relative, so a row that a few keys dominate moves by up to
+// that fraction of the spread of their values; over many keys the rounding
+// errors average out (N(0,1) data, 128 features: largest error about 4e-3 at
+// 2-8 keys, 1.3e-3 at 128, 3.3e-4 at 2048). Kernels whose matrix work is
+// the bound carry each weight's rounding remainder as a second bf16 operand
+// only for requests with fewer history keys than this.
+constexpr int64_t kSplitBelow = 2048;
+
+// History keys a row of request b meets over the whole call: the request's
+// length, or for a gathered call the most keys its list can name.
+__host__ __device__ inline int64_t row_history_keys(const ChunkParams& p, int32_t b) {
+    if (p.chunk_idx) return (int64_t)p.n_sel * p.chunk_len;
+    return p.req_len ? (int64_t)p.req_len[b] : p.full_len;
 }
 
 // Token range of slot s of (request b, KV head g) in a chunk call: the

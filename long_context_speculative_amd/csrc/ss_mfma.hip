@@ -19,8 +19,10 @@
 //                                    accumulator is rescaled only when some
 //                                    row's maximum grows
 //   O^T[x][row] += V^T P^T           B = P in registers straight from the S^T
-//                                    output (bf16), A = V^T read from a
-//                                    per-wave LDS tile that holds V transposed
+//                                    output, as two bf16 operands (the
+//                                    rounded weight and its rounding
+//                                    remainder), A = V^T read from a per-wave
+//                                    LDS tile that holds V transposed
 //                                    (key-contiguous rows)
 // The 4 waves' states are merged with Eq. (8) through LDS at the end and
 // written as the slot's state (m in natural-log units).
@@ -281,11 +283,12 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
             }
         }
 
-        // P = 2^(S - m) in bf16 (B operand of the PV product); l sums the
-        // rounded weights so numerator and denominator use the same values.
-        // The masked (candidate) tile also carries the rounding remainder as
-        // a second bf16 operand: a row that sees only a few candidates would
-        // otherwise feel the 2^-9 weight rounding at full strength.
+        // P = 2^(S - m) as two bf16 operands of the P V product, the rounded
+        // weight and its rounding remainder: with the weight alone a row that
+        // a few keys dominate (a short history, the candidate tile) would
+        // feel the 2^-8 rounding at full strength. The matrix cores are
+        // mostly idle in this HBM-bound kernel, so the second product costs
+        // no time. l sums the same two parts.
         bf16x8 pf[NRT], pr[NRT];
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt) {
@@ -296,14 +299,10 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
                 for (int j = 0; j < 4; ++j) {
                     const float pv = exp2_hw(sc[kt][rt][j] - m_run[rt]);
                     const __bf16 pb = (__bf16)pv;
+                    const __bf16 rb = (__bf16)(pv - (float)pb);
                     pf[rt][4 * kt + j] = pb;
-                    if (masked) {
-                        const __bf16 rb = (__bf16)(pv - (float)pb);
-                        pr[rt][4 * kt + j] = rb;
-                        ls += (float)pb + (float)rb;
-                    } else {
-                        ls += (float)pb;
-                    }
+                    pr[rt][4 * kt + j] = rb;
+                    ls += (float)pb + (float)rb;
                 }
             l_run[rt] += ls;
             if constexpr (STATS) bl[rt] += masked ? 0.f : ls;
@@ -320,7 +319,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
                 o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[xt][rt], 0, 0, 0);
-                if (masked) o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pr[rt], o[xt][rt], 0, 0, 0);
+                o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pr[rt], o[xt][rt], 0, 0, 0);
             }
         }
         wave_sync();

@@ -24,7 +24,10 @@
 //     reads V^T fragments with the transposing LDS read ds_read_b64_tr_b16;
 //   - l (the softmax denominator) comes out of the same MFMA as O^T through
 //     an all-ones A operand, so it sums exactly the bf16 weights that enter
-//     the numerator;
+//     the numerator; for a request with a short history, and for the
+//     candidate tiles, a second pass adds each weight's bf16 rounding
+//     remainder to both, so rows that a few keys dominate stay exact to
+//     about 2^-16;
 //   - the score scale is folded into the exponent (one FMA per score), and the
 //     running maximum is moved only when a row's maximum grows by more than
 //     2^8 over it (weights then stay <= 256; the rescale is rare);
@@ -222,7 +225,11 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
     // 32*su + 16 + ...); it receives feature 16*xt + l16 of keys
     // 32*su + 4*q4 .. +3 (and 32*su + 16 + 4*q4 .. +3): the keys of the P
     // slots it holds.
-    auto softmax_pv = [&](const int buf, const floatx4(&sc)[kKB][kRT]) __attribute__((always_inline)) {
+    // kLo: the same products with each weight's bf16 rounding remainder
+    // (the weights are recomputed, so the split path needs no more registers
+    // than the plain one).
+    auto pv_pass = [&](auto lo, const int buf, const floatx4(&sc)[kKB][kRT]) __attribute__((always_inline)) {
+        constexpr bool kLo = decltype(lo)::value;
 #pragma unroll
         for (int su = 0; su < kSub; ++su) {  // 32-key sub-tiles
             bf16x8 pf[kRT];
@@ -232,8 +239,17 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        pf[rt][4 * kt + j] = (__bf16)exp2_hw(fmaf(sc[2 * su + kt][rt][j], c, nm));
+                    for (int j = 0; j < 4; ++j) {
+                        float x = sc[2 * su + kt][rt][j];
+                        // the second pass recomputes its weights instead of
+                        // keeping the first pass's alive across its products
+                        if constexpr (kLo) asm volatile("" : "+v"(x));
+                        const float pv = exp2_hw(fmaf(x, c, nm));
+                        if constexpr (kLo)
+                            pf[rt][4 * kt + j] = (__bf16)(pv - (float)(__bf16)pv);
+                        else
+                            pf[rt][4 * kt + j] = (__bf16)pv;
+                    }
             }
             const uint16_t* vrow0 = &sm.v[buf][kTile * su + 4 * q4 + (l16 >> 2)][4 * (l16 & 3)];
             const uint16_t* vrow1 = vrow0 + 16 * kVRow;
@@ -250,6 +266,10 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
                     o[xt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[rt], o[xt][rt], 0, 0, 0);
             }
         }
+    };
+    auto softmax_pv = [&](auto split, const int buf, const floatx4(&sc)[kKB][kRT]) __attribute__((always_inline)) {
+        pv_pass(std::false_type{}, buf, sc);
+        if constexpr (decltype(split)::value) pv_pass(std::true_type{}, buf, sc);
     };
 
     // Software pipeline over the key tiles. Tiles 0 .. n_full-1 hold KT keys;
@@ -272,68 +292,93 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
 
     floatx4 sc_a[kKB][kRT], sc_b[kKB][kRT];
     float mc[kRT];
-    if (n_tiles > 0) {
-        fetch(tile_start(0), pa);
-        stage(0, pa);
-        fetch(tile_start(1), pb);
-        stage(1, pb);
-        fetch(tile_start(2), pa);
-    }
-    __syncthreads();
-    if (active && n_full > 0) {
-        qk(0, 0, sc_a);
-        row_max(sc_a, mc);
-        rescale(mc);
-    }
+    // Masks the keys at or past `valid` of a tile's scores.
+    auto mask_tail = [&](floatx4(&sc)[kKB][kRT], int valid) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kt = 0; kt < kKB; ++kt)
+#pragma unroll
+            for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (16 * kt + 4 * q4 + j >= valid) sc[kt][rt][j] = -INFINITY;
+    };
 
-    // Main loop: iterations t = 0 .. n_full - 2, unrolled by two (register
-    // sets pa / pb, score sets sc_a / sc_b alternate roles).
-    auto step = [&](auto compute, int t, int b_cur, floatx4(&sc_cur)[kKB][kRT], floatx4(&sc_next)[kKB][kRT],
-                    u32x4(&stage_set)[2][kPer], u32x4(&fetch_set)[2][kPer]) __attribute__((always_inline)) {
-        const int b1 = next_buf(b_cur), b2 = next_buf(b1);
-        fetch(tile_start(t + 3), fetch_set);
-        if constexpr (decltype(compute)::value) {
-            qk(b1, t + 1, sc_next);
-            softmax_pv(b_cur, sc_cur);
-            row_max(sc_next, mc);
+    // A request with a short history (row_history_keys below kSplitBelow)
+    // carries each weight's bf16 rounding remainder as a second operand (a
+    // second P V pass), tile by tile without the pipeline (a second
+    // pipelined loop would not fit the registers). The candidate tiles
+    // always do.
+    if (row_history_keys(p, b) < kSplitBelow) {
+        for (int t = 0; t < n_tiles; ++t) {
+            fetch(t0 + (int64_t)KT * t, pa);
+            if (t > 0) __syncthreads();  // the previous tile is consumed
+            stage(0, pa);
+            __syncthreads();
+            if (active) {
+                qk(0, t, sc_a);
+                mask_tail(sc_a, (int)min((int64_t)KT, t1 - t0 - (int64_t)KT * t));
+                row_max(sc_a, mc);
+                rescale(mc);
+                softmax_pv(std::true_type{}, 0, sc_a);
+            }
         }
-        stage(b2, stage_set);
-        if constexpr (decltype(compute)::value) rescale(mc);
+    } else {
+        if (n_tiles > 0) {
+            fetch(tile_start(0), pa);
+            stage(0, pa);
+            fetch(tile_start(1), pb);
+            stage(1, pb);
+            fetch(tile_start(2), pa);
+        }
         __syncthreads();
-    };
-    auto main_loop = [&](auto compute) __attribute__((always_inline)) {
-        int bi = 0;
-        for (int t = 0; t + 1 < n_full; t += 2) {
-            step(compute, t, bi, sc_a, sc_b, pa, pb);
-            bi = next_buf(bi);
-            if (t + 2 >= n_full) break;
-            step(compute, t + 1, bi, sc_b, sc_a, pb, pa);
-            bi = next_buf(bi);
-        }
-    };
-    if (active)
-        main_loop(std::integral_constant<bool, true>{});
-    else
-        main_loop(std::integral_constant<bool, false>{});
-
-    if (active) {
-        // Last full tile: S is in sc_a if n_full is odd, else in sc_b.
-        if (n_full > 0) softmax_pv((n_full - 1) % 3, (n_full & 1) ? sc_a : sc_b);
-        // The tail tile (staged by the loop or the prologue), with masking.
-        if (has_tail) {
-            const int bt = n_full % 3;
-            qk(bt, n_full, sc_a);
-            const int valid = (int)(t1 - t0 - (int64_t)KT * n_full);
-#pragma unroll
-            for (int kt = 0; kt < kKB; ++kt)
-#pragma unroll
-                for (int rt = 0; rt < kRT; ++rt)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (16 * kt + 4 * q4 + j >= valid) sc_a[kt][rt][j] = -INFINITY;
+        if (active && n_full > 0) {
+            qk(0, 0, sc_a);
             row_max(sc_a, mc);
             rescale(mc);
-            softmax_pv(bt, sc_a);
+        }
+
+        // Main loop: iterations t = 0 .. n_full - 2, unrolled by two (register
+        // sets pa / pb, score sets sc_a / sc_b alternate roles).
+        auto step = [&](auto compute, int t, int b_cur, floatx4(&sc_cur)[kKB][kRT], floatx4(&sc_next)[kKB][kRT],
+                        u32x4(&stage_set)[2][kPer], u32x4(&fetch_set)[2][kPer]) __attribute__((always_inline)) {
+            const int b1 = next_buf(b_cur), b2 = next_buf(b1);
+            fetch(tile_start(t + 3), fetch_set);
+            if constexpr (decltype(compute)::value) {
+                qk(b1, t + 1, sc_next);
+                softmax_pv(std::false_type{}, b_cur, sc_cur);
+                row_max(sc_next, mc);
+            }
+            stage(b2, stage_set);
+            if constexpr (decltype(compute)::value) rescale(mc);
+            __syncthreads();
+        };
+        auto main_loop = [&](auto compute) __attribute__((always_inline)) {
+            int bi = 0;
+            for (int t = 0; t + 1 < n_full; t += 2) {
+                step(compute, t, bi, sc_a, sc_b, pa, pb);
+                bi = next_buf(bi);
+                if (t + 2 >= n_full) break;
+                step(compute, t + 1, bi, sc_b, sc_a, pb, pa);
+                bi = next_buf(bi);
+            }
+        };
+        if (active)
+            main_loop(std::true_type{});
+        else
+            main_loop(std::false_type{});
+
+        if (active) {
+            // Last full tile: S is in sc_a if n_full is odd, else in sc_b.
+            if (n_full > 0) softmax_pv(std::false_type{}, (n_full - 1) % 3, (n_full & 1) ? sc_a : sc_b);
+            // The tail tile (staged by the loop or the prologue), with masking.
+            if (has_tail) {
+                const int bt = n_full % 3;
+                qk(bt, n_full, sc_a);
+                mask_tail(sc_a, (int)(t1 - t0 - (int64_t)KT * n_full));
+                row_max(sc_a, mc);
+                rescale(mc);
+                softmax_pv(std::false_type{}, bt, sc_a);
+            }
         }
     }
 
@@ -391,7 +436,7 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
                     none[rt] = m_run[rt] == -INFINITY;
                     if (none[rt]) m_run[rt] = 0.f;
                 }
-                softmax_pv(0, sc_a);
+                softmax_pv(std::true_type{}, 0, sc_a);
 #pragma unroll
                 for (int rt = 0; rt < kRT; ++rt)
                     if (none[rt]) m_run[rt] = -INFINITY;

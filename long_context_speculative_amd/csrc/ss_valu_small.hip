@@ -19,7 +19,9 @@
 //   P V      V goes to a per-wave LDS tile; lane l then owns output features
 //            2l, 2l+1 and accumulates p[row][key] * V[key][2l..2l+1] over the
 //            tile's keys, two keys per v_dot2_f32_bf16 (the bf16 weights are
-//            read from LDS as a broadcast; l sums the same rounded weights).
+//            read from LDS as a broadcast; l sums the same rounded weights;
+//            a request with a short history also takes each weight's
+//            rounding remainder, as a second pair of dot products).
 // The 4 waves' states are merged through LDS at the end.
 
 #include "ss_common.h"
@@ -44,6 +46,7 @@ struct SmallSmem {
         struct {
             uint16_t v[kWaves][kTile][kVRow];  // per-wave V tile
             uint32_t p[kWaves][RMAX][kTile / 2];  // per-wave bf16 weight pairs (keys 2j, 2j+1)
+            uint32_t pr[kWaves][RMAX][kTile / 2]; // their rounding remainders (short histories)
         } t;
         struct {
             float o[kWaves - 1][RMAX][D];
@@ -109,6 +112,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_valu_small_kernel(ChunkPara
     }
 
     const int n_tiles = (int)((t1 - t0 + kTile - 1) / kTile);
+    // A short history carries the weights' bf16 rounding remainders too.
+    const bool split = row_history_keys(p, b) < kSplitBelow;
     u32x4 kr[8], vr[8];
     // Lane's key of the tile (clamped into the range; masked below) and its
     // 64 features: 8 loads of 16 bytes.
@@ -172,12 +177,22 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_valu_small_kernel(ChunkPara
             }
             // bf16 weight; the pair (p[key], p[key + 1]) is packed by the lane
             // of the even key and stored for the P V products.
-            const __bf16 pb = (__bf16)exp2_hw(fmaf(sc[r], c, -m_ref[r]));
+            const float pv = exp2_hw(fmaf(sc[r], c, -m_ref[r]));
+            const __bf16 pb = (__bf16)pv;
             const uint32_t pbits = __builtin_bit_cast(uint16_t, pb);
             const uint32_t pnext = __shfl_down(pbits, 2);
             if (half == 0) {
                 l_part[r] += (float)pb;
                 if ((kk & 1) == 0) sm.u.t.p[w][r][kk >> 1] = pbits | (pnext << 16);
+            }
+            if (split) {
+                const __bf16 rb = (__bf16)(pv - (float)pb);
+                const uint32_t rbits = __builtin_bit_cast(uint16_t, rb);
+                const uint32_t rnext = __shfl_down(rbits, 2);
+                if (half == 0) {
+                    l_part[r] += (float)rb;
+                    if ((kk & 1) == 0) sm.u.t.pr[w][r][kk >> 1] = rbits | (rnext << 16);
+                }
             }
         }
         wave_sync();
@@ -204,6 +219,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_valu_small_kernel(ChunkPara
                 for (int j = 0; j < 4; ++j) {
                     o0[r] = dot2(pw[j], x0[j], o0[r]);
                     o1[r] = dot2(pw[j], x1[j], o1[r]);
+                }
+                if (split) {
+                    const u32x4 rr = *reinterpret_cast<const u32x4*>(&sm.u.t.pr[w][r][k >> 1]);
+                    const uint32_t rw[4] = {rr.x, rr.y, rr.z, rr.w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        o0[r] = dot2(rw[j], x0[j], o0[r]);
+                        o1[r] = dot2(rw[j], x1[j], o1[r]);
+                    }
                 }
             }
         }

@@ -64,7 +64,7 @@ def test_importance_selection_and_sparse_round(name):
     # importance
     imp_ref = sparse.block_importance(q, kh, vh, inp.hist_len, kc, vis, cfg.scale, block_len, sr.n_blocks)
     imp = sr.importance.cpu().numpy().astype(np.float64)
-    # bf16 weights move a block's l by at most 2^-9 relative (same weights in
+    # bf16 weights move a block's l by at most 2^-8 relative (same weights in
     # l and in the row's normaliser); fp32 inputs leave float rounding only
     rel = 2 ** -8 if cfg.dtype == "bf16" else 1e-5
     err = np.abs(imp - imp_ref) - rel * imp_ref
