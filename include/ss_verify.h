@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 11
+#define SS_ABI_VERSION 12
 
 /* status codes */
 #define SS_OK 0
@@ -268,6 +268,30 @@ SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, const void* q, 
  */
 SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in, const int32_t* slots_per_req,
                                float* o, float* lse, ss_stream_t stream);
+
+/*
+ * ss_verify_round -- one whole verification round on resident KV (section
+ * 4.2: the committed history and the masked candidate region in partial
+ * states, Eq. 7, folded by Eq. 8 into O = acc / l and lse, Eq. 9):
+ * ss_verify_history with the candidate region into slots [0, n_slots) of
+ * `work`, then ss_merge_states over those slots into o and lse.
+ *
+ *   q, hist, cand, parents, mask_out   as ss_verify_history (cand required)
+ *   n_slots   slots per (request, KV head) for the history cut, or 0: the
+ *             library's choice (one piece per work-group of one full launch
+ *             where the lengths are known on the host; 8 for ragged lengths
+ *             on the narrow MFMA kernel; +1 for the candidate slot on the
+ *             VALU engines), limited to work->n_slots
+ *   work      caller-allocated state slots (workspace); slots [0, n_slots)
+ *             are overwritten, their contents afterwards are not part of
+ *             the result
+ *   o, lse    as ss_merge_states
+ * Errors: as ss_verify_history and ss_merge_states; SS_ERR_INVALID_ARG if
+ * n_slots exceeds work->n_slots.
+ */
+SS_API int32_t ss_verify_round(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                               const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
+                               int32_t n_slots, const ss_state_t* work, float* o, float* lse, ss_stream_t stream);
 
 /*
  * ss_stream_history -- streamed verification over a history held in pinned

@@ -282,10 +282,14 @@ CandParams make_cand_params(const ss_problem_t* problem, const void* q, const ss
 
 }  // namespace
 
-extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
-                                            const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
-                                            const ss_block_stats_t* stats, int32_t n_slots, const ss_state_t* out,
-                                            int32_t slot_begin, ss_stream_t stream) {
+namespace {
+
+// ss_verify_history without the status bookkeeping of the export (shared
+// with the whole-round calls).
+int32_t verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                       const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
+                       const ss_block_stats_t* stats, int32_t n_slots, const ss_state_t* out, int32_t slot_begin,
+                       ss_stream_t stream) {
     if (!hist) return fail(SS_ERR_INVALID_ARG, "history view is NULL");
     if (n_slots < 1) return fail(SS_ERR_INVALID_ARG, "n_slots must be at least 1");
     // validation first (the chunk length does not change its outcome)
@@ -361,7 +365,18 @@ extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const v
         e = enqueue_chunk(problem, c, s);
     }
     if (e != hipSuccess) return fail(SS_ERR_HIP, "history kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return SS_OK;
+}
+
+}  // namespace
+
+extern "C" SS_API int32_t ss_verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                            const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
+                                            const ss_block_stats_t* stats, int32_t n_slots, const ss_state_t* out,
+                                            int32_t slot_begin, ss_stream_t stream) {
+    const int32_t rc = verify_history(problem, q, hist, cand, parents, mask_out, stats, n_slots, out, slot_begin,
+                                      stream);
+    return rc ? rc : ok();
 }
 
 extern "C" SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, const void* q, const ss_kv_view_t* cand,
@@ -380,14 +395,21 @@ extern "C" SS_API int32_t ss_verify_candidates(const ss_problem_t* problem, cons
     return ok();
 }
 
-extern "C" SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in,
-                                          const int32_t* slots_per_req, float* o, float* lse, ss_stream_t stream) {
-    int32_t rc = check_problem(problem);
-    if (rc) return rc;
-    if ((rc = check_state(in, "input"))) return rc;
+namespace {
+
+int32_t check_merge_out(const ss_problem_t* problem, const float* o, const float* lse) {
     if (!o || !lse) return fail(SS_ERR_INVALID_ARG, "o or lse is NULL");
     const int64_t n = (int64_t)problem->batch * problem->n_queries * problem->n_q_heads * problem->head_dim;
     if ((n + 255) / 256 > 0x7fffffff) return fail(SS_ERR_UNSUPPORTED, "output too large");
+    return SS_OK;
+}
+
+int32_t merge_states(const ss_problem_t* problem, const ss_state_t* in, const int32_t* slots_per_req, float* o,
+                     float* lse, ss_stream_t stream) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if ((rc = check_state(in, "input"))) return rc;
+    if ((rc = check_merge_out(problem, o, lse))) return rc;
     MergeParams m{};
     m.acc = in->acc;
     m.m = in->m;
@@ -402,7 +424,100 @@ extern "C" SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_
     m.lse = lse;
     hipError_t e = launch_merge(m, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(SS_ERR_HIP, "merge kernel launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return SS_OK;
+}
+
+// Slots per (request, KV head) of a whole-round call for this problem and
+// history view, before any capacity limit: one piece per work-group of one
+// full launch where the lengths are known on the host (uniform lengths on
+// the narrow MFMA kernel; the wide-row kernel's fixed chunks), 8 for ragged
+// lengths on the narrow kernel (the balanced cut grows its ranges when the
+// longest stream needs more), and one more for the candidate region on the
+// VALU engines.
+int32_t round_slots(const ss_problem_t* p, const ss_kv_view_t* hist, int32_t* n_slots) {
+    const int32_t group = p->n_q_heads / p->n_kv_heads;
+    const int32_t rows = p->n_queries * group;
+    const int64_t streams = (int64_t)p->batch * p->n_kv_heads;
+    int cus = 0;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "device query failed: %s", hipGetErrorString(e));
+    if (cus < 1) cus = 1;
+    int64_t s = 1;
+    switch (chunk_engine(p)) {
+        case ChunkEngine::kMfma:
+            s = hist->req_len ? 8 : cus / streams;
+            break;
+        case ChunkEngine::kMfmaWide: {
+            // 8-wave groups of 256 rows, one per CU; 4-wave groups of 128
+            // rows, two per CU
+            const int64_t per_group = rows > 128 ? 256 : 128, per_cu = rows > 128 ? 1 : 2;
+            s = per_cu * cus / (streams * ((rows + per_group - 1) / per_group));
+            break;
+        }
+        default:
+            s = 1 + 2 * (int64_t)cus / streams;
+            if (s > 9) s = 9;
+            break;
+    }
+    if (s < 1) s = 1;
+    if (chunk_engine(p) != ChunkEngine::kMfma && chunk_engine(p) != ChunkEngine::kMfmaWide && s < 2) s = 2;
+    if (s > 64) s = 64;
+    *n_slots = (int32_t)s;
+    return SS_OK;
+}
+
+// Everything a whole-round call checks before it enqueues anything (the
+// slot storage aside).
+int32_t validate_round(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                       const ss_kv_view_t* cand, const float* o, const float* lse) {
+    int32_t rc = check_problem(problem);
+    if (rc) return rc;
+    if (!q) return fail(SS_ERR_INVALID_ARG, "q is NULL");
+    if (!aligned16(q)) return fail(SS_ERR_INVALID_ARG, "q must be 16-byte aligned");
+    if ((rc = check_view(problem, hist, "history"))) return rc;
+    if (!cand) return fail(SS_ERR_INVALID_ARG, "candidate view is NULL");
+    if ((rc = check_cand(problem, cand))) return rc;
+    return check_merge_out(problem, o, lse);
+}
+
+// The round (history and candidates into slots [0, n_slots), then the
+// merge) on given slot storage.
+int32_t verify_round(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                     const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out, int32_t n_slots,
+                     const ss_state_t* st, float* o, float* lse, ss_stream_t stream) {
+    int32_t rc = verify_history(problem, q, hist, cand, parents, mask_out, nullptr, n_slots, st, 0, stream);
+    if (rc) return rc;
+    ss_state_t used = *st;  // the merge folds the slots this round wrote, not the whole storage
+    used.n_slots = n_slots;
+    return merge_states(problem, &used, nullptr, o, lse, stream);
+}
+
+}  // namespace
+
+extern "C" SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in,
+                                          const int32_t* slots_per_req, float* o, float* lse, ss_stream_t stream) {
+    const int32_t rc = merge_states(problem, in, slots_per_req, o, lse, stream);
+    return rc ? rc : ok();
+}
+
+extern "C" SS_API int32_t ss_verify_round(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                          const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
+                                          int32_t n_slots, const ss_state_t* work, float* o, float* lse,
+                                          ss_stream_t stream) {
+    int32_t rc = validate_round(problem, q, hist, cand, o, lse);
+    if (rc) return rc;
+    if ((rc = check_state(work, "workspace"))) return rc;
+    if (n_slots < 0) return fail(SS_ERR_INVALID_ARG, "n_slots is negative");
+    if (n_slots == 0) {
+        if ((rc = round_slots(problem, hist, &n_slots))) return rc;
+        if (n_slots > work->n_slots) n_slots = work->n_slots;
+    }
+    if (n_slots > work->n_slots)
+        return fail(SS_ERR_INVALID_ARG, "n_slots %d exceeds the workspace's %d slots", n_slots, work->n_slots);
+    rc = verify_round(problem, q, hist, cand, parents, mask_out, n_slots, work, o, lse, stream);
+    return rc ? rc : ok();
 }
 
 extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, const void* host_kv,

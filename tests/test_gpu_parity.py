@@ -545,6 +545,39 @@ def test_history_balanced_many_requests_and_empties():
         check_mask(rnd, inp)
 
 
+ROUND_CASES = {
+    "narrow_uniform": C["c2_qwen3_8b"].with_(batch=3, hist_len=3000, chunk_len=1024),
+    "narrow_ragged": C["c3_internlm25_7b_ragged"].with_(batch=7, hist_len=2500, ragged_lo=1, chunk_len=512),
+    "wide_tree": C["c4_tree_72b"].with_(batch=2, hist_len=2600, chunk_len=1024),
+    "wide_r96_ragged": C["c3_internlm25_7b_ragged"].with_(batch=3, n_queries=24, hist_len=2200, ragged_lo=1,
+                                                          chunk_len=300),
+    "valu_f32": C["c1_tiny_f32"],
+    "valu_small_rows": C["c2_qwen3_8b"].with_(batch=2, n_queries=2, hist_len=1500, chunk_len=512),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUND_CASES))
+@pytest.mark.parametrize("n_slots", [0, 3])
+def test_verify_round(name, n_slots):
+    """ss_verify_round (history and candidates into a workspace, then the
+    merge, in one call) against the oracle; the library's slot choice
+    (n_slots = 0) and a given one; the workspace starts as NaN."""
+    cfg = ROUND_CASES[name]
+    log(f"[round call] {name}: rows={cfg.rows} n_slots={n_slots}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp)
+    work = ss.StateBuffers(rnd.problem, 12, "cuda")
+    for t in (work.acc, work.m, work.l):
+        t.fill_(float("nan"))
+    rnd.mask_out.fill_(-1)
+    ss.ss_verify_round(rnd.problem, rnd.q, rnd.hist_view, rnd.cand_view, rnd.parents, rnd.mask_out, n_slots, work,
+                       rnd.o, rnd.lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
+
+
 def test_invalid_call_enqueues_nothing():
     cfg = SMALL["c2_small"]
     inp = wl.make_inputs(cfg)
