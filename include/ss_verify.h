@@ -48,7 +48,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 12
+#define SS_ABI_VERSION 13
 
 /* status codes */
 #define SS_OK 0
@@ -292,6 +292,29 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
 SS_API int32_t ss_verify_round(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
                                const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
                                int32_t n_slots, const ss_state_t* work, float* o, float* lse, ss_stream_t stream);
+
+/*
+ * ss_verify_round_noalloc -- ss_verify_round for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument, and the call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * The state slots live in a static device array of 64 MiB that every GPU
+ * the library runs on holds until the process ends; the slot count is the
+ * one ss_verify_round picks with n_slots = 0, cut down to what fits in the
+ * array. Every slot the call uses is written before it is read, so stale
+ * contents of an earlier call never reach the result. All calls on one GPU
+ * share that GPU's array: calls that overlap in time on one GPU (on
+ * different streams, or from several threads without ordering) race and
+ * give undefined results.
+ *   Arguments as ss_verify_round, without n_slots and work.
+ * Errors: as ss_verify_round; SS_ERR_UNSUPPORTED if not even one state slot
+ * (two on the VALU engines) of B * n_queries * Hq * (head_dim + 2) floats
+ * fits in the 64 MiB; SS_ERR_HIP if the array's device address cannot be
+ * obtained (looked up once per GPU on the first call there).
+ */
+SS_API int32_t ss_verify_round_noalloc(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
+                                       const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
+                                       float* o, float* lse, ss_stream_t stream);
 
 /*
  * ss_stream_history -- streamed verification over a history held in pinned

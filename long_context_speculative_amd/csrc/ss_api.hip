@@ -520,6 +520,75 @@ extern "C" SS_API int32_t ss_verify_round(const ss_problem_t* problem, const voi
     return rc ? rc : ok();
 }
 
+// ---------------------------------------------------------------------------
+// The whole round without a workspace argument, for callers that cannot
+// allocate: the state slots live in a static device array of every GPU the
+// library runs on.
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int64_t kRoundScratchBytes = (int64_t)64 << 20;
+
+// The slot storage of ss_verify_round_noalloc. Host code never uses this
+// name as an address: it is a host-side stand-in for the device array, whose
+// device address comes from hipGetSymbolAddress (one per GPU, kept below).
+__device__ __attribute__((aligned(256))) unsigned char scratch[kRoundScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kScratchDevices];
+
+// Device address of the current GPU's scratch array, looked up once per
+// device with that device current.
+int32_t scratch_ptr(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kScratchDevices) return fail(SS_ERR_UNSUPPORTED, "device %d beyond %d", dev, kScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(SS_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SS_OK;
+}
+
+}  // namespace
+
+extern "C" SS_API int32_t ss_verify_round_noalloc(const ss_problem_t* problem, const void* q,
+                                                  const ss_kv_view_t* hist, const ss_kv_view_t* cand,
+                                                  const int32_t* parents, uint64_t* mask_out, float* o, float* lse,
+                                                  ss_stream_t stream) {
+    int32_t rc = validate_round(problem, q, hist, cand, o, lse);
+    if (rc) return rc;
+    int32_t n_slots = 0;
+    if ((rc = round_slots(problem, hist, &n_slots))) return rc;
+    // slots that fit: acc [S][rows][d] + m [S][rows] + l [S][rows], fp32
+    const int64_t rows = (int64_t)problem->batch * problem->n_queries * problem->n_q_heads;
+    const int64_t slot_bytes = rows * (problem->head_dim + 2) * 4;
+    const bool valu = chunk_engine(problem) != ChunkEngine::kMfma && chunk_engine(problem) != ChunkEngine::kMfmaWide;
+    const int64_t fit = kRoundScratchBytes / slot_bytes;
+    if (fit < (valu ? 2 : 1))
+        return fail(SS_ERR_UNSUPPORTED, "the round needs %lld bytes of state per slot; the static scratch holds %lld",
+                    (long long)slot_bytes, (long long)kRoundScratchBytes);
+    if (n_slots > fit) n_slots = (int32_t)fit;
+    void* base = nullptr;
+    if ((rc = scratch_ptr(&base))) return rc;
+    float* f = static_cast<float*>(base);
+    ss_state_t st{};
+    st.acc = f;
+    st.m = f + (int64_t)n_slots * rows * problem->head_dim;
+    st.l = st.m + (int64_t)n_slots * rows;
+    st.n_slots = n_slots;
+    rc = verify_round(problem, q, hist, cand, parents, mask_out, n_slots, &st, o, lse, stream);
+    return rc ? rc : ok();
+}
+
 extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const void* q, const void* host_kv,
                                             const int32_t* req_len, int32_t chunk_len, int32_t n_chunks,
                                             int32_t chunks_per_copy, void* staging, int32_t n_buf,

@@ -35,7 +35,8 @@ EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chun
             "ss_verify_candidates", "ss_merge_states", "ss_stream_history", "ss_stream_timings", "ss_tree_mask_host",
             "ss_slot_tokens_host", "ss_history_plan_host", "ss_tier_migration_end", "ss_tier_migrate",
             "ss_kv_copy_rows", "ss_verify_chunk_gathered", "ss_block_importance", "ss_select_blocks",
-            "ss_read_probe", "ss_block_stats_bytes", "ss_block_importance_stats", "ss_verify_round")
+            "ss_read_probe", "ss_block_stats_bytes", "ss_block_importance_stats", "ss_verify_round",
+            "ss_verify_round_noalloc")
 
 
 class SSError(RuntimeError):
@@ -89,6 +90,8 @@ def lib() -> ctypes.CDLL:
                                         P(State), I32, VP]
         L.ss_verify_round.restype = I32
         L.ss_verify_round.argtypes = [P(Problem), VP, P(KVView), P(KVView), VP, VP, I32, P(State), VP, VP, VP]
+        L.ss_verify_round_noalloc.restype = I32
+        L.ss_verify_round_noalloc.argtypes = [P(Problem), VP, P(KVView), P(KVView), VP, VP, VP, VP, VP]
         L.ss_verify_candidates.restype = I32
         L.ss_verify_candidates.argtypes = [P(Problem), VP, P(KVView), VP, VP, P(State), I32, VP]
         L.ss_merge_states.restype = I32
@@ -241,6 +244,14 @@ def ss_verify_round(problem: Problem, q: torch.Tensor, hist: KVView, cand: KVVie
     _check(lib().ss_verify_round(ctypes.byref(problem), q.data_ptr(), ctypes.byref(hist), ctypes.byref(cand),
                                  _ptr(parents), _ptr(mask_out), n_slots, ctypes.byref(work.struct), o.data_ptr(),
                                  lse.data_ptr(), _stream(stream)))
+
+
+def ss_verify_round_noalloc(problem: Problem, q: torch.Tensor, hist: KVView, cand: KVView,
+                            parents: Optional[torch.Tensor], mask_out: Optional[torch.Tensor], o: torch.Tensor,
+                            lse: torch.Tensor, stream=None) -> None:
+    _check(lib().ss_verify_round_noalloc(ctypes.byref(problem), q.data_ptr(), ctypes.byref(hist),
+                                         ctypes.byref(cand), _ptr(parents), _ptr(mask_out), o.data_ptr(),
+                                         lse.data_ptr(), _stream(stream)))
 
 
 def ss_stream_history(problem: Problem, q: torch.Tensor, host_kv: torch.Tensor, chunk_len: int, n_chunks: int,
