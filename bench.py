@@ -4,12 +4,15 @@
 
 A step is one pass of the whole resident hot path over one batch of
 synthetic input already in HBM: ss_verify_history over every request's
-committed history (with the candidate region folded into the same launch
-where the narrow MFMA kernel serves the shape, else ss_verify_candidates
-after it) and ss_merge_states. The default workload is the Qwen3-8B-like
-layer: 16 requests, 32 query heads over 8 KV heads, head_dim 128, 32768
-committed bf16 tokens each, 6 queries (5 drafts + 1) under a causal
-candidate mask.
+committed history (with the candidate region folded into the same launch on
+the MFMA kernels, narrow and wide-row, else ss_verify_candidates after it)
+and ss_merge_states. The headline workload is the largest single-GPU one,
+the InternLM2.5-7B-like layer: 32 requests with ragged committed histories
+(uniform in [8192, 65536] tokens, seed-drawn), 32 query heads over 8 KV
+heads, head_dim 128, bf16, 5 queries (4 drafts + 1) under a causal
+candidate mask. The same line carries sub-records for the Qwen3-8B-like
+layer (uniform 32768 tokens, HBM-bound) and the 72B-like tree workload
+(64-node candidate tree under 8-way GQA, bound by the matrix cores).
 
 Prints ONE JSON line. value = effective KV GB/s = (history + candidate K/V
 bytes) / time per step. Also reported: verified query-tokens/s, the history
@@ -114,6 +117,20 @@ def read_traffic(cfg, split, fused):
     return float(m_bytes.group(1))
 
 
+def read_profile_value(cfg, key):
+    """A number recorded in the committed counter summary of cfg's history
+    launch, if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"chunk_kernel_{cfg.name}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m = re.search(re.escape(key) + r":\s*([0-9.eE+]+)", text)
+    if not m_hash or not m or m_hash.group(1) != source_hash(cfg):
+        return None
+    return float(m.group(1))
+
+
 def make_round(cfg, inp, cps="auto", engine="auto", split="balanced"):
     """The resident round in the launch configuration the benchmark times
     (rounds.BENCH_RESIDENT unless overridden)."""
@@ -122,17 +139,36 @@ def make_round(cfg, inp, cps="auto", engine="auto", split="balanced"):
     return rounds.ResidentRound(inp, engine=engine, **kw)
 
 
+# Sustained load after idle makes the device's clock and power management
+# swing for tens of milliseconds: traced on MI355X, the history launch runs
+# up to 40% slower a few milliseconds into a burst and returns to its steady
+# duration after about 30 ms. Every timed loop is therefore preceded by this
+# much untimed device work of the same kind.
+SETTLE_S = 0.3
+
+
+def settle(fn, seconds=SETTLE_S):
+    """Runs fn (an enqueue of device work) untimed for `seconds` of wall
+    time, synchronising every few calls."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_resident(cfg, steps, warmup, cps="auto", engine="auto", split="balanced"):
     """Step time over `steps` timed steps (events only at the two ends, so no
     marker sits between the launches), then the history launch's own
     duration from HIP events around each launch over another `steps` steps
-    on the same stream."""
+    on the same stream. Before each: `warmup` steps and the settle time."""
     inp = wl.make_inputs(cfg)
     rnd = make_round(cfg, inp, cps, engine, split)
     del inp
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         rnd.run()
+    settle(rnd.run)
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -142,6 +178,7 @@ def time_resident(cfg, steps, warmup, cps="auto", engine="auto", split="balanced
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_begin.elapsed_time(t_end) / steps
+    settle(rnd.run, 0.1)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for k in range(steps):
         ev[k][0].record(stream)
@@ -246,8 +283,7 @@ def read_probe(n_bytes=2 << 30, reps=10):
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     out = {"bytes": n_bytes}
     for name, wgs in (("one_per_cu_GBps", cus), ("eight_per_cu_GBps", 8 * cus)):
-        ss.ss_read_probe(src, wgs, sink)
-        torch.cuda.synchronize()
+        settle(lambda: ss.ss_read_probe(src, wgs, sink), 0.2)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
@@ -278,7 +314,7 @@ def time_sparse(cfg, block_len=512, k=16, reps=20):
     def timed(fn):
         for _ in range(3):
             fn()
-        torch.cuda.synchronize()
+        settle(fn, 0.1)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(reps):
@@ -390,15 +426,16 @@ def cpu_baseline(cfg, budget_s=15.0):
     q = inp.q.float().numpy()
     kc, vc = inp.k_cand.float().numpy(), inp.v_cand.float().numpy()
     kh, vh = inp.hist_per_request("k"), inp.hist_per_request("v")
-    done, slices = 0.0, 0
+    done, slices, keys = 0.0, 0, 0
     t0 = time.perf_counter()
     while done < budget_s:
         b, g = divmod(slices % (inp.cfg.batch * cfg.n_kv_heads), cfg.n_kv_heads)
         oracle.attention_reference(q, kh, vh, inp.hist_len, kc, vc, vis, cfg.scale, requests=[b], kv_heads=[g])
         slices += 1
+        keys += int(inp.hist_len[b]) + cfg.n_queries
         done = time.perf_counter() - t0
     row = 2 * cfg.head_dim * cfg.elem_bytes
-    kv = slices * (int(inp.hist_len.max()) + cfg.n_queries) * row
+    kv = keys * row
     cores = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
     # the whole tiny fp32 round (c1) on one thread
     from threadpoolctl import threadpool_limits
@@ -454,12 +491,74 @@ def counters_pass(cfg, cps="auto", engine="auto", split="balanced"):
           flush=True)
 
 
+DEFAULT_WORKLOAD = "c3_internlm25_7b_ragged"
+
+
+def workload_desc(cfg) -> str:
+    return (f"{cfg.name}: B={cfg.batch}, Hq={cfg.n_q_heads}, Hkv={cfg.n_kv_heads}, d={cfg.head_dim}, "
+            f"history={'U[%d, %d]' % (cfg.ragged_lo, cfg.hist_len) if cfg.ragged else cfg.hist_len}"
+            f" ({'ragged' if cfg.ragged else 'uniform'}), chunk={cfg.chunk_len}, q={cfg.n_queries}, mask={cfg.mask}")
+
+
+def resident_record(cfg, steps, warmup, cps, engine, split, probe):
+    """Step and history-launch times of one resident workload, with the
+    launch's roofline (HBM bytes, or MFMA FLOPs for wide row groups)."""
+    rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, steps, warmup, cps, engine, split)
+    kernel = "ss_verify_history" if rnd.split == "balanced" else "ss_verify_chunk"
+    hist_b, cand_b = kv_bytes(cfg, hist_len)
+    gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9
+    alg = launch_bytes(cfg, hist_len, rnd)
+    traffic = read_traffic(cfg, rnd.split, rnd.fused) if engine == "auto" else None
+    if cfg.rows > 32:
+        # wide row groups: the chunk kernel is bound by the matrix cores
+        flops = chunk_kernel_flops(cfg, hist_len)
+        tflops = flops / (ms_chunk * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None if traffic is None else int(traffic), "kernel": kernel,
+                "ms_per_launch": round(ms_chunk, 4), "algorithmic_flops_per_launch": flops,
+                "algorithmic_bytes_per_launch": alg,
+                "hbm_GBps_algorithmic": round(alg / (ms_chunk * 1e-3) / 1e9, 2)}
+        clock = read_profile_value(cfg, "sustained_clock_GHz")
+        if clock:
+            # the same fraction against the dense peak at the clock the
+            # launch sustained (rocprofv3 GRBM_GUI_ACTIVE over its duration)
+            roof["sustained_clock_GHz"] = clock
+            roof["frac_at_sustained_clock"] = round(tflops / (MFMA_BF16_PEAK_TFLOPS * clock / 2.4), 4)
+    else:
+        achieved = alg / (ms_chunk * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic),
+                "kernel": kernel, "ms_per_launch": round(ms_chunk, 4), "algorithmic_bytes_per_launch": alg}
+        if probe:
+            roof["frac_of_read_probe"] = round(achieved / max(probe["one_per_cu_GBps"], probe["eight_per_cu_GBps"]),
+                                               4)
+    rec = {
+        "config": {"workload": workload_desc(cfg), "batch": cfg.batch, "history_tokens": cfg.hist_len,
+                   "history_tokens_total": int(hist_b // (2 * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes)),
+                   "queries": cfg.n_queries,
+                   "split": rnd.split, "history_slots": rnd.n_hist_slots, "fused_candidates": rnd.fused,
+                   "chunks_per_slot": rnd.cps if rnd.split == "chunks" else None, "engine": engine},
+        "ms_per_step": round(ms_step, 4),
+        "effective_KV_GBps": round(gbs, 2),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "query_tokens_per_s": round(cfg.batch * cfg.n_queries / (ms_step * 1e-3), 1),
+        "roofline": roof,
+    }
+    del rnd
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="c2_qwen3_8b", choices=[k for k in wl.CONFIGS if not wl.CONFIGS[k].streamed])
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
+                    choices=[k for k in wl.CONFIGS if not wl.CONFIGS[k].streamed])
+    ap.add_argument("--no-extra-workloads", action="store_true",
+                    help="skip the c2 and c4 sub-records of the default run")
     ap.add_argument("--chunks-per-slot", type=int, default=0,
                     help="chunks merged per state slot (0: automatic, about two work-groups per compute unit)")
     ap.add_argument("--split", default=rounds.BENCH_RESIDENT["split"], choices=["balanced", "chunks"],
@@ -497,60 +596,36 @@ def main():
     # the read reference first, while the device is in the state the timed
     # steps start from (after seconds of streaming it reads measurably slower)
     probe = read_probe()
-    rnd, hist_len, ms_step, ms_chunk = time_resident(cfg, args.steps, args.warmup, cps, args.engine, args.split)
-    cps = rnd.cps
-    kernel = "ss_verify_history" if rnd.split == "balanced" else "ss_verify_chunk"
-    hist_slots = rnd.n_hist_slots
-    hist_b, cand_b = kv_bytes(cfg, hist_len)
-    gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9
-    alg = launch_bytes(cfg, hist_len, rnd)
-    fused = rnd.fused
-    traffic = read_traffic(cfg, rnd.split, rnd.fused) if args.engine == "auto" else None
-    if cfg.rows > 32:
-        # wide row groups: the chunk kernel is bound by the matrix cores
-        flops = chunk_kernel_flops(cfg, hist_len)
-        roof = {"bound": "mfma", "achieved": round(flops / (ms_chunk * 1e-3) / 1e12, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(flops / (ms_chunk * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": None if traffic is None else int(traffic), "kernel": kernel,
-                "ms_per_launch": round(ms_chunk, 4), "algorithmic_flops_per_launch": flops,
-                "algorithmic_bytes_per_launch": alg,
-                "hbm_GBps_algorithmic": round(alg / (ms_chunk * 1e-3) / 1e9, 2)}
-    else:
-        achieved = alg / (ms_chunk * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None if traffic is None else int(traffic),
-                "kernel": kernel, "ms_per_launch": round(ms_chunk, 4), "algorithmic_bytes_per_launch": alg}
-    del rnd
-    torch.cuda.empty_cache()
-    if roof["bound"] == "hbm":
-        roof["frac_of_read_probe"] = round(roof["achieved"] / max(probe["one_per_cu_GBps"], probe["eight_per_cu_GBps"]), 4)
-
+    head = resident_record(cfg, args.steps, args.warmup, cps, args.engine, args.split, probe)
     out = {
         "metric": "verification-attn effective KV GB/s (% of HBM peak) + verified query-tokens/s",
-        "value": round(gbs, 2),
+        "value": head["effective_KV_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1), bf16)",
-        "config": {"workload": f"{cfg.name}: B={cfg.batch}, Hq={cfg.n_q_heads}, Hkv={cfg.n_kv_heads}, "
-                               f"d={cfg.head_dim}, history={cfg.hist_len} ({'ragged' if cfg.ragged else 'uniform'}),"
-                               f" chunk={cfg.chunk_len}, q={cfg.n_queries}, mask={cfg.mask}",
-                   "batch": cfg.batch, "history_tokens": cfg.hist_len, "queries": cfg.n_queries,
-                   "split": args.split, "history_slots": hist_slots, "fused_candidates": fused,
-                   "chunks_per_slot": cps if args.split == "chunks" else None, "engine": args.engine},
-        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "query_tokens_per_s": round(cfg.batch * cfg.n_queries / (ms_step * 1e-3), 1),
-        "roofline": roof,
+        "config": head["config"],
+        "pct_hbm_peak": head["pct_hbm_peak"],
+        "query_tokens_per_s": head["query_tokens_per_s"],
+        "roofline": head["roofline"],
         "hbm_read_probe": probe,
     }
-    if args.workload == "c2_qwen3_8b" and not args.no_sparse:
-        out["sparse"] = time_sparse(cfg)
+    # the other resident workloads of the round, each in its own launch
+    # configuration: the uniform HBM-bound layer and the MFMA-bound tree
+    if not args.no_extra_workloads and args.workload == DEFAULT_WORKLOAD and not args.queries:
+        for key, name in (("c2", "c2_qwen3_8b"), ("c4", "c4_tree_72b")):
+            rec = resident_record(wl.CONFIGS[name], args.steps, args.warmup, "auto", args.engine, args.split, probe)
+            out[key] = {k: rec[k] for k in ("config", "ms_per_step", "effective_KV_GBps", "pct_hbm_peak",
+                                             "query_tokens_per_s", "roofline")}
+            torch.cuda.empty_cache()
+    if not args.no_sparse:
+        out["sparse"] = time_sparse(wl.CONFIGS["c2_qwen3_8b"])
         torch.cuda.empty_cache()
     if not args.no_streamed:
         out["streamed"] = time_streamed(wl.CONFIGS["c5_streamed"])

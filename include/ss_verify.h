@@ -15,8 +15,15 @@
  *   - Status: every call returns SS_OK (0) or a negative SS_ERR_* code; the
  *     message of the last failure on the calling thread is ss_last_error().
  *     Nothing throws across this boundary.
- *   - Validation is synchronous and complete before anything is enqueued: a
- *     call that returns an error has enqueued no work.
+ *   - Validation is synchronous and complete before anything is enqueued,
+ *     and every resource a call needs (events of the streaming pipeline) is
+ *     created before its first enqueue: a call that returns SS_ERR_INVALID_ARG
+ *     or SS_ERR_UNSUPPORTED has enqueued no work. SS_ERR_HIP means the HIP
+ *     runtime refused an enqueue; a call that enqueues several operations
+ *     (ss_verify_history, ss_verify_round, ss_stream_history, the tiering
+ *     copies) may then have enqueued the ones before it, which the caller
+ *     drains by synchronising its streams (a streaming ring is then reset, so
+ *     the next ss_stream_history call must not pass SS_STREAM_CONTINUE).
  *   - Ownership: the caller owns every buffer. The library never allocates
  *     or frees a caller buffer, and allocates no device memory. Buffers must
  *     stay valid until the caller has synchronised the streams it passed.

@@ -662,10 +662,17 @@ extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const v
     view.max_len = chunk_len;
     view.req_len = req_len;  // request b holds clamp(req_len[b] - j*C, 0, C) tokens of chunk j
 
-#define SS_TRY(call)                                                                              \
-    do {                                                                                          \
-        hipError_t err_ = (call);                                                                 \
-        if (err_ != hipSuccess) return fail(SS_ERR_HIP, "%s: %s", #call, hipGetErrorString(err_)); \
+    // A HIP error part-way leaves the earlier operations enqueued; the ring
+    // bookkeeping no longer matches what the streams will do, so it is reset
+    // (a following SS_STREAM_CONTINUE call is refused).
+#define SS_TRY(call)                                                            \
+    do {                                                                        \
+        hipError_t err_ = (call);                                               \
+        if (err_ != hipSuccess) {                                               \
+            ev.staging = nullptr;                                               \
+            ev.n_buf = 0;                                                       \
+            return fail(SS_ERR_HIP, "%s: %s", #call, hipGetErrorString(err_)); \
+        }                                                                       \
     } while (0)
 
     SS_TRY(hipEventRecord(ev.start, ks));

@@ -78,7 +78,8 @@ def mfma_fuses_candidates(cfg, engine="auto") -> bool:
 
 
 # Launch configuration of the resident round that the benchmark times.
-BENCH_RESIDENT = dict(split="balanced", chunks_per_slot="auto", history_slots="auto", fuse_candidates="auto")
+BENCH_RESIDENT = dict(split="balanced", chunks_per_slot="auto", history_slots="auto", fuse_candidates="auto",
+                      kv_layout="interleaved")
 
 
 ENGINES = {"auto": ss.SS_ENGINE_AUTO, "valu": ss.SS_ENGINE_VALU, "mfma": ss.SS_ENGINE_MFMA}
@@ -89,12 +90,23 @@ def _problem(cfg, engine="auto") -> ss.Problem:
                            cfg.torch_dtype, cfg.scale, ENGINES[engine])
 
 
+def interleave_kv(k: torch.Tensor, v: torch.Tensor) -> torch.Tensor:
+    """One device tensor holding the K row and the V row of every (token, KV
+    head) next to each other: the shape of k with an axis of 2 inserted
+    before the feature axis (index 0 = K, 1 = V), so one history stream is
+    one run of memory instead of two."""
+    return torch.stack((k, v), dim=-2).contiguous()
+
+
 class ResidentRound:
     def __init__(self, inp: VerifyInputs, device="cuda", chunk_len=None, chunks_per_slot=1, engine="auto",
-                 split="chunks", history_slots="auto", fuse_candidates=False):
+                 split="chunks", history_slots="auto", fuse_candidates=False, kv_layout="separate"):
         """split: "chunks" (ss_verify_chunk over chunks of chunk_len, merged
         chunks_per_slot at a time) or "balanced" (ss_verify_history with
         history_slots slots per stream).
+        kv_layout: "separate" (K and V in two tensors of the input layout)
+        or "interleaved" (one tensor, each token's K and V rows adjacent;
+        the view's strides and offsets step over both).
         fuse_candidates (balanced split only): True, False or "auto" (when
         an MFMA kernel serves the shape): pass the candidate region to
         ss_verify_history instead of a separate ss_verify_candidates.
@@ -111,21 +123,41 @@ class ResidentRound:
         if chunks_per_slot == "auto":
             chunks_per_slot = auto_chunks_per_slot(cfg, inp.hist_len, self.chunk_len, device_cus(device), engine)
         self.cps = chunks_per_slot
+        if kv_layout not in ("separate", "interleaved"):
+            raise ValueError(f"unknown kv_layout {kv_layout!r}")
+        self.kv_layout = kv_layout
         self.q = inp.q.to(device)
-        self.k_hist = inp.k_hist.to(device)
-        self.v_hist = inp.v_hist.to(device)
         self.max_len = int(inp.hist_len.max()) if len(inp.hist_len) else 0
         if cfg.ragged:
             self.hist_offset = torch.as_tensor(inp.hist_offset, dtype=torch.int64, device=device)
             self.hist_len = torch.as_tensor(inp.hist_len, dtype=torch.int32, device=device)
-            if cfg.packing == "head":
+        if kv_layout == "separate":
+            self.k_hist = inp.k_hist.to(device)
+            self.v_hist = inp.v_hist.to(device)
+            if not cfg.ragged:
+                self.hist_view = ss.head_major_view(self.k_hist, self.v_hist)
+            elif cfg.packing == "head":
                 self.hist_view = ss.head_packed_view(self.k_hist, self.v_hist, self.hist_offset, self.hist_len,
                                                      self.max_len)
             else:
                 self.hist_view = ss.token_major_view(self.k_hist, self.v_hist, self.hist_offset, self.hist_len,
                                                      self.max_len)
         else:
-            self.hist_view = ss.head_major_view(self.k_hist, self.v_hist)
+            # [B][Hkv][N][2][d], head-packed [Hkv][sum N][2][d] or
+            # token-packed [sum N][Hkv][2][d]
+            self.kv_hist = interleave_kv(inp.k_hist.to(device), inp.v_hist.to(device))
+            kv = self.kv_hist
+            v_at = kv.narrow(-2, 1, 1)  # the V rows: head_dim elements after each K row
+            if not cfg.ragged:
+                sb, sh, st = kv.stride(0), kv.stride(1), kv.stride(2)
+                self.hist_view = ss.make_view(kv, v_at, sb, sh, st, kv.shape[2])
+            else:
+                self.hist_offset2 = self.hist_offset * 2  # element offsets count K and V rows
+                if cfg.packing == "head":
+                    sh, st = kv.stride(0), kv.stride(1)
+                else:
+                    st, sh = kv.stride(0), kv.stride(1)
+                self.hist_view = ss.make_view(kv, v_at, 0, sh, st, self.max_len, self.hist_offset2, self.hist_len)
         self.k_cand = inp.k_cand.to(device)
         self.v_cand = inp.v_cand.to(device)
         self.cand_view = ss.head_major_view(self.k_cand, self.v_cand)

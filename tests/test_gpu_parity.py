@@ -117,6 +117,24 @@ def test_round_small(name):
         check_mask(rnd, inp)
 
 
+@pytest.mark.parametrize("name", ["c1", "c2_small", "c3_small", "c3_small_token", "c4_small", "bf16_d64",
+                                  "valu_r12_ragged", "wide_r96_ragged"])
+@pytest.mark.parametrize("split", ["chunks", "balanced"])
+def test_interleaved_kv_layout(name, split):
+    """One history tensor with each token's K and V rows adjacent (the
+    layout the benchmark uses): the views step over both rows."""
+    cfg = SMALL[name]
+    log(f"[interleaved] {name} {split}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, split=split, kv_layout="interleaved",
+                               fuse_candidates="auto" if split == "balanced" else False)
+    rnd.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
+
+
 @pytest.mark.parametrize("name", ["valu_r4", "bf16_small_rows", "valu_r12_ragged", "valu_r15", "c2_small"])
 def test_forced_valu_engine(name):
     """The VALU engine (SS_ENGINE_VALU) on bf16 shapes: the small-row kernel
