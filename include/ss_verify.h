@@ -70,6 +70,10 @@ extern "C" {
 /* ss_stream_history flags */
 #define SS_STREAM_TIMINGS 1  /* record per-chunk events for ss_stream_timings     */
 #define SS_STREAM_CONTINUE 2 /* continue the previous call's staging ring          */
+/* Ordering checks of the pipeline (diagnostic; the result must not change): */
+#define SS_STREAM_POISON 4   /* fill each staging buffer with NaN once it is free, */
+                             /* just before its copy                             */
+#define SS_STREAM_DELAY 8    /* hold the copy stream about 2 ms before each copy  */
 
 /* chunk-kernel engines (ss_problem_t.engine) */
 #define SS_ENGINE_AUTO 0 /* measured choice, see ss_verify_chunk                 */
@@ -345,6 +349,12 @@ SS_API int32_t ss_verify_round_noalloc(const ss_problem_t* problem, const void* 
  *   copy_stream, compute_stream  must differ; the copies run on the first,
  *                the chunk kernels on the second
  *   flags        SS_STREAM_TIMINGS: record per-chunk events (ss_stream_timings).
+ *                SS_STREAM_POISON, SS_STREAM_DELAY: diagnostics of the ordering
+ *                below. POISON overwrites every staging buffer with NaN on the
+ *                copy stream after its wait for the buffer's last reader and
+ *                before its copy; DELAY makes the copy stream sleep on the
+ *                host (a host function) about 2 ms before every copy. With
+ *                correct ordering neither changes any result.
  *                SS_STREAM_CONTINUE: the staging ring (same staging pointer,
  *                n_buf and buffer size) continues from the previous call on
  *                this device: each copy waits only until the last kernel that

@@ -3,6 +3,7 @@
 // staging buffers, a transfer stream and a compute stream, per-chunk events).
 
 #include <math.h>
+#include <time.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -195,6 +196,12 @@ struct StreamEvents {
 
 std::mutex g_ev_mutex;
 std::vector<StreamEvents> g_events;
+
+// SS_STREAM_DELAY: a host function on the copy stream that holds it.
+void copy_delay(void*) {
+    const struct timespec ts = {0, 2000000};
+    nanosleep(&ts, nullptr);
+}
 
 hipError_t grow(std::vector<hipEvent_t>& v, size_t n, unsigned flags) {
     while (v.size() < n) {
@@ -605,9 +612,12 @@ extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const v
         return fail(SS_ERR_INVALID_ARG, "slots [%d, %d) exceed n_slots %d", slot_begin, slot_begin + n_chunks,
                     out->n_slots);
     if (copy_stream == compute_stream) return fail(SS_ERR_INVALID_ARG, "copy and compute streams must differ");
-    if (flags & ~(SS_STREAM_TIMINGS | SS_STREAM_CONTINUE)) return fail(SS_ERR_INVALID_ARG, "unknown flags %d", flags);
+    if (flags & ~(SS_STREAM_TIMINGS | SS_STREAM_CONTINUE | SS_STREAM_POISON | SS_STREAM_DELAY))
+        return fail(SS_ERR_INVALID_ARG, "unknown flags %d", flags);
     const bool timed = flags & SS_STREAM_TIMINGS;
     const bool cont = flags & SS_STREAM_CONTINUE;
+    const bool poison = flags & SS_STREAM_POISON;
+    const bool delay = flags & SS_STREAM_DELAY;
 
     const int64_t es = elem_size(problem);
     const int64_t half = (int64_t)problem->batch * problem->n_kv_heads * chunk_len * problem->head_dim;
@@ -689,6 +699,8 @@ extern "C" SS_API int32_t ss_stream_history(const ss_problem_t* problem, const v
         char* buf = static_cast<char*>(staging) + (int64_t)bi * buf_bytes;
         const char* src = static_cast<const char*>(host_kv) + j0 * chunk_bytes;
         if (ev.used[bi]) SS_TRY(hipStreamWaitEvent(cs, ev.freed[bi], 0));
+        if (poison) SS_TRY(launch_word_fill(buf, buf_bytes, 0xffffffffu, cs));  // NaN in bf16 and fp32
+        if (delay) SS_TRY(hipLaunchHostFunc(cs, copy_delay, nullptr));
         if (timed) SS_TRY(hipEventRecord(ts->copy0[gi], cs));
         SS_TRY(hipMemcpyAsync(buf, src, nj * chunk_bytes, hipMemcpyHostToDevice, cs));
         if (timed) SS_TRY(hipEventRecord(ts->copy1[gi], cs));

@@ -369,5 +369,7 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 hipError_t launch_state_fill(float* acc, float* m, float* l, int64_t row_begin, int64_t n_rows, int head_dim,
                              hipStream_t stream);
 hipError_t launch_importance_stats(const StatsImportanceParams& p, hipStream_t stream);
+// The 32-bit word `word` repeated over bytes (a multiple of 16) at dst.
+hipError_t launch_word_fill(void* dst, int64_t bytes, uint32_t word, hipStream_t stream);
 
 }  // namespace ssv

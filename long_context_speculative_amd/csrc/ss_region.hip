@@ -261,7 +261,24 @@ __global__ __launch_bounds__(kThreads) void state_fill_kernel(float4* __restrict
     }
 }
 
+// A byte pattern over a buffer (a multiple of 16 bytes, 16-byte aligned).
+__global__ __launch_bounds__(kThreads) void word_fill_kernel(uint4* __restrict__ dst, int64_t n_vec, uint32_t word) {
+    const int64_t step = (int64_t)gridDim.x * kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n_vec; i += step)
+        dst[i] = make_uint4(word, word, word, word);
+}
+
 }  // namespace
+
+hipError_t launch_word_fill(void* dst, int64_t bytes, uint32_t word, hipStream_t stream) {
+    const int64_t n_vec = bytes / 16;
+    if (n_vec <= 0) return hipSuccess;
+    int64_t blocks = (n_vec + kThreads - 1) / kThreads;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(word_fill_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       static_cast<uint4*>(dst), n_vec, word);
+    return hipGetLastError();
+}
 
 int cand_row_blocks(int rows) { return (rows + kRowsPerBlock - 1) / kRowsPerBlock; }
 

@@ -254,13 +254,15 @@ class StreamedRound:
         self.copy_stream = torch.cuda.Stream(device=device)
         self.compute_stream = torch.cuda.Stream(device=device)
 
-    def run(self, record_timings=False):
-        """Enqueues the whole round; the result is ready once compute_stream is."""
+    def run(self, record_timings=False, checks=0):
+        """Enqueues the whole round; the result is ready once compute_stream is.
+        checks: ordering diagnostics of ss_stream_history (SS_STREAM_POISON,
+        SS_STREAM_DELAY)."""
         cs = self.compute_stream
         cs.wait_stream(torch.cuda.current_stream())
         ss.ss_stream_history(self.problem, self.q, self.host_kv, self.chunk_len, self.n_chunks, self.staging,
                              self.n_buf, self.state, 0, self.copy_stream, cs, record_timings,
-                             chunks_per_copy=self.chunks_per_copy)
+                             chunks_per_copy=self.chunks_per_copy, checks=checks)
         ss.ss_verify_candidates(self.problem, self.q, self.cand_view, self.parents, None, self.state,
                                 self.n_chunks, cs)
         ss.ss_merge_states(self.problem, self.state, None, self.o, self.lse, cs)
@@ -350,9 +352,14 @@ class TieredRound:
     """
 
     def __init__(self, cfg, hist_k, hist_v, tail_target=512, gran=256, chunk_len=512, max_tokens=None,
-                 q_max=None, device="cuda", n_buf=2, tail_slots=2):
+                 q_max=None, device="cuda", n_buf=2, tail_slots=2, overlap_migration=False):
         """hist_k, hist_v: per-request CPU tensors [Hkv][N_b][d] of the
-        initial committed history (cfg.torch_dtype)."""
+        initial committed history (cfg.torch_dtype).
+        overlap_migration: migrate() only starts the device-to-host copies,
+        on a stream of their own, and returns; the next verify() runs while
+        they are in flight (reading the tail rows they copy), and H moves to
+        E, with the tail compacted, once they have landed (finalize(), called
+        by verify() after it has enqueued its work)."""
         self.cfg = cfg
         self.problem = _problem(cfg)
         self.device = device
@@ -375,6 +382,10 @@ class TieredRound:
         self.cur = 0
         self.copy_stream = torch.cuda.Stream(device=device)
         self.compute_stream = torch.cuda.Stream(device=device)
+        self.overlap = overlap_migration
+        self.migrate_stream = torch.cuda.Stream(device=device) if overlap_migration else None
+        self.pending = None              # (E, copies-landed event) of a migration in flight
+        self.last_migration = None       # (start, end) timing events of the last migration copy
         self.state = ss.StateBuffers(self.problem, self.n_chunks_cap + tail_slots, device)
         self.o = torch.empty((b_, cfg.n_queries, cfg.n_q_heads, d), dtype=torch.float32, device=device)
         self.lse = torch.empty((b_, cfg.n_queries, cfg.n_q_heads), dtype=torch.float32, device=device)
@@ -449,6 +460,7 @@ class TieredRound:
                              self.mask_out, self.tail_slots, st, n_chunks, cs)
         ss.ss_merge_states(self.problem, st, None, self.o, self.lse, cs)
         torch.cuda.current_stream().wait_stream(cs)
+        self.finalize()
         return self.o, self.lse
 
     def commit(self, accepted):
@@ -462,18 +474,43 @@ class TieredRound:
         self.C = [c + int(a) for c, a in zip(self.C, accepted)]
         self._check_capacity()
 
-    def migrate(self):
+    def migrate(self, overlap=None):
         """Eq. (5) for every request; [H_b, E_b) goes to the host store, then
-        the tail is compacted so that row 0 is token E_b. Returns E."""
+        the tail is compacted so that row 0 is token E_b. Returns E. With
+        overlap (default: overlap_migration) the copies are only started
+        (see __init__)."""
+        overlap = self.overlap if overlap is None else overlap
+        self.finalize()
         ends = [ss.ss_tier_migration_end(h, c, self.tail_target, self.gran) for h, c in zip(self.H, self.C)]
         if all(e == h for e, h in zip(ends, self.H)):
             return ends
         cur = torch.cuda.current_stream()
-        self.copy_stream.wait_stream(cur)
+        if overlap and self.migrate_stream is None:
+            self.migrate_stream = torch.cuda.Stream(device=self.device)
+        stream = self.migrate_stream if overlap else self.copy_stream
+        stream.wait_stream(cur)
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
         ss.ss_tier_migrate(self.problem, self.tail_view(), self.H, self.H, ends, self.host_kv, self.chunk_len,
-                           self.n_chunks_cap, self.copy_stream)
+                           self.n_chunks_cap, stream)
+        t1.record(stream)
+        self.last_migration = (t0, t1)
+        self.pending = (ends, t1)
+        if not overlap:
+            self.finalize()
+        return ends
+
+    def finalize(self):
+        """Completes a migration whose copies were started: once they have
+        landed (stream order, no host wait), the tail is compacted so that
+        row 0 is token E_b, and H becomes E (section 4.1: H moves only after
+        the copy)."""
+        if self.pending is None:
+            return
+        ends, landed = self.pending
+        cur = torch.cuda.current_stream()
         # the sealed range is reclaimed on the GPU only after its copy landed
-        cur.wait_stream(self.copy_stream)
+        cur.wait_event(landed)
         nxt = 1 - self.cur
         k, v = self.tails[nxt]
         ss.ss_kv_copy_rows(self.problem, self.tail_view(), [e - h for e, h in zip(ends, self.H)],
@@ -481,7 +518,7 @@ class TieredRound:
                            [c - e for c, e in zip(self.C, ends)], cur)
         self.cur = nxt
         self.H = ends
-        return ends
+        self.pending = None
 
     # ---- inspection (tests) -------------------------------------------------
     def sealed_rows(self, b, which):

@@ -26,6 +26,8 @@ SS_BF16 = 1
 
 SS_STREAM_TIMINGS = 1
 SS_STREAM_CONTINUE = 2
+SS_STREAM_POISON = 4
+SS_STREAM_DELAY = 8
 
 SS_ENGINE_AUTO = 0
 SS_ENGINE_VALU = 1
@@ -257,8 +259,9 @@ def ss_verify_round_noalloc(problem: Problem, q: torch.Tensor, hist: KVView, can
 def ss_stream_history(problem: Problem, q: torch.Tensor, host_kv: torch.Tensor, chunk_len: int, n_chunks: int,
                       staging: torch.Tensor, n_buf: int, out: StateBuffers, slot_begin: int, copy_stream,
                       compute_stream, record_timings: bool = False, req_len: Optional[torch.Tensor] = None,
-                      chunks_per_copy: int = 1, continue_ring: bool = False) -> None:
-    flags = (SS_STREAM_TIMINGS if record_timings else 0) | (SS_STREAM_CONTINUE if continue_ring else 0)
+                      chunks_per_copy: int = 1, continue_ring: bool = False, checks: int = 0) -> None:
+    """checks: SS_STREAM_POISON and/or SS_STREAM_DELAY (ordering diagnostics)."""
+    flags = (SS_STREAM_TIMINGS if record_timings else 0) | (SS_STREAM_CONTINUE if continue_ring else 0) | checks
     _check(lib().ss_stream_history(ctypes.byref(problem), q.data_ptr(), host_kv.data_ptr(), _ptr(req_len), chunk_len,
                                    n_chunks, chunks_per_copy, staging.data_ptr(), n_buf, ctypes.byref(out.struct),
                                    slot_begin, _stream(copy_stream), _stream(compute_stream), flags))

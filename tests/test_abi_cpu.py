@@ -172,7 +172,7 @@ def test_candidates_and_stream_reject():
                              1, 2, 0)
     assert rc == ss.SS_ERR_INVALID_ARG          # chunks_per_copy 0
     rc = L.ss_stream_history(ctypes.byref(p), 4096, 4096, None, 64, 4, 1, 8192, 2, ctypes.byref(_state(4).struct), 0,
-                             1, 2, 4)
+                             1, 2, 16)
     assert rc == ss.SS_ERR_INVALID_ARG          # unknown flag
     rc = L.ss_merge_states(ctypes.byref(p), ctypes.byref(_state().struct), None, None, 4096, None)
     assert rc == ss.SS_ERR_INVALID_ARG

@@ -335,6 +335,42 @@ def test_streamed_matches_resident_and_oracle(n_buf, per_copy):
     assert rounds.exposed_wait((c0, c1, k0, k1)) >= 0
 
 
+@pytest.mark.parametrize("n_buf,per_copy", [(1, 1), (2, 1), (2, 2), (3, 2)])
+@pytest.mark.parametrize("checks", ["poison", "delay", "poison+delay"])
+def test_streamed_ordering_checks(n_buf, per_copy, checks):
+    """Ordering of the streaming pipeline (SpecStream section 4.2: a staging
+    buffer takes the next chunk only after every query of the group has
+    attended the chunk it holds). SS_STREAM_POISON overwrites each buffer
+    with NaN right after its wait for the last reader and before its copy,
+    so a kernel still reading it, or reading it before the copy landed,
+    would see NaN; SS_STREAM_DELAY holds the copy stream ~2 ms before every
+    copy, so compute that did not wait for its chunk would read the previous
+    contents. The result must match the oracle, with no NaN."""
+    cfg = SMALL["c5_small"].with_(hist_len=8 * 256, chunk_len=256)
+    flag = {"poison": ss.SS_STREAM_POISON, "delay": ss.SS_STREAM_DELAY,
+            "poison+delay": ss.SS_STREAM_POISON | ss.SS_STREAM_DELAY}[checks]
+    log(f"[stream checks] {checks}, n_buf {n_buf}, chunks per copy {per_copy}")
+    inp = wl.make_inputs(cfg)
+    o_ref, lse_ref = oracle_round(inp)
+    srd = rounds.StreamedRound(inp, n_buf=n_buf, chunks_per_copy=per_copy)
+    for rep in range(2):
+        srd.o.fill_(float("nan"))
+        srd.run(record_timings=True, checks=flag)
+        torch.cuda.synchronize()
+        o, lse = srd.o.cpu().numpy(), srd.lse.cpu().numpy()
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+        compare(cfg, o, lse, o_ref, lse_ref)
+        c0, c1, k0, k1 = ss.ss_stream_timings(srd.n_chunks)
+        assert all(c1[j] <= k0[j] + 1e-3 for j in range(srd.n_chunks))
+        if flag & ss.SS_STREAM_DELAY:
+            # every copy group waited ~2 ms on the host before its copy
+            starts = sorted(set(c0))
+            assert all(b - a >= 1.5 for a, b in zip(starts, starts[1:])), starts
+    # after the round the buffers hold the last copied chunks, not the poison
+    last = srd.staging[(srd.n_chunks // per_copy - 1) % n_buf].view(per_copy, -1)[-1]
+    assert torch.equal(last.cpu(), srd.host_kv[srd.n_chunks - 1])
+
+
 @pytest.mark.parametrize("n_buf,per_copy", [(1, 1), (2, 1), (2, 2), (3, 1)])
 def test_layered_stream_with_prefetch(n_buf, per_copy):
     """Three layers, each with its own host-resident history, the staging

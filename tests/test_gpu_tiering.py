@@ -59,8 +59,18 @@ CASES = {
 }
 
 
+def _check_store(tr, hist_k, hist_v, c_ref):
+    for b in range(len(c_ref)):
+        for which, src in (("k", hist_k), ("v", hist_v)):
+            assert torch.equal(tr.sealed_rows(b, which), src[b][:, :tr.H[b]]), (b, which, "host store")
+            assert torch.equal(tr.tail_rows(b, which), src[b][:, tr.H[b]:c_ref[b]]), (b, which, "tail")
+
+
 @pytest.mark.parametrize("name", list(CASES))
-def test_tiered_rounds(name):
+@pytest.mark.parametrize("overlap", [False, True])
+def test_tiered_rounds(name, overlap):
+    """overlap: migrate() only starts the copies; the next round's
+    verification runs while they are in flight and H advances after it."""
     case = CASES[name]
     cfg = case["cfg"]
     b_, hq, hkv, d, nq = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.n_queries
@@ -72,7 +82,8 @@ def test_tiered_rounds(name):
     hist_v = [draw((hkv, n, d), gen, dt) for n in lens]
     log(f"[tiered] {name}: lengths {lens}, T={case['tail']}, g={case['gran']}, C={case['chunk']}")
     tr = rounds.TieredRound(cfg, hist_k, hist_v, tail_target=case["tail"], gran=case["gran"],
-                            chunk_len=case["chunk"], max_tokens=max(lens) + 16 * nq * case["rounds"])
+                            chunk_len=case["chunk"], max_tokens=max(lens) + 16 * nq * case["rounds"],
+                            overlap_migration=overlap)
     # the oracle's Eq. (5) trajectory
     h_ref = [tiering.migration_end(0, n, case["tail"], case["gran"]) for n in lens]
     assert tr.H == h_ref
@@ -86,9 +97,13 @@ def test_tiered_rounds(name):
         if cfg.mask == "tree":
             parents = np.stack([wl.draw_tree(int(rng.integers(1000)), b, nq, cfg.tree_depth_cap) for b in range(b_)])
         log(f"  round {r}: H={tr.H} C={tr.C}")
+        h_want = list(tr.pending[0]) if tr.pending is not None else list(tr.H)
         tr.verify(q.cuda(), kc.cuda(), vc.cuda(),
                   None if parents is None else torch.as_tensor(parents, dtype=torch.int32, device="cuda"))
         torch.cuda.synchronize()
+        # a migration started in the previous round has completed behind it
+        assert tr.pending is None and tr.H == h_want
+        _check_store(tr, hist_k, hist_v, c_ref)
         vis = np.stack([oracle.tree_mask(parents[b]) if parents is not None else oracle.chain_mask(nq)
                         for b in range(b_)])
         o_ref, lse_ref = oracle.attention_reference(
@@ -118,13 +133,18 @@ def test_tiered_rounds(name):
         ends = tr.migrate()
         torch.cuda.synchronize()
         want = [tiering.migration_end(h, c, case["tail"], case["gran"]) for h, c in zip(h_before, c_ref)]
-        assert ends == want and tr.H == want
+        assert ends == want
+        if overlap and want != h_before:
+            assert tr.H == h_before and tr.pending is not None     # H moves only once the copy landed
+        else:
+            assert tr.H == want
+            _check_store(tr, hist_k, hist_v, c_ref)
         moved += sum(e > h for e, h in zip(want, h_before))
         for b in range(b_):
             # rollback stayed disjoint from the host history
             assert not tiering.overlaps((c_ref[b], c_ref[b] + nq - acc[b]), (0, h_before[b]))
-            for which, src in (("k", hist_k), ("v", hist_v)):
-                assert torch.equal(tr.sealed_rows(b, which), src[b][:, :tr.H[b]]), (b, which, "host store")
-                assert torch.equal(tr.tail_rows(b, which), src[b][:, tr.H[b]:c_ref[b]]), (b, which, "tail")
+    tr.finalize()
+    torch.cuda.synchronize()
+    _check_store(tr, hist_k, hist_v, c_ref)
     if case["gran"] <= 48:
         assert moved >= 2, "the case meant to migrate between rounds never did"
