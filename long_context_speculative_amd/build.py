@@ -1,8 +1,9 @@
 """Builds libssverify.so (HIP, gfx950) in-tree, next to this file.
 
-    python -m long_context_speculative_amd.build
+    python -m long_context_speculative_amd.build [--asan]
 
-Every call recompiles. Objects go to _build/ at the repository root; the
+Every call recompiles. --asan builds the host-sanitizer variant into
+_build/asan/ (for the CPU tests; see ASAN_FLAGS). Objects go to _build/ at the repository root; the
 shared library lands in the package directory, where the binding loads it.
 """
 
@@ -51,26 +52,44 @@ def _run(cmd):
     return r.stdout
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# Host AddressSanitizer build: the host side of every file (argument
+# validation, plans, tree masks, copy address arithmetic, the streaming
+# bookkeeping) instrumented, device code built as usual. The flags apply to
+# the host compilation only. Loaded through SS_VERIFY_LIB with the ASan
+# runtime preloaded (see asan_runtime()).
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libssverify.so")
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's ASan runtime (to LD_PRELOAD into Python)."""
+    return _run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"]).strip()
+
+
+def build(verbose: bool = False, asan: bool = False) -> str:
+    out_dir = ASAN_DIR if asan else BUILD
+    lib = ASAN_LIB if asan else LIB
+    extra = ASAN_FLAGS if asan else []
+    os.makedirs(out_dir, exist_ok=True)
     cc = hipcc()
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(out_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([cc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *HIP_FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(len(cmds)) as ex:
         outs = list(ex.map(_run, cmds))
-    tmp = LIB + ".tmp"
-    outs.append(_run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]))
-    os.replace(tmp, LIB)
+    tmp = lib + ".tmp"
+    outs.append(_run([cc, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, *objs, "-o", tmp]))
+    os.replace(tmp, lib)
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, asan="--asan" in sys.argv))

@@ -14,7 +14,10 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssverify.so")
+# The in-tree build; SS_VERIFY_LIB names another build of the same library
+# (the host AddressSanitizer build of build.py --asan, for the CPU tests).
+LIB_PATH = os.environ.get("SS_VERIFY_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libssverify.so")
 
 SS_OK = 0
 SS_ERR_INVALID_ARG = -1
