@@ -539,11 +539,13 @@ def resident_record(cfg, steps, warmup, cps, engine, split, probe):
                 "ms_per_launch": round(ms_chunk, 4), "algorithmic_flops_per_launch": flops,
                 "algorithmic_bytes_per_launch": alg,
                 "hbm_GBps_algorithmic": round(alg / (ms_chunk * 1e-3) / 1e9, 2)}
-        clock = read_profile_value(cfg, "sustained_clock_GHz")
-        if clock:
-            # the same fraction against the dense peak at the clock the
-            # launch sustained (rocprofv3 GRBM_GUI_ACTIVE over its duration)
-            roof["sustained_clock_GHz"] = clock
+        cycles = read_profile_value(cfg, "grbm_active_cycles_per_xcd")
+        if cycles:
+            # The launch's active GPU cycles (rocprofv3 GRBM_GUI_ACTIVE, per
+            # XCD) over its duration here is the clock it sustained; the dense
+            # peak scales with the clock (2.5 PFLOP/s at 2.4 GHz).
+            clock = cycles / (ms_chunk * 1e-3) / 1e9
+            roof["sustained_clock_GHz"] = round(clock, 3)
             roof["frac_at_sustained_clock"] = round(tflops / (MFMA_BF16_PEAK_TFLOPS * clock / 2.4), 4)
     else:
         achieved = alg / (ms_chunk * 1e-3) / 1e9
