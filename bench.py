@@ -17,7 +17,9 @@ layer (uniform 32768 tokens, HBM-bound) and the 72B-like tree workload
 Prints ONE JSON line. value = effective KV GB/s = (history + candidate K/V
 bytes) / time per step. Also reported: verified query-tokens/s, the history
 launch's roofline (algorithmic bytes, or FLOPs for wide row groups, per
-launch / its event-timed duration), the streamed path on the streamed
+launch / its event-timed duration; for the MFMA-bound launch also against
+a same-run matrix-core probe on N(0,1) bf16 operands, whose rate sets the
+attainable ceiling for such data), the streamed path on the streamed
 workload (host-link GB/s against a plain pinned H2D copy of the same bytes),
 and the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
@@ -294,6 +296,32 @@ def read_probe(n_bytes=2 << 30, reps=10):
     del src
     torch.cuda.empty_cache()
     return out
+
+
+def mfma_probe(iters=4096, reps=20):
+    """Same-run matrix-core reference (ss_mfma_probe): bf16 MFMA products and
+    nothing else, two work-groups of four waves per CU (two waves per SIMD, as
+    the wide-row kernel runs), on N(0,1) bf16 operands like the attention
+    inputs. The clock the chip holds depends on the operand values, so this is
+    the attainable rate for such data; the published peak assumes 2.4 GHz."""
+    from long_context_speculative_amd import ssverify as ss
+    cus = rounds.device_cus()
+    ops = torch.randn(1 << 22, dtype=torch.bfloat16, device="cuda")
+    sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+    wgs = 2 * cus
+    settle(lambda: ss.ss_mfma_probe(ops, iters, wgs, sink), 0.2)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        flops = ss.ss_mfma_probe(ops, iters, wgs, sink)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    tflops = flops / (ms * 1e-3) / 1e12
+    del ops
+    torch.cuda.empty_cache()
+    return {"TFLOPs": round(tflops, 1), "frac_of_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "ms_per_launch": round(ms, 4), "work_groups": wgs, "operands": "N(0,1) bf16"}
 
 
 def time_sparse(cfg, block_len=512, k=16, reps=20):
@@ -593,6 +621,8 @@ def main():
     ap.add_argument("--no-sparse", action="store_true", help="skip the block-statistics / sparse leg")
     ap.add_argument("--streamed-only", action="store_true",
                     help="run only the streamed leg (c5_streamed) and print its record (for traces of that path)")
+    ap.add_argument("--mfma-probe-only", action="store_true",
+                    help="only the matrix-core reference (ss_mfma_probe) on N(0,1) bf16 operands")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection pass: one plain elementwise copy of 1 GiB (the calibration kernel "
                          "of known size), then one step of the workload; prints nothing else")
@@ -605,6 +635,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.mfma_probe_only:
+        print(json.dumps({"mfma_probe": mfma_probe()}), flush=True)
+        return
     if args.streamed_only:
         print(json.dumps({"streamed": time_streamed(wl.CONFIGS["c5_streamed"])}), flush=True)
         return
@@ -646,6 +679,10 @@ def main():
             out[key] = {k: rec[k] for k in ("config", "ms_per_step", "effective_KV_GBps", "pct_hbm_peak",
                                              "query_tokens_per_s", "roofline")}
             torch.cuda.empty_cache()
+        # the matrix-core reference after the timed launches (it heats the chip)
+        out["mfma_probe"] = mfma_probe()
+        roof = out["c4"]["roofline"]
+        roof["frac_of_mfma_probe"] = round(roof["achieved"] / out["mfma_probe"]["TFLOPs"], 4)
     if not args.no_sparse:
         out["sparse"] = time_sparse(wl.CONFIGS["c2_qwen3_8b"])
         torch.cuda.empty_cache()

@@ -55,7 +55,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 13
+#define SS_ABI_VERSION 14
 
 /* status codes */
 #define SS_OK 0
@@ -487,6 +487,24 @@ SS_API int32_t ss_kv_copy_rows(const ss_problem_t* problem, const ss_kv_view_t* 
  */
 SS_API int32_t ss_read_probe(const void* src, int64_t bytes, int32_t n_work_groups, uint32_t* sink,
                              ss_stream_t stream);
+
+/*
+ * ss_mfma_probe -- measurement reference, not part of the method: the bf16
+ * matrix-core rate the device sustains on given operand values. n_work_groups
+ * work-groups of four waves; each wave loads 16 operand fragments (8 bf16 per
+ * lane each: 8192 bf16, a window of operands chosen by the wave's index) once
+ * and then runs iters x 8 independent v_mfma_f32_16x16x32_bf16 products on
+ * them, nothing else in its loop. One launch performs
+ * n_work_groups * 4 * iters * 8 * 16384 floating-point operations.
+ * operands: device bf16, 16-byte aligned, n_operands >= 8192 (more gives the
+ * waves different windows). sink: device float [256], written only for one
+ * particular result value. The clock a launch holds depends on the operand
+ * values (the chip's power draw does), so the benchmark fills operands like
+ * the attention inputs (N(0,1) bf16) and reports the MFMA-bound kernel against
+ * this rate as well as against the published peak.
+ */
+SS_API int32_t ss_mfma_probe(const void* operands, int64_t n_operands, int32_t iters, int32_t n_work_groups,
+                             float* sink, ss_stream_t stream);
 
 /*
  * Host-side helpers that expose the integer rules the kernels apply. They run

@@ -980,6 +980,17 @@ extern "C" SS_API int32_t ss_read_probe(const void* src, int64_t bytes, int32_t 
     return ok();
 }
 
+extern "C" SS_API int32_t ss_mfma_probe(const void* operands, int64_t n_operands, int32_t iters,
+                                        int32_t n_work_groups, float* sink, ss_stream_t stream) {
+    if (!operands || !sink) return fail(SS_ERR_INVALID_ARG, "operands or sink is NULL");
+    if (!aligned16(operands) || n_operands < mfma_probe_wave_elems() || iters <= 0 || n_work_groups <= 0)
+        return fail(SS_ERR_INVALID_ARG, "operands must be 16-byte aligned with n_operands >= %lld, iters > 0, "
+                    "n_work_groups > 0", (long long)mfma_probe_wave_elems());
+    hipError_t e = launch_mfma_probe(operands, n_operands, iters, n_work_groups, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(SS_ERR_HIP, "matrix-core probe launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 extern "C" SS_API int32_t ss_tree_mask_host(const int32_t* parents, int32_t n, uint64_t* out) {
     if (!parents || !out) return fail(SS_ERR_INVALID_ARG, "parents or out is NULL");
     if (n < 0 || n > 64) return fail(SS_ERR_INVALID_ARG, "n must be in [0, 64]");

@@ -363,6 +363,10 @@ int cand_row_blocks(int rows);
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream);
 hipError_t launch_importance(const ImportanceParams& p, hipStream_t stream);
 hipError_t launch_read_probe(const void* src, int64_t bytes, int32_t n_wg, uint32_t* sink, hipStream_t stream);
+// bf16 elements one wave of the matrix-core probe loads (its operand window).
+int64_t mfma_probe_wave_elems();
+hipError_t launch_mfma_probe(const void* ops, int64_t n_ops, int32_t iters, int32_t n_wg, float* sink,
+                             hipStream_t stream);
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 // Empty states (m = -inf, l = 0, acc = 0) in rows [row_begin, row_begin +
 // n_rows) of a state buffer (a row: head_dim accumulators, one m, one l).

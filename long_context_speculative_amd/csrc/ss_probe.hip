@@ -1,8 +1,18 @@
-// Same-run HBM read reference of libssverify's measurement: how fast this
-// device streams a buffer it only reads, with the history kernels' load
-// shape (16-byte non-temporal loads, eight in flight per lane) and either
-// their launch shape (one work-group per CU, each a contiguous span) or
-// more work-groups. The history kernels' bandwidth is reported against it.
+// Same-run references of libssverify's measurement.
+//
+// Read probe: how fast this device streams a buffer it only reads, with the
+// history kernels' load shape (16-byte non-temporal loads, eight in flight per
+// lane) and either their launch shape (one work-group per CU, each a
+// contiguous span) or more work-groups. The history kernels' bandwidth is
+// reported against it.
+//
+// Matrix-core probe: the bf16 MFMA rate this device sustains on given operand
+// data, with nothing but matrix instructions in the loop. The MI355X's power
+// draw, and with it the clock it holds, depends on the operand values: the
+// same instruction stream runs near the 2.4 GHz peak clock on constant
+// operands and well below it on random ones, so the rate on operands drawn
+// like the workload's is the attainable ceiling the MFMA-bound kernel is
+// reported against, beside the published peak.
 
 #include "ss_common.h"
 
@@ -33,7 +43,53 @@ __global__ __launch_bounds__(kThreads) void read_probe_kernel(const u32x4* __res
     if (acc == 0x9e3779b9u) sink[blockIdx.x & 255] = acc;
 }
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+constexpr int kMfmaSets = 8;    // operand sets per wave (registers), rotated over the chains
+constexpr int kMfmaChains = 8;  // independent accumulators: no product waits for the previous one
+constexpr int kMfmaWaveElems = 2 * kMfmaSets * 64 * 8;  // bf16 a wave loads (A and B sets)
+
+// Each wave loads its operand sets from a window of the buffer once, then runs
+// iters x kMfmaChains 16x16x32 bf16 products, chain j using A set j and
+// B set j+3 (mod kMfmaSets).
+__global__ __launch_bounds__(kThreads, 2) void mfma_probe_kernel(const uint16_t* __restrict__ ops, int64_t windows,
+                                                              int iters, float* sink) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const uint16_t* base = ops + (wave % windows) * kMfmaWaveElems;
+    bf16x8 a[kMfmaSets], b[kMfmaSets];
+#pragma unroll
+    for (int s = 0; s < kMfmaSets; ++s) {
+        a[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + (s * 64 + lane) * 8));
+        b[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + ((kMfmaSets + s) * 64 + lane) * 8));
+    }
+    floatx4 c[kMfmaChains];
+#pragma unroll
+    for (int j = 0; j < kMfmaChains; ++j) c[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < kMfmaChains; ++j)
+            c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j % kMfmaSets], b[(j + 3) % kMfmaSets], c[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMfmaChains; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+    // keeps the products alive; the sink is written only for one specific value
+    if (s == 1234.5f) sink[blockIdx.x & 255] = s;
+}
+
 }  // namespace
+
+int64_t mfma_probe_wave_elems() { return kMfmaWaveElems; }
+
+hipError_t launch_mfma_probe(const void* ops, int64_t n_ops, int32_t iters, int32_t n_wg, float* sink,
+                             hipStream_t stream) {
+    const int64_t windows = n_ops / kMfmaWaveElems;
+    if (n_wg <= 0 || iters <= 0 || windows <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(mfma_probe_kernel, dim3(n_wg), dim3(kThreads), 0, stream, static_cast<const uint16_t*>(ops),
+                       windows, iters, sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_read_probe(const void* src, int64_t bytes, int32_t n_wg, uint32_t* sink, hipStream_t stream) {
     const int64_t n_vec = bytes / 16;

@@ -41,7 +41,7 @@ EXPORTED = ("ss_abi_version", "ss_last_error", "ss_state_bytes", "ss_verify_chun
             "ss_slot_tokens_host", "ss_history_plan_host", "ss_tier_migration_end", "ss_tier_migrate",
             "ss_kv_copy_rows", "ss_verify_chunk_gathered", "ss_block_importance", "ss_select_blocks",
             "ss_read_probe", "ss_block_stats_bytes", "ss_block_importance_stats", "ss_verify_round",
-            "ss_verify_round_noalloc")
+            "ss_verify_round_noalloc", "ss_mfma_probe")
 
 
 class SSError(RuntimeError):
@@ -129,6 +129,8 @@ def lib() -> ctypes.CDLL:
         L.ss_select_blocks.argtypes = [P(Problem), VP, I32, VP, I32, I32, I32, VP, VP]
         L.ss_read_probe.restype = I32
         L.ss_read_probe.argtypes = [VP, I64, I32, VP, VP]
+        L.ss_mfma_probe.restype = I32
+        L.ss_mfma_probe.argtypes = [VP, I64, I32, I32, VP, VP]
         _lib = L
     return _lib
 
@@ -381,3 +383,14 @@ def ss_read_probe(src: torch.Tensor, n_work_groups: int, sink: torch.Tensor, str
     """Reads all of src (a 16-byte multiple) with n_work_groups contiguous spans."""
     _check(lib().ss_read_probe(src.data_ptr(), src.numel() * src.element_size(), n_work_groups, sink.data_ptr(),
                                _stream(stream)))
+
+
+MFMA_PROBE_FLOPS_PER_WAVE_ITER = 8 * 16384  # eight 16x16x32 products per wave and iteration
+
+
+def ss_mfma_probe(operands: torch.Tensor, iters: int, n_work_groups: int, sink: torch.Tensor, stream=None) -> int:
+    """Matrix-core probe over bf16 operands (>= 8192 elements); returns the
+    launch's floating-point operation count (work-groups of four waves)."""
+    _check(lib().ss_mfma_probe(operands.data_ptr(), operands.numel(), iters, n_work_groups, sink.data_ptr(),
+                               _stream(stream)))
+    return n_work_groups * 4 * iters * MFMA_PROBE_FLOPS_PER_WAVE_ITER

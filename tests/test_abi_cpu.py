@@ -406,3 +406,21 @@ def test_tier_copies_reject():
                              rows(30, 0), None) == ss.SS_ERR_INVALID_ARG      # past the destination rows
     assert L.ss_kv_copy_rows(ctypes.byref(p), ctypes.byref(tail), rows(0, 0), ctypes.byref(tail), rows(0, 0),
                              rows(-1, 0), None) == ss.SS_ERR_INVALID_ARG
+
+
+def test_probes_reject():
+    L = ss.lib()
+    # read probe: NULL buffers, misalignment, no bytes, no work-groups
+    assert L.ss_read_probe(None, 4096, 1, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_read_probe(4096, 4096, 1, None, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_read_probe(4100, 4096, 1, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_read_probe(4096, 8, 1, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_read_probe(4096, 4096, 0, 4096, None) == ss.SS_ERR_INVALID_ARG
+    # matrix-core probe: a wave needs a window of 8192 bf16 operands
+    assert L.ss_mfma_probe(None, 8192, 1, 1, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_mfma_probe(4096, 8192, 1, 1, None, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_mfma_probe(4104, 8192, 1, 1, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_mfma_probe(4096, 8191, 1, 1, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_mfma_probe(4096, 8192, 0, 1, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert L.ss_mfma_probe(4096, 8192, 1, 0, 4096, None) == ss.SS_ERR_INVALID_ARG
+    assert "8192" in L.ss_last_error().decode()
