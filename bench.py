@@ -514,9 +514,11 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def counters_pass(cfg, cps="auto", engine="auto", split="balanced"):
+def counters_pass(cfg, cps="auto", engine="auto", split="balanced", settle_s=0.0):
     """One calibration kernel of known traffic (torch.neg over 2^30 bytes of
-    bf16: reads 1 GiB, writes 1 GiB), then one step of the workload."""
+    bf16: reads 1 GiB, writes 1 GiB), then one step of the workload; with
+    settle_s > 0, that many seconds of the same steps before the last one (so
+    the last dispatches run in the steady state the timed loops measure)."""
     src = torch.randn(1 << 29, device="cuda").to(torch.bfloat16)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -528,6 +530,8 @@ def counters_pass(cfg, cps="auto", engine="auto", split="balanced"):
     rnd = make_round(cfg, inp, cps, engine, split)
     del inp
     torch.cuda.synchronize()
+    if settle_s > 0:
+        settle(rnd.run, settle_s)
     rnd.run()
     cps = rnd.cps
     torch.cuda.synchronize()
@@ -626,6 +630,8 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection pass: one plain elementwise copy of 1 GiB (the calibration kernel "
                          "of known size), then one step of the workload; prints nothing else")
+    ap.add_argument("--counters-settle", type=float, default=0.0,
+                    help="with --counters: seconds of the same steps before the last one (steady-state dispatches)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the verification path runs on a "
@@ -646,7 +652,7 @@ def main():
         cfg = cfg.with_(n_queries=args.queries, name=f"{cfg.name}_q{args.queries}")
     cps = args.chunks_per_slot or "auto"
     if args.counters:
-        counters_pass(cfg, cps, args.engine, args.split)
+        counters_pass(cfg, cps, args.engine, args.split, args.counters_settle)
         return
     # the read reference first, while the device is in the state the timed
     # steps start from (after seconds of streaming it reads measurably slower)
