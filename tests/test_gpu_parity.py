@@ -54,6 +54,14 @@ SMALL = {
                                                            chunk_len=300),
     "wide_r192_tree": C["c4_tree_72b"].with_(batch=2, n_queries=24, hist_len=999, chunk_len=256),
     "wide_r320_tree": C["c4_tree_72b"].with_(batch=1, n_queries=40, hist_len=1200, chunk_len=1000),
+    # other GQA group sizes: one query head per KV head (plain multi-head
+    # attention), two, and sixteen (96 rows: the wide-row kernel)
+    "mha_g1": C["c2_qwen3_8b"].with_(batch=2, n_q_heads=8, n_kv_heads=8, hist_len=1234, chunk_len=512),
+    "mha_g1_tree_wide": C["c4_tree_72b"].with_(batch=1, n_q_heads=4, n_kv_heads=4, n_queries=40, hist_len=700,
+                                               chunk_len=256),
+    "gqa_g2_ragged": C["c3_internlm25_7b_ragged"].with_(batch=3, n_q_heads=8, n_kv_heads=4, hist_len=1500,
+                                                        ragged_lo=1, chunk_len=512),
+    "gqa_g16_wide": C["c2_qwen3_8b"].with_(batch=2, n_q_heads=32, n_kv_heads=2, hist_len=900, chunk_len=256),
 }
 
 
@@ -407,6 +415,10 @@ BALANCED = {
     "c1_fallback_s3": ("c1", 3),
     "wide_fallback_s3": ("wide_r96_ragged", 3),
     "c2_one_slot": ("c2_small", 1),
+    # GQA group sizes 1, 2 and 16
+    "mha_g1_s3": ("mha_g1", 3),
+    "gqa_g2_ragged_s4": ("gqa_g2_ragged", 4),
+    "gqa_g16_wide_s3": ("gqa_g16_wide", 3),
 }
 
 
