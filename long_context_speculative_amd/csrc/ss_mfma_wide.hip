@@ -13,7 +13,7 @@
 //     overlaps the other's matrix work;
 //   - key tiles of KT (32, or 64 for groups of eight waves) are copied once
 //     per work-group into LDS, K and V both in their natural [key][feature]
-//     layout (rows padded so the reads are free of bank conflicts), in a ring
+//     layout (rows padded; see kRow and kVRow), in a ring
 //     of three buffers, loads issued three tiles ahead; a 64-key tile halves
 //     the barriers and row-maximum reductions per key (about 5% on a 512-row
 //     group) at 105 KB of LDS, which one eight-wave group per CU affords;
@@ -50,8 +50,14 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int kTile = 32;       // keys per MFMA sub-tile (KT keys per iteration)
-constexpr int kRow = D + 8;     // bf16 per staged K row (16-byte pad: 16-byte reads of 16 rows hit 64 banks)
-constexpr int kVRow = D + 16;   // bf16 per staged V row (32-byte pad: 8-byte transposing reads of 8 rows hit 64 banks)
+// Row pitches of the staged tiles. The transposing V reads are free of bank
+// conflicts at a 32-byte pad. The 16-byte K fragment reads are free of them at
+// a 32-byte pad too, but at the 16-byte pad used here they spend about a third
+// of their LDS cycles in conflicts; the conflict-free pitch is still slower on
+// MI355X: the launch is held by the chip's power limit, and with the stall
+// cycles gone it runs at a lower clock (fewer cycles, longer time).
+constexpr int kRow = D + 8;     // bf16 per staged K row (16-byte pad)
+constexpr int kVRow = D + 16;   // bf16 per staged V row (32-byte pad)
 constexpr int kNS = D / 32;     // 32-feature steps of S = K Q^T
 constexpr int kNXT = D / 16;    // 16-feature tiles of O^T
 constexpr float kGrowLog2 = 8.f;  // rescale threshold (log2 units)
