@@ -98,37 +98,46 @@ def source_hash(cfg, engine="auto") -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(cfg, split, fused):
+def profile_matches(text, cfg, split, fused, slots) -> bool:
+    """Whether a committed counter summary was taken on the current kernel
+    source with the same history cut, candidate placement and slot count."""
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_split = re.search(r"history_split:\s*(\w+)", text)
+    m_fused = re.search(r"fused_candidates:\s*(\w+)", text)
+    m_slots = re.search(r"history_slots:\s*(\d+)", text)
+    if not m_hash or m_hash.group(1) != source_hash(cfg):
+        return False
+    if (m_split.group(1) if m_split else "chunks") != split:
+        return False
+    if (m_fused.group(1) == "True" if m_fused else False) != fused:
+        return False
+    return m_slots is not None and int(m_slots.group(1)) == slots
+
+
+def read_traffic(cfg, split, fused, slots):
     """HBM bytes per chunk-kernel launch from the committed rocprofv3 counter
     summary, if it was taken on the current kernel source with the same
-    history cut and candidate placement; else None."""
+    history cut, candidate placement and slot count; else None."""
     path = os.path.join(ROOT, "profiles", f"chunk_kernel_{cfg.name}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    m_split = re.search(r"history_split:\s*(\w+)", text)
-    m_fused = re.search(r"fused_candidates:\s*(\w+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(cfg):
-        return None
-    if (m_split.group(1) if m_split else "chunks") != split:
-        return None
-    if (m_fused.group(1) == "True" if m_fused else False) != fused:
+    if not m_bytes or not profile_matches(text, cfg, split, fused, slots):
         return None
     return float(m_bytes.group(1))
 
 
-def read_profile_value(cfg, key):
+def read_profile_value(cfg, key, split, fused, slots):
     """A number recorded in the committed counter summary of cfg's history
-    launch, if it was taken on the current kernel source; else None."""
+    launch, if it was taken in the same configuration (profile_matches);
+    else None."""
     path = os.path.join(ROOT, "profiles", f"chunk_kernel_{cfg.name}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
     m = re.search(re.escape(key) + r":\s*([0-9.eE+]+)", text)
-    if not m_hash or not m or m_hash.group(1) != source_hash(cfg):
+    if not m or not profile_matches(text, cfg, split, fused, slots):
         return None
     return float(m.group(1))
 
@@ -560,7 +569,7 @@ def resident_record(cfg, steps, warmup, cps, engine, split, probe):
     hist_b, cand_b = kv_bytes(cfg, hist_len)
     gbs = (hist_b + cand_b) / (ms_step * 1e-3) / 1e9
     alg = launch_bytes(cfg, hist_len, rnd)
-    traffic = read_traffic(cfg, rnd.split, rnd.fused) if engine == "auto" else None
+    traffic = read_traffic(cfg, rnd.split, rnd.fused, rnd.n_hist_slots) if engine == "auto" else None
     if cfg.rows > 32:
         # wide row groups: the chunk kernel is bound by the matrix cores
         flops = chunk_kernel_flops(cfg, hist_len)
@@ -571,7 +580,7 @@ def resident_record(cfg, steps, warmup, cps, engine, split, probe):
                 "ms_per_launch": round(ms_chunk, 4), "algorithmic_flops_per_launch": flops,
                 "algorithmic_bytes_per_launch": alg,
                 "hbm_GBps_algorithmic": round(alg / (ms_chunk * 1e-3) / 1e9, 2)}
-        cycles = read_profile_value(cfg, "grbm_active_cycles_per_xcd")
+        cycles = read_profile_value(cfg, "grbm_active_cycles_per_xcd", rnd.split, rnd.fused, rnd.n_hist_slots)
         if cycles:
             # The launch's active GPU cycles (rocprofv3 GRBM_GUI_ACTIVE, per
             # XCD) over its duration here is the clock it sustained; the dense

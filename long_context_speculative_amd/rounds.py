@@ -51,9 +51,16 @@ def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
     the longest stream does not force ranges longer than an even share over
     the launch (wgs_per_cu work-groups per compute unit), plus one for the
     range boundaries. Uniform lengths: one chunk per work-group of that
-    launch. Wide row groups use the fixed cut of 4 chunks per slot."""
+    launch. Wide row groups on the MFMA kernel: one wave of work-groups
+    (8-wave groups of 256 rows, one per compute unit, or 4-wave groups of 128
+    rows, two per unit), the slot count ss_verify_round picks; other wide
+    shapes use the fixed cut of 4 chunks per slot."""
     pads = [-(-int(n) // 128) * 128 for n in hist_len]
     pad_max = max(pads, default=0)
+    if cfg.rows > 32 and mfma_fuses_candidates(cfg, engine):
+        per_group, per_cu = (256, 1) if cfg.rows > 128 else (128, 2)
+        groups = -(-cfg.rows // per_group)
+        return min(64, max(1, per_cu * cus // (cfg.batch * cfg.n_kv_heads * groups)))
     if cfg.rows > 32:
         return max(1, -(-pad_max // (4 * cfg.chunk_len)))
     wave = wgs_per_cu(cfg, engine) * cus
