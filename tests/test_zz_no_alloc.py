@@ -4,7 +4,8 @@ against ss_verify_round on a caller-allocated workspace (the same kernels
 and the same cut, so the results are bit for bit the same) and against the
 fp64 oracle at the parity tolerance, over consecutive calls whose later
 inputs are smaller than the first (the array keeps the earlier call's
-contents)."""
+contents); and captured in a HIP graph and replayed, against the eager
+call."""
 
 import sys
 
@@ -92,3 +93,49 @@ def test_noalloc_round_rejects_oversized_state():
     assert e.value.code == ss.SS_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert (rnd.o == 7.0).all()
+
+
+GRAPH_CASES = {
+    "narrow_ragged": C["c3_internlm25_7b_ragged"].with_(batch=8, hist_len=5000, ragged_lo=1, chunk_len=1024),
+    "wide_tree": C["c4_tree_72b"].with_(batch=2, hist_len=2600, chunk_len=1024),
+}
+
+
+@pytest.mark.parametrize("name", list(GRAPH_CASES))
+def test_noalloc_round_replayed_from_a_graph(name):
+    """The callers the entry point is for capture it: the round recorded in a
+    HIP graph (torch.cuda.graph on the capturing stream) and replayed four
+    times, with other device work and a synchronisation between replays and
+    the outputs poisoned before each, gives the eager call's O, lse and mask
+    bit for bit every time."""
+    cfg = GRAPH_CASES[name]
+    log(f"[no-alloc graph] {name}: B={cfg.batch} rows={cfg.rows} history<={cfg.hist_len}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp)
+    args = (rnd.problem, rnd.q, rnd.hist_view, rnd.cand_view, rnd.parents, rnd.mask_out, rnd.o, rnd.lse)
+    ss.ss_verify_round_noalloc(*args)
+    torch.cuda.synchronize()
+    o_ref, lse_ref, mask_ref = rnd.o.clone(), rnd.lse.clone(), rnd.mask_out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ss.ss_verify_round_noalloc(*args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ss.ss_verify_round_noalloc(*args)
+    other = torch.empty(1 << 22, device="cuda")
+    for rep in range(4):
+        rnd.o.fill_(float("nan"))
+        rnd.lse.fill_(float("nan"))
+        rnd.mask_out.fill_(-1)
+        other.normal_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(rnd.o, o_ref), (name, rep)
+        assert torch.equal(rnd.lse, lse_ref), (name, rep)
+        assert torch.equal(rnd.mask_out, mask_ref), (name, rep)
+        log(f"  replay {rep}: identical to the eager call")
+    del graph
