@@ -724,3 +724,43 @@ def test_size_extremes(name):
         log(f"[extremes] {name}: oracle slice b={b} g={g}")
         o_ref, lse_ref = oracle_round(inp, requests=[b], kv_heads=[g])
         compare(cfg, o, lse, o_ref, lse_ref, rows_of(cfg, b, g))
+
+
+def _random_case(seed):
+    """A seeded random shape within the library's limits: dtype, head_dim,
+    GQA group, queries and mask, lengths (uniform or ragged, head- or
+    token-packed), chunk length, history cut, K/V layout, chunks per slot."""
+    r = np.random.default_rng(7000 + seed)
+    dtype = "f32" if r.random() < 0.15 else "bf16"
+    head_dim = 64 if r.random() < 0.2 else 128
+    n_kv = int(r.choice([1, 2, 3, 4]))
+    group = int(r.choice([1, 2, 3, 4, 5, 8, 16]))
+    mask = "tree" if r.random() < 0.4 else "causal"
+    n_q = int(r.integers(2, 65)) if mask == "tree" else int(r.integers(1, 13))
+    hist = int(r.integers(0, 3001))
+    ragged_lo = int(r.integers(1, hist + 1)) if hist > 0 and r.random() < 0.5 else 0
+    cfg = C["c2_qwen3_8b"].with_(
+        name=f"random{seed}", batch=int(r.integers(1, 7)), n_q_heads=n_kv * group, n_kv_heads=n_kv,
+        head_dim=head_dim, dtype=dtype, hist_len=hist, chunk_len=int(r.choice([64, 100, 256, 320, 512, 1024])),
+        n_queries=n_q, mask=mask, seed=100 + seed, ragged_lo=ragged_lo,
+        packing="token" if ragged_lo and r.random() < 0.3 else "head")
+    kw = dict(split="balanced" if r.random() < 0.6 else "chunks",
+              kv_layout="interleaved" if r.random() < 0.5 else "separate",
+              chunks_per_slot=int(r.choice([1, 2, 3])), fuse_candidates=r.random() < 0.5)
+    return cfg, kw
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(seed):
+    """Seeded random combinations of shape, mask, lengths, cut and layout
+    against the fp64 oracle (O and lse at the tolerance, the mask bit for
+    bit)."""
+    cfg, kw = _random_case(seed)
+    log(f"[random {seed}] {cfg} {kw}")
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, **kw)
+    rnd.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
