@@ -764,3 +764,27 @@ def test_random_shapes(seed):
     o_ref, lse_ref = oracle_round(inp)
     compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
     check_mask(rnd, inp)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_streamed(seed):
+    """The streamed round on seeded random shapes (heads, group, queries and
+    mask, chunk length and count) and staging rings (buffers, chunks per
+    copy), against the fp64 oracle."""
+    r = np.random.default_rng(9000 + seed)
+    n_kv = int(r.choice([1, 2, 4]))
+    group = int(r.choice([1, 2, 4, 8]))
+    mask = "tree" if r.random() < 0.4 else "causal"
+    chunk = int(r.choice([128, 256, 500, 1024]))
+    cfg = C["c5_streamed"].with_(
+        name=f"streamed_random{seed}", batch=int(r.integers(1, 5)), n_q_heads=n_kv * group, n_kv_heads=n_kv,
+        n_queries=int(r.integers(2, 33)) if mask == "tree" else int(r.integers(1, 9)), mask=mask,
+        chunk_len=chunk, hist_len=chunk * int(r.integers(1, 9)), seed=200 + seed)
+    n_buf, per_copy = int(r.integers(1, 4)), int(r.integers(1, 4))
+    log(f"[streamed random {seed}] {cfg} n_buf={n_buf} chunks_per_copy={per_copy}")
+    inp = wl.make_inputs(cfg)
+    srd = rounds.StreamedRound(inp, n_buf=n_buf, chunks_per_copy=per_copy)
+    srd.run()
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, srd.o.cpu().numpy(), srd.lse.cpu().numpy(), o_ref, lse_ref)
