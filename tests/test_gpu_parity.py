@@ -534,9 +534,14 @@ SHORT_KERNELS = {
 }
 
 
-@pytest.mark.parametrize("hist", [0, 1, 3, 8, 31, 64])
+# A uniform view needs at least one token; zero-token requests go through
+# the ragged layout (and test_empty_history_and_zero_lengths).
+SHORT_LENGTHS = [(layout, hist) for layout in ("uniform", "ragged") for hist in (0, 1, 3, 8, 31, 64)
+                 if layout == "ragged" or hist > 0]
+
+
+@pytest.mark.parametrize("layout,hist", SHORT_LENGTHS)
 @pytest.mark.parametrize("kernel", list(SHORT_KERNELS))
-@pytest.mark.parametrize("layout", ["uniform", "ragged"])
 @pytest.mark.parametrize("path", ["chunks", "balanced"])
 def test_short_histories(kernel, hist, layout, path):
     """Requests whose whole committed history is 0-64 tokens (the GPU region
@@ -548,8 +553,6 @@ def test_short_histories(kernel, hist, layout, path):
     kw = dict(SHORT_KERNELS[kernel])
     engine = kw.pop("engine")
     if layout == "uniform":
-        if hist == 0:
-            pytest.skip("a uniform view needs at least one token")
         cfg = C["c2_qwen3_8b"].with_(batch=3, hist_len=hist, chunk_len=128, **kw)
     else:
         cfg = C["c3_internlm25_7b_ragged"].with_(batch=3, hist_len=64, ragged_lo=64, chunk_len=128, **kw)
