@@ -368,7 +368,12 @@ SS_API int32_t ss_verify_round_noalloc(const ss_problem_t* problem, const void* 
  * chunks and marks the buffer free. Without SS_STREAM_CONTINUE the first
  * copy also waits for all work already enqueued on the compute stream. The
  * call returns without synchronising; candidates and merge may follow on
- * the compute stream.
+ * the compute stream. Calls on one device may overlap in time on different
+ * stream pairs when each has its own staging buffers: they share the
+ * device's event objects, but every wait a call enqueues refers to a mark
+ * that call recorded (events are recorded and waited under a lock, and a
+ * wait takes the event as it was recorded when the wait was enqueued).
+ * SS_STREAM_CONTINUE continues the device's most recent call.
  * Errors: as ss_verify_chunk; SS_ERR_INVALID_ARG if the streams are equal,
  * on unknown flags, or on SS_STREAM_CONTINUE with a different ring.
  */

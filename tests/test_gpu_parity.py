@@ -379,6 +379,40 @@ def test_streamed_ordering_checks(n_buf, per_copy, checks):
     assert torch.equal(last.cpu(), srd.host_kv[srd.n_chunks - 1])
 
 
+def test_streamed_calls_overlap_on_two_stream_pairs():
+    """Two streaming calls on one device, each with its own copy and compute
+    streams and staging buffers, enqueued back to back with nothing ordering
+    them (the first held back by SS_STREAM_DELAY, the second poisoning its
+    buffers): both give the results of the same calls run one after the
+    other, bit for bit. The calls share the device's event objects; every
+    wait refers to a mark its own call recorded."""
+    cfgs = [SMALL["c5_small"].with_(hist_len=8 * 256, chunk_len=256),
+            SMALL["c5_small"].with_(batch=3, n_queries=4, hist_len=6 * 256, chunk_len=256, seed=77)]
+    rnds = [rounds.StreamedRound(wl.make_inputs(c), n_buf=2) for c in cfgs]
+    refs = []
+    for r in rnds:
+        r.run()
+        torch.cuda.synchronize()
+        refs.append((r.o.clone(), r.lse.clone()))
+    streams = [(torch.cuda.Stream(), torch.cuda.Stream()) for _ in rnds]
+    for rep in range(2):
+        torch.cuda.synchronize()
+        for r in rnds:
+            r.o.fill_(float("nan"))
+            r.lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        for i, (r, (cp, cs)) in enumerate(zip(rnds, streams)):
+            ss.ss_stream_history(r.problem, r.q, r.host_kv, r.chunk_len, r.n_chunks, r.staging, r.n_buf, r.state, 0,
+                                 cp, cs, checks=ss.SS_STREAM_DELAY if i == 0 else ss.SS_STREAM_POISON)
+            ss.ss_verify_candidates(r.problem, r.q, r.cand_view, r.parents, None, r.state, r.n_chunks, cs)
+            ss.ss_merge_states(r.problem, r.state, None, r.o, r.lse, cs)
+        torch.cuda.synchronize()
+        for i, (r, (o_ref, lse_ref)) in enumerate(zip(rnds, refs)):
+            assert torch.equal(r.o, o_ref), (rep, i)
+            assert torch.equal(r.lse, lse_ref), (rep, i)
+        log(f"  overlapping calls, repetition {rep}: both identical to the sequential runs")
+
+
 @pytest.mark.parametrize("n_buf,per_copy", [(1, 1), (2, 1), (2, 2), (3, 1)])
 def test_layered_stream_with_prefetch(n_buf, per_copy):
     """Three layers, each with its own host-resident history, the staging
