@@ -175,6 +175,7 @@ def time_resident(cfg, steps, warmup, cps="auto", engine="auto", split="balanced
     on the same stream. Before each: `warmup` steps and the settle time."""
     inp = wl.make_inputs(cfg)
     rnd = make_round(cfg, inp, cps, engine, split)
+    rnd.inputs_sha256 = wl.input_digest(inp)
     del inp
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
@@ -615,7 +616,8 @@ def resident_record(cfg, steps, warmup, cps, engine, split, probe):
             roof["frac_of_read_probe"] = round(achieved / max(probe["one_per_cu_GBps"], probe["eight_per_cu_GBps"]),
                                                4)
     rec = {
-        "config": {"workload": workload_desc(cfg), "batch": cfg.batch, "history_tokens": cfg.hist_len,
+        "config": {"workload": workload_desc(cfg), "seed": cfg.seed, "inputs_sha256": rnd.inputs_sha256,
+                   "batch": cfg.batch, "history_tokens": cfg.hist_len,
                    "history_tokens_total": int(hist_b // (2 * cfg.n_kv_heads * cfg.head_dim * cfg.elem_bytes)),
                    "queries": cfg.n_queries,
                    "split": rnd.split, "history_slots": rnd.n_hist_slots, "fused_candidates": rnd.fused,

@@ -35,6 +35,7 @@ Logical layouts handed out:
 from __future__ import annotations
 
 import dataclasses
+import hashlib
 import math
 import os
 from concurrent.futures import ThreadPoolExecutor
@@ -197,6 +198,19 @@ class VerifyInputs:
         """Indexable as view[b][g] -> numpy float32 [N_b][d] (converted lazily,
         one (request, KV head) slice at a time)."""
         return _HistView(self, which)
+
+
+def input_digest(inp: VerifyInputs) -> str:
+    """SHA-256 (hex) over the bytes of every input, in this order: q, the K
+    and V history, the K and V candidates (each in its stored layout), the
+    history lengths (int32) and, for trees, the parents (int32)."""
+    h = hashlib.sha256()
+    for t in (inp.q, inp.k_hist, inp.v_hist, inp.k_cand, inp.v_cand):
+        h.update(t.contiguous().reshape(-1).view(torch.uint8).numpy().data)
+    h.update(np.ascontiguousarray(inp.hist_len, dtype=np.int32).tobytes())
+    if inp.parents is not None:
+        h.update(np.ascontiguousarray(inp.parents, dtype=np.int32).tobytes())
+    return h.hexdigest()
 
 
 class _HistView:

@@ -424,3 +424,16 @@ def test_probes_reject():
     assert L.ss_mfma_probe(4096, 8192, 0, 1, 4096, None) == ss.SS_ERR_INVALID_ARG
     assert L.ss_mfma_probe(4096, 8192, 1, 0, 4096, None) == ss.SS_ERR_INVALID_ARG
     assert "8192" in L.ss_last_error().decode()
+
+
+def test_input_digest_follows_the_seed():
+    """The seeded inputs are a function of the config alone: the same seed
+    gives the same bytes (digest), another seed other bytes; ragged lengths
+    and tree parents enter the digest."""
+    for cfg in (workloads.CONFIGS["c1_tiny_f32"],
+                workloads.CONFIGS["c3_internlm25_7b_ragged"].with_(batch=3, hist_len=700, ragged_lo=1, chunk_len=128),
+                workloads.CONFIGS["c4_tree_72b"].with_(batch=2, hist_len=300, chunk_len=128)):
+        a = workloads.input_digest(workloads.make_inputs(cfg))
+        assert a == workloads.input_digest(workloads.make_inputs(cfg))
+        assert a != workloads.input_digest(workloads.make_inputs(cfg.with_(seed=cfg.seed + 1)))
+        assert len(a) == 64
