@@ -47,10 +47,9 @@ def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int, engine="auto") -> i
 
 
 def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
-    """Slots per stream for ss_verify_history. Ragged lengths: enough that
-    the longest stream does not force ranges longer than an even share over
-    the launch (wgs_per_cu work-groups per compute unit), plus one for the
-    range boundaries. Uniform lengths: one chunk per work-group of that
+    """Slots per stream for ss_verify_history. Ragged lengths: as many as the
+    longest stream has pieces when every work-group of the launch
+    (wgs_per_cu per compute unit) takes an even share of the line. Uniform lengths: one chunk per work-group of that
     launch. Wide row groups on the MFMA kernel: one wave of work-groups
     (8-wave groups of 256 rows, one per compute unit, or 4-wave groups of 128
     rows, two per unit), the slot count ss_verify_round picks; other wide
@@ -69,7 +68,12 @@ def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
     total = sum(pads) * cfg.n_kv_heads
     if total == 0:
         return 2
-    return max(2, -(-pad_max * wave // total) + 2)
+    # Tokens per work-group of the balanced cut (an even share, rounded up to
+    # 128): a stream of pad tokens then spans at most ceil(pad / L) work-group
+    # ranges, plus one when it straddles a boundary. With that many slots the
+    # cut's cap pad_max / (slots - 1) stays below L, so L is the even share.
+    piece = max(128, -(-(-(-total // wave)) // 128) * 128)
+    return max(2, -(-pad_max // piece) + 1)
 
 
 def narrow_mfma(cfg, engine="auto") -> bool:

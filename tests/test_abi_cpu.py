@@ -437,3 +437,31 @@ def test_input_digest_follows_the_seed():
         assert a == workloads.input_digest(workloads.make_inputs(cfg))
         assert a != workloads.input_digest(workloads.make_inputs(cfg.with_(seed=cfg.seed + 1)))
         assert len(a) == 64
+
+
+def test_auto_history_slots_keep_the_even_cut():
+    """The resident round's slot count for ragged lengths on the narrow
+    kernels is the least that keeps the balanced cut at an even share of the
+    line: with it, the plan's tokens per work-group are the even share
+    (rounded up to 128) and every slot is written once; with one slot fewer
+    the cut's cap would lengthen the ranges."""
+    from long_context_speculative_amd import rounds
+    base = workloads.CONFIGS["c3_internlm25_7b_ragged"]
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        b, hkv, mx = int(rng.integers(1, 80)), int(rng.integers(1, 9)), int(rng.integers(1, 70000))
+        lens = rng.integers(0, mx + 1, size=b).astype(np.int32)
+        if rng.random() < 0.2:
+            lens[:] = 0
+            lens[0] = mx
+        cfg = base.with_(batch=b, n_kv_heads=hkv, n_q_heads=4 * hkv, hist_len=mx, ragged_lo=1)
+        n_wg = int(rng.choice([64, 128, 256, 304]))
+        slots = rounds.auto_history_slots(cfg, lens, n_wg)
+        total = sum(-(-int(n) // 128) * 128 for n in lens) * hkv
+        even = max(128, -(-(-(-total // n_wg)) // 128) * 128)
+        plan, piece = ss.ss_history_plan_host(lens, hkv, mx, n_wg, slots)
+        assert (plan[..., 3] == 1).all()
+        if total:
+            assert piece == even, (b, hkv, mx, n_wg, slots)
+        if slots > 2:
+            assert ss.ss_history_plan_host(lens, hkv, mx, n_wg, slots - 1)[1] > even
