@@ -104,7 +104,9 @@ typedef struct ss_problem {
  * strides. Request b holds len_b tokens: req_len[b] (device array) if not
  * NULL, else max_len. A len_b above max_len is read as max_len.
  * Alignment: k and v 16-byte aligned; strides and offsets multiples of
- * 16 bytes' worth of elements.
+ * 16 bytes' worth of elements. Offsets and stride_b, stride_h are 64-bit
+ * throughout; stride_t may be at most 2^24 elements (SS_ERR_UNSUPPORTED
+ * above: keys inside a tile are addressed by 32-bit offsets).
  * Covers head-major [B][Hkv][N][d], token-major ragged [sum N_b][Hkv][d]
  * and staging-chunk layouts.
  */

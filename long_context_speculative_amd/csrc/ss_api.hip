@@ -74,6 +74,11 @@ int32_t check_view(const ss_problem_t* p, const ss_kv_view_t* v, const char* nam
         return fail(SS_ERR_INVALID_ARG, "%s strides must be multiples of 16 bytes", name);
     if (v->max_len > 1 && v->stride_t < p->head_dim)
         return fail(SS_ERR_INVALID_ARG, "%s stride_t is smaller than head_dim", name);
+    // The kernels address a key inside a tile of at most 64 keys by a 32-bit
+    // offset from the tile's first key (64-bit): keys * stride_t stays below
+    // 2^31 for any stride_t up to 2^24 elements.
+    if (v->stride_t > ((int64_t)1 << 24))
+        return fail(SS_ERR_UNSUPPORTED, "%s stride_t above 2^24 elements", name);
     return SS_OK;
 }
 

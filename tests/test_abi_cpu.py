@@ -465,3 +465,14 @@ def test_auto_history_slots_keep_the_even_cut():
             assert piece == even, (b, hkv, mx, n_wg, slots)
         if slots > 2:
             assert ss.ss_history_plan_host(lens, hkv, mx, n_wg, slots - 1)[1] > even
+
+
+def test_view_token_stride_limit():
+    """A token stride above 2^24 elements is refused before anything is
+    enqueued (keys inside a tile are addressed by 32-bit offsets)."""
+    L = ss.lib()
+    p = _problem()
+    st = ctypes.byref(_state(4).struct)
+    big = ss.KVView(4096, 8192, 0, 0, (1 << 24) + 8, None, None, 1024)
+    assert L.ss_verify_chunk(ctypes.byref(p), 4096, ctypes.byref(big), 64, 0, 4, 1, st, 0, None) == ss.SS_ERR_UNSUPPORTED
+    assert "2^24" in L.ss_last_error().decode()

@@ -731,16 +731,29 @@ def test_full_size_sampled(name):
 # size extremes
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["one_request_1m_tokens", "many_short_requests", "max_candidates_tree"])
+@pytest.mark.parametrize("name", ["one_request_1m_tokens", "many_short_requests", "max_candidates_tree",
+                                  "history_above_2g_elements", "wide_history_above_2g_elements"])
 def test_size_extremes(name):
     """One request with a million committed tokens (the balanced cut splits
     its streams over the whole device), 1024 requests with short ragged
-    histories, and the largest candidate region (64 tree nodes under 8-way
-    GQA: 512 rows), each in the benchmark's launch configuration; sampled
-    (request, KV head) slices against the oracle."""
+    histories, the largest candidate region (64 tree nodes under 8-way GQA:
+    512 rows), and histories whose K and V tensors hold more than 2^31
+    elements each (2.15M tokens x 8 KV heads x 128; every offset past 2^31
+    must be 64-bit: the narrow kernel, and the wide-row kernel with 40 rows),
+    each in the benchmark's launch configuration; sampled (request, KV head)
+    slices against the oracle (the last KV head lies past 2^31 elements)."""
     if name == "one_request_1m_tokens":
         cfg = C["c2_qwen3_8b"].with_(batch=1, hist_len=1 << 20, chunk_len=4096)
         picks = [(0, 0), (0, 5)]
+    elif name == "history_above_2g_elements":
+        cfg = C["c2_qwen3_8b"].with_(batch=1, hist_len=2_150_000, chunk_len=4096)
+        assert cfg.n_kv_heads * cfg.hist_len * cfg.head_dim > 1 << 31
+        picks = [(0, 0), (0, 7)]
+    elif name == "wide_history_above_2g_elements":
+        cfg = C["c4_tree_72b"].with_(batch=1, n_q_heads=8, n_kv_heads=8, n_queries=40, hist_len=2_150_000,
+                                     chunk_len=4096)
+        assert cfg.rows > 32 and cfg.n_kv_heads * cfg.hist_len * cfg.head_dim > 1 << 31
+        picks = [(0, 7)]
     elif name == "many_short_requests":
         cfg = C["c3_internlm25_7b_ragged"].with_(batch=1024, hist_len=600, ragged_lo=300, chunk_len=256)
         picks = [(0, 0), (511, 3), (1023, 7)]
