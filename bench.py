@@ -352,6 +352,35 @@ def mfma_probe(iters=4096, reps=20):
             "ms_per_launch": round(ms, 4), "work_groups": wgs, "operands": "N(0,1) bf16"}
 
 
+def hold(workload, seconds, probe=False):
+    """Back-to-back calls of one workload's resident round (or of the
+    matrix-core probe) for `seconds`, synchronising every 8 calls; prints a
+    line when the loop starts and one with the time per call at the end."""
+    from long_context_speculative_amd import ssverify as ss
+    if probe:
+        ops = torch.randn(1 << 22, dtype=torch.bfloat16, device="cuda")
+        sink = torch.zeros(256, dtype=torch.float32, device="cuda")
+        wgs = 2 * rounds.device_cus()
+        fn, name = (lambda: ss.ss_mfma_probe(ops, 4096, wgs, sink)), "mfma_probe"
+    else:
+        cfg = wl.CONFIGS[workload]
+        inp = wl.make_inputs(cfg)
+        rnd = make_round(cfg, inp)
+        del inp
+        fn, name = rnd.run, workload
+    fn()
+    torch.cuda.synchronize()
+    print(json.dumps({"hold": name, "seconds": seconds, "state": "running"}), flush=True)
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+        n += 8
+    print(json.dumps({"hold": name, "calls": n, "ms_per_call": round((time.perf_counter() - t0) / n * 1e3, 4)}),
+          flush=True)
+
+
 def time_sparse(cfg, block_len=512, k=16, reps=20):
     """Block statistics and block-sparse verification on the resident
     workload, with the importance signal taken two ways: from a full round
@@ -656,6 +685,10 @@ def main():
                     help="run only the streamed leg (c5_streamed) and print its record (for traces of that path)")
     ap.add_argument("--mfma-probe-only", action="store_true",
                     help="only the matrix-core reference (ss_mfma_probe) on N(0,1) bf16 operands")
+    ap.add_argument("--hold", type=float, default=0.0,
+                    help="run the workload's resident round (with --mfma-probe-only: the probe) back to back for "
+                         "this many seconds and print its time per call; for power and clock readings taken "
+                         "meanwhile by another tool")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection pass: one plain elementwise copy of 1 GiB (the calibration kernel "
                          "of known size), then one step of the workload; prints nothing else")
@@ -670,6 +703,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.hold > 0:
+        hold(args.workload, args.hold, args.mfma_probe_only)
+        return
     if args.mfma_probe_only:
         print(json.dumps({"mfma_probe": mfma_probe()}), flush=True)
         return
