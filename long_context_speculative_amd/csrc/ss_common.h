@@ -281,9 +281,11 @@ __host__ __device__ inline int32_t chunk_view_len(const ChunkParams& p, int32_t 
 // by up to 2^-8 relative, so a row that a few keys dominate moves by up to
 // that fraction of the spread of their values; over many keys the rounding
 // errors average out (N(0,1) data, 128 features: largest error about 4e-3 at
-// 2-8 keys, 1.3e-3 at 128, 3.3e-4 at 2048). Kernels whose matrix work is
-// the bound carry each weight's rounding remainder as a second bf16 operand
-// only for requests with fewer history keys than this.
+// 2-8 keys, 1.3e-3 at 128, 3.3e-4 at 2048) unless the scores are peaked. The
+// wide-row kernel, whose matrix work is the bound, carries each weight's
+// rounding remainder as a second bf16 operand for requests with fewer
+// history keys than this; for longer ones it checks each piece afterwards
+// and attends it again with the remainders where a few keys dominate a row.
 constexpr int64_t kSplitBelow = 2048;
 
 // History keys a row of request b meets over the whole call: the request's

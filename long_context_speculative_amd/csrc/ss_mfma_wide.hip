@@ -61,6 +61,9 @@ constexpr int kVRow = D + 16;   // bf16 per staged V row (32-byte pad)
 constexpr int kNS = D / 32;     // 32-feature steps of S = K Q^T
 constexpr int kNXT = D / 16;    // 16-feature tiles of O^T
 constexpr float kGrowLog2 = 8.f;  // rescale threshold (log2 units)
+// A piece attended without the weights' rounding remainders is attended again
+// with them when some row's largest weight exceeds this share of its sum.
+constexpr float kShareMax = 1.f / 32.f;
 
 // 16-byte aligned so that the 16-byte staging stores and K reads are single
 // ds_write_b128 / ds_read_b128 (with only the 8-byte alignment of the
@@ -70,6 +73,7 @@ struct alignas(16) WideSmem {
     uint16_t k[3][KT][kRow];
     uint16_t v[3][KT][kVRow];
     uint64_t cbits[64];  // candidate visibility bits (n_queries <= 64)
+    int32_t again;       // some wave needs the piece attended again
 };
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -309,12 +313,10 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
                     if (16 * kt + 4 * q4 + j >= valid) sc[kt][rt][j] = -INFINITY;
     };
 
-    // A request with a short history (row_history_keys below kSplitBelow)
-    // carries each weight's bf16 rounding remainder as a second operand (a
-    // second P V pass), tile by tile without the pipeline (a second
-    // pipelined loop would not fit the registers). The candidate tiles
-    // always do.
-    if (row_history_keys(p, b) < kSplitBelow) {
+    // The piece tile by tile without the pipeline, each weight's bf16
+    // rounding remainder carried as a second operand (a second P V pass; a
+    // second pipelined loop would not fit the registers).
+    auto careful_pass = [&]() __attribute__((always_inline)) {
         for (int t = 0; t < n_tiles; ++t) {
             fetch(t0 + (int64_t)KT * t, pa);
             if (t > 0) __syncthreads();  // the previous tile is consumed
@@ -328,7 +330,29 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
                 softmax_pv(std::true_type{}, 0, sc_a);
             }
         }
+    };
+
+    // A request with a short history (row_history_keys below kSplitBelow)
+    // takes the careful pass. A longer one takes the pipelined loop without
+    // the remainders: a weight's rounding moves a row's result by up to
+    // 2^-8 of that weight's share of the row's sum, and over many keys the
+    // errors average out, unless a few keys dominate the row. So the loop
+    // tracks each row's largest score, and where some row's largest weight
+    // is more than kShareMax of its sum (the rounding error's spread is then
+    // up to sqrt(kShareMax) of the single-weight one), the work-group attends
+    // the piece again with the careful pass. The candidate tiles always
+    // carry the remainders.
+    if (row_history_keys(p, b) < kSplitBelow) {
+        careful_pass();
     } else {
+        float m_top[kRT];  // largest c-scaled score of each row so far
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) m_top[rt] = -INFINITY;
+        auto track = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int rt = 0; rt < kRT; ++rt) m_top[rt] = fmaxf(m_top[rt], mc[rt]);
+        };
+        if (tid == 0) sm.again = 0;
         if (n_tiles > 0) {
             fetch(tile_start(0), pa);
             stage(0, pa);
@@ -340,6 +364,7 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
         if (active && n_full > 0) {
             qk(0, 0, sc_a);
             row_max(sc_a, mc);
+            track();
             rescale(mc);
         }
 
@@ -353,6 +378,7 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
                 qk(b1, t + 1, sc_next);
                 softmax_pv(std::false_type{}, b_cur, sc_cur);
                 row_max(sc_next, mc);
+                track();
             }
             stage(b2, stage_set);
             if constexpr (decltype(compute)::value) rescale(mc);
@@ -382,9 +408,27 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
                 qk(bt, n_full, sc_a);
                 mask_tail(sc_a, (int)(t1 - t0 - (int64_t)KT * n_full));
                 row_max(sc_a, mc);
+                track();
                 rescale(mc);
                 softmax_pv(std::false_type{}, bt, sc_a);
             }
+        }
+        bool big = false;
+        if (active) {
+#pragma unroll
+            for (int rt = 0; rt < kRT; ++rt) big |= exp2_hw(m_top[rt] - m_run[rt]) > kShareMax * ol[rt][0];
+        }
+        if (__ballot(big) && lane == 0) atomicOr(&sm.again, 1);
+        __syncthreads();  // every wave's verdict is in; the ring buffers are free
+        if (__builtin_amdgcn_readfirstlane(sm.again)) {
+#pragma unroll
+            for (int rt = 0; rt < kRT; ++rt) {
+                m_run[rt] = -INFINITY;
+                ol[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int xt = 0; xt < kNXT; ++xt) o[xt][rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
+            careful_pass();
         }
     }
 

@@ -20,8 +20,8 @@
 //            2l, 2l+1 and accumulates p[row][key] * V[key][2l..2l+1] over the
 //            tile's keys, two keys per v_dot2_f32_bf16 (the bf16 weights are
 //            read from LDS as a broadcast; l sums the same rounded weights;
-//            a request with a short history also takes each weight's
-//            rounding remainder, as a second pair of dot products).
+//            each weight's rounding remainder follows as a second pair of
+//            dot products).
 // The 4 waves' states are merged through LDS at the end.
 
 #include "ss_common.h"
@@ -112,8 +112,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_valu_small_kernel(ChunkPara
     }
 
     const int n_tiles = (int)((t1 - t0 + kTile - 1) / kTile);
-    // A short history carries the weights' bf16 rounding remainders too.
-    const bool split = row_history_keys(p, b) < kSplitBelow;
+    // The weights' bf16 rounding remainders are carried too: where a few
+    // keys dominate a row (a short history, or peaked scores over a long
+    // one) the rounding does not average out.
+    const bool split = true;
     u32x4 kr[8], vr[8];
     // Lane's key of the tile (clamped into the range; masked below) and its
     // 64 features: 8 loads of 16 bytes.

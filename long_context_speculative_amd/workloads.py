@@ -64,6 +64,7 @@ class VerifyConfig:
     tree_depth_cap: int = 8
     streamed: bool = False      # history sits in pinned host memory
     packing: str = "head"       # ragged layout: "head" [Hkv][sum N][d] or "token" [sum N][Hkv][d]
+    score_scale: float = 0.0    # > 0: the score scale; else 1/sqrt(d)
 
     @property
     def group(self) -> int:
@@ -88,8 +89,9 @@ class VerifyConfig:
 
     @property
     def scale(self) -> float:
-        """1/sqrt(d), rounded to float32 (the value the library receives)."""
-        return float(np.float32(1.0 / math.sqrt(self.head_dim)))
+        """score_scale if set, else 1/sqrt(d); rounded to float32 (the value
+        the library receives)."""
+        return float(np.float32(self.score_scale if self.score_scale > 0 else 1.0 / math.sqrt(self.head_dim)))
 
     def with_(self, **kw) -> "VerifyConfig":
         return dataclasses.replace(self, **kw)
