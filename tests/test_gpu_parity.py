@@ -795,17 +795,20 @@ def _random_case(seed):
         head_dim=head_dim, dtype=dtype, hist_len=hist, chunk_len=int(r.choice([64, 100, 256, 320, 512, 1024])),
         n_queries=n_q, mask=mask, seed=100 + seed, ragged_lo=ragged_lo,
         packing="token" if ragged_lo and r.random() < 0.3 else "head")
-    # a third of the cases use another score scale: small (flat weights) or
-    # large (scores spread over tens of log2 units, so the running maximum
-    # moves by more than the kernels' rescale threshold)
-    cfg = cfg.with_(score_scale=float(r.choice([0.0, 0.0, 0.02, 0.3, 0.6])) if r.random() < 0.5 else 0.0)
+    # a third of the bf16 cases use another score scale: small (flat weights)
+    # or large (scores spread over tens of log2 units: the running maximum
+    # moves by more than the kernels' rescale threshold and a few keys
+    # dominate). fp32 cases keep 1/sqrt(d): at |lse| near 30 the 1e-5 bound is
+    # a few fp32 ulps, which plain fp32 arithmetic itself does not meet.
+    scale = float(r.choice([0.0, 0.0, 0.02, 0.3, 0.6])) if r.random() < 0.5 else 0.0
+    cfg = cfg.with_(score_scale=scale if dtype == "bf16" else 0.0)
     kw = dict(split="balanced" if r.random() < 0.6 else "chunks",
               kv_layout="interleaved" if r.random() < 0.5 else "separate",
               chunks_per_slot=int(r.choice([1, 2, 3])), fuse_candidates=r.random() < 0.5)
     return cfg, kw
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_shapes(seed):
     """Seeded random combinations of shape, mask, lengths, cut and layout
     against the fp64 oracle (O and lse at the tolerance, the mask bit for
@@ -821,7 +824,7 @@ def test_random_shapes(seed):
     check_mask(rnd, inp)
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", range(16))
 def test_random_streamed(seed):
     """The streamed round on seeded random shapes (heads, group, queries and
     mask, chunk length and count) and staging rings (buffers, chunks per
@@ -834,7 +837,8 @@ def test_random_streamed(seed):
     cfg = C["c5_streamed"].with_(
         name=f"streamed_random{seed}", batch=int(r.integers(1, 5)), n_q_heads=n_kv * group, n_kv_heads=n_kv,
         n_queries=int(r.integers(2, 33)) if mask == "tree" else int(r.integers(1, 9)), mask=mask,
-        chunk_len=chunk, hist_len=chunk * int(r.integers(1, 9)), seed=200 + seed)
+        chunk_len=chunk, hist_len=chunk * int(r.integers(1, 9)), seed=200 + seed,
+        score_scale=float(r.choice([0.0, 0.0, 0.3, 0.6])))
     n_buf, per_copy = int(r.integers(1, 4)), int(r.integers(1, 4))
     log(f"[streamed random {seed}] {cfg} n_buf={n_buf} chunks_per_copy={per_copy}")
     inp = wl.make_inputs(cfg)
