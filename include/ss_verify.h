@@ -292,9 +292,12 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
  *   q, hist, cand, parents, mask_out   as ss_verify_history (cand required)
  *   n_slots   slots per (request, KV head) for the history cut, or 0: the
  *             library's choice (one piece per work-group of one full launch
- *             where the lengths are known on the host; 8 for ragged lengths
- *             on the narrow MFMA kernel; +1 for the candidate slot on the
- *             VALU engines), limited to work->n_slots
+ *             where the lengths are known on the host; for ragged lengths
+ *             on the narrow MFMA kernel 1 -- a work-group per stream -- when
+ *             hist->max_len <= 6144 with at least one stream per compute
+ *             unit, or <= 3072 with three per four units, else 8 for the
+ *             balanced cut; +1 for the candidate slot on the VALU engines),
+ *             limited to work->n_slots
  *   work      caller-allocated state slots (workspace); slots [0, n_slots)
  *             are overwritten, their contents afterwards are not part of
  *             the result

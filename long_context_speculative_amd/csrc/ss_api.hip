@@ -439,13 +439,25 @@ int32_t merge_states(const ss_problem_t* problem, const ss_state_t* in, const in
     return SS_OK;
 }
 
+// Ragged histories on the narrow MFMA kernel that run faster as one piece per
+// stream (a work-group per (request, KV head), all in parallel) than under
+// the balanced cut, whose work-groups run two or three short pieces one
+// after another, each paying its start and its merge. Measured on MI355X
+// (256 CUs), lengths uniform in [n/8, n]: 1.05-1.5x faster up to n = 6144
+// with at least one stream per CU (even or slower at 8192), and up to 3072
+// with three streams per four CUs; fewer streams leave CUs idle.
+bool one_piece_per_stream(int64_t max_len, int64_t streams, int64_t cus) {
+    return (max_len <= 6144 && streams >= cus) || (max_len <= 3072 && 4 * streams >= 3 * cus);
+}
+
 // Slots per (request, KV head) of a whole-round call for this problem and
 // history view, before any capacity limit: one piece per work-group of one
 // full launch where the lengths are known on the host (uniform lengths on
-// the narrow MFMA kernel; the wide-row kernel's fixed chunks), 8 for ragged
-// lengths on the narrow kernel (the balanced cut grows its ranges when the
-// longest stream needs more), and one more for the candidate region on the
-// VALU engines.
+// the narrow MFMA kernel; the wide-row kernel's fixed chunks); for ragged
+// lengths on the narrow kernel one (one_piece_per_stream, judged by the
+// view's max_len) or 8 (the balanced cut grows its ranges when the longest
+// stream needs more); and one more for the candidate region on the VALU
+// engines.
 int32_t round_slots(const ss_problem_t* p, const ss_kv_view_t* hist, int32_t* n_slots) {
     const int32_t group = p->n_q_heads / p->n_kv_heads;
     const int32_t rows = p->n_queries * group;
@@ -459,7 +471,10 @@ int32_t round_slots(const ss_problem_t* p, const ss_kv_view_t* hist, int32_t* n_
     int64_t s = 1;
     switch (chunk_engine(p)) {
         case ChunkEngine::kMfma:
-            s = hist->req_len ? 8 : cus / streams;
+            if (!hist->req_len)
+                s = cus / streams;
+            else
+                s = one_piece_per_stream(hist->max_len, streams, cus) ? 1 : 8;
             break;
         case ChunkEngine::kMfmaWide: {
             // 8-wave groups of 256 rows, one per CU; 4-wave groups of 128

@@ -46,8 +46,22 @@ def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int, engine="auto") -> i
     return max(1, units // (wgs_per_cu(cfg, engine) * cus))
 
 
+def one_piece_per_stream(max_len: int, streams: int, cus: int) -> bool:
+    """Whether ragged histories on the narrow MFMA kernel run faster as one
+    piece per stream (one slot: a work-group per (request, KV head), all in
+    parallel) than under the balanced cut, whose work-groups run two or
+    three short pieces one after another, each paying its start and merge.
+    Measured on MI355X (256 CUs), lengths uniform in [n/8, n]: one piece per
+    stream is 1.05-1.5x faster up to n = 6144 with at least one stream per
+    CU (even or slower at 8192), and up to 3072 with three streams per four
+    CUs; with fewer streams it leaves CUs idle. The library's own slot choice
+    (ss_verify_round with n_slots = 0) applies the same rule."""
+    return (max_len <= 6144 and streams >= cus) or (max_len <= 3072 and 4 * streams >= 3 * cus)
+
+
 def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
-    """Slots per stream for ss_verify_history. Ragged lengths: as many as the
+    """Slots per stream for ss_verify_history. Ragged lengths on the narrow
+    MFMA kernel: one when one_piece_per_stream holds, else as many as the
     longest stream has pieces when every work-group of the launch
     (wgs_per_cu per compute unit) takes an even share of the line. Uniform lengths: one chunk per work-group of that
     launch. Wide row groups on the MFMA kernel: one wave of work-groups
@@ -68,6 +82,9 @@ def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
     total = sum(pads) * cfg.n_kv_heads
     if total == 0:
         return 2
+    if narrow_mfma(cfg, engine) and one_piece_per_stream(max((int(n) for n in hist_len), default=0),
+                                                          cfg.batch * cfg.n_kv_heads, cus):
+        return 1
     # Tokens per work-group of the balanced cut (an even share, rounded up to
     # 128): a stream of pad tokens then spans at most ceil(pad / L) work-group
     # ranges, plus one when it straddles a boundary. With that many slots the

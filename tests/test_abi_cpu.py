@@ -457,6 +457,9 @@ def test_auto_history_slots_keep_the_even_cut():
         cfg = base.with_(batch=b, n_kv_heads=hkv, n_q_heads=4 * hkv, hist_len=mx, ragged_lo=1)
         n_wg = int(rng.choice([64, 128, 256, 304]))
         slots = rounds.auto_history_slots(cfg, lens, n_wg)
+        if rounds.one_piece_per_stream(int(lens.max()), b * hkv, n_wg) and lens.any():
+            assert slots == 1
+            continue
         total = sum(-(-int(n) // 128) * 128 for n in lens) * hkv
         even = max(128, -(-(-(-total // n_wg)) // 128) * 128)
         plan, piece = ss.ss_history_plan_host(lens, hkv, mx, n_wg, slots)
@@ -465,6 +468,31 @@ def test_auto_history_slots_keep_the_even_cut():
             assert piece == even, (b, hkv, mx, n_wg, slots)
         if slots > 2:
             assert ss.ss_history_plan_host(lens, hkv, mx, n_wg, slots - 1)[1] > even
+
+
+def test_short_ragged_histories_take_one_piece_per_stream():
+    """The slot rule for ragged histories on the narrow MFMA kernel: one slot
+    (a work-group per stream) when the longest history is at most 6144 tokens
+    with at least one stream per compute unit, or at most 3072 with three
+    streams per four units; the balanced cut otherwise, and always on the
+    VALU engine."""
+    from long_context_speculative_amd import rounds
+    base = workloads.CONFIGS["c3_internlm25_7b_ragged"]  # 8 KV heads, 20 rows per KV head
+    cus = 256
+    cases = [(32, 6144, 1), (32, 6145, None), (32, 512, 1), (24, 3072, 1), (24, 3073, None), (23, 3072, None),
+             (16, 2048, None), (64, 6144, 1), (64, 8192, None)]
+    for batch, mx, want in cases:
+        cfg = base.with_(batch=batch, hist_len=mx, ragged_lo=1)
+        lens = np.full(batch, mx // 2, dtype=np.int32)
+        lens[0] = mx
+        assert rounds.one_piece_per_stream(mx, batch * 8, cus) == (want == 1), (batch, mx)
+        slots = rounds.auto_history_slots(cfg, lens, cus)
+        if want == 1:
+            assert slots == 1, (batch, mx)
+        else:
+            assert slots >= 2, (batch, mx)
+    # the VALU engine keeps the balanced count
+    assert rounds.auto_history_slots(base.with_(batch=32, hist_len=2048), np.full(32, 2048), cus, "valu") >= 2
 
 
 def test_view_token_stride_limit():

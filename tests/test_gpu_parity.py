@@ -651,6 +651,9 @@ def test_history_balanced_many_requests_and_empties():
 ROUND_CASES = {
     "narrow_uniform": C["c2_qwen3_8b"].with_(batch=3, hist_len=3000, chunk_len=1024),
     "narrow_ragged": C["c3_internlm25_7b_ragged"].with_(batch=7, hist_len=2500, ragged_lo=1, chunk_len=512),
+    # 256 streams of at most 3000 tokens: the library's choice is one piece per stream
+    "narrow_ragged_short_many": C["c3_internlm25_7b_ragged"].with_(batch=32, hist_len=3000, ragged_lo=1,
+                                                                   chunk_len=512),
     "wide_tree": C["c4_tree_72b"].with_(batch=2, hist_len=2600, chunk_len=1024),
     "wide_r96_ragged": C["c3_internlm25_7b_ragged"].with_(batch=3, n_queries=24, hist_len=2200, ragged_lo=1,
                                                           chunk_len=300),
@@ -679,6 +682,35 @@ def test_verify_round(name, n_slots):
     o_ref, lse_ref = oracle_round(inp)
     compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
     check_mask(rnd, inp)
+
+
+def test_round_slot_choice_short_ragged():
+    """ss_verify_round with n_slots = 0 on short ragged histories with at
+    least one stream per compute unit takes one piece per stream (its result
+    is the n_slots = 1 call's, bit for bit), and the Python helper's count
+    agrees; both match the oracle."""
+    cfg = ROUND_CASES["narrow_ragged_short_many"]
+    cus = rounds.device_cus()
+    streams = cfg.batch * cfg.n_kv_heads
+    inp = wl.make_inputs(cfg)
+    expect_one = rounds.one_piece_per_stream(int(inp.hist_len.max()), streams, cus)
+    log(f"[round slots] {streams} streams, longest history {int(inp.hist_len.max())}, {cus} CUs: one piece "
+        f"per stream expected: {expect_one}")
+    assert (rounds.auto_history_slots(cfg, inp.hist_len, cus) == 1) == expect_one
+    rnd = rounds.ResidentRound(inp)
+    work = ss.StateBuffers(rnd.problem, 12, "cuda")
+    outs = {}
+    for n_slots in (0, 1):
+        o, lse = torch.full_like(rnd.o, float("nan")), torch.full_like(rnd.lse, float("nan"))
+        ss.ss_verify_round(rnd.problem, rnd.q, rnd.hist_view, rnd.cand_view, rnd.parents, rnd.mask_out, n_slots,
+                           work, o, lse)
+        torch.cuda.synchronize()
+        outs[n_slots] = (o, lse)
+    if expect_one:
+        assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    o_ref, lse_ref = oracle_round(inp)
+    for n_slots in (0, 1):
+        compare(cfg, outs[n_slots][0].cpu().numpy(), outs[n_slots][1].cpu().numpy(), o_ref, lse_ref)
 
 
 def test_invalid_call_enqueues_nothing():
