@@ -527,7 +527,9 @@ SS_API int32_t ss_mfma_probe(const void* operands, int64_t n_operands, int32_t i
  *   covers for a request of len tokens.
  * ss_history_plan_host: the balanced cut of ss_verify_history for host
  *   lengths lens[batch] (clamped to [0, max_len]) over n_wg work-groups and
- *   n_slots >= 2 slots. For every slot (b, g, k) of
+ *   n_slots >= 2 slots (streams laid end to end, each padded to 128 tokens
+ *   and followed by a gap of 512 line positions that charges the start of a
+ *   piece; each work-group an even share of that line). For every slot (b, g, k) of
  *   plan[batch][n_kv_heads][n_slots][4] it stores {work-group, t0, t1,
  *   writes}: the work-group that writes it, the token range it covers
  *   (t0 = t1 = -1 for a slot filled with the empty state) and how many

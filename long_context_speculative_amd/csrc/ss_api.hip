@@ -1036,7 +1036,7 @@ extern "C" SS_API int32_t ss_history_plan_host(const int32_t* lens, int32_t batc
     int64_t total = 0, pad_max = 0;
     for (int32_t b = 0; b < batch; ++b) {
         const int64_t pad = plan_pad(len_of(b));
-        total += pad;
+        total += plan_span(len_of(b));
         if (pad > pad_max) pad_max = pad;
     }
     total *= n_kv_heads;
@@ -1053,7 +1053,7 @@ extern "C" SS_API int32_t ss_history_plan_host(const int32_t* lens, int32_t batc
         int32_t b_first = batch;
         int64_t line = 0, start = 0;
         for (int32_t b = 0; b < batch; ++b) {
-            const int64_t span = (int64_t)n_kv_heads * plan_pad(len_of(b));
+            const int64_t span = (int64_t)n_kv_heads * plan_span(len_of(b));
             if (start + span > lo || start >= lo) {
                 b_first = b;
                 line = start;

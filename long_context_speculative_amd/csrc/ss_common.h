@@ -35,17 +35,26 @@ __host__ __device__ inline void slot_tokens(int32_t len, int32_t chunk_len, int3
 // SpecStream section 4.2 makes the merged result independent of where the
 // history is cut, so the cuts are placed for an even load: the streams
 // (request b, KV head g) are laid end to end on one line, b-major, each
-// padded to a multiple of kPlanAlign tokens, and work-group w of n_wg takes
-// the line positions [w*L, (w+1)*L). L is the larger of total/n_wg and
-// pad_max/(n_slots-1), rounded up to kPlanAlign, so that no stream is cut
-// into more than n_slots pieces. Piece k of a stream that starts at line
-// position o is its part inside work-group floor(o/L)+k's range; it goes to
-// slot k; the slots after a stream's last piece hold empty states. A request
-// of length 0 has no pieces: the work-group whose range holds its line
-// position (the last busy one if that is past the end) owns its empty slots
-// (and the candidate region when it is folded in). The kernels leave empty
-// slots to a fill before the launch; fill_end records them for the host.
+// padded to a multiple of kPlanAlign tokens and followed by a gap of
+// plan_charge positions that stands for the cost of starting a piece, and
+// work-group w of n_wg takes the line positions [w*L, (w+1)*L). L is the
+// larger of total/n_wg (total counting the gaps) and pad_max/(n_slots-1),
+// rounded up to kPlanAlign, so that no stream is cut into more than n_slots
+// pieces. Piece k of a stream whose tokens sit at line positions [o, o+pad)
+// is their part inside work-group floor(o/L)+k's range; it goes to slot k;
+// the slots after a stream's last piece hold empty states. A stream of
+// length 0 has no pieces: the work-group whose range holds its position o
+// owns its empty slots (and the candidate region when it is folded in). The
+// kernels leave empty slots to a fill before the launch; fill_end records
+// them for the host.
 constexpr int kPlanAlign = 128;
+// Line positions charged per stream: a work-group pays about 6 us per piece
+// (the walk step, Q and the first loads, the merge across waves and the slot
+// write, the pipeline drained), the time it streams about 370 tokens in, so
+// ranges that hold more stream starts get fewer tokens. Measured on MI355X,
+// rounds of 8K-16K-token ragged histories run 6-8% faster with any charge
+// from 256 to 512; 512 leaves the 64K-token rounds as they were.
+constexpr int kPlanCharge = 512;
 
 __host__ __device__ inline int32_t clamp_len(int32_t len, int32_t max_len) {
     return len < 0 ? 0 : (len > max_len ? max_len : len);
@@ -53,6 +62,17 @@ __host__ __device__ inline int32_t clamp_len(int32_t len, int32_t max_len) {
 
 __host__ __device__ inline int64_t plan_pad(int32_t len, int32_t align = kPlanAlign) {
     return ((int64_t)len + align - 1) / align * align;
+}
+
+// The gap after each stream on the line, a multiple of align so that every
+// stream starts at an aligned position.
+__host__ __device__ inline int64_t plan_charge(int32_t align = kPlanAlign) {
+    return ((int64_t)kPlanCharge + align - 1) / align * align;
+}
+
+// Line positions of one stream: its padded tokens and the gap after them.
+__host__ __device__ inline int64_t plan_span(int32_t len, int32_t align = kPlanAlign) {
+    return plan_pad(len, align) + plan_charge(align);
 }
 
 // Tokens per work-group; n_slots >= 2, n_wg >= 1.
@@ -99,35 +119,32 @@ __host__ __device__ inline bool plan_next(const LenFn& len_of, int32_t batch, in
     const int64_t w_last = plan_last_wg(total, piece_len);
     if (w > w_last) return false;
     while (c.b < batch) {
-        if (c.line >= hi && w != w_last) return false;
+        // streams only start later from here on: none reaches w's range
+        if (c.line >= hi) return false;
         const int32_t len = len_of(c.b);
-        const int64_t pad = plan_pad(len, align);
-        if (pad == 0) {
-            const int64_t at = c.line / piece_len;
-            if ((at < w_last ? at : w_last) == w && c.g < n_kv_heads) {
-                out = PlanPiece{c.b, c.g, -1, n_slots, 0, 0};
-                ++c.g;
+        const int64_t pad = plan_pad(len, align), span = pad + plan_charge(align);
+        while (c.g < n_kv_heads) {
+            const int64_t o = c.line + (int64_t)c.g * span;
+            if (o >= hi) return false;
+            const int32_t g = c.g++;
+            if (pad == 0) {
+                // no tokens: the range that holds o owns the stream
+                if (o < lo) continue;
+                out = PlanPiece{c.b, g, -1, n_slots, 0, 0};
                 return true;
             }
-        } else {
-            while (c.g < n_kv_heads) {
-                const int64_t o = c.line + (int64_t)c.g * pad;
-                // streams only start later from here on: none reaches w's range
-                if (o >= hi) return false;
-                const int32_t g = c.g++;
-                if (o + pad <= lo) continue;
-                const int32_t k = (int32_t)(w - o / piece_len);
-                const int32_t n_pieces = (int32_t)((o + pad - 1) / piece_len - o / piece_len + 1);
-                int64_t t0 = lo - o, t1 = hi - o;
-                if (t0 < 0) t0 = 0;
-                if (t1 > pad) t1 = pad;
-                if (t0 > len) t0 = len;
-                if (t1 > len) t1 = len;
-                out = PlanPiece{c.b, g, k, k == n_pieces - 1 ? n_slots : k + 1, t0, t1};
-                return true;
-            }
+            if (o + pad <= lo) continue;
+            const int32_t k = (int32_t)(w - o / piece_len);
+            const int32_t n_pieces = (int32_t)((o + pad - 1) / piece_len - o / piece_len + 1);
+            int64_t t0 = lo - o, t1 = hi - o;
+            if (t0 < 0) t0 = 0;
+            if (t1 > pad) t1 = pad;
+            if (t0 > len) t0 = len;
+            if (t1 > len) t1 = len;
+            out = PlanPiece{c.b, g, k, k == n_pieces - 1 ? n_slots : k + 1, t0, t1};
+            return true;
         }
-        c.line += (int64_t)n_kv_heads * pad;
+        c.line += (int64_t)n_kv_heads * span;
         ++c.b;
         c.g = 0;
     }

@@ -578,7 +578,8 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
     int64_t total = 0, pad_max = 0;
     for (int b0 = 0; b0 < p.batch; b0 += 64) {
         const int b = b0 + lane;
-        int64_t sum = b < p.batch ? plan_pad(len_of(b), p.plan_align) : 0, mx = sum;
+        int64_t mx = b < p.batch ? plan_pad(len_of(b), p.plan_align) : 0;
+        int64_t sum = b < p.batch ? mx + plan_charge(p.plan_align) : 0;
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
             sum += __shfl_xor(sum, off);
@@ -599,7 +600,7 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p
     int64_t line = 0, carry = 0;
     for (int b0 = 0; b0 < p.batch; b0 += 64) {
         const int b = b0 + lane;
-        const int64_t span = b < p.batch ? (int64_t)p.n_kv_heads * plan_pad(len_of(b), p.plan_align) : 0;
+        const int64_t span = b < p.batch ? (int64_t)p.n_kv_heads * plan_span(len_of(b), p.plan_align) : 0;
         int64_t incl = span;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {

@@ -46,6 +46,11 @@ def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int, engine="auto") -> i
     return max(1, units // (wgs_per_cu(cfg, engine) * cus))
 
 
+# Line positions the balanced cut charges per stream for starting a piece
+# (kPlanCharge of the library's plan, at its 128-token alignment).
+PLAN_CHARGE = 512
+
+
 def one_piece_per_stream(max_len: int, streams: int, cus: int) -> bool:
     """Whether ragged histories on the narrow MFMA kernel run faster as one
     piece per stream (one slot: a work-group per (request, KV head), all in
@@ -79,9 +84,10 @@ def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
     wave = wgs_per_cu(cfg, engine) * cus
     if not cfg.ragged:
         return max(1, wave // (cfg.batch * cfg.n_kv_heads))
-    total = sum(pads) * cfg.n_kv_heads
-    if total == 0:
+    if not any(pads):
         return 2
+    # the line also holds a gap of PLAN_CHARGE positions after every stream
+    total = (sum(pads) + PLAN_CHARGE * len(pads)) * cfg.n_kv_heads
     if narrow_mfma(cfg, engine) and one_piece_per_stream(max((int(n) for n in hist_len), default=0),
                                                           cfg.batch * cfg.n_kv_heads, cus):
         return 1

@@ -220,17 +220,22 @@ def test_slot_tokens_host_tile_history():
     assert ss.ss_slot_tokens_host(1000, 64, 3, 5, 2, 2) == (7 * 64, 8 * 64)
 
 
+CHARGE = 512  # line positions the cut charges per stream (kPlanCharge)
+
+
 def _check_plan(lens, hkv, max_len, n_wg, n_slots):
     """Invariants of the balanced cut of ss_verify_history: every slot of
     every stream is written exactly once; the computed pieces of a stream
     come first and tile [0, len) in order; the rest are empty fills; no
-    work-group outside the grid is used, and no work-group gets more than
-    piece_len (padded) tokens or more than its share plus one alignment
-    step."""
+    work-group outside the grid is used; no work-group gets more than
+    piece_len (padded) tokens, nor more line positions than piece_len plus
+    one charge when the charge of every stream it finishes is counted; the
+    ranges are an even share of the line (tokens and charges) plus one
+    alignment step unless the slot budget needs more."""
     plan, piece_len = ss.ss_history_plan_host(lens, hkv, max_len, n_wg, n_slots)
     lens_c = np.clip(np.asarray(lens, dtype=np.int64), 0, max_len)
     pad = -(-lens_c // 128) * 128
-    total = int(pad.sum()) * hkv
+    total = (int(pad.sum()) + CHARGE * len(lens_c)) * hkv
     assert piece_len % 128 == 0 and piece_len >= 128
     # the cut grows past an even share only to respect the slot budget
     even = -(-total // n_wg)
@@ -238,6 +243,7 @@ def _check_plan(lens, hkv, max_len, n_wg, n_slots):
     assert piece_len < max(even, cap, 128) + 128
     assert (plan[..., 3] == 1).all(), "a slot written zero or several times"
     load = {}
+    charged = {}
     for b, n in enumerate(lens_c):
         for g in range(hkv):
             e = plan[b, g]
@@ -245,6 +251,9 @@ def _check_plan(lens, hkv, max_len, n_wg, n_slots):
             assert computed == list(range(len(computed)))
             if n == 0:
                 assert not computed
+                # the work-group whose range holds the stream's line position
+                o = (int(pad[:b].sum()) + CHARGE * b) * hkv + g * CHARGE
+                assert (e[:, 0] == min(o // piece_len, n_wg - 1)).all()
                 continue
             assert computed, "a non-empty stream without pieces"
             assert e[0, 1] == 0 and e[computed[-1], 2] == n
@@ -260,7 +269,9 @@ def _check_plan(lens, hkv, max_len, n_wg, n_slots):
             # consecutive pieces go to consecutive work-groups
             wgs = [int(e[k, 0]) for k in computed]
             assert wgs == list(range(wgs[0], wgs[0] + len(wgs)))
+            charged[wgs[-1]] = charged.get(wgs[-1], 0) + CHARGE
     assert all(v <= piece_len for v in load.values())
+    assert all(v + charged.get(w, 0) <= piece_len + CHARGE for w, v in load.items())
     return plan, piece_len
 
 
@@ -278,19 +289,25 @@ def test_history_plan_host_random(seed):
 
 
 def test_history_plan_host_cases():
-    # uniform lengths: equal ranges, one stream per pair of work-groups
+    # uniform lengths: equal ranges, about one stream per pair of work-groups
     plan, L = _check_plan([32768] * 16, 8, 32768, 256, 4)
-    assert L == 16384 and int(plan[..., 0].max()) == 255
+    # (32768 + 512) * 128 / 256 positions per range; the last stream's tokens end in range 255
+    assert L == 16640 and int(plan[..., 0].max()) == (127 * (32768 + CHARGE) + 32768 - 1) // L
     # the ragged long-history shape: every work-group gets an even share
     lens = workloads.draw_lengths(workloads.CONFIGS["c3_internlm25_7b_ragged"]).astype(np.int64)
     plan, L = _check_plan(lens, 8, int(max(lens)), 512, 6)
-    assert L == -(-(-(-lens // 128) * 128).sum() * 8 // 512 // 128) * 128
+    assert L == -(-(-(-((-(-lens // 128) * 128).sum() + CHARGE * len(lens)) * 8 // 512)) // 128) * 128
+    # a range holding more stream starts gets fewer tokens: 64 streams of
+    # 1000 tokens (1024 padded, 1536 with the charge) on 22 work-groups
+    plan, L = _check_plan([1000] * 64, 1, 1000, 22, 3)
+    assert L == -(-(-(-64 * (1024 + CHARGE) // 22)) // 128) * 128 == 4480
     # a slot budget too small for an even cut widens the ranges
     plan, L = _check_plan([100000], 1, 100000, 512, 2)
     assert L >= 100096 // 1 and (plan[0, 0, :, 1] >= 0).sum() <= 2
-    # only empty requests: all slots filled empty by work-group 0
+    # only empty requests: every slot filled empty, each stream by the
+    # work-group whose range holds its charge
     plan, L = _check_plan([0, 0, 0], 4, 10, 8, 3)
-    assert (plan[..., 0] == 0).all() and (plan[..., 1] == -1).all()
+    assert (plan[..., 1] == -1).all() and int(plan[..., 0].max()) > 0
     # lengths past max_len are clamped, negative ones read as empty
     _check_plan([5000, -3, 10**6], 2, 4096, 16, 4)
     with pytest.raises(ss.SSError):
@@ -460,7 +477,7 @@ def test_auto_history_slots_keep_the_even_cut():
         if rounds.one_piece_per_stream(int(lens.max()), b * hkv, n_wg) and lens.any():
             assert slots == 1
             continue
-        total = sum(-(-int(n) // 128) * 128 for n in lens) * hkv
+        total = sum(-(-int(n) // 128) * 128 + CHARGE for n in lens) * hkv
         even = max(128, -(-(-(-total // n_wg)) // 128) * 128)
         plan, piece = ss.ss_history_plan_host(lens, hkv, mx, n_wg, slots)
         assert (plan[..., 3] == 1).all()
