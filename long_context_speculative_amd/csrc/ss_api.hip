@@ -443,11 +443,11 @@ int32_t merge_states(const ss_problem_t* problem, const ss_state_t* in, const in
 // stream (a work-group per (request, KV head), all in parallel) than under
 // the balanced cut, whose work-groups run two or three short pieces one
 // after another, each paying its start and its merge. Measured on MI355X
-// (256 CUs), lengths uniform in [n/8, n]: 1.05-1.5x faster up to n = 6144
-// with at least one stream per CU (even or slower at 8192), and up to 3072
-// with three streams per four CUs; fewer streams leave CUs idle.
+// (256 CUs), lengths uniform in [n/8, n]: 1.07-1.33x faster at n <= 2048
+// with 192 to 1024 streams, even at 3072-4096, slower beyond; fewer streams
+// leave CUs idle.
 bool one_piece_per_stream(int64_t max_len, int64_t streams, int64_t cus) {
-    return (max_len <= 6144 && streams >= cus) || (max_len <= 3072 && 4 * streams >= 3 * cus);
+    return max_len <= 2048 && 4 * streams >= 3 * cus;
 }
 
 // Slots per (request, KV head) of a whole-round call for this problem and

@@ -57,11 +57,11 @@ def one_piece_per_stream(max_len: int, streams: int, cus: int) -> bool:
     parallel) than under the balanced cut, whose work-groups run two or
     three short pieces one after another, each paying its start and merge.
     Measured on MI355X (256 CUs), lengths uniform in [n/8, n]: one piece per
-    stream is 1.05-1.5x faster up to n = 6144 with at least one stream per
-    CU (even or slower at 8192), and up to 3072 with three streams per four
-    CUs; with fewer streams it leaves CUs idle. The library's own slot choice
-    (ss_verify_round with n_slots = 0) applies the same rule."""
-    return (max_len <= 6144 and streams >= cus) or (max_len <= 3072 and 4 * streams >= 3 * cus)
+    stream is 1.07-1.33x faster at n <= 2048 with 192 to 1024 streams, even
+    at 3072-4096 and slower beyond; with fewer streams it leaves CUs idle.
+    The library's own slot choice (ss_verify_round with n_slots = 0) applies
+    the same rule."""
+    return max_len <= 2048 and 4 * streams >= 3 * cus
 
 
 def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:

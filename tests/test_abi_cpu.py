@@ -489,15 +489,14 @@ def test_auto_history_slots_keep_the_even_cut():
 
 def test_short_ragged_histories_take_one_piece_per_stream():
     """The slot rule for ragged histories on the narrow MFMA kernel: one slot
-    (a work-group per stream) when the longest history is at most 6144 tokens
-    with at least one stream per compute unit, or at most 3072 with three
-    streams per four units; the balanced cut otherwise, and always on the
-    VALU engine."""
+    (a work-group per stream) when the longest history is at most 2048 tokens
+    with at least three streams per four compute units; the balanced cut
+    otherwise, and always on the VALU engine."""
     from long_context_speculative_amd import rounds
     base = workloads.CONFIGS["c3_internlm25_7b_ragged"]  # 8 KV heads, 20 rows per KV head
     cus = 256
-    cases = [(32, 6144, 1), (32, 6145, None), (32, 512, 1), (24, 3072, 1), (24, 3073, None), (23, 3072, None),
-             (16, 2048, None), (64, 6144, 1), (64, 8192, None)]
+    cases = [(32, 2048, 1), (32, 2049, None), (32, 512, 1), (24, 2048, 1), (23, 2048, None), (24, 3072, None),
+             (16, 2048, None), (128, 2048, 1), (128, 4096, None)]
     for batch, mx, want in cases:
         cfg = base.with_(batch=batch, hist_len=mx, ragged_lo=1)
         lens = np.full(batch, mx // 2, dtype=np.int32)

@@ -651,8 +651,8 @@ def test_history_balanced_many_requests_and_empties():
 ROUND_CASES = {
     "narrow_uniform": C["c2_qwen3_8b"].with_(batch=3, hist_len=3000, chunk_len=1024),
     "narrow_ragged": C["c3_internlm25_7b_ragged"].with_(batch=7, hist_len=2500, ragged_lo=1, chunk_len=512),
-    # 256 streams of at most 3000 tokens: the library's choice is one piece per stream
-    "narrow_ragged_short_many": C["c3_internlm25_7b_ragged"].with_(batch=32, hist_len=3000, ragged_lo=1,
+    # 256 streams of at most 2000 tokens: the library's choice is one piece per stream
+    "narrow_ragged_short_many": C["c3_internlm25_7b_ragged"].with_(batch=32, hist_len=2000, ragged_lo=1,
                                                                    chunk_len=512),
     "wide_tree": C["c4_tree_72b"].with_(batch=2, hist_len=2600, chunk_len=1024),
     "wide_r96_ragged": C["c3_internlm25_7b_ragged"].with_(batch=3, n_queries=24, hist_len=2200, ragged_lo=1,
