@@ -287,7 +287,10 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
  * 4.2: the committed history and the masked candidate region in partial
  * states, Eq. 7, folded by Eq. 8 into O = acc / l and lse, Eq. 9):
  * ss_verify_history with the candidate region into slots [0, n_slots) of
- * `work`, then ss_merge_states over those slots into o and lse.
+ * `work`, then ss_merge_states over those slots into o and lse. With one
+ * slot on the narrow MFMA engine the history launch writes o and lse itself
+ * (the merge of a single state, with the merge's arithmetic) and no merge
+ * launch follows; `work` is then not written.
  *
  *   q, hist, cand, parents, mask_out   as ss_verify_history (cand required)
  *   n_slots   slots per (request, KV head) for the history cut, or 0: the

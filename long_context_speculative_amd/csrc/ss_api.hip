@@ -296,12 +296,22 @@ CandParams make_cand_params(const ss_problem_t* problem, const void* q, const ss
 
 namespace {
 
+// Where a whole-round call wants O and lse (see finish in verify_history).
+struct FinishOut {
+    float* o;
+    float* lse;
+};
+
 // ss_verify_history without the status bookkeeping of the export (shared
-// with the whole-round calls).
+// with the whole-round calls). With `fin` (whole-round calls), a round of
+// one slot per stream on the narrow MFMA kernel writes the finished rows
+// into fin->o / fin->lse instead of the slots, and *merged is set: the
+// caller then launches no merge.
 int32_t verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
                        const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out,
                        const ss_block_stats_t* stats, int32_t n_slots, const ss_state_t* out, int32_t slot_begin,
-                       ss_stream_t stream) {
+                       ss_stream_t stream, const FinishOut* fin = nullptr, bool* merged = nullptr) {
+    if (merged) *merged = false;
     if (!hist) return fail(SS_ERR_INVALID_ARG, "history view is NULL");
     if (n_slots < 1) return fail(SS_ERR_INVALID_ARG, "n_slots must be at least 1");
     // validation first (the chunk length does not change its outcome)
@@ -365,6 +375,12 @@ int32_t verify_history(const ss_problem_t* problem, const void* q, const ss_kv_v
                               problem->head_dim, s);
         if (e != hipSuccess) return fail(SS_ERR_HIP, "candidate kernel launch failed: %s", hipGetErrorString(e));
     }
+    // one slot per stream, every stream's candidates in it: the slot is the result
+    const bool finish = fin && narrow && !stats && hist_slots == 1 && (fuse || !cand);
+    if (finish) {
+        c.fin_o = fin->o;
+        c.fin_lse = fin->lse;
+    }
     if (narrow && hist->req_len && hist_slots >= 2) {
         c.plan_slots = hist_slots;
         // every slot starts empty; pieces overwrite theirs
@@ -377,6 +393,7 @@ int32_t verify_history(const ss_problem_t* problem, const void* q, const ss_kv_v
         e = enqueue_chunk(problem, c, s);
     }
     if (e != hipSuccess) return fail(SS_ERR_HIP, "history kernel launch failed: %s", hipGetErrorString(e));
+    if (merged) *merged = finish;
     return SS_OK;
 }
 
@@ -514,8 +531,11 @@ int32_t validate_round(const ss_problem_t* problem, const void* q, const ss_kv_v
 int32_t verify_round(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
                      const ss_kv_view_t* cand, const int32_t* parents, uint64_t* mask_out, int32_t n_slots,
                      const ss_state_t* st, float* o, float* lse, ss_stream_t stream) {
-    int32_t rc = verify_history(problem, q, hist, cand, parents, mask_out, nullptr, n_slots, st, 0, stream);
-    if (rc) return rc;
+    const FinishOut fin{o, lse};
+    bool merged = false;
+    int32_t rc = verify_history(problem, q, hist, cand, parents, mask_out, nullptr, n_slots, st, 0, stream, &fin,
+                                &merged);
+    if (rc || merged) return rc;
     ss_state_t used = *st;  // the merge folds the slots this round wrote, not the whole storage
     used.n_slots = n_slots;
     return merge_states(problem, &used, nullptr, o, lse, stream);

@@ -477,9 +477,19 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
         if (r >= p.rows) continue;
         const int i = r / p.group, h = at.g() * p.group + r % p.group;
         const int64_t row = (((int64_t)at.slot() * p.batch + at.b()) * p.n_queries + i) * p.n_q_heads + h;
+        // One slot per stream in a whole-round call (fin_o): the merge of a
+        // single state is O = acc / l, lse = m + ln l, written here with the
+        // merge kernel's arithmetic instead of the slot.
+        const int64_t orow = ((int64_t)at.b() * p.n_queries + i) * p.n_q_heads + h;
+        const float m_nat = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
+        const bool seen = m_nat != -INFINITY && l_run[rt] > 0.f;
         if (w == 0 && q4 == 0) {
-            p.m[row] = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
-            p.l[row] = l_run[rt];
+            if (p.fin_o) {
+                p.fin_lse[orow] = seen ? m_nat + __builtin_amdgcn_logf(l_run[rt]) * kLn2 : -INFINITY;
+            } else {
+                p.m[row] = m_nat;
+                p.l[row] = l_run[rt];
+            }
         }
 #pragma unroll
         for (int xt = 0; xt < NXT; ++xt) {
@@ -496,7 +506,13 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
                 }
                 v[j] = x;
             }
-            *reinterpret_cast<floatx4*>(p.acc + row * D + 16 * xt + 4 * q4) = v;
+            if (p.fin_o) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = seen ? v[j] / l_run[rt] : 0.f;
+                *reinterpret_cast<floatx4*>(p.fin_o + orow * D + 16 * xt + 4 * q4) = v;
+            } else {
+                *reinterpret_cast<floatx4*>(p.acc + row * D + 16 * xt + 4 * q4) = v;
+            }
         }
     }
 }

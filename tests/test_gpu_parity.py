@@ -684,6 +684,60 @@ def test_verify_round(name, n_slots):
     check_mask(rnd, inp)
 
 
+ONE_SLOT_CASES = {
+    "ragged_empties": C["c3_internlm25_7b_ragged"].with_(batch=70, hist_len=2000, ragged_lo=1, chunk_len=256),
+    "ragged_no_history": C["c3_internlm25_7b_ragged"].with_(batch=4, hist_len=300, ragged_lo=1, chunk_len=128),
+    "ragged_tree_32_rows": C["c3_internlm25_7b_ragged"].with_(batch=5, n_queries=8, mask="tree", hist_len=3000,
+                                                              ragged_lo=1, chunk_len=512),
+    "uniform": C["c2_qwen3_8b"].with_(batch=3, hist_len=3000, chunk_len=1024),
+    "uniform_4_rows": C["c2_qwen3_8b"].with_(batch=2, n_queries=1, hist_len=1500, chunk_len=512),
+}
+
+
+@pytest.mark.parametrize("name", list(ONE_SLOT_CASES))
+def test_round_one_slot_writes_the_result(name):
+    """ss_verify_round with one slot per stream on the narrow MFMA engine
+    writes O and lse from the history launch (no merge launch): the same
+    values as ss_verify_history into one slot followed by ss_merge_states,
+    with the outputs poisoned before each call; the workspace is left
+    untouched; the result matches the oracle. Ragged cases include empty
+    requests, with and without any history."""
+    cfg = ONE_SLOT_CASES[name]
+    inp = wl.make_inputs(cfg)
+    if cfg.ragged:
+        inp.hist_len = inp.hist_len.copy()
+        if name == "ragged_empties":
+            inp.hist_len[[0, 5, 6, 40, 68, 69]] = 0
+            inp.hist_len[7], inp.hist_len[8], inp.hist_len[9] = 1, 128, 129
+        elif name == "ragged_no_history":
+            inp.hist_len[:] = 0
+    log(f"[one-slot round] {name}: rows={cfg.rows}")
+    rnd = rounds.ResidentRound(inp, split="balanced", history_slots=1, fuse_candidates=True)
+    assert rnd.n_call_slots == 1
+    # the launch path: one slot, then the merge
+    rnd.o.fill_(float("nan"))
+    rnd.lse.fill_(float("nan"))
+    rnd.run()
+    torch.cuda.synchronize()
+    o_m, lse_m, mask_m = rnd.o.clone(), rnd.lse.clone(), rnd.mask_out.clone()
+    work = ss.StateBuffers(rnd.problem, 4, "cuda")
+    for t in (work.acc, work.m, work.l):
+        t.fill_(float("nan"))
+    for rep in range(2):
+        rnd.o.fill_(float("nan"))
+        rnd.lse.fill_(float("nan"))
+        rnd.mask_out.fill_(-1)
+        ss.ss_verify_round(rnd.problem, rnd.q, rnd.hist_view, rnd.cand_view, rnd.parents, rnd.mask_out, 1, work,
+                           rnd.o, rnd.lse)
+        torch.cuda.synchronize()
+        assert torch.equal(rnd.o, o_m) and torch.equal(rnd.lse, lse_m), (name, rep)
+        assert torch.equal(rnd.mask_out, mask_m), (name, rep)
+    assert torch.isnan(work.m).all() and torch.isnan(work.acc).all()
+    o_ref, lse_ref = oracle_round(inp)
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
+
+
 def test_round_slot_choice_short_ragged():
     """ss_verify_round with n_slots = 0 on short ragged histories with at
     least one stream per compute unit takes one piece per stream (its result
