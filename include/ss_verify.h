@@ -297,9 +297,9 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
  *             library's choice (one piece per work-group of one full launch
  *             where the lengths are known on the host; for ragged lengths
  *             on the narrow MFMA kernel 1 -- a work-group per stream -- when
- *             hist->max_len <= 2048 with at least three streams per four
- *             compute units, else 8 for the balanced cut; +1 for the
- *             candidate slot on the VALU engines),
+ *             hist->max_len <= 4096 with at least one stream per compute
+ *             unit or <= 2048 with three per four units, else 8 for the
+ *             balanced cut; +1 for the candidate slot on the VALU engines),
  *             limited to work->n_slots
  *   work      caller-allocated state slots (workspace); slots [0, n_slots)
  *             are overwritten, their contents afterwards are not part of

@@ -456,15 +456,17 @@ int32_t merge_states(const ss_problem_t* problem, const ss_state_t* in, const in
     return SS_OK;
 }
 
-// Ragged histories on the narrow MFMA kernel that run faster as one piece per
-// stream (a work-group per (request, KV head), all in parallel) than under
-// the balanced cut, whose work-groups run two or three short pieces one
-// after another, each paying its start and its merge. Measured on MI355X
-// (256 CUs), lengths uniform in [n/8, n]: 1.07-1.33x faster at n <= 2048
-// with 192 to 1024 streams, even at 3072-4096, slower beyond; fewer streams
-// leave CUs idle.
+// Ragged histories on the narrow MFMA kernel whose whole-round call runs
+// faster as one piece per stream (a work-group per (request, KV head), all
+// in parallel, finishing O and lse in the same launch) than under the
+// balanced cut, whose work-groups run two or three short pieces one after
+// another, each paying its start and its merge, and then a merge launch.
+// Measured on MI355X (256 CUs), whole-round calls, lengths uniform in
+// [n/8, n]: with at least one stream per CU 1.25-1.35x faster at n = 2048,
+// 1.03-1.06x at 4096, slower from 5120; with 192 streams 1.23x at 2048, even
+// at 3072; fewer streams leave CUs idle.
 bool one_piece_per_stream(int64_t max_len, int64_t streams, int64_t cus) {
-    return max_len <= 2048 && 4 * streams >= 3 * cus;
+    return (max_len <= 4096 && streams >= cus) || (max_len <= 2048 && 4 * streams >= 3 * cus);
 }
 
 // Slots per (request, KV head) of a whole-round call for this problem and

@@ -56,11 +56,12 @@ def one_piece_per_stream(max_len: int, streams: int, cus: int) -> bool:
     piece per stream (one slot: a work-group per (request, KV head), all in
     parallel) than under the balanced cut, whose work-groups run two or
     three short pieces one after another, each paying its start and merge.
-    Measured on MI355X (256 CUs), lengths uniform in [n/8, n]: one piece per
-    stream is 1.07-1.33x faster at n <= 2048 with 192 to 1024 streams, even
-    at 3072-4096 and slower beyond; with fewer streams it leaves CUs idle.
-    The library's own slot choice (ss_verify_round with n_slots = 0) applies
-    the same rule."""
+    Measured on MI355X (256 CUs), lengths uniform in [n/8, n], history and
+    merge launches: one piece per stream is 1.07-1.33x faster at n <= 2048
+    with 192 to 1024 streams, even at 3072-4096 and slower beyond; with
+    fewer streams it leaves CUs idle. (The library's own slot choice for
+    ss_verify_round, whose one-slot rounds also skip the merge launch, takes
+    one slot up to 4096 tokens when every CU has a stream.)"""
     return max_len <= 2048 and 4 * streams >= 3 * cus
 
 
