@@ -28,6 +28,9 @@ SEQUENCE = [
     ("narrow_ragged_large", C["c3_internlm25_7b_ragged"].with_(batch=24, hist_len=9000, ragged_lo=1,
                                                                 chunk_len=1024)),
     ("wide_tree", C["c4_tree_72b"].with_(batch=2, hist_len=3000, chunk_len=1024)),
+    # 256 streams of at most 2000 tokens: one slot per stream, O and lse from the history launch
+    ("narrow_ragged_one_slot", C["c3_internlm25_7b_ragged"].with_(batch=32, hist_len=2000, ragged_lo=1,
+                                                                  chunk_len=512)),
     ("narrow_uniform_small", C["c2_qwen3_8b"].with_(batch=2, hist_len=1500, chunk_len=512)),
     ("valu_small_rows", C["c2_qwen3_8b"].with_(batch=2, n_queries=2, hist_len=700, chunk_len=256)),
     ("f32_tiny", C["c1_tiny_f32"]),
@@ -98,6 +101,8 @@ def test_noalloc_round_rejects_oversized_state():
 GRAPH_CASES = {
     "narrow_ragged": C["c3_internlm25_7b_ragged"].with_(batch=8, hist_len=5000, ragged_lo=1, chunk_len=1024),
     "wide_tree": C["c4_tree_72b"].with_(batch=2, hist_len=2600, chunk_len=1024),
+    "narrow_ragged_one_slot": C["c3_internlm25_7b_ragged"].with_(batch=32, hist_len=1800, ragged_lo=1,
+                                                                 chunk_len=512),
 }
 
 
