@@ -288,7 +288,7 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
  * states, Eq. 7, folded by Eq. 8 into O = acc / l and lse, Eq. 9):
  * ss_verify_history with the candidate region into slots [0, n_slots) of
  * `work`, then ss_merge_states over those slots into o and lse. With one
- * slot on the narrow MFMA engine the history launch writes o and lse itself
+ * slot on the MFMA engines the history launch writes o and lse itself
  * (the merge of a single state, with the merge's arithmetic) and no merge
  * launch follows; `work` is then not written.
  *

@@ -304,7 +304,7 @@ struct FinishOut {
 
 // ss_verify_history without the status bookkeeping of the export (shared
 // with the whole-round calls). With `fin` (whole-round calls), a round of
-// one slot per stream on the narrow MFMA kernel writes the finished rows
+// one slot per stream on the MFMA kernels (narrow and wide-row) writes the finished rows
 // into fin->o / fin->lse instead of the slots, and *merged is set: the
 // caller then launches no merge.
 int32_t verify_history(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist,
@@ -376,7 +376,8 @@ int32_t verify_history(const ss_problem_t* problem, const void* q, const ss_kv_v
         if (e != hipSuccess) return fail(SS_ERR_HIP, "candidate kernel launch failed: %s", hipGetErrorString(e));
     }
     // one slot per stream, every stream's candidates in it: the slot is the result
-    const bool finish = fin && narrow && !stats && hist_slots == 1 && (fuse || !cand);
+    const bool finish =
+        fin && (narrow || engine == ChunkEngine::kMfmaWide) && !stats && hist_slots == 1 && (fuse || !cand);
     if (finish) {
         c.fin_o = fin->o;
         c.fin_lse = fin->lse;

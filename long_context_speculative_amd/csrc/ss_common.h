@@ -258,7 +258,7 @@ struct ChunkParams {
     // Tokens of every request's whole history when req_len is NULL (the view
     // may show only a part of it, as a staging chunk does).
     int64_t full_len;
-    // Whole-round calls with one slot per stream (narrow MFMA chunk kernel):
+    // Whole-round calls with one slot per stream (MFMA chunk kernels):
     // fin_o [B][n_queries][Hq][d] and fin_lse [B][n_queries][Hq] receive the
     // finished rows instead of the slot states. NULL: write the slots.
     float* fin_o;

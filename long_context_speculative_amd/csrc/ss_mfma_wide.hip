@@ -84,7 +84,10 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
         (__attribute__((address_space(3))) s16x4*)(reinterpret_cast<uintptr_t>(p)));
 }
 
-template <int NW, int kRT, int KT>
+// FIN: one slot per stream in a whole-round call, the rows finished into
+// p.fin_o / p.fin_lse instead of the slot (a variant of its own: at 256
+// registers the plain kernel has no room for the other epilogue).
+template <int NW, int kRT, int KT, bool FIN>
 __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk_mfma_wide_kernel(ChunkParams p, int row_groups) {
     static_assert(KT % kTile == 0, "an iteration is whole sub-tiles");
     constexpr int kSub = KT / kTile;           // 32-key sub-tiles per iteration
@@ -501,13 +504,32 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
         if (r >= p.rows) continue;
         const int i = r / p.group, h = g * p.group + r % p.group;
         const int64_t row = (((int64_t)(p.slot_begin + s) * p.batch + b) * p.n_queries + i) * p.n_q_heads + h;
+        const float m_nat = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
+        const float lr = ol[rt][0];  // every lane holds its row's l
+        // One slot per stream in a whole-round call (fin_o): the merge of a
+        // single state, O = acc / l and lse = m + ln l, with the merge
+        // kernel's arithmetic, written instead of the slot.
+        constexpr bool fin = FIN;
+        const int64_t orow = ((int64_t)b * p.n_queries + i) * p.n_q_heads + h;
+        const bool seen = m_nat != -INFINITY && lr > 0.f;
         if (q4 == 0) {
-            p.m[row] = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
-            p.l[row] = ol[rt][0];
+            if constexpr (fin) {
+                p.fin_lse[orow] = seen ? m_nat + __builtin_amdgcn_logf(lr) * kLn2 : -INFINITY;
+            } else {
+                p.m[row] = m_nat;
+                p.l[row] = lr;
+            }
         }
+        float* dst = (fin ? p.fin_o + orow * D : p.acc + row * D) + 4 * q4;
 #pragma unroll
-        for (int xt = 0; xt < kNXT; ++xt)
-            *reinterpret_cast<floatx4*>(p.acc + row * D + 16 * xt + 4 * q4) = o[xt][rt];
+        for (int xt = 0; xt < kNXT; ++xt) {
+            floatx4 v = o[xt][rt];
+            if constexpr (fin) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) v[j] = seen ? v[j] / lr : 0.f;
+            }
+            *reinterpret_cast<floatx4*>(dst + 16 * xt) = v;
+        }
     }
 }
 
@@ -518,7 +540,10 @@ hipError_t launch_wide_t(const ChunkParams& p, hipStream_t stream) {
     const int64_t gx = (units + 7) / 8 * 8 * row_groups;
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     dim3 grid((unsigned)gx, 1, p.batch);
-    hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW, kRT, KT>), grid, dim3(64 * NW), 0, stream, p, row_groups);
+    if (p.fin_o)
+        hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW, kRT, KT, true>), grid, dim3(64 * NW), 0, stream, p, row_groups);
+    else
+        hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW, kRT, KT, false>), grid, dim3(64 * NW), 0, stream, p, row_groups);
     return hipGetLastError();
 }
 

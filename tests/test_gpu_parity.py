@@ -691,13 +691,19 @@ ONE_SLOT_CASES = {
                                                               ragged_lo=1, chunk_len=512),
     "uniform": C["c2_qwen3_8b"].with_(batch=3, hist_len=3000, chunk_len=1024),
     "uniform_4_rows": C["c2_qwen3_8b"].with_(batch=2, n_queries=1, hist_len=1500, chunk_len=512),
+    # wide-row kernel: 8-wave groups (512 rows per KV head, a tree) and 4-wave groups (96 rows)
+    "wide_tree": C["c4_tree_72b"].with_(batch=2, hist_len=2600, chunk_len=1024),
+    "wide_tree_short_histories": C["c4_tree_72b"].with_(batch=3, hist_len=70, ragged_lo=1, chunk_len=64),
+    "wide_96_rows_ragged": C["c3_internlm25_7b_ragged"].with_(batch=3, n_queries=24, hist_len=2200, ragged_lo=1,
+                                                              chunk_len=300),
 }
 
 
 @pytest.mark.parametrize("name", list(ONE_SLOT_CASES))
 def test_round_one_slot_writes_the_result(name):
-    """ss_verify_round with one slot per stream on the narrow MFMA engine
-    writes O and lse from the history launch (no merge launch): the same
+    """ss_verify_round with one slot per stream on the MFMA engines (narrow
+    and wide-row) writes O and lse from the history launch (no merge
+    launch): the same
     values as ss_verify_history into one slot followed by ss_merge_states,
     with the outputs poisoned before each call; the workspace is left
     untouched; the result matches the oracle. Ragged cases include empty
