@@ -13,9 +13,11 @@
 // product, every row's softmax one wave's reduction, and every (row, 4
 // features) output one thread's sum over candidates. n_cand <= 64.
 //
-// merge_kernel: one wave per output row; lane s reads slot s's (m, l), the
-// wave reduces the common maximum, and every lane folds its features of all
-// slots (Eq. 8) before dividing by l.
+// merge_kernel: one thread per (output row, 4 features), D/4 threads per
+// row; each finds the row's common maximum over its slots' m, then folds
+// the slots in slot order (Eq. 8: l and its 4 accumulator features, one
+// 16-byte load per slot) and divides by l. No lane exchanges, and every
+// slot's loads are independent of the others'.
 
 #include "ss_common.h"
 
@@ -183,61 +185,48 @@ __global__ __launch_bounds__(kThreads) void candidates_kernel(CandParams p) {
 // Eq. (8) over the slots of one row, then O = a / l and lse = m + ln l.
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_kernel(MergeParams p) {
-    constexpr int F = D / 64;  // features per lane
+    constexpr int TPR = D / 4;  // threads per row
     const int64_t n_rows = (int64_t)p.batch * p.n_queries * p.n_q_heads;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t row = t / TPR;
+    const int x = (int)(t % TPR) * 4;  // first of the thread's 4 features
     if (row >= n_rows) return;
     const int b = (int)(row / ((int64_t)p.n_queries * p.n_q_heads));
     int ns = p.n_slots;
     if (p.slots_per_req) ns = min(max(p.slots_per_req[b], 0), p.n_slots);
 
     float mx = -INFINITY;
-    for (int s0 = 0; s0 < ns; s0 += 64) {
-        const int s = s0 + lane;
-        if (s < ns) mx = fmaxf(mx, p.m[s * n_rows + row]);
-    }
-    mx = wave_max(mx);
-
+    for (int s = 0; s < ns; ++s) mx = fmaxf(mx, p.m[s * n_rows + row]);
     float lsum = 0.f;
-    float a[F];
-#pragma unroll
-    for (int j = 0; j < F; ++j) a[j] = 0.f;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     if (mx != -INFINITY) {
-        for (int s0 = 0; s0 < ns; s0 += 64) {
-            const int s = s0 + lane;
-            float f = 0.f, lf = 0.f;
-            if (s < ns) {
-                const float m_s = p.m[s * n_rows + row];
-                f = (m_s == -INFINITY) ? 0.f : exp2_hw((m_s - mx) * kLog2e);
-                lf = f * p.l[s * n_rows + row];
+        // four slots' loads at a time, then their folds in slot order
+        for (int s0 = 0; s0 < ns; s0 += 4) {
+            float ms[4], ls[4];
+            float4 vs[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int s = min(s0 + u, ns - 1);
+                ms[u] = p.m[s * n_rows + row];
+                ls[u] = p.l[s * n_rows + row];
+                vs[u] = *reinterpret_cast<const float4*>(p.acc + (s * n_rows + row) * D + x);
             }
-            lsum += wave_sum(lf);
-            const int cnt = min(64, ns - s0);
-            // issue the loads of up to 8 slots, then fold them
-            for (int j0 = 0; j0 < cnt; j0 += 8) {
-                float vals[8][F];
-                float fs[8];
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int j = min(j0 + u, cnt - 1);
-                    fs[u] = (j0 + u < cnt) ? __shfl(f, j) : 0.f;
-                    const float* src = p.acc + ((s0 + j) * n_rows + row) * D + F * lane;
-#pragma unroll
-                    for (int t = 0; t < F; ++t) vals[u][t] = src[t];
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-#pragma unroll
-                    for (int t = 0; t < F; ++t) a[t] = fmaf(fs[u], vals[u][t], a[t]);
+            for (int u = 0; u < 4; ++u) {
+                if (s0 + u >= ns) break;
+                const float f = (ms[u] == -INFINITY) ? 0.f : exp2_hw((ms[u] - mx) * kLog2e);
+                lsum = fmaf(f, ls[u], lsum);
+                a.x = fmaf(f, vs[u].x, a.x);
+                a.y = fmaf(f, vs[u].y, a.y);
+                a.z = fmaf(f, vs[u].z, a.z);
+                a.w = fmaf(f, vs[u].w, a.w);
             }
         }
     }
     const bool seen = lsum > 0.f;
-    float* dst = p.o + row * D + F * lane;
-#pragma unroll
-    for (int t = 0; t < F; ++t) dst[t] = seen ? a[t] / lsum : 0.f;
-    if (lane == 0) p.lse[row] = seen ? mx + __builtin_amdgcn_logf(lsum) * kLn2 : -INFINITY;
+    const float4 o = seen ? make_float4(a.x / lsum, a.y / lsum, a.z / lsum, a.w / lsum) : make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(p.o + row * D + x) = o;
+    if (x == 0) p.lse[row] = seen ? mx + __builtin_amdgcn_logf(lsum) * kLn2 : -INFINITY;
 }
 
 template <typename T, int D>
@@ -305,7 +294,9 @@ hipError_t launch_state_fill(float* acc, float* m, float* l, int64_t row_begin, 
 
 hipError_t launch_merge(const MergeParams& p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.batch * p.n_queries * p.n_q_heads;
-    const int64_t blocks = (rows + kThreads / 64 - 1) / (kThreads / 64);
+    const int64_t threads = rows * (p.head_dim / 4);
+    const int64_t blocks = (threads + kThreads - 1) / kThreads;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     if (p.head_dim == 64)
         hipLaunchKernelGGL(merge_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
     else
