@@ -52,10 +52,11 @@ CSRC = "long_context_speculative_amd/csrc/"
 def chunk_kernel_sources(cfg, engine="auto"):
     """Source files of the chunk kernel that serves cfg (mirrors the library's
     engine choice)."""
-    mfma_ok = cfg.dtype == "bf16" and cfg.head_dim == 128
-    if engine == "valu" or not mfma_ok:
-        main = "ss_valu_small.hip" if mfma_ok and cfg.rows < 16 else "ss_valu.hip"
-    elif cfg.rows <= 32:
+    bf16_128 = cfg.dtype == "bf16" and cfg.head_dim == 128
+    narrow = cfg.dtype == "bf16" and cfg.head_dim in (64, 128) and cfg.rows <= 32
+    if engine == "valu" or not (narrow or bf16_128):
+        main = "ss_valu_small.hip" if bf16_128 and cfg.rows < 16 else "ss_valu.hip"
+    elif narrow:
         main = "ss_mfma.hip"
     else:
         main = "ss_mfma_wide.hip"

@@ -78,7 +78,7 @@ extern "C" {
 /* chunk-kernel engines (ss_problem_t.engine) */
 #define SS_ENGINE_AUTO 0 /* measured choice, see ss_verify_chunk                 */
 #define SS_ENGINE_VALU 1 /* vector ALU only (keeps the matrix cores free)      */
-#define SS_ENGINE_MFMA 2 /* matrix cores; bf16 with head_dim 128 only          */
+#define SS_ENGINE_MFMA 2 /* matrix cores; bf16 (head_dim 64: up to 32 rows)   */
 
 /* A hipStream_t handle (NULL = default stream). */
 typedef void* ss_stream_t;
@@ -179,14 +179,15 @@ SS_API int64_t ss_state_bytes(const ss_problem_t* problem, int32_t n_slots);
  *              empty for that request
  *   out        slots [slot_begin, slot_begin + ceil(n_chunks/cps)) must lie
  *              in [0, out->n_slots); they are overwritten
- * Engines (problem->engine). SS_ENGINE_AUTO runs bf16 with head_dim 128 on
- * the matrix cores: one MFMA kernel for up to 32 rows per KV head
- * (R = n_queries * G, padded to a 16-row tile) and one for more rows; fp32
- * and head_dim 64 run on a VALU kernel. On gfx950 the padded MFMA kernel
- * stays bound by HBM down to a single row, ahead of the VALU kernels, so
- * AUTO never picks VALU for bf16 / head_dim 128. SS_ENGINE_VALU forces the
- * VALU kernels (a small-row kernel below 16 rows); SS_ENGINE_MFMA is
- * SS_ERR_UNSUPPORTED outside bf16 / head_dim 128.
+ * Engines (problem->engine). SS_ENGINE_AUTO runs bf16 on the matrix cores:
+ * one MFMA kernel for up to 32 rows per KV head (R = n_queries * G, padded
+ * to a 16-row tile; head_dim 128 or 64) and one for more rows (head_dim
+ * 128); fp32, and head_dim 64 beyond 32 rows, run on a VALU kernel. On
+ * gfx950 the padded MFMA kernel stays bound by HBM down to a single row,
+ * ahead of the VALU kernels, so AUTO never picks VALU where an MFMA kernel
+ * applies. SS_ENGINE_VALU forces the VALU kernels (a small-row kernel below
+ * 16 rows of bf16 / head_dim 128); SS_ENGINE_MFMA is SS_ERR_UNSUPPORTED for
+ * fp32 and for head_dim 64 beyond 32 rows.
  * Errors: SS_ERR_INVALID_ARG for null pointers, non-positive sizes, slots
  * out of range, bad alignment; SS_ERR_UNSUPPORTED for head_dim outside
  * {64, 128}; SS_ERR_HIP if the launch fails.

@@ -49,12 +49,12 @@ int32_t check_problem(const ss_problem_t* p) {
     if (!isfinite(p->scale) || !(p->scale > 0.f)) return fail(SS_ERR_INVALID_ARG, "scale must be finite and positive");
     if (p->engine != SS_ENGINE_AUTO && p->engine != SS_ENGINE_VALU && p->engine != SS_ENGINE_MFMA)
         return fail(SS_ERR_INVALID_ARG, "unknown engine %d", p->engine);
-    if (p->engine == SS_ENGINE_MFMA && !(p->dtype == SS_BF16 && p->head_dim == 128))
-        return fail(SS_ERR_UNSUPPORTED, "the MFMA engine needs bf16 and head_dim 128");
     if (p->head_dim != 64 && p->head_dim != 128)
         return fail(SS_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", p->head_dim);
     if (p->batch > 65535) return fail(SS_ERR_UNSUPPORTED, "batch above 65535");
     const int64_t rows = (int64_t)p->n_queries * (p->n_q_heads / p->n_kv_heads);
+    if (p->engine == SS_ENGINE_MFMA && !(p->dtype == SS_BF16 && (p->head_dim == 128 || rows <= 32)))
+        return fail(SS_ERR_UNSUPPORTED, "the MFMA engine needs bf16, and head_dim 128 above 32 rows per KV head");
     const int64_t row_blocks = (rows + kValuRows - 1) / kValuRows;
     if ((int64_t)p->n_kv_heads * row_blocks > 65535 || (int64_t)p->n_kv_heads * cand_row_blocks((int)rows) > 65535)
         return fail(SS_ERR_UNSUPPORTED, "too many rows per request");
@@ -89,21 +89,24 @@ int32_t check_state(const ss_state_t* s, const char* name) {
     return SS_OK;
 }
 
-// Which chunk kernel serves a problem. AUTO: bf16 with head_dim 128 runs on
-// the matrix cores (rows up to 32 on the MFMA kernel, padded to a 16-row
-// tile; more rows on the wide-row MFMA kernel). Measured on gfx950, the
-// padded MFMA kernel stays HBM-bound down to a single row per KV head, while
-// the VALU kernels are bound by vector and LDS issue, so AUTO keeps VALU for
-// fp32 and head_dim 64. VALU forces the vector kernels (the small-row kernel
-// below 16 rows of bf16 / head_dim 128).
+// Which chunk kernel serves a problem. AUTO: bf16 runs on the matrix cores
+// (rows up to 32 on the MFMA kernel, padded to a 16-row tile, head_dim 128
+// or 64; more rows on the wide-row MFMA kernel, head_dim 128). Measured on
+// gfx950, the padded MFMA kernel stays HBM-bound down to a single row per KV
+// head, while the VALU kernels are bound by vector and LDS issue, so AUTO
+// keeps VALU for fp32 and for head_dim 64 beyond 32 rows. VALU forces the
+// vector kernels (the small-row kernel below 16 rows of bf16 / head_dim 128).
 enum class ChunkEngine { kValu, kValuSmall, kMfma, kMfmaWide };
 
 ChunkEngine chunk_engine(const ss_problem_t* p) {
     const int rows = p->n_queries * (p->n_q_heads / p->n_kv_heads);
-    const bool mfma_ok = p->dtype == SS_BF16 && p->head_dim == 128;
-    if (p->engine == SS_ENGINE_VALU || !mfma_ok)
-        return (mfma_ok && rows < 16) ? ChunkEngine::kValuSmall : ChunkEngine::kValu;
-    return rows <= 32 ? ChunkEngine::kMfma : ChunkEngine::kMfmaWide;
+    const bool bf16_128 = p->dtype == SS_BF16 && p->head_dim == 128;
+    // the narrow kernel takes head_dim 64 too; the wide-row kernel 128 only
+    const bool narrow = p->dtype == SS_BF16 && (p->head_dim == 128 || p->head_dim == 64) && rows <= 32;
+    const bool wide = bf16_128 && rows > 32;
+    if (p->engine == SS_ENGINE_VALU || !(narrow || wide))
+        return (bf16_128 && rows < 16) ? ChunkEngine::kValuSmall : ChunkEngine::kValu;
+    return narrow ? ChunkEngine::kMfma : ChunkEngine::kMfmaWide;
 }
 
 int32_t validate_chunk(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist, int32_t chunk_len,

@@ -158,6 +158,10 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
 
     const int n_tiles = tl.n_tiles();
     uint16_t(*vt)[kVtRow] = sm.u.vt[w];
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+    constexpr int VH = D / 64;  // V key groups per lane (see load_v_at)
+    const int vx = D == 128 ? 8 * l16 : 8 * (l16 & 7);
+    auto v_kg = [&](int h) { return D == 128 ? q4 + 4 * h : q4 + 4 * (l16 >> 3); };
 
     // Loads address a tile as a uniform base (scalar registers) plus a 32-bit
     // per-lane offset. Keys past the range are clamped to its last key so
@@ -174,20 +178,23 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
             for (int k = 0; k < NS; ++k) dst[kt][k] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tb + off + 32 * k));
         }
     };
-    // V rows 4*kg + e (kg = q4 + 4*h), features 8*l16 .. +7.
-    auto load_v_at = [&](const uint16_t* tb, int stride, int last, u32x4(&dst)[2][4]) {
+    // V rows 4*kg + e, features vx .. vx+7: with D = 128, key groups
+    // kg = q4 + 4*h (h = 0, 1) at vx = 8*l16; with D = 64 the upper half of
+    // each 16-lane group takes the other 16 keys, kg = q4 + 4*(l16 >> 3) at
+    // vx = 8*(l16 & 7), one key group per lane.
+    auto load_v_at = [&](const uint16_t* tb, int stride, int last, u32x4(&dst)[VH][4]) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < VH; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int off = min(4 * (q4 + 4 * h) + e, last) * stride + 8 * l16;
+                const int off = min(4 * v_kg(h) + e, last) * stride + vx;
                 dst[h][e] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tb + off));
             }
     };
     const int sti = (int)st;
     // Tile tau's loads (tk: its first token, valid > 0: its keys).
     auto load_k = [&](int64_t tk, int valid, u32x4(&dst)[2][NS]) { load_k_at(kp + tk * st, sti, valid - 1, dst); };
-    auto load_v = [&](int64_t tk, int valid, u32x4(&dst)[2][4]) { load_v_at(vp + tk * st, sti, valid - 1, dst); };
+    auto load_v = [&](int64_t tk, int valid, u32x4(&dst)[VH][4]) { load_v_at(vp + tk * st, sti, valid - 1, dst); };
 
     // Block statistics: the running state of the keys of the current block
     // (stats_block tokens) that this wave attends, written out when the
@@ -221,18 +228,18 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
     // One tile: the first `valid` keys, and of those only the ones whose bit
     // is set in vis[rt] (per lane row) when `masked`. after_stage runs once
     // V is in LDS (its registers are free), after_s once S^T has read K.
-    auto consume = [&](u32x4(&kf)[2][NS], u32x4(&vr)[2][4], int valid, bool masked, const uint32_t(&vis)[NRT],
+    auto consume = [&](u32x4(&kf)[2][NS], u32x4(&vr)[VH][4], int valid, bool masked, const uint32_t(&vis)[NRT],
                        auto after_stage, auto after_s) {
         // Stage V transposed: vt[x][key] holds 4 keys per 8-byte word.
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int kg = q4 + 4 * h;
+        for (int h = 0; h < VH; ++h) {
+            const int kg = v_kg(h);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t d0 = vr[h][0][i], d1 = vr[h][1][i], d2 = vr[h][2][i], d3 = vr[h][3][i];
                 const u32x2 lo{(d0 & 0xffffu) | (d1 << 16), (d2 & 0xffffu) | (d3 << 16)};
                 const u32x2 hi{(d0 >> 16) | (d1 & 0xffff0000u), (d2 >> 16) | (d3 & 0xffff0000u)};
-                const int x = 8 * l16 + 2 * i;
+                const int x = vx + 2 * i;
                 *reinterpret_cast<u32x2*>(&vt[x][4 * kg]) = lo;
                 *reinterpret_cast<u32x2*>(&vt[x + 1][4 * kg]) = hi;
             }
@@ -329,7 +336,7 @@ __device__ __forceinline__ void mfma_piece(const ChunkParams& p, MfmaSmem<D, NRT
     };
 
     const uint32_t no_vis[NRT] = {};
-    u32x4 kf[2][NS], vr[2][4];
+    u32x4 kf[2][NS], vr[VH][4];
     int tau = w;
     if constexpr (!kGather) {
         const int64_t t0 = tl.t0;
@@ -728,9 +735,11 @@ hipError_t launch_hist_t(const ChunkParams& p, hipStream_t stream) {
 
 }  // namespace
 
-// The V staging map gives each of 16 lanes 8 features of a key: head_dim 128.
+// head_dim 128 or 64 (the V staging map gives each lane 8 features of one
+// or two key groups), up to 32 rows.
 hipError_t launch_chunk_mfma(const ChunkParams& p, int head_dim, hipStream_t stream) {
-    if (head_dim != 128 || p.rows > 32) return hipErrorInvalidValue;
+    if ((head_dim != 128 && head_dim != 64) || p.rows > 32) return hipErrorInvalidValue;
+    if (head_dim == 64) return p.rows > 16 ? launch_t<64, 2>(p, stream) : launch_t<64, 1>(p, stream);
     return p.rows > 16 ? launch_t<128, 2>(p, stream) : launch_t<128, 1>(p, stream);
 }
 
@@ -740,7 +749,8 @@ hipError_t mfma_wave_work_groups(int rows, int* n) {
 }
 
 hipError_t launch_history_mfma(const ChunkParams& p, int head_dim, hipStream_t stream) {
-    if (head_dim != 128 || p.rows > 32 || p.plan_slots < 2) return hipErrorInvalidValue;
+    if ((head_dim != 128 && head_dim != 64) || p.rows > 32 || p.plan_slots < 2) return hipErrorInvalidValue;
+    if (head_dim == 64) return p.rows > 16 ? launch_hist_t<64, 2>(p, stream) : launch_hist_t<64, 1>(p, stream);
     return p.rows > 16 ? launch_hist_t<128, 2>(p, stream) : launch_hist_t<128, 1>(p, stream);
 }
 

@@ -101,15 +101,16 @@ def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
 
 
 def narrow_mfma(cfg, engine="auto") -> bool:
-    """Whether the library runs this shape on its narrow MFMA kernels."""
-    return engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim == 128 and cfg.rows <= 32
+    """Whether the library runs this shape on its narrow MFMA kernels
+    (bf16, head_dim 128 or 64, up to 32 rows per KV head)."""
+    return engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim in (64, 128) and cfg.rows <= 32
 
 
 def mfma_fuses_candidates(cfg, engine="auto") -> bool:
     """Whether ss_verify_history folds the candidate region into the history
     launch (the MFMA kernels, narrow and wide-row) instead of giving it a
     slot of its own."""
-    return engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim == 128
+    return narrow_mfma(cfg, engine) or (engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim == 128)
 
 
 # Launch configuration of the resident round that the benchmark times.

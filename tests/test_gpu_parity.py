@@ -822,6 +822,74 @@ def test_full_size_sampled(name):
         compare(cfg, o, lse, o_ref, lse_ref, rows_of(cfg, b, g))
 
 
+D64_CASES = {
+    "uniform": C["c2_qwen3_8b"].with_(batch=3, head_dim=64, hist_len=3000, chunk_len=1024),
+    "ragged_empties": C["c3_internlm25_7b_ragged"].with_(batch=70, head_dim=64, hist_len=2500, ragged_lo=1,
+                                                         chunk_len=256),
+    "ragged_tree_32_rows": C["c3_internlm25_7b_ragged"].with_(batch=5, head_dim=64, n_queries=8, mask="tree",
+                                                              hist_len=3000, ragged_lo=1, chunk_len=512),
+    "rows_4": C["c2_qwen3_8b"].with_(batch=2, head_dim=64, n_queries=1, hist_len=1500, chunk_len=512),
+    "short_histories": C["c3_internlm25_7b_ragged"].with_(batch=9, head_dim=64, hist_len=64, ragged_lo=1,
+                                                          chunk_len=32),
+}
+
+
+@pytest.mark.parametrize("name", list(D64_CASES))
+def test_head_dim_64_on_the_matrix_cores(name):
+    """bf16 with head_dim 64 and up to 32 rows per KV head runs on the narrow
+    MFMA kernels (the V staging map with one key group per lane): the
+    benchmark's launch configuration (balanced cut, candidates folded in),
+    the chunked split, the whole-round call with the library's slot choice
+    and with one slot, and the forced VALU engine all match the oracle.
+    Ragged cases include empty requests."""
+    cfg = D64_CASES[name]
+    assert rounds.narrow_mfma(cfg)
+    inp = wl.make_inputs(cfg)
+    if name == "ragged_empties":
+        inp.hist_len = inp.hist_len.copy()
+        inp.hist_len[[0, 5, 6, 40, 68, 69]] = 0
+        inp.hist_len[7], inp.hist_len[8], inp.hist_len[9] = 1, 128, 129
+    o_ref, lse_ref = oracle_round(inp)
+    for label, kw in (("balanced", dict(rounds.BENCH_RESIDENT)),
+                      ("balanced, 3 slots", dict(rounds.BENCH_RESIDENT, history_slots=3)),
+                      ("chunks", dict(split="chunks", chunks_per_slot=2)),
+                      ("valu", dict(split="chunks", chunks_per_slot=2, engine="valu"))):
+        log(f"[d64] {name}: {label}")
+        rnd = rounds.ResidentRound(inp, **kw)
+        rnd.run()
+        torch.cuda.synchronize()
+        compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+        check_mask(rnd, inp)
+    rnd = rounds.ResidentRound(inp)
+    work = ss.StateBuffers(rnd.problem, 12, "cuda")
+    for n_slots in (0, 1):
+        log(f"[d64] {name}: round call, n_slots={n_slots}")
+        rnd.o.fill_(float("nan"))
+        rnd.lse.fill_(float("nan"))
+        ss.ss_verify_round(rnd.problem, rnd.q, rnd.hist_view, rnd.cand_view, rnd.parents, rnd.mask_out, n_slots,
+                           work, rnd.o, rnd.lse)
+        torch.cuda.synchronize()
+        compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+
+
+def test_head_dim_64_full_size_sampled():
+    """The InternLM2.5-like ragged layer with head_dim 64 at full size (32
+    requests up to 65,536 tokens), in the benchmark's launch configuration,
+    on sampled (request, KV head) slices against the oracle."""
+    cfg = C["c3_internlm25_7b_ragged"].with_(head_dim=64)
+    inp = wl.make_inputs(cfg)
+    rnd = rounds.ResidentRound(inp, **rounds.BENCH_RESIDENT)
+    rnd.run()
+    torch.cuda.synchronize()
+    o, lse = rnd.o.cpu().numpy(), rnd.lse.cpu().numpy()
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    check_mask(rnd, inp)
+    for b, g in ((0, 0), (cfg.batch - 1, cfg.n_kv_heads - 1), (int(np.argmax(inp.hist_len)), 3)):
+        log(f"[d64 full] oracle slice b={b} g={g}")
+        o_ref, lse_ref = oracle_round(inp, requests=[b], kv_heads=[g])
+        compare(cfg, o, lse, o_ref, lse_ref, rows_of(cfg, b, g))
+
+
 # ---------------------------------------------------------------------------
 # size extremes
 # ---------------------------------------------------------------------------
