@@ -22,8 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libssverify.so")
 
-SOURCES = ["ss_api.hip", "ss_valu.hip", "ss_mfma.hip", "ss_region.hip", "ss_mfma_wide.hip", "ss_valu_small.hip",
-           "ss_sparse.hip", "ss_probe.hip"]
+SOURCES = ["ss_api.hip", "ss_valu.hip", "ss_mfma.hip", "ss_mfma_f32.hip", "ss_region.hip", "ss_mfma_wide.hip",
+           "ss_valu_small.hip", "ss_sparse.hip", "ss_probe.hip"]
 
 # Packed-fp32 instructions are switched off for all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -373,6 +373,7 @@ constexpr int kValuRows = 32;
 // Launchers (defined in the kernel translation units).
 hipError_t launch_chunk_valu(const ChunkParams& p, int dtype, int head_dim, hipStream_t stream);
 hipError_t launch_chunk_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
+hipError_t launch_chunk_mfma_f32(const ChunkParams& p, int head_dim, hipStream_t stream);
 // Balanced split of the whole resident history over one work-group per CU
 // (narrow MFMA kernel); p.plan_slots slots from p.slot_begin.
 hipError_t launch_history_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
