@@ -514,6 +514,12 @@ int32_t round_slots(const ss_problem_t* p, const ss_kv_view_t* hist, int32_t* n_
             s = per_cu * cus / (streams * ((rows + per_group - 1) / per_group));
             break;
         }
+        case ChunkEngine::kMfmaF32:
+            // uniform lengths: one work-group per CU (measured: 2 slots 381 us,
+            // 4 slots 404 us on a c2-shaped fp32 round), plus the candidate slot
+            s = hist->req_len ? 1 + 2 * (int64_t)cus / streams : 1 + (int64_t)cus / streams;
+            if (s > 9) s = 9;
+            break;
         default:
             s = 1 + 2 * (int64_t)cus / streams;
             if (s > 9) s = 9;

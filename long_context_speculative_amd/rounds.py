@@ -84,6 +84,8 @@ def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
         return max(1, -(-pad_max // (4 * cfg.chunk_len)))
     wave = wgs_per_cu(cfg, engine) * cus
     if not cfg.ragged:
+        if f32_mfma(cfg, engine):
+            wave = cus  # one work-group per CU streams faster here too
         return max(1, wave // (cfg.batch * cfg.n_kv_heads))
     if not any(pads):
         return 2
@@ -104,6 +106,12 @@ def narrow_mfma(cfg, engine="auto") -> bool:
     """Whether the library runs this shape on its narrow MFMA kernels
     (bf16, head_dim 128 or 64, up to 32 rows per KV head)."""
     return engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim in (64, 128) and cfg.rows <= 32
+
+
+def f32_mfma(cfg, engine="auto") -> bool:
+    """Whether the library runs this shape on its fp32 MFMA kernel (fp32, up
+    to 32 rows per KV head)."""
+    return engine != "valu" and cfg.dtype == "f32" and cfg.rows <= 32
 
 
 def mfma_fuses_candidates(cfg, engine="auto") -> bool:

@@ -872,6 +872,51 @@ def test_head_dim_64_on_the_matrix_cores(name):
         compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
 
 
+F32_CASES = {
+    "tiny_d64": C["c1_tiny_f32"],
+    "uniform_d128": C["c2_qwen3_8b"].with_(batch=3, dtype="f32", hist_len=3000, chunk_len=1024),
+    "ragged_empties_d128": C["c3_internlm25_7b_ragged"].with_(batch=20, dtype="f32", hist_len=2500, ragged_lo=1,
+                                                              chunk_len=256),
+    "tree_32_rows_d64": C["c3_internlm25_7b_ragged"].with_(batch=5, dtype="f32", head_dim=64, n_queries=8,
+                                                           mask="tree", hist_len=3000, ragged_lo=1, chunk_len=512),
+    "rows_4_d128": C["c2_qwen3_8b"].with_(batch=2, dtype="f32", n_queries=1, hist_len=1500, chunk_len=512),
+    "short_histories_d128": C["c3_internlm25_7b_ragged"].with_(batch=9, dtype="f32", hist_len=40, ragged_lo=1,
+                                                               chunk_len=16),
+}
+
+
+@pytest.mark.parametrize("name", list(F32_CASES))
+def test_fp32_on_both_engines(name):
+    """fp32 inputs up to 32 rows per KV head run on the fp32 MFMA kernel
+    (AUTO), and on the VALU kernel when forced: both, under the chunked
+    split and the fixed cut of ss_verify_history, and the whole-round call,
+    match the oracle within 1e-5. Ragged cases include empty requests."""
+    cfg = F32_CASES[name]
+    assert rounds.f32_mfma(cfg)
+    inp = wl.make_inputs(cfg)
+    if name == "ragged_empties_d128":
+        inp.hist_len = inp.hist_len.copy()
+        inp.hist_len[[0, 5, 19]] = 0
+        inp.hist_len[7] = 1
+    o_ref, lse_ref = oracle_round(inp)
+    for engine in ("auto", "valu"):
+        for label, kw in (("chunks", dict(split="chunks", chunks_per_slot=2)),
+                          ("history cut", dict(split="balanced", history_slots=3))):
+            log(f"[fp32] {name}: {engine}, {label}")
+            rnd = rounds.ResidentRound(inp, engine=engine, **kw)
+            rnd.run()
+            torch.cuda.synchronize()
+            compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+            check_mask(rnd, inp)
+    rnd = rounds.ResidentRound(inp)
+    work = ss.StateBuffers(rnd.problem, 12, "cuda")
+    rnd.o.fill_(float("nan"))
+    ss.ss_verify_round(rnd.problem, rnd.q, rnd.hist_view, rnd.cand_view, rnd.parents, rnd.mask_out, 0, work, rnd.o,
+                       rnd.lse)
+    torch.cuda.synchronize()
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+
+
 def test_head_dim_64_full_size_sampled():
     """The InternLM2.5-like ragged layer with head_dim 64 at full size (32
     requests up to 65,536 tokens), in the benchmark's launch configuration,
