@@ -55,7 +55,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 14
+#define SS_ABI_VERSION 15
 
 /* status codes */
 #define SS_OK 0
