@@ -1,4 +1,5 @@
-// MFMA bf16 chunk kernel of libssverify, for 16..32 rows per KV head.
+// MFMA bf16 chunk kernels of libssverify, for up to 32 rows per KV head
+// (padded to a 16-row tile) and head_dim 128 or 64.
 //
 // SpecStream ("Resource-Efficient Speculative Decoding for Long-Context LLM
 // Serving"), section 4.2: a history chunk serves the whole verification query
