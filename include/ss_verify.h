@@ -55,7 +55,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 15
+#define SS_ABI_VERSION 16
 
 /* status codes */
 #define SS_OK 0
@@ -179,10 +179,11 @@ SS_API int64_t ss_state_bytes(const ss_problem_t* problem, int32_t n_slots);
  *              empty for that request
  *   out        slots [slot_begin, slot_begin + ceil(n_chunks/cps)) must lie
  *              in [0, out->n_slots); they are overwritten
- * Engines (problem->engine). SS_ENGINE_AUTO runs bf16 on the matrix cores:
- * one MFMA kernel for up to 32 rows per KV head (R = n_queries * G, padded
- * to a 16-row tile; head_dim 128 or 64) and one for more rows (head_dim
- * 128); fp32, and head_dim 64 beyond 32 rows, run on a VALU kernel. On
+ * Engines (problem->engine). SS_ENGINE_AUTO runs on the matrix cores: for
+ * bf16 one MFMA kernel for up to 32 rows per KV head (R = n_queries * G,
+ * padded to a 16-row tile; head_dim 128 or 64) and one for more rows
+ * (head_dim 128); for fp32 one MFMA kernel for up to 32 rows (head_dim 128
+ * or 64). Beyond 32 rows, fp32 and head_dim 64 run on a VALU kernel. On
  * gfx950 the padded MFMA kernel stays bound by HBM down to a single row,
  * ahead of the VALU kernels, so AUTO never picks VALU where an MFMA kernel
  * applies. SS_ENGINE_VALU forces the VALU kernels (a small-row kernel below
@@ -210,28 +211,32 @@ SS_API int32_t ss_verify_chunk(const ss_problem_t* problem, const void* q, const
  *               then the call's slots hold history and candidates together
  *   parents, mask_out  as ss_verify_candidates (used only with cand)
  *   n_slots     slots per (request, KV head) the call may use, >= 1 (>= 2
- *               with cand on the VALU engines); the call writes
+ *               with cand on the fp32 and VALU engines); the call writes
  *               exactly slots [slot_begin, slot_begin + n_slots) of every
  *               row, the ones it does not need as empty states
- * With the narrow MFMA kernel (AUTO or MFMA engine, bf16, head_dim 128,
- * R <= 32):
- *   - ragged lengths (hist->req_len given) and n_slots >= 2: the streams
+ * With the narrow MFMA kernel (AUTO or MFMA engine, bf16, head_dim 128 or
+ * 64, R <= 32), and for ragged lengths also with the fp32 MFMA kernel (fp32,
+ * R <= 32), where "slots" below are the history's (n_slots, or n_slots - 1
+ * after the candidate slot):
+ *   - ragged lengths (hist->req_len given) and at least 2 slots: the streams
  *     (request, KV head) are laid end to end, each padded to a multiple of
  *     128 tokens, and cut into equal ranges, one per work-group of a single
- *     full wave of the device; a stream is cut into at most n_slots pieces
- *     (the ranges grow when n_slots is too small for an even cut);
+ *     full wave of the device; a stream is cut into at most as many pieces
+ *     as there are slots (the ranges grow when there are too few slots for
+ *     an even cut);
  *   - uniform lengths (req_len NULL): every stream is cut into
  *     P = min(n_slots, max(1, W / (B * Hkv))) equal chunks, W the
  *     work-groups of one full wave, i.e. n_slots = W / (B * Hkv) gives one
- *     chunk per work-group.
- * Other engines, and ragged lengths with n_slots = 1, cut every request
- * into n_slots chunks of ceil(max_len / n_slots) tokens. Chunks are rounded
- * up to a multiple of 128 tokens and run as ss_verify_chunk with
- * chunks_per_slot 1; chunks past a request's end are empty slots.
+ *     chunk per work-group (narrow kernel only).
+ * Other engines, and ragged lengths with one slot, cut every request
+ * into as many chunks as there are slots, of ceil(max_len / slots)
+ * tokens. Chunks are rounded up to a multiple of 128 tokens and run as
+ * ss_verify_chunk with chunks_per_slot 1; chunks past a request's end are
+ * empty slots.
  * Candidates: the MFMA kernels (narrow and wide-row) attend them as masked
  * key tiles after the history, in the work-groups that hold a stream's
- * first piece (no extra launch, no extra slot); the VALU engines run
- * ss_verify_candidates into slot_begin and cut the history into the
+ * first piece (no extra launch, no extra slot); the fp32 and VALU engines
+ * run ss_verify_candidates into slot_begin and cut the history into the
  * remaining n_slots - 1 slots.
  * stats: NULL, or record block statistics (narrow MFMA kernel only,
  *   SS_ERR_UNSUPPORTED otherwise): the cut is aligned to block_len (no block
@@ -300,7 +305,8 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
  *             on the narrow MFMA kernel 1 -- a work-group per stream -- when
  *             hist->max_len <= 4096 with at least one stream per compute
  *             unit or <= 2048 with three per four units, else 8 for the
- *             balanced cut; +1 for the candidate slot on the VALU engines),
+ *             balanced cut, on the fp32 MFMA kernel 8; +1 for the
+ *             candidate slot on the fp32 and VALU engines),
  *             limited to work->n_slots
  *   work      caller-allocated state slots (workspace); slots [0, n_slots)
  *             are overwritten, their contents afterwards are not part of

@@ -393,14 +393,15 @@ int32_t verify_history(const ss_problem_t* problem, const void* q, const ss_kv_v
         c.fin_o = fin->o;
         c.fin_lse = fin->lse;
     }
-    if (narrow && hist->req_len && hist_slots >= 2) {
+    // ragged lengths on the narrow and the fp32 MFMA kernels: the balanced cut
+    if ((narrow || engine == ChunkEngine::kMfmaF32) && hist->req_len && hist_slots >= 2) {
         c.plan_slots = hist_slots;
         // every slot starts empty; pieces overwrite theirs
         const int64_t rows = (int64_t)problem->batch * problem->n_queries * problem->n_q_heads;
         e = launch_state_fill(out->acc, out->m, out->l, (int64_t)hist_begin * rows, (int64_t)hist_slots * rows,
                               problem->head_dim, s);
         if (e != hipSuccess) return fail(SS_ERR_HIP, "state fill failed: %s", hipGetErrorString(e));
-        e = launch_history_mfma(c, problem->head_dim, s);
+        e = narrow ? launch_history_mfma(c, problem->head_dim, s) : launch_history_mfma_f32(c, problem->head_dim, s);
     } else {
         e = enqueue_chunk(problem, c, s);
     }
@@ -487,8 +488,8 @@ bool one_piece_per_stream(int64_t max_len, int64_t streams, int64_t cus) {
 // the narrow MFMA kernel; the wide-row kernel's fixed chunks); for ragged
 // lengths on the narrow kernel one (one_piece_per_stream, judged by the
 // view's max_len) or 8 (the balanced cut grows its ranges when the longest
-// stream needs more); and one more for the candidate region on the VALU
-// engines.
+// stream needs more), on the fp32 MFMA kernel 8; and one more for the
+// candidate region on the fp32 and VALU engines.
 int32_t round_slots(const ss_problem_t* p, const ss_kv_view_t* hist, int32_t* n_slots) {
     const int32_t group = p->n_q_heads / p->n_kv_heads;
     const int32_t rows = p->n_queries * group;
@@ -515,9 +516,10 @@ int32_t round_slots(const ss_problem_t* p, const ss_kv_view_t* hist, int32_t* n_
             break;
         }
         case ChunkEngine::kMfmaF32:
-            // uniform lengths: one work-group per CU (measured: 2 slots 381 us,
-            // 4 slots 404 us on a c2-shaped fp32 round), plus the candidate slot
-            s = hist->req_len ? 1 + 2 * (int64_t)cus / streams : 1 + (int64_t)cus / streams;
+            // the candidate slot, plus: uniform lengths one work-group per CU
+            // (measured: 2 slots 381 us, 4 slots 404 us on a c2-shaped fp32
+            // round); ragged lengths 8 for the balanced cut
+            s = hist->req_len ? 9 : 1 + (int64_t)cus / streams;
             if (s > 9) s = 9;
             break;
         default:

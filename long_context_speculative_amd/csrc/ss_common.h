@@ -334,6 +334,96 @@ __host__ __device__ inline void piece_tokens(const ChunkParams& p, int32_t len, 
     *t1 = e;
 }
 
+// ---------------------------------------------------------------------------
+// The walk of a history launch over the balanced cut (device side).
+// ---------------------------------------------------------------------------
+
+// x of lane 0 in every lane, held in scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Where work-group w of a history launch of gridDim.x work-groups starts:
+// the line's length and the piece length of the cut, and a cursor at the
+// first request whose streams end after w*L, or that starts at or after it.
+// Every wave computes the same (64-lane scans over the requests). False
+// when w owns no range.
+struct PlanStart {
+    int64_t total, piece_len;
+    PlanCursor cursor;
+};
+
+__device__ __forceinline__ bool plan_start(const ChunkParams& p, int64_t w, PlanStart& st) {
+    const int lane = threadIdx.x & 63;
+    auto len_of = [&](int32_t b) { return clamp_len(p.req_len ? p.req_len[b] : p.max_len, p.max_len); };
+
+    // Line length and longest padded stream.
+    int64_t total = 0, pad_max = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int b = b0 + lane;
+        int64_t mx = b < p.batch ? plan_pad(len_of(b), p.plan_align) : 0;
+        int64_t sum = b < p.batch ? mx + plan_charge(p.plan_align) : 0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            sum += __shfl_xor(sum, off);
+            mx = max(mx, (int64_t)__shfl_xor(mx, off));
+        }
+        total += sum;
+        pad_max = max(pad_max, mx);
+    }
+    total = uniform64(total * p.n_kv_heads);
+    pad_max = uniform64(pad_max);
+    const int64_t piece_len = plan_piece_len(total, pad_max, (int32_t)gridDim.x, p.plan_slots, p.plan_align);
+    if (w > plan_last_wg(total, piece_len)) return false;
+    const int64_t lo = w * piece_len;
+
+    // First request whose streams end after lo, or that starts at or after it.
+    int32_t b_first = p.batch;
+    int64_t line = 0, carry = 0;
+    for (int b0 = 0; b0 < p.batch; b0 += 64) {
+        const int b = b0 + lane;
+        const int64_t span = b < p.batch ? (int64_t)p.n_kv_heads * plan_span(len_of(b), p.plan_align) : 0;
+        int64_t incl = span;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int64_t t = __shfl_up(incl, off);
+            if (lane >= off) incl += t;
+        }
+        const int64_t start = carry + incl - span;
+        const uint64_t hit = __ballot(b < p.batch && (start + span > lo || start >= lo));
+        if (hit) {
+            const int first = __ffsll((unsigned long long)hit) - 1;
+            b_first = b0 + first;
+            line = __shfl(start, first);
+            break;
+        }
+        carry += __shfl(incl, 63);
+    }
+    st.total = total;
+    st.piece_len = piece_len;
+    st.cursor = PlanCursor{__builtin_amdgcn_readfirstlane(b_first), 0, uniform64(line)};
+    return true;
+}
+
+// One step of the walk, kept out of line (inline: one definition across
+// translation units; noinline: it runs on one lane between pieces, and
+// inlined its 64-bit arithmetic would hold registers that the key loop
+// needs).
+__device__ inline __noinline__ int32_t plan_step(const int32_t* req_len, int32_t max_len, int32_t batch,
+                                                 int32_t n_kv_heads, int64_t piece_len, int64_t total,
+                                                 int32_t n_slots, int64_t w, PlanCursor* cursor, PlanPiece* out,
+                                                 int32_t align) {
+    auto len_of = [&](int32_t b) { return clamp_len(req_len ? req_len[b] : max_len, max_len); };
+    PlanCursor c = *cursor;
+    PlanPiece pc;
+    const bool more = plan_next(len_of, batch, n_kv_heads, piece_len, total, n_slots, w, c, pc, align);
+    *cursor = c;
+    if (more) *out = pc;
+    return more ? 1 : 0;
+}
+
 struct ImportanceParams {
     const float* m;
     const float* l;
@@ -377,6 +467,8 @@ hipError_t launch_chunk_mfma_f32(const ChunkParams& p, int head_dim, hipStream_t
 // Balanced split of the whole resident history over one work-group per CU
 // (narrow MFMA kernel); p.plan_slots slots from p.slot_begin.
 hipError_t launch_history_mfma(const ChunkParams& p, int head_dim, hipStream_t stream);
+// The same cut on the fp32 MFMA kernel (no statistics, no candidate region).
+hipError_t launch_history_mfma_f32(const ChunkParams& p, int head_dim, hipStream_t stream);
 // Work-groups of one launch of the narrow MFMA kernels that covers the
 // current device: one per CU.
 hipError_t mfma_wave_work_groups(int rows, int* n);

@@ -569,87 +569,22 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_kernel(ChunkParams p) 
     }
 }
 
-__device__ __forceinline__ int64_t uniform64(int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-// One step of the walk, kept out of line: it runs on one lane between
-// pieces, and inlined its 64-bit arithmetic would hold registers that the
-// key loop needs.
-__device__ __noinline__ int32_t plan_step(const int32_t* req_len, int32_t max_len, int32_t batch, int32_t n_kv_heads,
-                                          int64_t piece_len, int64_t total, int32_t n_slots, int64_t w,
-                                          PlanCursor* cursor, PlanPiece* out, int32_t align) {
-    auto len_of = [&](int32_t b) { return clamp_len(req_len ? req_len[b] : max_len, max_len); };
-    PlanCursor c = *cursor;
-    PlanPiece pc;
-    const bool more = plan_next(len_of, batch, n_kv_heads, piece_len, total, n_slots, w, c, pc, align);
-    *cursor = c;
-    if (more) *out = pc;
-    return more ? 1 : 0;
-}
-
 // The whole resident history of every request, cut into balanced pieces
 // (the line split of plan_next) over gridDim.x work-groups.
 template <int D, int NRT, bool STATS>
 __global__ __launch_bounds__(kThreads, 2) void history_mfma_kernel(ChunkParams p) {
     __shared__ MfmaSmem<D, NRT> sm;
-    const int lane = threadIdx.x & 63;
-    auto len_of = [&](int32_t b) { return clamp_len(p.req_len ? p.req_len[b] : p.max_len, p.max_len); };
-
-    // Line length and longest padded stream; every wave computes the same.
-    int64_t total = 0, pad_max = 0;
-    for (int b0 = 0; b0 < p.batch; b0 += 64) {
-        const int b = b0 + lane;
-        int64_t mx = b < p.batch ? plan_pad(len_of(b), p.plan_align) : 0;
-        int64_t sum = b < p.batch ? mx + plan_charge(p.plan_align) : 0;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            sum += __shfl_xor(sum, off);
-            mx = max(mx, (int64_t)__shfl_xor(mx, off));
-        }
-        total += sum;
-        pad_max = max(pad_max, mx);
-    }
-    total = uniform64(total * p.n_kv_heads);
-    pad_max = uniform64(pad_max);
-    const int64_t piece_len = plan_piece_len(total, pad_max, (int32_t)gridDim.x, p.plan_slots, p.plan_align);
     const int64_t w = blockIdx.x;
-    if (w > plan_last_wg(total, piece_len)) return;
-    const int64_t lo = w * piece_len;
-
-    // First request whose streams end after lo, or that starts at or after it.
-    int32_t b_first = p.batch;
-    int64_t line = 0, carry = 0;
-    for (int b0 = 0; b0 < p.batch; b0 += 64) {
-        const int b = b0 + lane;
-        const int64_t span = b < p.batch ? (int64_t)p.n_kv_heads * plan_span(len_of(b), p.plan_align) : 0;
-        int64_t incl = span;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int64_t t = __shfl_up(incl, off);
-            if (lane >= off) incl += t;
-        }
-        const int64_t start = carry + incl - span;
-        const uint64_t hit = __ballot(b < p.batch && (start + span > lo || start >= lo));
-        if (hit) {
-            const int first = __ffsll((unsigned long long)hit) - 1;
-            b_first = b0 + first;
-            line = __shfl(start, first);
-            break;
-        }
-        carry += __shfl(incl, 63);
-    }
-    line = uniform64(line);
-    b_first = __builtin_amdgcn_readfirstlane(b_first);
+    PlanStart st;
+    if (!plan_start(p, w, st)) return;
+    const int64_t total = st.total, piece_len = st.piece_len;
 
     // The walk runs on one lane with its cursor in LDS, so nothing of it is
     // held in registers across a piece.
     __shared__ PlanCursor cursor;
     __shared__ PlanPiece piece;
     __shared__ int32_t has_piece;
-    if (threadIdx.x == 0) cursor = PlanCursor{b_first, 0, line};
+    if (threadIdx.x == 0) cursor = st.cursor;
     for (;;) {
         __syncthreads();  // the previous piece is done with LDS; the cursor is visible
         if (threadIdx.x == 0)

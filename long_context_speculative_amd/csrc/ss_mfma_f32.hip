@@ -66,22 +66,15 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // State of tokens [t0, t1) of stream (b, g) for every row of the KV head,
-// written to slot s of the launch (p.slot_begin + s).
+// written to slot `slot` of the state buffer.
 template <int D, int NRT>
-__global__ __launch_bounds__(kThreads, 2) void chunk_mfma_f32_kernel(ChunkParams p) {
-    __shared__ F32Smem<D, NRT> sm;
+__device__ __forceinline__ void f32_piece(const ChunkParams& p, F32Smem<D, NRT>& sm, int b, int g, int slot,
+                                          int64_t t0, int64_t t1) {
     constexpr int NF = D / 4;    // features per lane group (the contraction's steps for S)
     constexpr int NXT = D / 16;  // 16-feature output tiles for O^T
     static_assert(NXT % kWaves == 0, "feature tiles split evenly over the waves");
-    const int s = blockIdx.x / p.n_kv_heads;
-    const int g = blockIdx.x % p.n_kv_heads;
-    const int b = blockIdx.z;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int l16 = lane & 15, q4 = lane >> 4;
-
-    const int32_t len = chunk_view_len(p, b);
-    int64_t t0, t1;
-    piece_tokens(p, len, b, g, s, &t0, &t1);
 
     const int64_t base = (p.req_offset ? p.req_offset[b] : (int64_t)b * p.stride_b) + (int64_t)g * p.stride_h;
     const float* __restrict__ kp = static_cast<const float*>(p.k) + base;
@@ -276,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_f32_kernel(ChunkParams
         const int r = l16 + 16 * rt;
         if (r >= p.rows) continue;
         const int i = r / p.group, h = g * p.group + r % p.group;
-        const int64_t row = (((int64_t)(p.slot_begin + s) * p.batch + b) * p.n_queries + i) * p.n_q_heads + h;
+        const int64_t row = (((int64_t)slot * p.batch + b) * p.n_queries + i) * p.n_q_heads + h;
         if (w == 0 && q4 == 0) {
             p.m[row] = (m_run[rt] == -INFINITY) ? -INFINITY : m_run[rt] * kLn2;
             p.l[row] = l_run[rt];
@@ -301,11 +294,100 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_mfma_f32_kernel(ChunkParams
     }
 }
 
+// Slot s of the launch (p.slot_begin + s) of stream (blockIdx.z, g): its
+// piece by fixed chunks.
+template <int D, int NRT>
+__global__ __launch_bounds__(kThreads, 2) void chunk_mfma_f32_kernel(ChunkParams p) {
+    __shared__ F32Smem<D, NRT> sm;
+    const int s = blockIdx.x / p.n_kv_heads;
+    const int g = blockIdx.x % p.n_kv_heads;
+    const int b = blockIdx.z;
+    int64_t t0, t1;
+    piece_tokens(p, chunk_view_len(p, b), b, g, s, &t0, &t1);
+    f32_piece<D, NRT>(p, sm, b, g, p.slot_begin + s, t0, t1);
+}
+
+// The whole resident history of every request, cut into balanced pieces
+// (the line split of plan_next) over gridDim.x work-groups, one per CU;
+// work-group w computes the pieces of its range one after another, each
+// into its slot (p.plan_slots slots from p.slot_begin; slots without a
+// piece keep the empty states written before the launch).
+template <int D, int NRT>
+__global__ __launch_bounds__(kThreads, 2) void history_mfma_f32_kernel(ChunkParams p) {
+    __shared__ F32Smem<D, NRT> sm;
+    const int64_t w = blockIdx.x;
+    PlanStart st;
+    if (!plan_start(p, w, st)) return;
+    const int64_t total = st.total, piece_len = st.piece_len;
+
+    // The walk runs on one lane with its cursor in LDS.
+    __shared__ PlanCursor cursor;
+    __shared__ PlanPiece piece;
+    __shared__ int32_t has_piece;
+    if (threadIdx.x == 0) cursor = st.cursor;
+    for (;;) {
+        __syncthreads();  // the previous piece is done with LDS; the cursor is visible
+        if (threadIdx.x == 0)
+            has_piece = plan_step(p.req_len, p.max_len, p.batch, p.n_kv_heads, piece_len, total, p.plan_slots, w,
+                                  &cursor, const_cast<PlanPiece*>(&piece), p.plan_align);
+        __syncthreads();
+        if (!__builtin_amdgcn_readfirstlane(has_piece)) break;
+        // Re-read the arguments for every piece: held across the loop they
+        // would take scalar registers the key loop needs. (The host pass
+        // only checks this body; the kernarg segment exists on the device.)
+#if defined(__HIP_DEVICE_COMPILE__)
+        const __attribute__((address_space(4))) ChunkParams* args =
+            (const __attribute__((address_space(4))) ChunkParams*)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(args));
+        const ChunkParams pa = *args;
+#else
+        const ChunkParams& pa = p;
+#endif
+        const volatile PlanPiece* pc = &piece;
+        const int32_t k = __builtin_amdgcn_readfirstlane(pc->k);
+        if (k >= pa.plan_slots) break;  // cannot happen with plan_piece_len; never write past the slots
+        if (k < 0) continue;
+        f32_piece<D, NRT>(pa, sm, __builtin_amdgcn_readfirstlane(pc->b), __builtin_amdgcn_readfirstlane(pc->g),
+                          pa.slot_begin + k, uniform64(pc->t0), uniform64(pc->t1));
+    }
+}
+
 template <int D, int NRT>
 hipError_t launch_f32_t(const ChunkParams& p, hipStream_t stream) {
     const int64_t gx = (int64_t)p.n_items * p.n_kv_heads;
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((chunk_mfma_f32_kernel<D, NRT>), dim3((unsigned)gx, 1, p.batch), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+// Work-groups of one history launch: one per CU (one wave per SIMD, as the
+// narrow bf16 kernel's history launch), queried once per device.
+constexpr int kMaxDevices = 64;
+
+hipError_t history_wgs(int* out) {
+    static int wgs[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    int n = __atomic_load_n(&wgs[dev], __ATOMIC_RELAXED);
+    if (n <= 0) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        n = cus > 0 ? cus : 1;
+        __atomic_store_n(&wgs[dev], n, __ATOMIC_RELAXED);
+    }
+    *out = n;
+    return hipSuccess;
+}
+
+template <int D, int NRT>
+hipError_t launch_hist_f32_t(const ChunkParams& p, hipStream_t stream) {
+    int n = 0;
+    hipError_t e = history_wgs(&n);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((history_mfma_f32_kernel<D, NRT>), dim3(n), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -318,6 +400,16 @@ hipError_t launch_chunk_mfma_f32(const ChunkParams& p, int head_dim, hipStream_t
         return hipErrorInvalidValue;
     if (head_dim == 64) return p.rows > 16 ? launch_f32_t<64, 2>(p, stream) : launch_f32_t<64, 1>(p, stream);
     return p.rows > 16 ? launch_f32_t<128, 2>(p, stream) : launch_f32_t<128, 1>(p, stream);
+}
+
+// The balanced cut on the fp32 kernel: fp32, head_dim 128 or 64, up to 32
+// rows, p.plan_slots >= 2, no block statistics, no candidate region.
+hipError_t launch_history_mfma_f32(const ChunkParams& p, int head_dim, hipStream_t stream) {
+    if ((head_dim != 128 && head_dim != 64) || p.rows > 32 || p.plan_slots < 2 || p.stats || p.with_cand ||
+        p.chunk_idx)
+        return hipErrorInvalidValue;
+    if (head_dim == 64) return p.rows > 16 ? launch_hist_f32_t<64, 2>(p, stream) : launch_hist_f32_t<64, 1>(p, stream);
+    return p.rows > 16 ? launch_hist_f32_t<128, 2>(p, stream) : launch_hist_f32_t<128, 1>(p, stream);
 }
 
 }  // namespace ssv

@@ -27,11 +27,11 @@ def device_cus(device="cuda") -> int:
 
 
 def wgs_per_cu(cfg, engine="auto") -> int:
-    """Work-groups per compute unit in one launch: one for the narrow MFMA
-    kernels (two co-resident 4-wave work-groups progress unevenly, and the
-    one left alone at the end streams slower), two for the other chunk
-    kernels."""
-    return 1 if narrow_mfma(cfg, engine) else 2
+    """Work-groups per compute unit in one launch: one for the narrow bf16
+    and the fp32 MFMA kernels (two co-resident 4-wave work-groups progress
+    unevenly, and the one left alone at the end streams slower), two for
+    the other chunk kernels."""
+    return 1 if narrow_mfma(cfg, engine) or f32_mfma(cfg, engine) else 2
 
 
 def auto_chunks_per_slot(cfg, hist_len, chunk_len, cus: int, engine="auto") -> int:
@@ -67,9 +67,10 @@ def one_piece_per_stream(max_len: int, streams: int, cus: int) -> bool:
 
 def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
     """Slots per stream for ss_verify_history. Ragged lengths on the narrow
-    MFMA kernel: one when one_piece_per_stream holds, else as many as the
-    longest stream has pieces when every work-group of the launch
-    (wgs_per_cu per compute unit) takes an even share of the line. Uniform lengths: one chunk per work-group of that
+    MFMA kernel: one when one_piece_per_stream holds, else (and on the other
+    kernels) as many as the longest stream has pieces when every work-group
+    of the launch (wgs_per_cu per compute unit) takes an even share of the
+    line. Uniform lengths: one chunk per work-group of that
     launch. Wide row groups on the MFMA kernel: one wave of work-groups
     (8-wave groups of 256 rows, one per compute unit, or 4-wave groups of 128
     rows, two per unit), the slot count ss_verify_round picks; other wide
@@ -84,8 +85,6 @@ def auto_history_slots(cfg, hist_len, cus: int, engine="auto") -> int:
         return max(1, -(-pad_max // (4 * cfg.chunk_len)))
     wave = wgs_per_cu(cfg, engine) * cus
     if not cfg.ragged:
-        if f32_mfma(cfg, engine):
-            wave = cus  # one work-group per CU streams faster here too
         return max(1, wave // (cfg.batch * cfg.n_kv_heads))
     if not any(pads):
         return 2

@@ -917,11 +917,51 @@ def test_fp32_on_both_engines(name):
     compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
 
 
-def test_head_dim_64_full_size_sampled():
-    """The InternLM2.5-like ragged layer with head_dim 64 at full size (32
-    requests up to 65,536 tokens), in the benchmark's launch configuration,
-    on sampled (request, KV head) slices against the oracle."""
-    cfg = C["c3_internlm25_7b_ragged"].with_(head_dim=64)
+F32_CUT_CASES = {
+    # 16 streams over the whole device: every stream is cut into as many
+    # pieces as it has slots, and with few slots the ranges grow
+    "few_long_streams": C["c3_internlm25_7b_ragged"].with_(batch=2, dtype="f32", hist_len=20000, ragged_lo=5000,
+                                                           chunk_len=1024),
+    # 320 streams of odd lengths (none a multiple of 128), empties included
+    "many_odd_streams": C["c3_internlm25_7b_ragged"].with_(batch=40, dtype="f32", hist_len=3001, ragged_lo=1,
+                                                           chunk_len=256),
+    "tree_d64": C["c3_internlm25_7b_ragged"].with_(batch=6, dtype="f32", head_dim=64, n_queries=8, mask="tree",
+                                                   hist_len=9000, ragged_lo=1, chunk_len=512),
+}
+
+
+@pytest.mark.parametrize("slots", [2, 5, 8])
+@pytest.mark.parametrize("name", list(F32_CUT_CASES))
+def test_fp32_balanced_cut(name, slots):
+    """Ragged fp32 histories on the balanced cut (the fp32 MFMA kernel's
+    history launch, one work-group per CU walking its range) with 2, 5 and
+    8 history slots match the oracle within 1e-5."""
+    cfg = F32_CUT_CASES[name]
+    assert rounds.f32_mfma(cfg) and cfg.ragged
+    inp = wl.make_inputs(cfg)
+    if name == "many_odd_streams":
+        inp.hist_len = inp.hist_len.copy()
+        inp.hist_len[[3, 17]] = 0
+        # 128k + 1 tokens (never longer than generated): a one-token tail tile
+        n = inp.hist_len[[4, 21]]
+        assert (n >= 1).all()
+        inp.hist_len[[4, 21]] = n - (n - 1) % 128
+    o_ref, lse_ref = oracle_round(inp)
+    log(f"[fp32 cut] {name}: {slots} slots")
+    rnd = rounds.ResidentRound(inp, split="balanced", history_slots=slots)
+    rnd.run()
+    torch.cuda.synchronize()
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
+
+
+@pytest.mark.parametrize("variant", ["d64", "f32"])
+def test_full_size_sampled_variants(variant):
+    """The InternLM2.5-like ragged layer at full size (32 requests up to
+    65,536 tokens) with head_dim 64, and in fp32 (the fp32 MFMA kernel on the
+    balanced cut), in the benchmark's launch configuration, on sampled
+    (request, KV head) slices against the oracle."""
+    cfg = C["c3_internlm25_7b_ragged"].with_(**({"head_dim": 64} if variant == "d64" else {"dtype": "f32"}))
     inp = wl.make_inputs(cfg)
     rnd = rounds.ResidentRound(inp, **rounds.BENCH_RESIDENT)
     rnd.run()
@@ -930,7 +970,7 @@ def test_head_dim_64_full_size_sampled():
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     check_mask(rnd, inp)
     for b, g in ((0, 0), (cfg.batch - 1, cfg.n_kv_heads - 1), (int(np.argmax(inp.hist_len)), 3)):
-        log(f"[d64 full] oracle slice b={b} g={g}")
+        log(f"[{variant} full] oracle slice b={b} g={g}")
         o_ref, lse_ref = oracle_round(inp, requests=[b], kv_heads=[g])
         compare(cfg, o, lse, o_ref, lse_ref, rows_of(cfg, b, g))
 
