@@ -53,12 +53,12 @@ def chunk_kernel_sources(cfg, engine="auto"):
     """Source files of the chunk kernel that serves cfg (mirrors the library's
     engine choice)."""
     bf16_128 = cfg.dtype == "bf16" and cfg.head_dim == 128
-    narrow = cfg.dtype == "bf16" and cfg.head_dim in (64, 128) and cfg.rows <= 32
+    mfma_bf16 = cfg.dtype == "bf16" and cfg.head_dim in (64, 128)
     if engine != "valu" and cfg.dtype == "f32" and cfg.rows <= 32:
         main = "ss_mfma_f32.hip"
-    elif engine == "valu" or not (narrow or bf16_128):
+    elif engine == "valu" or not mfma_bf16:
         main = "ss_valu_small.hip" if bf16_128 and cfg.rows < 16 else "ss_valu.hip"
-    elif narrow:
+    elif cfg.rows <= 32:
         main = "ss_mfma.hip"
     else:
         main = "ss_mfma_wide.hip"

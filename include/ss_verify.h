@@ -55,7 +55,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 16
+#define SS_ABI_VERSION 17
 
 /* status codes */
 #define SS_OK 0
@@ -181,14 +181,14 @@ SS_API int64_t ss_state_bytes(const ss_problem_t* problem, int32_t n_slots);
  *              in [0, out->n_slots); they are overwritten
  * Engines (problem->engine). SS_ENGINE_AUTO runs on the matrix cores: for
  * bf16 one MFMA kernel for up to 32 rows per KV head (R = n_queries * G,
- * padded to a 16-row tile; head_dim 128 or 64) and one for more rows
- * (head_dim 128); for fp32 one MFMA kernel for up to 32 rows (head_dim 128
- * or 64). Beyond 32 rows, fp32 and head_dim 64 run on a VALU kernel. On
- * gfx950 the padded MFMA kernel stays bound by HBM down to a single row,
- * ahead of the VALU kernels, so AUTO never picks VALU where an MFMA kernel
- * applies. SS_ENGINE_VALU forces the VALU kernels (a small-row kernel below
- * 16 rows of bf16 / head_dim 128); SS_ENGINE_MFMA is SS_ERR_UNSUPPORTED for
- * fp32 and for head_dim 64 beyond 32 rows.
+ * padded to a 16-row tile) and one for more rows, both for head_dim 128 and
+ * 64; for fp32 one MFMA kernel for up to 32 rows (head_dim 128 or 64).
+ * Beyond 32 rows, fp32 runs on a VALU kernel. On gfx950 the padded MFMA
+ * kernel stays bound by HBM down to a single row, ahead of the VALU kernels,
+ * so AUTO never picks VALU where an MFMA kernel applies. SS_ENGINE_VALU
+ * forces the VALU kernels (a small-row kernel below 16 rows of bf16 /
+ * head_dim 128); SS_ENGINE_MFMA is SS_ERR_UNSUPPORTED for fp32 beyond 32
+ * rows.
  * Errors: SS_ERR_INVALID_ARG for null pointers, non-positive sizes, slots
  * out of range, bad alignment; SS_ERR_UNSUPPORTED for head_dim outside
  * {64, 128}; SS_ERR_HIP if the launch fails.

@@ -53,8 +53,8 @@ int32_t check_problem(const ss_problem_t* p) {
         return fail(SS_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", p->head_dim);
     if (p->batch > 65535) return fail(SS_ERR_UNSUPPORTED, "batch above 65535");
     const int64_t rows = (int64_t)p->n_queries * (p->n_q_heads / p->n_kv_heads);
-    if (p->engine == SS_ENGINE_MFMA && !(rows <= 32 || (p->dtype == SS_BF16 && p->head_dim == 128)))
-        return fail(SS_ERR_UNSUPPORTED, "the MFMA engine needs bf16 and head_dim 128 above 32 rows per KV head");
+    if (p->engine == SS_ENGINE_MFMA && !(rows <= 32 || p->dtype == SS_BF16))
+        return fail(SS_ERR_UNSUPPORTED, "the MFMA engine needs bf16 above 32 rows per KV head");
     const int64_t row_blocks = (rows + kValuRows - 1) / kValuRows;
     if ((int64_t)p->n_kv_heads * row_blocks > 65535 || (int64_t)p->n_kv_heads * cand_row_blocks((int)rows) > 65535)
         return fail(SS_ERR_UNSUPPORTED, "too many rows per request");
@@ -90,21 +90,21 @@ int32_t check_state(const ss_state_t* s, const char* name) {
 }
 
 // Which chunk kernel serves a problem. AUTO: bf16 runs on the matrix cores
-// (rows up to 32 on the MFMA kernel, padded to a 16-row tile, head_dim 128
-// or 64; more rows on the wide-row MFMA kernel, head_dim 128), and so does
-// fp32 up to 32 rows (the fp32 MFMA kernel). Measured on gfx950, the padded
-// MFMA kernels stay far ahead of the VALU kernels, which are bound by vector
-// and LDS issue, so AUTO keeps VALU only where no MFMA kernel applies (fp32
-// or head_dim 64 beyond 32 rows). VALU forces the vector kernels (the
-// small-row kernel below 16 rows of bf16 / head_dim 128).
+// (rows up to 32 on the MFMA kernel, padded to a 16-row tile; more rows on
+// the wide-row MFMA kernel; head_dim 128 or 64 on both), and so does fp32 up
+// to 32 rows (the fp32 MFMA kernel). Measured on gfx950, the padded MFMA
+// kernels stay far ahead of the VALU kernels, which are bound by vector and
+// LDS issue, so AUTO keeps VALU only where no MFMA kernel applies (fp32
+// beyond 32 rows). VALU forces the vector kernels (the small-row kernel
+// below 16 rows of bf16 / head_dim 128).
 enum class ChunkEngine { kValu, kValuSmall, kMfma, kMfmaWide, kMfmaF32 };
 
 ChunkEngine chunk_engine(const ss_problem_t* p) {
     const int rows = p->n_queries * (p->n_q_heads / p->n_kv_heads);
     const bool bf16_128 = p->dtype == SS_BF16 && p->head_dim == 128;
-    // the narrow kernel takes head_dim 64 too; the wide-row kernel 128 only
-    const bool narrow = p->dtype == SS_BF16 && (p->head_dim == 128 || p->head_dim == 64) && rows <= 32;
-    const bool wide = bf16_128 && rows > 32;
+    // both MFMA kernels take head_dim 128 and 64 (the only ones check_problem admits)
+    const bool narrow = p->dtype == SS_BF16 && rows <= 32;
+    const bool wide = p->dtype == SS_BF16 && rows > 32;
     // fp32 with up to 32 rows: the fp32 matrix-core kernel
     const bool f32 = p->dtype == SS_F32 && rows <= 32;
     if (p->engine == SS_ENGINE_VALU || !(narrow || wide || f32))

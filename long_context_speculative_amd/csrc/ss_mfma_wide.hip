@@ -1,5 +1,6 @@
 // MFMA bf16 chunk kernel of libssverify for wide row groups (more than 32
-// rows per KV head, e.g. a 64-node candidate tree under 8-way GQA: 512 rows).
+// rows per KV head, e.g. a 64-node candidate tree under 8-way GQA: 512 rows),
+// head_dim 128 or 64.
 //
 // SpecStream ("Resource-Efficient Speculative Decoding for Long-Context LLM
 // Serving"), section 4.2: one history chunk serves the whole query group; its
@@ -48,30 +49,35 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int D = 128;
 constexpr int kTile = 32;       // keys per MFMA sub-tile (KT keys per iteration)
-// Row pitches of the staged tiles. The transposing V reads are free of bank
-// conflicts at a 32-byte pad. The 16-byte K fragment reads are free of them at
-// a 32-byte pad too, but at the 16-byte pad used here they spend about a third
-// of their LDS cycles in conflicts; the conflict-free pitch is still slower on
-// MI355X: the launch is held by the chip's power limit, and with the stall
-// cycles gone it runs at a lower clock (fewer cycles, longer time).
-constexpr int kRow = D + 8;     // bf16 per staged K row (16-byte pad)
-constexpr int kVRow = D + 16;   // bf16 per staged V row (32-byte pad)
-constexpr int kNS = D / 32;     // 32-feature steps of S = K Q^T
-constexpr int kNXT = D / 16;    // 16-feature tiles of O^T
 constexpr float kGrowLog2 = 8.f;  // rescale threshold (log2 units)
 // A piece attended without the weights' rounding remainders is attended again
 // with them when some row's largest weight exceeds this share of its sum.
 constexpr float kShareMax = 1.f / 32.f;
 
+// Row pitches of the staged tiles (head_dim D = 128 or 64). At D = 128 the
+// transposing V reads are free of bank conflicts at a 32-byte pad, and so
+// are the 16-byte K fragment reads; at the 16-byte K pad used here those
+// spend about a third of their LDS cycles in conflicts, yet the
+// conflict-free pitch is slower on MI355X: the launch is held by the chip's
+// power limit, and with the stall cycles gone it runs at a lower clock
+// (fewer cycles, longer time).
+template <int D>
+struct WideDims {
+    static constexpr int kRow = D + 8;     // bf16 per staged K row (16-byte pad)
+    static constexpr int kVRow = D + 16;   // bf16 per staged V row (32-byte pad)
+    static constexpr int kNS = D / 32;     // 32-feature steps of S = K Q^T
+    static constexpr int kNXT = D / 16;    // 16-feature tiles of O^T
+    static constexpr int kRowPieces = D / 8;  // 16-byte pieces per key row
+};
+
 // 16-byte aligned so that the 16-byte staging stores and K reads are single
 // ds_write_b128 / ds_read_b128 (with only the 8-byte alignment of the
 // member types the compiler splits them into pairs of 8-byte accesses).
-template <int KT>
+template <int D, int KT>
 struct alignas(16) WideSmem {
-    uint16_t k[3][KT][kRow];
-    uint16_t v[3][KT][kVRow];
+    uint16_t k[3][KT][WideDims<D>::kRow];
+    uint16_t v[3][KT][WideDims<D>::kVRow];
     uint64_t cbits[64];  // candidate visibility bits (n_queries <= 64)
     int32_t again;       // some wave needs the piece attended again
 };
@@ -87,8 +93,11 @@ __device__ __forceinline__ s16x4 lds_read_tr(const uint16_t* p) {
 // FIN: one slot per stream in a whole-round call, the rows finished into
 // p.fin_o / p.fin_lse instead of the slot (a variant of its own: at 256
 // registers the plain kernel has no room for the other epilogue).
-template <int NW, int kRT, int KT, bool FIN>
+template <int D, int NW, int kRT, int KT, bool FIN>
 __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk_mfma_wide_kernel(ChunkParams p, int row_groups) {
+    constexpr int kVRow = WideDims<D>::kVRow;
+    constexpr int kNS = WideDims<D>::kNS, kNXT = WideDims<D>::kNXT, kRP = WideDims<D>::kRowPieces;
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
     static_assert(KT % kTile == 0, "an iteration is whole sub-tiles");
     constexpr int kSub = KT / kTile;           // 32-key sub-tiles per iteration
     constexpr int kKB = 2 * kSub;              // 16-key blocks per iteration
@@ -96,7 +105,7 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
     constexpr int kPieces = KT * (D / 8);      // 16-byte pieces per K (or V) tile
     constexpr int kPer = kPieces / T;          // pieces of K and of V per thread
     static_assert(kPieces % T == 0, "tile pieces must divide evenly");
-    __shared__ WideSmem<KT> sm;
+    __shared__ WideSmem<D, KT> sm;
 
     // Work-group -> (unit u = (slot, KV head), row group): eight consecutive
     // units go to the eight XCDs (dispatch is round-robin over them), and the
@@ -156,8 +165,8 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
     const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
     const int n_tiles = (int)((t1 - t0 + KT - 1) / KT);
 
-    // Staging: thread tid copies K and V pieces u = tid + j*T (key u / 16,
-    // features 8*(u % 16) .. +7). Keys past the range are clamped to its last
+    // Staging: thread tid copies K and V pieces u = tid + j*T (key u / kRP,
+    // features 8*(u % kRP) .. +7). Keys past the range are clamped to its last
     // key (finite values; their scores are masked).
     u32x4 pa[2][kPer], pb[2][kPer];
     auto fetch = [&](int64_t tk, u32x4(&pre)[2][kPer]) __attribute__((always_inline)) {
@@ -167,7 +176,7 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int u = tid + j * T;
-            const int off = min(u >> 4, last) * sti + 8 * (u & 15);
+            const int off = min(u / kRP, last) * sti + 8 * (u % kRP);
             pre[0][j] = *reinterpret_cast<const u32x4*>(kb + off);
             pre[1][j] = *reinterpret_cast<const u32x4*>(vb + off);
         }
@@ -176,8 +185,8 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
             const int u = tid + j * T;
-            *reinterpret_cast<u32x4*>(&sm.k[buf][u >> 4][8 * (u & 15)]) = pre[0][j];
-            *reinterpret_cast<u32x4*>(&sm.v[buf][u >> 4][8 * (u & 15)]) = pre[1][j];
+            *reinterpret_cast<u32x4*>(&sm.k[buf][u / kRP][8 * (u % kRP)]) = pre[0][j];
+            *reinterpret_cast<u32x4*>(&sm.v[buf][u / kRP][8 * (u % kRP)]) = pre[1][j];
         }
     };
 
@@ -457,7 +466,7 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
                 const int u = tid + j * T;
-                const int off = (c0 + min(u >> 4, last)) * cst + 8 * (u & 15);
+                const int off = (c0 + min(u / kRP, last)) * cst + 8 * (u % kRP);
                 pa[0][j] = *reinterpret_cast<const u32x4*>(ckp + off);
                 pa[1][j] = *reinterpret_cast<const u32x4*>(cvp + off);
             }
@@ -533,7 +542,7 @@ __global__ __launch_bounds__(64 * NW, (kRT == 2 && KT == 32) ? 2 : 1) void chunk
     }
 }
 
-template <int NW, int kRT, int KT>
+template <int D, int NW, int kRT, int KT>
 hipError_t launch_wide_t(const ChunkParams& p, hipStream_t stream) {
     const int row_groups = (p.rows + 16 * kRT * NW - 1) / (16 * kRT * NW);
     const int64_t units = (int64_t)p.n_items * p.n_kv_heads;
@@ -541,21 +550,28 @@ hipError_t launch_wide_t(const ChunkParams& p, hipStream_t stream) {
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     dim3 grid((unsigned)gx, 1, p.batch);
     if (p.fin_o)
-        hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW, kRT, KT, true>), grid, dim3(64 * NW), 0, stream, p, row_groups);
+        hipLaunchKernelGGL((chunk_mfma_wide_kernel<D, NW, kRT, KT, true>), grid, dim3(64 * NW), 0, stream, p, row_groups);
     else
-        hipLaunchKernelGGL((chunk_mfma_wide_kernel<NW, kRT, KT, false>), grid, dim3(64 * NW), 0, stream, p, row_groups);
+        hipLaunchKernelGGL((chunk_mfma_wide_kernel<D, NW, kRT, KT, false>), grid, dim3(64 * NW), 0, stream, p, row_groups);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_wide_d(const ChunkParams& p, hipStream_t stream) {
+    // 32 rows per wave: up to 128 rows in one group of four waves (32-key
+    // tiles, two groups per CU), more rows in groups of eight waves (two per
+    // SIMD, 64-key tiles, one group per CU).
+    if (p.rows <= 128) return launch_wide_t<D, 4, 2, 32>(p, stream);
+    return launch_wide_t<D, 8, 2, 64>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_chunk_mfma_wide(const ChunkParams& p, int head_dim, hipStream_t stream) {
-    if (head_dim != D || p.rows <= 32) return hipErrorInvalidValue;
-    // 32 rows per wave: up to 128 rows in one group of four waves (32-key
-    // tiles, two groups per CU), more rows in groups of eight waves (two per
-    // SIMD, 64-key tiles, one group per CU).
-    if (p.rows <= 128) return launch_wide_t<4, 2, 32>(p, stream);
-    return launch_wide_t<8, 2, 64>(p, stream);
+    if (p.rows <= 32) return hipErrorInvalidValue;
+    if (head_dim == 128) return launch_wide_d<128>(p, stream);
+    if (head_dim == 64) return launch_wide_d<64>(p, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace ssv

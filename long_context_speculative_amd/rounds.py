@@ -117,7 +117,7 @@ def mfma_fuses_candidates(cfg, engine="auto") -> bool:
     """Whether ss_verify_history folds the candidate region into the history
     launch (the MFMA kernels, narrow and wide-row) instead of giving it a
     slot of its own."""
-    return narrow_mfma(cfg, engine) or (engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim == 128)
+    return narrow_mfma(cfg, engine) or (engine != "valu" and cfg.dtype == "bf16" and cfg.head_dim in (64, 128))
 
 
 # Launch configuration of the resident round that the benchmark times.

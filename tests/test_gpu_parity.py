@@ -564,6 +564,8 @@ SHORT_KERNELS = {
     "narrow_mfma": dict(n_q_heads=32, n_kv_heads=8, n_queries=6, mask="causal", engine="auto"),
     "wide_mfma_r128": dict(n_q_heads=16, n_kv_heads=2, n_queries=16, mask="tree", engine="auto"),
     "wide_mfma_r512": dict(n_q_heads=64, n_kv_heads=8, n_queries=64, mask="tree", engine="auto"),
+    "wide_mfma_r128_d64": dict(n_q_heads=16, n_kv_heads=2, n_queries=16, mask="tree", engine="auto", head_dim=64),
+    "wide_mfma_r512_d64": dict(n_q_heads=64, n_kv_heads=8, n_queries=64, mask="tree", engine="auto", head_dim=64),
     "valu_small_r8": dict(n_q_heads=32, n_kv_heads=8, n_queries=2, mask="causal", engine="valu"),
 }
 
@@ -872,6 +874,54 @@ def test_head_dim_64_on_the_matrix_cores(name):
         compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
 
 
+D64_WIDE_CASES = {
+    "tree_512_rows": C["c4_tree_72b"].with_(batch=2, head_dim=64, hist_len=5000, chunk_len=1024),
+    "tree_128_rows_ragged_empties": C["c3_internlm25_7b_ragged"].with_(
+        batch=12, n_q_heads=16, n_kv_heads=2, n_queries=16, mask="tree", head_dim=64, hist_len=4000, ragged_lo=1,
+        chunk_len=512),
+    "rows_40": C["c2_qwen3_8b"].with_(batch=3, n_q_heads=16, n_kv_heads=4, n_queries=10, head_dim=64,
+                                      hist_len=3000, chunk_len=512),
+}
+
+
+@pytest.mark.parametrize("name", list(D64_WIDE_CASES))
+def test_head_dim_64_wide_rows(name):
+    """bf16 with head_dim 64 and more than 32 rows per KV head runs on the
+    wide-row MFMA kernel (eight-wave groups of 256 rows, or four-wave groups
+    of 128): the benchmark's launch configuration (balanced cut, candidates
+    folded in), the chunked split, the whole-round call with the library's
+    slot choice and with one slot (O and lse written by the history launch),
+    and the forced VALU engine all match the oracle. The ragged case has
+    empty requests and requests below the short-history threshold."""
+    cfg = D64_WIDE_CASES[name]
+    assert cfg.rows > 32 and rounds.mfma_fuses_candidates(cfg) and not rounds.narrow_mfma(cfg)
+    inp = wl.make_inputs(cfg)
+    if name == "tree_128_rows_ragged_empties":
+        inp.hist_len = inp.hist_len.copy()
+        inp.hist_len[[0, 5, 11]] = 0
+        inp.hist_len[6], inp.hist_len[7], inp.hist_len[8] = 1, 2047, 2048
+    o_ref, lse_ref = oracle_round(inp)
+    for label, kw in (("balanced", dict(rounds.BENCH_RESIDENT)),
+                      ("chunks", dict(split="chunks", chunks_per_slot=2)),
+                      ("valu", dict(split="chunks", chunks_per_slot=2, engine="valu"))):
+        log(f"[d64 wide] {name}: {label}")
+        rnd = rounds.ResidentRound(inp, **kw)
+        rnd.run()
+        torch.cuda.synchronize()
+        compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+        check_mask(rnd, inp)
+    rnd = rounds.ResidentRound(inp)
+    work = ss.StateBuffers(rnd.problem, 64, "cuda")
+    for n_slots in (0, 1):
+        log(f"[d64 wide] {name}: round call, n_slots={n_slots}")
+        rnd.o.fill_(float("nan"))
+        rnd.lse.fill_(float("nan"))
+        ss.ss_verify_round(rnd.problem, rnd.q, rnd.hist_view, rnd.cand_view, rnd.parents, rnd.mask_out, n_slots,
+                           work, rnd.o, rnd.lse)
+        torch.cuda.synchronize()
+        compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+
+
 F32_CASES = {
     "tiny_d64": C["c1_tiny_f32"],
     "uniform_d128": C["c2_qwen3_8b"].with_(batch=3, dtype="f32", hist_len=3000, chunk_len=1024),
@@ -955,13 +1005,22 @@ def test_fp32_balanced_cut(name, slots):
     check_mask(rnd, inp)
 
 
-@pytest.mark.parametrize("variant", ["d64", "f32"])
+FULL_VARIANTS = {
+    "d64": C["c3_internlm25_7b_ragged"].with_(head_dim=64),
+    "f32": C["c3_internlm25_7b_ragged"].with_(dtype="f32"),
+    "tree_d64": C["c4_tree_72b"].with_(head_dim=64),
+}
+
+
+@pytest.mark.parametrize("variant", list(FULL_VARIANTS))
 def test_full_size_sampled_variants(variant):
     """The InternLM2.5-like ragged layer at full size (32 requests up to
     65,536 tokens) with head_dim 64, and in fp32 (the fp32 MFMA kernel on the
-    balanced cut), in the benchmark's launch configuration, on sampled
-    (request, KV head) slices against the oracle."""
-    cfg = C["c3_internlm25_7b_ragged"].with_(**({"head_dim": 64} if variant == "d64" else {"dtype": "f32"}))
+    balanced cut), and the 72B-like tree round at full size (4 requests of
+    131,072 tokens, 512 rows per KV head) with head_dim 64 (the wide-row
+    kernel), in the benchmark's launch configuration, on sampled (request,
+    KV head) slices against the oracle."""
+    cfg = FULL_VARIANTS[variant]
     inp = wl.make_inputs(cfg)
     rnd = rounds.ResidentRound(inp, **rounds.BENCH_RESIDENT)
     rnd.run()
@@ -1106,6 +1165,9 @@ PEAKED = {
     "valu_small_r8": (C["c2_qwen3_8b"].with_(batch=2, n_queries=2, hist_len=5000, chunk_len=1024), "valu"),
     "bf16_d64": (C["c2_qwen3_8b"].with_(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=64, hist_len=3000,
                                         chunk_len=512), "auto"),
+    "wide_r512_tree_d64": (C["c4_tree_72b"].with_(batch=1, head_dim=64, hist_len=6000, chunk_len=1024), "auto"),
+    "wide_r96_d64": (C["c2_qwen3_8b"].with_(batch=2, n_q_heads=32, n_kv_heads=2, n_queries=6, head_dim=64,
+                                            hist_len=5000, chunk_len=1024), "auto"),
 }
 
 
