@@ -54,7 +54,7 @@ def chunk_kernel_sources(cfg, engine="auto"):
     engine choice)."""
     bf16_128 = cfg.dtype == "bf16" and cfg.head_dim == 128
     mfma_bf16 = cfg.dtype == "bf16" and cfg.head_dim in (64, 128)
-    if engine != "valu" and cfg.dtype == "f32" and cfg.rows <= 32:
+    if engine != "valu" and cfg.dtype == "f32":
         main = "ss_mfma_f32.hip"
     elif engine == "valu" or not mfma_bf16:
         main = "ss_valu_small.hip" if bf16_128 and cfg.rows < 16 else "ss_valu.hip"

@@ -55,7 +55,7 @@ extern "C" {
 #define SS_API
 #endif
 
-#define SS_ABI_VERSION 17
+#define SS_ABI_VERSION 18
 
 /* status codes */
 #define SS_OK 0
@@ -179,16 +179,14 @@ SS_API int64_t ss_state_bytes(const ss_problem_t* problem, int32_t n_slots);
  *              empty for that request
  *   out        slots [slot_begin, slot_begin + ceil(n_chunks/cps)) must lie
  *              in [0, out->n_slots); they are overwritten
- * Engines (problem->engine). SS_ENGINE_AUTO runs on the matrix cores: for
- * bf16 one MFMA kernel for up to 32 rows per KV head (R = n_queries * G,
- * padded to a 16-row tile) and one for more rows, both for head_dim 128 and
- * 64; for fp32 one MFMA kernel for up to 32 rows (head_dim 128 or 64).
- * Beyond 32 rows, fp32 runs on a VALU kernel. On gfx950 the padded MFMA
- * kernel stays bound by HBM down to a single row, ahead of the VALU kernels,
- * so AUTO never picks VALU where an MFMA kernel applies. SS_ENGINE_VALU
- * forces the VALU kernels (a small-row kernel below 16 rows of bf16 /
- * head_dim 128); SS_ENGINE_MFMA is SS_ERR_UNSUPPORTED for fp32 beyond 32
- * rows.
+ * Engines (problem->engine). SS_ENGINE_AUTO (the same as SS_ENGINE_MFMA)
+ * runs every shape on the matrix cores: for bf16 one MFMA kernel for up to
+ * 32 rows per KV head (R = n_queries * G, padded to a 16-row tile) and one
+ * for more rows; for fp32 one MFMA kernel (one work-group per 32 rows beyond
+ * 32); all for head_dim 128 and 64. On gfx950 the padded MFMA kernel stays
+ * bound by HBM down to a single row, ahead of the VALU kernels.
+ * SS_ENGINE_VALU forces the VALU kernels (a small-row kernel below 16 rows
+ * of bf16 / head_dim 128).
  * Errors: SS_ERR_INVALID_ARG for null pointers, non-positive sizes, slots
  * out of range, bad alignment; SS_ERR_UNSUPPORTED for head_dim outside
  * {64, 128}; SS_ERR_HIP if the launch fails.
@@ -305,7 +303,8 @@ SS_API int32_t ss_merge_states(const ss_problem_t* problem, const ss_state_t* in
  *             on the narrow MFMA kernel 1 -- a work-group per stream -- when
  *             hist->max_len <= 4096 with at least one stream per compute
  *             unit or <= 2048 with three per four units, else 8 for the
- *             balanced cut, on the fp32 MFMA kernel 8; +1 for the
+ *             balanced cut, on the fp32 MFMA kernel 8 (beyond 32 rows
+ *             about two work-groups per compute unit); +1 for the
  *             candidate slot on the fp32 and VALU engines),
  *             limited to work->n_slots
  *   work      caller-allocated state slots (workspace); slots [0, n_slots)

@@ -53,8 +53,6 @@ int32_t check_problem(const ss_problem_t* p) {
         return fail(SS_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", p->head_dim);
     if (p->batch > 65535) return fail(SS_ERR_UNSUPPORTED, "batch above 65535");
     const int64_t rows = (int64_t)p->n_queries * (p->n_q_heads / p->n_kv_heads);
-    if (p->engine == SS_ENGINE_MFMA && !(rows <= 32 || p->dtype == SS_BF16))
-        return fail(SS_ERR_UNSUPPORTED, "the MFMA engine needs bf16 above 32 rows per KV head");
     const int64_t row_blocks = (rows + kValuRows - 1) / kValuRows;
     if ((int64_t)p->n_kv_heads * row_blocks > 65535 || (int64_t)p->n_kv_heads * cand_row_blocks((int)rows) > 65535)
         return fail(SS_ERR_UNSUPPORTED, "too many rows per request");
@@ -89,28 +87,23 @@ int32_t check_state(const ss_state_t* s, const char* name) {
     return SS_OK;
 }
 
-// Which chunk kernel serves a problem. AUTO: bf16 runs on the matrix cores
-// (rows up to 32 on the MFMA kernel, padded to a 16-row tile; more rows on
-// the wide-row MFMA kernel; head_dim 128 or 64 on both), and so does fp32 up
-// to 32 rows (the fp32 MFMA kernel). Measured on gfx950, the padded MFMA
-// kernels stay far ahead of the VALU kernels, which are bound by vector and
-// LDS issue, so AUTO keeps VALU only where no MFMA kernel applies (fp32
-// beyond 32 rows). VALU forces the vector kernels (the small-row kernel
-// below 16 rows of bf16 / head_dim 128).
+// Which chunk kernel serves a problem. AUTO (and MFMA): every shape runs on
+// the matrix cores: bf16 with up to 32 rows on the MFMA kernel (padded to a
+// 16-row tile), more rows on the wide-row MFMA kernel, fp32 on the fp32 MFMA
+// kernel (row groups of 32 beyond 32 rows); head_dim 128 or 64 on all.
+// Measured on gfx950, the padded MFMA kernels stay far ahead of the VALU
+// kernels, which are bound by vector and LDS issue. VALU forces the vector
+// kernels (the small-row kernel below 16 rows of bf16 / head_dim 128); they
+// also serve fp32 chunk lists (gathered verification).
 enum class ChunkEngine { kValu, kValuSmall, kMfma, kMfmaWide, kMfmaF32 };
 
 ChunkEngine chunk_engine(const ss_problem_t* p) {
     const int rows = p->n_queries * (p->n_q_heads / p->n_kv_heads);
     const bool bf16_128 = p->dtype == SS_BF16 && p->head_dim == 128;
-    // both MFMA kernels take head_dim 128 and 64 (the only ones check_problem admits)
-    const bool narrow = p->dtype == SS_BF16 && rows <= 32;
-    const bool wide = p->dtype == SS_BF16 && rows > 32;
-    // fp32 with up to 32 rows: the fp32 matrix-core kernel
-    const bool f32 = p->dtype == SS_F32 && rows <= 32;
-    if (p->engine == SS_ENGINE_VALU || !(narrow || wide || f32))
-        return (bf16_128 && rows < 16) ? ChunkEngine::kValuSmall : ChunkEngine::kValu;
-    if (f32) return ChunkEngine::kMfmaF32;
-    return narrow ? ChunkEngine::kMfma : ChunkEngine::kMfmaWide;
+    // every MFMA kernel takes head_dim 128 and 64 (the only ones check_problem admits)
+    if (p->engine == SS_ENGINE_VALU) return (bf16_128 && rows < 16) ? ChunkEngine::kValuSmall : ChunkEngine::kValu;
+    if (p->dtype == SS_F32) return ChunkEngine::kMfmaF32;
+    return rows <= 32 ? ChunkEngine::kMfma : ChunkEngine::kMfmaWide;
 }
 
 int32_t validate_chunk(const ss_problem_t* problem, const void* q, const ss_kv_view_t* hist, int32_t chunk_len,
@@ -393,8 +386,10 @@ int32_t verify_history(const ss_problem_t* problem, const void* q, const ss_kv_v
         c.fin_o = fin->o;
         c.fin_lse = fin->lse;
     }
-    // ragged lengths on the narrow and the fp32 MFMA kernels: the balanced cut
-    if ((narrow || engine == ChunkEngine::kMfmaF32) && hist->req_len && hist_slots >= 2) {
+    // ragged lengths on the narrow and the fp32 MFMA kernels (up to 32 rows,
+    // one work-group per piece): the balanced cut
+    const bool f32_cut = engine == ChunkEngine::kMfmaF32 && c.rows <= 32;
+    if ((narrow || f32_cut) && hist->req_len && hist_slots >= 2) {
         c.plan_slots = hist_slots;
         // every slot starts empty; pieces overwrite theirs
         const int64_t rows = (int64_t)problem->batch * problem->n_queries * problem->n_q_heads;
@@ -518,8 +513,13 @@ int32_t round_slots(const ss_problem_t* p, const ss_kv_view_t* hist, int32_t* n_
         case ChunkEngine::kMfmaF32:
             // the candidate slot, plus: uniform lengths one work-group per CU
             // (measured: 2 slots 381 us, 4 slots 404 us on a c2-shaped fp32
-            // round); ragged lengths 8 for the balanced cut
-            s = hist->req_len ? 9 : 1 + (int64_t)cus / streams;
+            // round); ragged lengths 8 for the balanced cut; beyond 32 rows
+            // (fixed chunks, a work-group per row group of 32) about two
+            // work-groups per CU
+            if (rows > 32)
+                s = 1 + 2 * (int64_t)cus / (streams * ((rows + 31) / 32));
+            else
+                s = hist->req_len ? 9 : 1 + (int64_t)cus / streams;
             if (s > 9) s = 9;
             break;
         default:

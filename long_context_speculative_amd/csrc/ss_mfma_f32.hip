@@ -1,5 +1,5 @@
-// fp32 MFMA chunk kernel of libssverify: fp32 inputs, head_dim 128 or 64, up
-// to 32 rows per KV head.
+// fp32 MFMA chunk kernel of libssverify: fp32 inputs, head_dim 128 or 64; up
+// to 32 rows per KV head in one work-group, more rows in row groups of 32.
 //
 // SpecStream ("Resource-Efficient Speculative Decoding for Long-Context LLM
 // Serving"), section 4.2: a history chunk serves the whole verification query
@@ -7,7 +7,10 @@
 // slot's keys in tiles of 16; wave w takes tiles w, w+4, ... Every wave holds
 // all R = n_queries * G rows of the KV head (padded to 16 or 32), so each K
 // and V byte is read from HBM once and feeds every query and every head of
-// the GQA group.
+// the GQA group. Beyond 32 rows the fixed-chunk kernel runs one work-group
+// per row group of 32 rows; the row groups of one piece sit 8 work-group ids
+// apart, which the round-robin dispatch places on the same XCD, so all but
+// the first read the piece from that XCD's L2.
 //
 // Per tile, with v_mfma_f32_16x16x4_f32 (A 16x4: lane l holds A[l%16][l/16];
 // B 4x16: B[l/16][l%16]; C 16x16: lane l holds C[4*(l/16)+i][l%16]):
@@ -65,11 +68,12 @@ __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// State of tokens [t0, t1) of stream (b, g) for every row of the KV head,
-// written to slot `slot` of the state buffer.
+// State of tokens [t0, t1) of stream (b, g) for rows r0 .. r0 + 16*NRT - 1
+// of the KV head (those below p.rows), written to slot `slot` of the state
+// buffer.
 template <int D, int NRT>
 __device__ __forceinline__ void f32_piece(const ChunkParams& p, F32Smem<D, NRT>& sm, int b, int g, int slot,
-                                          int64_t t0, int64_t t1) {
+                                          int64_t t0, int64_t t1, int r0) {
     constexpr int NF = D / 4;    // features per lane group (the contraction's steps for S)
     constexpr int NXT = D / 16;  // 16-feature output tiles for O^T
     static_assert(NXT % kWaves == 0, "feature tiles split evenly over the waves");
@@ -81,11 +85,11 @@ __device__ __forceinline__ void f32_piece(const ChunkParams& p, F32Smem<D, NRT>&
     const float* __restrict__ vp = static_cast<const float*>(p.v) + base;
     const int64_t st = p.stride_t;
 
-    // Q^T operand: row r = l16 + 16*rt, features 16u + 4*q4 .. +3 for u < NF/4.
+    // Q^T operand: row r = r0 + l16 + 16*rt, features 16u + 4*q4 .. +3 for u < NF/4.
     float qf[NRT][NF];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-        const int r = l16 + 16 * rt;
+        const int r = r0 + l16 + 16 * rt;
         if (r < p.rows) {
             const int i = r / p.group, h = g * p.group + r % p.group;
             const float* qrow = static_cast<const float*>(p.q) + ((int64_t)(b * p.n_queries + i) * p.n_q_heads + h) * D +
@@ -266,7 +270,7 @@ __device__ __forceinline__ void f32_piece(const ChunkParams& p, F32Smem<D, NRT>&
     }
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-        const int r = l16 + 16 * rt;
+        const int r = r0 + l16 + 16 * rt;
         if (r >= p.rows) continue;
         const int i = r / p.group, h = g * p.group + r % p.group;
         const int64_t row = (((int64_t)slot * p.batch + b) * p.n_queries + i) * p.n_q_heads + h;
@@ -295,16 +299,24 @@ __device__ __forceinline__ void f32_piece(const ChunkParams& p, F32Smem<D, NRT>&
 }
 
 // Slot s of the launch (p.slot_begin + s) of stream (blockIdx.z, g): its
-// piece by fixed chunks.
+// piece by fixed chunks, for the rows of row group rg (32 rows each). Unit
+// u = s * n_kv_heads + g; with one row group the work-group id is u, with
+// more, eight consecutive units go to the eight XCDs and the row groups of a
+// unit are 8 ids apart (same XCD, so they share its L2).
 template <int D, int NRT>
-__global__ __launch_bounds__(kThreads, 2) void chunk_mfma_f32_kernel(ChunkParams p) {
+__global__ __launch_bounds__(kThreads, 2) void chunk_mfma_f32_kernel(ChunkParams p, int row_groups) {
     __shared__ F32Smem<D, NRT> sm;
-    const int s = blockIdx.x / p.n_kv_heads;
-    const int g = blockIdx.x % p.n_kv_heads;
+    const int x = blockIdx.x;
+    const int x_hi = x / (8 * row_groups), rem = x % (8 * row_groups);
+    const int rg = row_groups == 1 ? 0 : rem / 8;
+    const int u = row_groups == 1 ? x : x_hi * 8 + rem % 8;
+    if (u >= p.n_items * p.n_kv_heads) return;
+    const int s = u / p.n_kv_heads;
+    const int g = u % p.n_kv_heads;
     const int b = blockIdx.z;
     int64_t t0, t1;
     piece_tokens(p, chunk_view_len(p, b), b, g, s, &t0, &t1);
-    f32_piece<D, NRT>(p, sm, b, g, p.slot_begin + s, t0, t1);
+    f32_piece<D, NRT>(p, sm, b, g, p.slot_begin + s, t0, t1, 32 * rg);
 }
 
 // The whole resident history of every request, cut into balanced pieces
@@ -348,15 +360,18 @@ __global__ __launch_bounds__(kThreads, 2) void history_mfma_f32_kernel(ChunkPara
         if (k >= pa.plan_slots) break;  // cannot happen with plan_piece_len; never write past the slots
         if (k < 0) continue;
         f32_piece<D, NRT>(pa, sm, __builtin_amdgcn_readfirstlane(pc->b), __builtin_amdgcn_readfirstlane(pc->g),
-                          pa.slot_begin + k, uniform64(pc->t0), uniform64(pc->t1));
+                          pa.slot_begin + k, uniform64(pc->t0), uniform64(pc->t1), 0);
     }
 }
 
 template <int D, int NRT>
 hipError_t launch_f32_t(const ChunkParams& p, hipStream_t stream) {
-    const int64_t gx = (int64_t)p.n_items * p.n_kv_heads;
+    const int row_groups = (p.rows + 31) / 32;
+    const int64_t units = (int64_t)p.n_items * p.n_kv_heads;
+    const int64_t gx = row_groups == 1 ? units : (units + 7) / 8 * 8 * row_groups;
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((chunk_mfma_f32_kernel<D, NRT>), dim3((unsigned)gx, 1, p.batch), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((chunk_mfma_f32_kernel<D, NRT>), dim3((unsigned)gx, 1, p.batch), dim3(kThreads), 0, stream, p,
+                       row_groups);
     return hipGetLastError();
 }
 
@@ -393,10 +408,11 @@ hipError_t launch_hist_f32_t(const ChunkParams& p, hipStream_t stream) {
 
 }  // namespace
 
-// fp32, head_dim 128 or 64, up to 32 rows; contiguous pieces only (no chunk
-// lists, no block statistics, no candidate region).
+// fp32, head_dim 128 or 64, any row count (row groups of 32 beyond 32 rows);
+// contiguous pieces only (no chunk lists, no block statistics, no candidate
+// region).
 hipError_t launch_chunk_mfma_f32(const ChunkParams& p, int head_dim, hipStream_t stream) {
-    if ((head_dim != 128 && head_dim != 64) || p.rows > 32 || p.chunk_idx || p.stats || p.with_cand)
+    if ((head_dim != 128 && head_dim != 64) || p.rows <= 0 || p.chunk_idx || p.stats || p.with_cand)
         return hipErrorInvalidValue;
     if (head_dim == 64) return p.rows > 16 ? launch_f32_t<64, 2>(p, stream) : launch_f32_t<64, 1>(p, stream);
     return p.rows > 16 ? launch_f32_t<128, 2>(p, stream) : launch_f32_t<128, 1>(p, stream);

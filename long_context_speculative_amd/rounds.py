@@ -108,9 +108,10 @@ def narrow_mfma(cfg, engine="auto") -> bool:
 
 
 def f32_mfma(cfg, engine="auto") -> bool:
-    """Whether the library runs this shape on its fp32 MFMA kernel (fp32, up
-    to 32 rows per KV head)."""
-    return engine != "valu" and cfg.dtype == "f32" and cfg.rows <= 32
+    """Whether the library runs this shape on its fp32 MFMA kernel (every
+    fp32 shape outside the forced VALU engine; one work-group per piece up to
+    32 rows per KV head, one per row group of 32 beyond)."""
+    return engine != "valu" and cfg.dtype == "f32"
 
 
 def mfma_fuses_candidates(cfg, engine="auto") -> bool:

@@ -106,7 +106,6 @@ def _state(n_slots=4):
     ("bad_cps", ss.SS_ERR_INVALID_ARG),
     ("bad_stride", ss.SS_ERR_INVALID_ARG),
     ("bad_engine", ss.SS_ERR_INVALID_ARG),
-    ("mfma_fp32_wide", ss.SS_ERR_UNSUPPORTED),
     ("negative_scale", ss.SS_ERR_INVALID_ARG),
 ])
 def test_verify_chunk_rejects(case, code):
@@ -138,8 +137,6 @@ def test_verify_chunk_rejects(case, code):
         view = _view(stride_t=100)
     if case == "bad_engine":
         p = _problem(engine=7)
-    if case == "mfma_fp32_wide":  # the MFMA engines take fp32 up to 32 rows per KV head (here 8 x 8)
-        p = _problem(engine=ss.SS_ENGINE_MFMA, dtype=ss.SS_F32, n_queries=8, n_q_heads=16)
     if case == "negative_scale":
         p = _problem(scale=-0.1)
     rc = L.ss_verify_chunk(ctypes.byref(p), q, ctypes.byref(view), args["chunk_len"], args["chunk_begin"],

@@ -932,18 +932,30 @@ F32_CASES = {
     "rows_4_d128": C["c2_qwen3_8b"].with_(batch=2, dtype="f32", n_queries=1, hist_len=1500, chunk_len=512),
     "short_histories_d128": C["c3_internlm25_7b_ragged"].with_(batch=9, dtype="f32", hist_len=40, ragged_lo=1,
                                                                chunk_len=16),
+    # beyond 32 rows: one work-group per row group of 32 rows
+    "tree_512_rows_d128": C["c4_tree_72b"].with_(batch=2, dtype="f32", hist_len=2000, chunk_len=512),
+    "tree_96_rows_d128_ragged": C["c3_internlm25_7b_ragged"].with_(batch=7, dtype="f32", n_queries=12, n_q_heads=64,
+                                                                   mask="tree", hist_len=3000, ragged_lo=1,
+                                                                   chunk_len=512),
+    "rows_40_d64": C["c2_qwen3_8b"].with_(batch=3, dtype="f32", head_dim=64, n_queries=10, n_q_heads=16,
+                                          n_kv_heads=4, hist_len=2500, chunk_len=256),
 }
 
 
 @pytest.mark.parametrize("name", list(F32_CASES))
 def test_fp32_on_both_engines(name):
-    """fp32 inputs up to 32 rows per KV head run on the fp32 MFMA kernel
-    (AUTO), and on the VALU kernel when forced: both, under the chunked
-    split and the fixed cut of ss_verify_history, and the whole-round call,
-    match the oracle within 1e-5. Ragged cases include empty requests."""
+    """fp32 inputs run on the fp32 MFMA kernel (AUTO; beyond 32 rows per KV
+    head one work-group per row group of 32), and on the VALU kernel when
+    forced: both, under the chunked split and ss_verify_history, and the
+    whole-round call, match the oracle within 1e-5. Ragged cases include
+    empty requests."""
     cfg = F32_CASES[name]
     assert rounds.f32_mfma(cfg)
     inp = wl.make_inputs(cfg)
+    if name == "tree_96_rows_d128_ragged":
+        inp.hist_len = inp.hist_len.copy()
+        inp.hist_len[[1, 6]] = 0
+        inp.hist_len[2] = 1
     if name == "ragged_empties_d128":
         inp.hist_len = inp.hist_len.copy()
         inp.hist_len[[0, 5, 19]] = 0
