@@ -46,6 +46,7 @@ from long_context_speculative_amd import workloads as wl  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
 CSRC = "long_context_speculative_amd/csrc/"
 
 
@@ -622,11 +623,13 @@ def resident_record(cfg, steps, warmup, cps, engine, split, probe):
     alg = launch_bytes(cfg, hist_len, rnd)
     traffic = read_traffic(cfg, rnd.split, rnd.fused, rnd.n_hist_slots) if engine == "auto" else None
     if cfg.rows > 32:
-        # wide row groups: the chunk kernel is bound by the matrix cores
+        # wide row groups: the chunk kernel is bound by the matrix cores (the
+        # dense peak of the input type)
         flops = chunk_kernel_flops(cfg, hist_len)
         tflops = flops / (ms_chunk * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        peak = MFMA_F32_PEAK_TFLOPS if cfg.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                 "traffic": None if traffic is None else int(traffic), "kernel": kernel,
                 "ms_per_launch": round(ms_chunk, 4), "algorithmic_flops_per_launch": flops,
                 "algorithmic_bytes_per_launch": alg,
@@ -638,7 +641,7 @@ def resident_record(cfg, steps, warmup, cps, engine, split, probe):
             # peak scales with the clock (2.5 PFLOP/s at 2.4 GHz).
             clock = cycles / (ms_chunk * 1e-3) / 1e9
             roof["sustained_clock_GHz"] = round(clock, 3)
-            roof["frac_at_sustained_clock"] = round(tflops / (MFMA_BF16_PEAK_TFLOPS * clock / 2.4), 4)
+            roof["frac_at_sustained_clock"] = round(tflops / (peak * clock / 2.4), 4)
     else:
         achieved = alg / (ms_chunk * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -681,6 +684,8 @@ def main():
     ap.add_argument("--engine", default="auto", choices=list(rounds.ENGINES),
                     help="chunk-kernel engine (ss_problem_t.engine)")
     ap.add_argument("--queries", type=int, default=0, help="override the workload's queries per request")
+    ap.add_argument("--head-dim", type=int, default=0, choices=[0, 64, 128], help="override the workload's head_dim")
+    ap.add_argument("--dtype", default="", choices=["", "bf16", "f32"], help="override the workload's input type")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-streamed", action="store_true", help="skip the streamed, tiered and layered legs")
     ap.add_argument("--no-sparse", action="store_true", help="skip the block-statistics / sparse leg")
@@ -718,6 +723,11 @@ def main():
     cfg = wl.CONFIGS[args.workload]
     if args.queries:
         cfg = cfg.with_(n_queries=args.queries, name=f"{cfg.name}_q{args.queries}")
+    if args.head_dim and args.head_dim != cfg.head_dim:
+        cfg = cfg.with_(head_dim=args.head_dim, name=f"{cfg.name}_d{args.head_dim}")
+    if args.dtype and args.dtype != cfg.dtype:
+        cfg = cfg.with_(dtype=args.dtype, name=f"{cfg.name}_{args.dtype}")
+    overridden = cfg.name != args.workload
     cps = args.chunks_per_slot or "auto"
     if args.counters:
         counters_pass(cfg, cps, args.engine, args.split, args.counters_settle)
@@ -738,7 +748,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1), bf16)",
+        "data": f"synthetic (seeded N(0,1), {cfg.dtype})",
         "config": head["config"],
         "pct_hbm_peak": head["pct_hbm_peak"],
         "query_tokens_per_s": head["query_tokens_per_s"],
@@ -747,7 +757,7 @@ def main():
     }
     # the other resident workloads of the round, each in its own launch
     # configuration: the uniform HBM-bound layer and the MFMA-bound tree
-    if not args.no_extra_workloads and args.workload == DEFAULT_WORKLOAD and not args.queries:
+    if not args.no_extra_workloads and args.workload == DEFAULT_WORKLOAD and not overridden:
         for key, name in (("c2", "c2_qwen3_8b"), ("c4", "c4_tree_72b")):
             rec = resident_record(wl.CONFIGS[name], args.steps, args.warmup, "auto", args.engine, args.split, probe)
             out[key] = {k: rec[k] for k in ("config", "ms_per_step", "effective_KV_GBps", "pct_hbm_peak",
