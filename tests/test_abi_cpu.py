@@ -517,3 +517,40 @@ def test_view_token_stride_limit():
     big = ss.KVView(4096, 8192, 0, 0, (1 << 24) + 8, None, None, 1024)
     assert L.ss_verify_chunk(ctypes.byref(p), 4096, ctypes.byref(big), 64, 0, 4, 1, st, 0, None) == ss.SS_ERR_UNSUPPORTED
     assert "2^24" in L.ss_last_error().decode()
+
+
+def _gpu_present() -> bool:
+    import torch
+    return torch.cuda.is_available()
+
+
+@pytest.mark.skipif(_gpu_present(), reason="passes fake device pointers past validation: only where no GPU can "
+                                           "run them")
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("head_dim", [64, 128])
+@pytest.mark.parametrize("rows", [(1, 4), (6, 4), (10, 4), (64, 8)])
+@pytest.mark.parametrize("engine", ["auto", "mfma", "valu"])
+def test_candidate_placement_mirror(dtype, head_dim, rows, engine):
+    """The binding's mirror of the library's engine choice
+    (rounds.mfma_fuses_candidates: the bf16 MFMA kernels, narrow and
+    wide-row, attend the candidate region inside the history launch; the
+    fp32 and VALU engines give it a slot of its own) agrees with the library:
+    with one slot and a candidate view, ss_verify_history refuses the call
+    (SS_ERR_INVALID_ARG, before any device work) exactly when the engine does
+    not fold the candidates in; otherwise it passes validation and fails only
+    at the device (there is none here: SS_ERR_HIP)."""
+    from long_context_speculative_amd import rounds
+    q, group = rows
+    cfg = workloads.CONFIGS["c2_qwen3_8b"].with_(dtype=dtype, head_dim=head_dim, n_queries=q,
+                                                 n_q_heads=2 * group, n_kv_heads=2)
+    p = _problem(dtype=ss.SS_F32 if dtype == "f32" else ss.SS_BF16, head_dim=head_dim, n_queries=q,
+                 n_q_heads=2 * group, n_kv_heads=2, engine=rounds.ENGINES[engine])
+    es = 4 if dtype == "f32" else 2
+    stride = 256 // es * ((head_dim * es + 255) // 256)  # a multiple of 16 bytes and >= head_dim
+    view = _view(max_len=1000, stride_t=stride)
+    cand = _view(max_len=q, stride_t=stride)
+    L = ss.lib()
+    rc = L.ss_verify_history(ctypes.byref(p), 4096, ctypes.byref(view), ctypes.byref(cand), None, None, None, 1,
+                             ctypes.byref(_state(4).struct), 0, None)
+    fused = rounds.mfma_fuses_candidates(cfg, engine)
+    assert rc == (ss.SS_ERR_HIP if fused else ss.SS_ERR_INVALID_ARG), (rc, L.ss_last_error().decode())
