@@ -1149,7 +1149,11 @@ def test_random_shapes(seed):
     check_mask(rnd, inp)
 
 
-@pytest.mark.parametrize("seed", range(16))
+# SS_RANDOM_STREAMED_SEEDS=a:b widens the sweep (default 0:16)
+RANDOM_STREAMED_SEEDS = range(*(int(x) for x in os.environ.get("SS_RANDOM_STREAMED_SEEDS", "0:16").split(":")))
+
+
+@pytest.mark.parametrize("seed", RANDOM_STREAMED_SEEDS)
 def test_random_streamed(seed):
     """The streamed round on seeded random shapes (heads, group, queries and
     mask, chunk length and count) and staging rings (buffers, chunks per
