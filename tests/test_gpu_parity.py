@@ -1234,3 +1234,38 @@ def test_late_dominant_key(name):
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle_round(inp)
     compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+
+
+WIDE_RAGGED = {
+    "tree_512_rows": C["c4_tree_72b"].with_(batch=6, hist_len=6000, ragged_lo=1, chunk_len=1024),
+    "tree_128_rows": C["c4_tree_72b"].with_(batch=9, n_queries=16, hist_len=5000, ragged_lo=1, chunk_len=1024),
+}
+
+
+@pytest.mark.parametrize("slots", [2, 3, 8])
+@pytest.mark.parametrize("name", list(WIDE_RAGGED))
+def test_wide_ragged_balanced_cut(name, slots):
+    """Ragged histories on the wide-row kernel (fixed chunks per slot, the
+    candidate region with each stream's first chunk): with empty requests,
+    requests below the short-history threshold and few or many slots, O, lse
+    and the mask match the oracle, and so does the whole-round call."""
+    cfg = WIDE_RAGGED[name]
+    inp = wl.make_inputs(cfg)
+    inp.hist_len = inp.hist_len.copy()
+    inp.hist_len[[0, 4]] = 0
+    inp.hist_len[1], inp.hist_len[2] = 1, 2047
+    o_ref, lse_ref = oracle_round(inp)
+    log(f"[wide ragged] {name}: {slots} slots, rows={cfg.rows}")
+    rnd = rounds.ResidentRound(inp, **dict(rounds.BENCH_RESIDENT, history_slots=slots))
+    for t in (rnd.state.acc, rnd.state.m, rnd.state.l):
+        t.fill_(float("nan"))
+    rnd.run()
+    torch.cuda.synchronize()
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
+    check_mask(rnd, inp)
+    work = ss.StateBuffers(rnd.problem, 8, "cuda")
+    rnd.o.fill_(float("nan"))
+    ss.ss_verify_round(rnd.problem, rnd.q, rnd.hist_view, rnd.cand_view, rnd.parents, rnd.mask_out, 0, work, rnd.o,
+                       rnd.lse)
+    torch.cuda.synchronize()
+    compare(cfg, rnd.o.cpu().numpy(), rnd.lse.cpu().numpy(), o_ref, lse_ref)
